@@ -1,0 +1,183 @@
+/* lca.h - C ABI of the latent-condensed MLA kernels for MI355X (gfx950).
+ *
+ * The method is Latent-Condensed Attention (LCA) as described on the page
+ * "Latent-Condensed Transformer for Efficient Long Context Modeling"
+ * (papernotes.org notes on the ACL 2026 paper, arXiv 2604.12452), run directly
+ * over a Multi-head Latent Attention (MLA) cache as described on the page
+ * "新一代开源大模型架构演进与注意力机制深度对比解析" (cloud.baidu.com), section
+ * 三.1: every token caches a latent row and heads project it back up at
+ * compute time.
+ *
+ * A cached token is one row of a 512-wide latent c_KV and a 64-wide decoupled
+ * RoPE key k_R (the page's C^KV and K^R, 研究背景 / 核心矛盾). The history older
+ * than the last w tokens is cut into m = floor((L - w) / g) groups of g tokens
+ * (方法详解 / 整体框架). Each group becomes one representative row: its c_KV is
+ * the softmax-weighted sum of the group's c_KV rows, weighted by the
+ * importance of each token to the summary query (关键设计 1), and its k_R is
+ * the k_R of the group's most important token (关键设计 2). Attention then runs
+ * over [representatives ++ the uncompressed rows] (整体框架, flowchart E -> F).
+ *
+ * Conventions shared by every call:
+ *  - Device buffers are owned by the caller. The library never allocates or
+ *    frees device memory; scratch space comes from a caller workspace.
+ *  - Inputs are never written. Outputs are fully written, except that
+ *    lca_condense writes only the representative rows it is asked for.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; 0 = the null stream)
+ *    and never synchronise. Argument errors are returned synchronously as a
+ *    negative lca_status_t with text from lca_last_error(); a launch failure
+ *    returns LCA_ERR_HIP. Device faults surface at the caller's next sync.
+ *  - Strides are in elements. Row starts must be 16-byte aligned and token
+ *    strides multiples of 8 elements (vectorised 16-byte loads).
+ *  - bf16 values are stored as raw bfloat16; f32 inputs of the attention
+ *    paths are rounded to bf16 (nearest even) where they feed the matrix
+ *    cores. Accumulation is fp32 everywhere.
+ *  - Results are bitwise deterministic for fixed inputs and arguments.
+ */
+#ifndef LCA_H_
+#define LCA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LCA_VERSION 1000 /* major*1000 + minor */
+#define LCA_D_C 512      /* latent c_KV width */
+#define LCA_D_R 64       /* decoupled RoPE key width */
+#define LCA_D_ROW 576    /* one cached row: c_KV ++ k_R */
+#define LCA_D_V 128      /* per-head value width of W_UV */
+#define LCA_MAX_G 32     /* largest supported group size (powers of two) */
+
+typedef enum {
+  LCA_OK = 0,
+  LCA_ERR_INVALID_ARG = -1, /* null pointer, bad size, misalignment, out-of-range rows */
+  LCA_ERR_UNSUPPORTED = -2, /* a size the kernels are not built for (e.g. H % 16 != 0) */
+  LCA_ERR_WORKSPACE = -3,   /* workspace pointer null or smaller than required */
+  LCA_ERR_HIP = -4          /* the HIP runtime refused a launch */
+} lca_status_t;
+
+typedef enum { LCA_BF16 = 0, LCA_F32 = 1 } lca_dtype_t;
+
+/* A latent cache (or representative) tensor of B sequences.
+ * c_KV of token t of sequence b starts at  c  + b*c_seq_stride  + t*c_tok_stride,
+ * k_R  of token t of sequence b starts at  kr + b*kr_seq_stride + t*kr_tok_stride.
+ * A packed [B, L, 576] buffer is c = base, kr = base + 512 with equal strides. */
+typedef struct {
+  void* c;
+  void* kr;
+  int64_t c_seq_stride, c_tok_stride;
+  int64_t kr_seq_stride, kr_tok_stride;
+  int32_t dtype; /* lca_dtype_t, shared by c and kr */
+} lca_latent_t;
+
+/* Grouping of a cache of L tokens: m groups [j g, (j+1) g) for j < m, raw rows
+ * [raw_begin, raw_end) = [m g, L), n_entries = m + (L - m g) attended rows. */
+typedef struct {
+  int64_t m, raw_begin, raw_end, n_entries;
+} lca_plan_t;
+
+int lca_version(void);
+
+/* Text of the last error on the calling thread ("" after success). */
+const char* lca_last_error(void);
+
+/* Host-only. m = floor((L - w) / g) when L > w, else 0 (方法详解 / 整体框架);
+ * the (L - w) mod g tokens left over stay raw. L, w >= 0, 1 <= g. */
+int lca_plan(int64_t L, int64_t w, int32_t g, lca_plan_t* out);
+
+/* Workspace bytes lca_condense needs: one fp32 summary query per sequence
+ * (q_row_step == 0) or per sequence and group (q_row_step > 0). */
+size_t lca_condense_workspace_size(int32_t B, int64_t n_groups, int64_t q_row_step);
+
+/* Condense groups [group_begin, group_begin + n_groups) of every sequence
+ * (关键设计 1 and 关键设计 2).
+ *
+ *  cache        c_KV / k_R of the token rows; group j reads tokens [j g, (j+1) g).
+ *  g            group size: a power of two, 1 <= g <= LCA_MAX_G.
+ *  q            absorbed queries [B, T, H, 576] (row t, head h of sequence b at
+ *               q + b*q_seq_stride + t*q_tok_stride + h*576), dtype q_dtype.
+ *  q_row0,      group group_begin + n takes its summary query from query rows
+ *  q_row_step   [q_row0 + n*q_row_step, ... + g): the mean over those g tokens
+ *               and all H heads (the page's mean of the most recent g queries).
+ *               Decode uses q_row_step = 0 (one shared summary query); chunked
+ *               prefill uses q_row0 = (group_begin + 1) g, q_row_step = g (the g
+ *               queries that follow each group). All rows must lie in [0, T).
+ *  sm_scale     >= 0. Importance s_i = qbar . [c_i ; k_R_i]; weights
+ *               alpha = softmax(sm_scale * s) over the group.
+ *  reps         receives row j (for j in the range) of every sequence:
+ *               c_rep = sum_i alpha_i c_i (fp32 accumulation, stored in
+ *               reps->dtype) and k_rep = k_R of the anchor I_j.
+ *  anchor_idx   int32 [B, *]: anchor_idx[b*anchor_seq_stride + j] = I_j, the
+ *               absolute token index of the group's largest score (lowest
+ *               index on ties).
+ *  alpha        optional fp32 [B, *, g]: alpha[b*alpha_seq_stride + j*g + i].
+ *  workspace    >= lca_condense_workspace_size(B, n_groups, q_row_step) bytes,
+ *               16-byte aligned; overwritten.
+ * n_groups == 0 is a no-op. */
+int lca_condense(const lca_latent_t* cache, int32_t B, int32_t g, int64_t group_begin,
+                 int64_t n_groups, const void* q, int32_t q_dtype, int64_t q_seq_stride,
+                 int64_t q_tok_stride, int64_t T, int32_t H, int64_t q_row0,
+                 int64_t q_row_step, float sm_scale, const lca_latent_t* reps,
+                 int32_t* anchor_idx, int64_t anchor_seq_stride, float* alpha,
+                 int64_t alpha_seq_stride, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
+/* Workspace bytes mla_latent_attn_decode needs for up to max_entries
+ * attended rows per sequence (split-K partial results). */
+size_t mla_latent_attn_decode_workspace_size(int32_t B, int32_t H, int64_t max_entries);
+
+/* One decode step of MLA attention over a condensed latent cache
+ * (整体框架, flowchart E -> F: representatives concatenated with the window,
+ * then standard attention).
+ *
+ *  q        absorbed queries [B, H, 576] (head h of sequence b at
+ *           q + b*q_seq_stride + h*576), H a multiple of 16.
+ *  reps     entries [0, m) of each sequence are representative rows 0..m-1.
+ *  raw      entries [m, m + raw_end - raw_begin) are cache rows
+ *           [raw_begin, raw_end). reps->dtype must equal raw->dtype.
+ *           Plain MLA is m = 0, raw = [0, L).
+ *  For every head: z_e = sm_scale * q_h . [c_e ; k_R_e], p = softmax(z),
+ *  o_latent[b, h, :] = sum_e p_e c_e  (fp32 [B, H, 512], contiguous) and
+ *  lse[b, h] = log(sum_e exp(z_e))    (fp32 [B, H], optional).
+ *  The per-head value is o_latent[b, h] @ W_UV[h] (mla_up_proj).
+ *  workspace >= mla_latent_attn_decode_workspace_size(B, H, m + raw_end -
+ *  raw_begin) bytes, 16-byte aligned; overwritten. */
+int mla_latent_attn_decode(const void* q, int32_t q_dtype, int64_t q_seq_stride, int32_t B,
+                           int32_t H, const lca_latent_t* reps, int64_t m,
+                           const lca_latent_t* raw, int64_t raw_begin, int64_t raw_end,
+                           float sm_scale, float* o_latent, float* lse, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* Chunked prefill attention of one sequence over a condensed latent cache.
+ * Query i of the chunk sits at absolute position t = chunk_start + i (its
+ * absorbed query at q + i*q_tok_stride + h*576, H a multiple of 16) and
+ * attends to representatives [0, m) (all visible) and raw cache rows
+ * [raw_begin, t] (causal, inclusive). Requires raw_begin <= chunk_start.
+ * The groups a chunk sees are frozen before its window: with window w and
+ * group size g the caller passes m = floor((chunk_start - w) / g) (0 when
+ * chunk_start <= w) and raw_begin = m g, after condensing those groups with
+ * the g queries that follow each one.
+ *  o_latent [C, H, 512] contiguous, dtype o_dtype; lse [C, H] fp32, optional. */
+int mla_latent_attn_prefill_chunk(const void* q, int32_t q_dtype, int64_t q_tok_stride,
+                                  int64_t chunk_start, int32_t C, int32_t H,
+                                  const lca_latent_t* reps, int64_t m,
+                                  const lca_latent_t* raw, int64_t raw_begin, float sm_scale,
+                                  void* o_latent, int32_t o_dtype, float* lse,
+                                  hipStream_t stream);
+
+/* Per-head value up-projection (the MLA page's projection back to the head
+ * space, 三.1): out[t, h, :] = o_latent[t, h, :] @ W_UV[h].
+ *  o_latent [T, H, 512] contiguous (bf16 or f32); w_uv [H, 512, 128]
+ *  contiguous (bf16 or f32); out [T, H, 128] contiguous, dtype out_dtype.
+ *  bf16 matrix-core products with fp32 accumulation. T == 0 is a no-op. */
+int mla_up_proj(const void* o_latent, int32_t o_dtype, int64_t T, int32_t H, const void* w_uv,
+                int32_t w_dtype, void* out, int32_t out_dtype, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCA_H_ */

@@ -122,3 +122,49 @@ def w_uv(cfg: int, H: int, bf16: bool = True) -> np.ndarray:
 def w_uk(cfg: int, H: int, bf16: bool = True) -> np.ndarray:
     w = rng(cfg, ID_WUK).standard_normal((H, D_C, D_V), dtype=np.float32) * np.float32(1.0 / np.sqrt(D_C))
     return bf16_round(w) if bf16 else w
+
+
+# ------------------------------------------------------------------------
+# Device-side generation for the benchmark's large workloads (same recipe,
+# torch's Philox generator instead of PCG64, so values differ from the numpy
+# draws but follow the same distributions). The benchmark's CPU baseline
+# copies the sequences it samples back to the host.
+def latent_cache_torch(seed: int, B: int, L: int, device="cuda", dtype=None):
+    """Packed [B, L, 576] cache: N(0,1) c_KV and RoPE-rotated N(0,1) k_R."""
+    import torch
+    dtype = dtype or torch.bfloat16
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = torch.empty((B, L, D_ROW), dtype=dtype, device=device)
+    step = max(1, (1 << 24) // max(1, L * D_ROW))  # bound the fp32 temporaries
+    half = D_R // 2
+    inv = 10000.0 ** (-torch.arange(half, device=device, dtype=torch.float64) * 2.0 / D_R)
+    ang = torch.arange(L, device=device, dtype=torch.float64)[:, None] * inv[None, :]
+    cos, sin = torch.cos(ang).float(), torch.sin(ang).float()
+    for b0 in range(0, B, step):
+        b1 = min(B, b0 + step)
+        x = torch.randn((b1 - b0, L, D_ROW), generator=g, device=device, dtype=torch.float32)
+        k1, k2 = x[..., D_C:D_C + half].clone(), x[..., D_C + half:].clone()
+        x[..., D_C:D_C + half] = k1 * cos - k2 * sin
+        x[..., D_C + half:] = k1 * sin + k2 * cos
+        out[b0:b1] = x.to(dtype)
+    return out
+
+
+def queries_torch(seed: int, shape, device="cuda", dtype=None):
+    """Absorbed queries N(0, 1/576) of the given shape (last axis 576)."""
+    import torch
+    dtype = dtype or torch.bfloat16
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return (torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+            * (1.0 / np.sqrt(D_ROW))).to(dtype)
+
+
+def w_uv_torch(seed: int, H: int, device="cuda", dtype=None):
+    import torch
+    dtype = dtype or torch.bfloat16
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return (torch.randn((H, D_C, D_V), generator=g, device=device, dtype=torch.float32)
+            * (1.0 / np.sqrt(D_C))).to(dtype)

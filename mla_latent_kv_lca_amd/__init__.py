@@ -1,0 +1,229 @@
+"""Python binding of liblca.so (latent-condensed MLA kernels for MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of include/lca.h. torch provides device memory and
+the current stream. There is no fallback: if the library is not built, every
+call raises.
+
+Entry points (same names as the C ABI):
+  lca_plan, lca_condense, mla_latent_attn_decode,
+  mla_latent_attn_prefill_chunk, mla_up_proj,
+  lca_condense_workspace_size, mla_latent_attn_decode_workspace_size,
+  lca_version, lca_last_error
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_void_p
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblca.so")
+
+LCA_OK, LCA_ERR_INVALID_ARG, LCA_ERR_UNSUPPORTED, LCA_ERR_WORKSPACE, LCA_ERR_HIP = 0, -1, -2, -3, -4
+LCA_BF16, LCA_F32 = 0, 1
+D_C, D_R, D_ROW, D_V = 512, 64, 576, 128
+
+# every symbol include/lca.h declares
+EXPORTS = ("lca_version", "lca_last_error", "lca_plan", "lca_condense_workspace_size",
+           "lca_condense", "mla_latent_attn_decode_workspace_size", "mla_latent_attn_decode",
+           "mla_latent_attn_prefill_chunk", "mla_up_proj")
+
+
+class LcaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"lca status {status}: {msg}")
+        self.status = status
+
+
+class LatentT(ctypes.Structure):
+    _fields_ = [("c", c_void_p), ("kr", c_void_p), ("c_seq_stride", c_int64),
+                ("c_tok_stride", c_int64), ("kr_seq_stride", c_int64),
+                ("kr_tok_stride", c_int64), ("dtype", c_int32)]
+
+
+class PlanT(ctypes.Structure):
+    _fields_ = [("m", c_int64), ("raw_begin", c_int64), ("raw_end", c_int64),
+                ("n_entries", c_int64)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load liblca.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m mla_latent_kv_lca_amd.build` (or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = POINTER
+    lib.lca_version.restype = c_int32
+    lib.lca_version.argtypes = []
+    lib.lca_last_error.restype = c_char_p
+    lib.lca_last_error.argtypes = []
+    lib.lca_plan.restype = c_int32
+    lib.lca_plan.argtypes = [c_int64, c_int64, c_int32, P(PlanT)]
+    lib.lca_condense_workspace_size.restype = c_size_t
+    lib.lca_condense_workspace_size.argtypes = [c_int32, c_int64, c_int64]
+    lib.lca_condense.restype = c_int32
+    lib.lca_condense.argtypes = [P(LatentT), c_int32, c_int32, c_int64, c_int64, c_void_p, c_int32,
+                                 c_int64, c_int64, c_int64, c_int32, c_int64, c_int64, c_float,
+                                 P(LatentT), c_void_p, c_int64, c_void_p, c_int64, c_void_p,
+                                 c_size_t, c_void_p]
+    lib.mla_latent_attn_decode_workspace_size.restype = c_size_t
+    lib.mla_latent_attn_decode_workspace_size.argtypes = [c_int32, c_int32, c_int64]
+    lib.mla_latent_attn_decode.restype = c_int32
+    lib.mla_latent_attn_decode.argtypes = [c_void_p, c_int32, c_int64, c_int32, c_int32, P(LatentT),
+                                           c_int64, P(LatentT), c_int64, c_int64, c_float,
+                                           c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.mla_latent_attn_prefill_chunk.restype = c_int32
+    lib.mla_latent_attn_prefill_chunk.argtypes = [c_void_p, c_int32, c_int64, c_int64, c_int32,
+                                                  c_int32, P(LatentT), c_int64, P(LatentT),
+                                                  c_int64, c_float, c_void_p, c_int32, c_void_p,
+                                                  c_void_p]
+    lib.mla_up_proj.restype = c_int32
+    lib.mla_up_proj.argtypes = [c_void_p, c_int32, c_int64, c_int32, c_void_p, c_int32, c_void_p,
+                                c_int32, c_void_p]
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != LCA_OK:
+        raise LcaError(status, load().lca_last_error().decode())
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return LCA_BF16
+    if t.dtype == torch.float32:
+        return LCA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use bfloat16 or float32")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def latent(c: torch.Tensor, kr: torch.Tensor) -> LatentT:
+    """Describe c_KV [B, L, 512] (or [L, 512]) and k_R [B, L, 64] views."""
+    if c.dtype != kr.dtype:
+        raise TypeError("c and kr must share a dtype")
+    if c.shape[-1] != D_C or kr.shape[-1] != D_R or c.stride(-1) != 1 or kr.stride(-1) != 1:
+        raise ValueError("c must end in a contiguous 512-wide axis and kr in a 64-wide axis")
+    cs = c.stride(0) if c.dim() == 3 else 0
+    ks = kr.stride(0) if kr.dim() == 3 else 0
+    return LatentT(c.data_ptr(), kr.data_ptr(), cs, c.stride(-2), ks, kr.stride(-2), dtype_code(c))
+
+
+def packed_latent(cache: torch.Tensor) -> LatentT:
+    """Describe a packed [B, L, 576] (or [L, 576]) cache: c = [..., :512], kr = [..., 512:]."""
+    return latent(cache[..., :D_C], cache[..., D_C:])
+
+
+# ----------------------------------------------------------------- calls ---
+def lca_version() -> int:
+    return load().lca_version()
+
+
+def lca_last_error() -> str:
+    return load().lca_last_error().decode()
+
+
+def lca_plan(L: int, w: int, g: int) -> dict:
+    out = PlanT()
+    _check(load().lca_plan(L, w, g, ctypes.byref(out)))
+    return {"m": out.m, "raw_begin": out.raw_begin, "raw_end": out.raw_end,
+            "n_entries": out.n_entries}
+
+
+def lca_condense_workspace_size(B: int, n_groups: int, q_row_step: int) -> int:
+    return load().lca_condense_workspace_size(B, n_groups, q_row_step)
+
+
+def mla_latent_attn_decode_workspace_size(B: int, H: int, max_entries: int) -> int:
+    return load().mla_latent_attn_decode_workspace_size(B, H, max_entries)
+
+
+def _workspace(nbytes: int, like: torch.Tensor, ws):
+    if ws is not None:
+        return ws
+    return torch.empty(max(16, (nbytes + 15) // 16 * 16), dtype=torch.uint8, device=like.device)
+
+
+def lca_condense(cache: LatentT, B: int, g: int, group_begin: int, n_groups: int,
+                 q: torch.Tensor, q_row0: int, q_row_step: int, sm_scale: float,
+                 reps: LatentT, anchor: torch.Tensor, alpha: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None, stream=None) -> None:
+    """Condense groups [group_begin, group_begin + n_groups) (q: [B, T, H, 576];
+    anchor: int32 [B, *]; alpha: fp32 [B, *, g] or None)."""
+    if q.dim() != 4 or q.shape[-1] != D_ROW or q.stride(-1) != 1 or q.stride(-2) != D_ROW:
+        raise ValueError("q must be [B, T, H, 576] with contiguous heads")
+    if anchor.dtype != torch.int32:
+        raise TypeError("anchor must be int32")
+    ws = _workspace(lca_condense_workspace_size(B, n_groups, q_row_step), q, workspace)
+    _check(load().lca_condense(
+        ctypes.byref(cache), B, g, group_begin, n_groups, q.data_ptr(), dtype_code(q), q.stride(0),
+        q.stride(1), q.shape[1], q.shape[2], q_row0, q_row_step, sm_scale, ctypes.byref(reps),
+        anchor.data_ptr(), anchor.stride(0), _ptr(alpha), 0 if alpha is None else alpha.stride(0),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def mla_latent_attn_decode(q: torch.Tensor, reps: LatentT | None, m: int, raw: LatentT | None,
+                           raw_begin: int, raw_end: int, sm_scale: float, o_latent: torch.Tensor,
+                           lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                           stream=None) -> None:
+    """q [B, H, 576]; o_latent fp32 [B, H, 512] contiguous; lse fp32 [B, H] or None."""
+    if q.dim() != 3 or q.shape[-1] != D_ROW or q.stride(-1) != 1 or q.stride(-2) != D_ROW:
+        raise ValueError("q must be [B, H, 576] with contiguous heads")
+    B, H = q.shape[0], q.shape[1]
+    if o_latent.dtype != torch.float32 or not o_latent.is_contiguous() or o_latent.shape != (B, H, D_C):
+        raise ValueError("o_latent must be a contiguous fp32 [B, H, 512] tensor")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous fp32 [B, H] tensor")
+    n = m + raw_end - raw_begin
+    ws = _workspace(mla_latent_attn_decode_workspace_size(B, H, max(n, 1)), q, workspace)
+    _check(load().mla_latent_attn_decode(
+        q.data_ptr(), dtype_code(q), q.stride(0), B, H,
+        None if reps is None else ctypes.byref(reps), m,
+        None if raw is None else ctypes.byref(raw), raw_begin, raw_end, sm_scale,
+        o_latent.data_ptr(), _ptr(lse), ws.data_ptr(), ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
+def mla_latent_attn_prefill_chunk(q: torch.Tensor, chunk_start: int, reps: LatentT | None, m: int,
+                                  raw: LatentT, raw_begin: int, sm_scale: float,
+                                  o_latent: torch.Tensor, lse: torch.Tensor | None = None,
+                                  stream=None) -> None:
+    """q [C, H, 576] (queries at positions chunk_start ..); o_latent [C, H, 512]."""
+    if q.dim() != 3 or q.shape[-1] != D_ROW or q.stride(-1) != 1 or q.stride(-2) != D_ROW:
+        raise ValueError("q must be [C, H, 576] with contiguous heads")
+    C, H = q.shape[0], q.shape[1]
+    if not o_latent.is_contiguous() or o_latent.shape != (C, H, D_C):
+        raise ValueError("o_latent must be a contiguous [C, H, 512] tensor")
+    _check(load().mla_latent_attn_prefill_chunk(
+        q.data_ptr(), dtype_code(q), q.stride(0), chunk_start, C, H,
+        None if reps is None else ctypes.byref(reps), m, ctypes.byref(raw), raw_begin, sm_scale,
+        o_latent.data_ptr(), dtype_code(o_latent), _ptr(lse), _stream(stream)))
+
+
+def mla_up_proj(o_latent: torch.Tensor, w_uv: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    """o_latent [T, H, 512], w_uv [H, 512, 128], out [T, H, 128], all contiguous."""
+    for name, t in (("o_latent", o_latent), ("w_uv", w_uv), ("out", out)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    T, H = o_latent.shape[0], o_latent.shape[1]
+    if o_latent.shape[2] != D_C or tuple(w_uv.shape) != (H, D_C, D_V) or tuple(out.shape) != (T, H, D_V):
+        raise ValueError("shapes must be o_latent [T,H,512], w_uv [H,512,128], out [T,H,128]")
+    _check(load().mla_up_proj(o_latent.data_ptr(), dtype_code(o_latent), T, H, w_uv.data_ptr(),
+                              dtype_code(w_uv), out.data_ptr(), dtype_code(out), _stream(stream)))

@@ -1,0 +1,205 @@
+// Host side of the C ABI declared in include/lca.h: argument validation, the
+// grouping plan, workspace sizing, thread-local error text and kernel
+// dispatch on the caller's stream. No device memory is allocated here.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "lca.h"
+#include "lca_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return LCA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(LCA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool valid_dtype(int32_t d) { return d == LCA_BF16 || d == LCA_F32; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool mult8(int64_t s) { return s % 8 == 0; }
+
+// A latent tensor used for 16-byte row loads/stores.
+int check_latent(const lca_latent_t* t, const char* name, bool need_c, bool need_kr) {
+  if (t == nullptr) return fail(LCA_ERR_INVALID_ARG, "%s is null", name);
+  if (!valid_dtype(t->dtype)) return fail(LCA_ERR_INVALID_ARG, "%s->dtype %d is not LCA_BF16/LCA_F32", name, t->dtype);
+  if (need_c && (t->c == nullptr || !aligned16(t->c)))
+    return fail(LCA_ERR_INVALID_ARG, "%s->c must be a non-null 16-byte aligned pointer", name);
+  if (need_kr && (t->kr == nullptr || !aligned16(t->kr)))
+    return fail(LCA_ERR_INVALID_ARG, "%s->kr must be a non-null 16-byte aligned pointer", name);
+  if (!mult8(t->c_seq_stride) || !mult8(t->c_tok_stride) || !mult8(t->kr_seq_stride) ||
+      !mult8(t->kr_tok_stride) || t->c_tok_stride < 0 || t->kr_tok_stride < 0 ||
+      t->c_seq_stride < 0 || t->kr_seq_stride < 0)
+    return fail(LCA_ERR_INVALID_ARG, "%s strides must be non-negative multiples of 8 elements", name);
+  return LCA_OK;
+}
+
+int check_scale(float s) {
+  if (!std::isfinite(s) || s < 0.f) return fail(LCA_ERR_INVALID_ARG, "sm_scale must be finite and >= 0");
+  return LCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lca_version(void) { return LCA_VERSION; }
+
+const char* lca_last_error(void) { return g_err.c_str(); }
+
+int lca_plan(int64_t L, int64_t w, int32_t g, lca_plan_t* out) {
+  if (out == nullptr) return fail(LCA_ERR_INVALID_ARG, "out is null");
+  if (L < 0 || w < 0 || g < 1) return fail(LCA_ERR_INVALID_ARG, "need L >= 0, w >= 0, g >= 1");
+  const int64_t m = L > w ? (L - w) / g : 0;
+  out->m = m;
+  out->raw_begin = m * g;
+  out->raw_end = L;
+  out->n_entries = m + (L - m * g);
+  return ok();
+}
+
+size_t lca_condense_workspace_size(int32_t B, int64_t n_groups, int64_t q_row_step) {
+  if (B < 1 || n_groups < 0) return 0;
+  const int64_t nq = q_row_step != 0 ? n_groups : (n_groups > 0 ? 1 : 0);
+  return (size_t)B * (size_t)nq * LCA_D_ROW * sizeof(float);
+}
+
+int lca_condense(const lca_latent_t* cache, int32_t B, int32_t g, int64_t group_begin,
+                 int64_t n_groups, const void* q, int32_t q_dtype, int64_t q_seq_stride,
+                 int64_t q_tok_stride, int64_t T, int32_t H, int64_t q_row0,
+                 int64_t q_row_step, float sm_scale, const lca_latent_t* reps,
+                 int32_t* anchor_idx, int64_t anchor_seq_stride, float* alpha,
+                 int64_t alpha_seq_stride, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
+  int rc;
+  if ((rc = check_latent(cache, "cache", true, true)) != LCA_OK) return rc;
+  if ((rc = check_latent(reps, "reps", true, true)) != LCA_OK) return rc;
+  if (B < 1 || B > 65535) return fail(LCA_ERR_INVALID_ARG, "B must be in [1, 65535]");
+  if (g < 1 || g > LCA_MAX_G || (g & (g - 1)) != 0)
+    return fail(LCA_ERR_UNSUPPORTED, "g = %d: supported group sizes are powers of two up to %d", g, LCA_MAX_G);
+  if (H < 1) return fail(LCA_ERR_INVALID_ARG, "H must be >= 1");
+  if (group_begin < 0 || n_groups < 0) return fail(LCA_ERR_INVALID_ARG, "group_begin and n_groups must be >= 0");
+  if (n_groups > ((int64_t)1 << 32)) return fail(LCA_ERR_UNSUPPORTED, "too many groups in one call");
+  if (q == nullptr || !aligned16(q)) return fail(LCA_ERR_INVALID_ARG, "q must be a non-null 16-byte aligned pointer");
+  if (!valid_dtype(q_dtype)) return fail(LCA_ERR_INVALID_ARG, "q_dtype %d is not LCA_BF16/LCA_F32", q_dtype);
+  if (!mult8(q_seq_stride) || !mult8(q_tok_stride) || q_seq_stride < 0 || q_tok_stride < 0)
+    return fail(LCA_ERR_INVALID_ARG, "q strides must be non-negative multiples of 8 elements");
+  if (anchor_idx == nullptr) return fail(LCA_ERR_INVALID_ARG, "anchor_idx is null");
+  if (anchor_seq_stride < 0 || alpha_seq_stride < 0) return fail(LCA_ERR_INVALID_ARG, "negative output stride");
+  if ((rc = check_scale(sm_scale)) != LCA_OK) return rc;
+  if (q_row0 < 0 || q_row_step < 0) return fail(LCA_ERR_INVALID_ARG, "q_row0 and q_row_step must be >= 0");
+  if (n_groups == 0) return ok();
+  const int64_t last_row = q_row0 + (n_groups - 1) * q_row_step + g - 1;
+  if (last_row >= T) return fail(LCA_ERR_INVALID_ARG, "summary-query rows reach row %lld but T = %lld", (long long)last_row, (long long)T);
+  if (q_row_step != 0 && n_groups > 0x7fffffff) return fail(LCA_ERR_UNSUPPORTED, "too many summary queries");
+  const size_t need = lca_condense_workspace_size(B, n_groups, q_row_step);
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need)
+    return fail(LCA_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
+  return hip_status(lca::launch_condense(*cache, B, g, group_begin, n_groups, q, q_dtype, q_seq_stride,
+                                         q_tok_stride, H, q_row0, q_row_step, sm_scale, *reps,
+                                         anchor_idx, anchor_seq_stride, alpha, alpha_seq_stride,
+                                         static_cast<float*>(workspace), stream),
+                    "lca_condense launch");
+}
+
+size_t mla_latent_attn_decode_workspace_size(int32_t B, int32_t H, int64_t max_entries) {
+  if (B < 1 || H < 16 || H % 16 != 0 || max_entries < 1) return 0;
+  const lca::DecodeSplit sp = lca::decode_split(B, H / 16, max_entries);
+  return lca::decode_workspace_bytes(B, H / 16, sp.S);
+}
+
+int mla_latent_attn_decode(const void* q, int32_t q_dtype, int64_t q_seq_stride, int32_t B,
+                           int32_t H, const lca_latent_t* reps, int64_t m,
+                           const lca_latent_t* raw, int64_t raw_begin, int64_t raw_end,
+                           float sm_scale, float* o_latent, float* lse, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  int rc;
+  if (q == nullptr || !aligned16(q)) return fail(LCA_ERR_INVALID_ARG, "q must be a non-null 16-byte aligned pointer");
+  if (!valid_dtype(q_dtype)) return fail(LCA_ERR_INVALID_ARG, "q_dtype %d is not LCA_BF16/LCA_F32", q_dtype);
+  if (!mult8(q_seq_stride) || q_seq_stride < 0) return fail(LCA_ERR_INVALID_ARG, "q_seq_stride must be a non-negative multiple of 8");
+  if (B < 1 || B > 65535) return fail(LCA_ERR_INVALID_ARG, "B must be in [1, 65535]");
+  if (H < 16 || H % 16 != 0 || H / 16 > 65535) return fail(LCA_ERR_UNSUPPORTED, "H = %d: the head count must be a positive multiple of 16", H);
+  if (m < 0 || raw_begin < 0 || raw_end < raw_begin) return fail(LCA_ERR_INVALID_ARG, "need m >= 0 and 0 <= raw_begin <= raw_end");
+  const int64_t n = m + (raw_end - raw_begin);
+  if (n < 1) return fail(LCA_ERR_INVALID_ARG, "nothing to attend: m + raw_end - raw_begin must be >= 1");
+  if (m > 0 && (rc = check_latent(reps, "reps", true, true)) != LCA_OK) return rc;
+  if (raw_end > raw_begin && (rc = check_latent(raw, "raw", true, true)) != LCA_OK) return rc;
+  if (m > 0 && raw_end > raw_begin && reps->dtype != raw->dtype)
+    return fail(LCA_ERR_UNSUPPORTED, "reps and raw must share one dtype");
+  if ((rc = check_scale(sm_scale)) != LCA_OK) return rc;
+  if (o_latent == nullptr || !aligned16(o_latent)) return fail(LCA_ERR_INVALID_ARG, "o_latent must be a non-null 16-byte aligned pointer");
+  const lca::DecodeSplit sp = lca::decode_split(B, H / 16, n);
+  const size_t need = lca::decode_workspace_bytes(B, H / 16, sp.S);
+  if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need))
+    return fail(LCA_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
+  const lca_latent_t none = {nullptr, nullptr, 0, 0, 0, 0, m > 0 ? reps->dtype : raw->dtype};
+  const lca_latent_t& rp = m > 0 ? *reps : none;
+  const lca_latent_t& rw = raw_end > raw_begin ? *raw : none;
+  return hip_status(lca::launch_decode(q, q_dtype, q_seq_stride, B, H, rp, m, rw, raw_begin, raw_end,
+                                       sm_scale, o_latent, lse, workspace, stream),
+                    "mla_latent_attn_decode launch");
+}
+
+int mla_latent_attn_prefill_chunk(const void* q, int32_t q_dtype, int64_t q_tok_stride,
+                                  int64_t chunk_start, int32_t C, int32_t H,
+                                  const lca_latent_t* reps, int64_t m,
+                                  const lca_latent_t* raw, int64_t raw_begin, float sm_scale,
+                                  void* o_latent, int32_t o_dtype, float* lse,
+                                  hipStream_t stream) {
+  int rc;
+  if (q == nullptr || !aligned16(q)) return fail(LCA_ERR_INVALID_ARG, "q must be a non-null 16-byte aligned pointer");
+  if (!valid_dtype(q_dtype)) return fail(LCA_ERR_INVALID_ARG, "q_dtype %d is not LCA_BF16/LCA_F32", q_dtype);
+  if (!mult8(q_tok_stride) || q_tok_stride < 0) return fail(LCA_ERR_INVALID_ARG, "q_tok_stride must be a non-negative multiple of 8");
+  if (C < 1) return fail(LCA_ERR_INVALID_ARG, "C must be >= 1");
+  if (H < 16 || H % 16 != 0 || H / 16 > 65535) return fail(LCA_ERR_UNSUPPORTED, "H = %d: the head count must be a positive multiple of 16", H);
+  if (m < 0 || raw_begin < 0 || chunk_start < raw_begin)
+    return fail(LCA_ERR_INVALID_ARG, "need m >= 0 and 0 <= raw_begin <= chunk_start");
+  if (m > 0 && (rc = check_latent(reps, "reps", true, true)) != LCA_OK) return rc;
+  if ((rc = check_latent(raw, "raw", true, true)) != LCA_OK) return rc;
+  if (m > 0 && reps->dtype != raw->dtype) return fail(LCA_ERR_UNSUPPORTED, "reps and raw must share one dtype");
+  if ((rc = check_scale(sm_scale)) != LCA_OK) return rc;
+  if (!valid_dtype(o_dtype)) return fail(LCA_ERR_INVALID_ARG, "o_dtype %d is not LCA_BF16/LCA_F32", o_dtype);
+  if (o_latent == nullptr || !aligned16(o_latent)) return fail(LCA_ERR_INVALID_ARG, "o_latent must be a non-null 16-byte aligned pointer");
+  const lca_latent_t none = {nullptr, nullptr, 0, 0, 0, 0, raw->dtype};
+  return hip_status(lca::launch_prefill(q, q_dtype, q_tok_stride, chunk_start, C, H, m > 0 ? *reps : none,
+                                        m, *raw, raw_begin, sm_scale, o_latent, o_dtype, lse, stream),
+                    "mla_latent_attn_prefill_chunk launch");
+}
+
+int mla_up_proj(const void* o_latent, int32_t o_dtype, int64_t T, int32_t H, const void* w_uv,
+                int32_t w_dtype, void* out, int32_t out_dtype, hipStream_t stream) {
+  if (T < 0) return fail(LCA_ERR_INVALID_ARG, "T must be >= 0");
+  if (H < 1 || H > 65535) return fail(LCA_ERR_INVALID_ARG, "H must be in [1, 65535]");
+  if (!valid_dtype(o_dtype) || !valid_dtype(w_dtype) || !valid_dtype(out_dtype))
+    return fail(LCA_ERR_INVALID_ARG, "dtypes must be LCA_BF16 or LCA_F32");
+  if (T == 0) return ok();
+  if (o_latent == nullptr || !aligned16(o_latent) || w_uv == nullptr || !aligned16(w_uv) ||
+      out == nullptr || !aligned16(out))
+    return fail(LCA_ERR_INVALID_ARG, "o_latent, w_uv and out must be non-null 16-byte aligned pointers");
+  if ((T + 63) / 64 > 0x7fffffff) return fail(LCA_ERR_UNSUPPORTED, "T too large");
+  return hip_status(lca::launch_up_proj(o_latent, o_dtype, T, H, w_uv, w_dtype, out, out_dtype, stream),
+                    "mla_up_proj launch");
+}
+
+}  // extern "C"

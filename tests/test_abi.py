@@ -1,0 +1,138 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every symbol include/lca.h declares, computes the grouping plan, and rejects
+bad arguments before touching the device."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import mla_latent_kv_lca_amd as lca
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "lca.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^(?:int|size_t|const char\*)\s+(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = lca.load()
+    declared = _header_functions()
+    assert set(declared) == set(lca.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version():
+    assert lca.lca_version() == 1000
+
+
+def test_plan_matches_golden():
+    with open(os.path.join(ROOT, "tests", "golden", "plan_counts.json")) as f:
+        gold = json.load(f)
+    for case in gold["cases"]:
+        p = lca.lca_plan(case["L"], case["w"], case["g"])
+        assert p["m"] == case["m"]
+        assert p["raw_begin"] == case["m"] * case["g"]
+        assert p["raw_end"] == case["L"]
+        assert p["n_entries"] == case["m"] + case["L"] - case["m"] * case["g"]
+
+
+def test_plan_rejects_bad_args():
+    with pytest.raises(lca.LcaError) as e:
+        lca.lca_plan(10, 4, 0)
+    assert e.value.status == lca.LCA_ERR_INVALID_ARG
+    assert "g >= 1" in lca.lca_last_error()
+    assert lca.lca_plan(10, 4, 2)["m"] == 3 and lca.lca_last_error() == ""
+
+
+def test_workspace_sizes():
+    assert lca.lca_condense_workspace_size(32, 1984, 0) == 32 * 576 * 4
+    assert lca.lca_condense_workspace_size(1, 256, 16) == 256 * 576 * 4
+    assert lca.lca_condense_workspace_size(0, 1, 0) == 0
+    # one split needs no workspace; more splits need partials of 16 x 514 floats
+    small = lca.mla_latent_attn_decode_workspace_size(512, 16, 32)
+    assert small == 0
+    big = lca.mla_latent_attn_decode_workspace_size(1, 16, 66496)
+    assert big > 0 and big % (16 * 514 * 4) == 0
+    assert lca.mla_latent_attn_decode_workspace_size(1, 24, 100) == 0  # unsupported H
+
+
+def _lat(ptr=16, dtype=0, stride=576):
+    return lca.LatentT(ptr, ptr, 0, stride, 0, stride, dtype)
+
+
+def _condense(lib, cache, reps, **kw):
+    a = dict(B=1, g=16, gb=0, n=1, q=64, qdt=0, qss=0, qts=576 * 16, T=16, H=16, r0=0, rs=0,
+             sm=1.0, anchor=64, aseq=0, alpha=None, alseq=0, ws=64, wsb=4096)
+    a.update(kw)
+    return lib.lca_condense(None if cache is None else ctypes.byref(cache), a["B"], a["g"], a["gb"],
+                            a["n"], a["q"], a["qdt"], a["qss"], a["qts"], a["T"], a["H"], a["r0"],
+                            a["rs"], a["sm"], None if reps is None else ctypes.byref(reps),
+                            a["anchor"], a["aseq"], a["alpha"], a["alseq"], a["ws"], a["wsb"], None)
+
+
+def test_condense_argument_errors():
+    lib = lca.load()
+    ok_lat = _lat()
+    assert _condense(lib, None, ok_lat) == lca.LCA_ERR_INVALID_ARG
+    assert "cache is null" in lca.lca_last_error()
+    assert _condense(lib, ok_lat, ok_lat, g=12) == lca.LCA_ERR_UNSUPPORTED
+    assert _condense(lib, ok_lat, ok_lat, g=64) == lca.LCA_ERR_UNSUPPORTED
+    assert _condense(lib, _lat(ptr=18), ok_lat) == lca.LCA_ERR_INVALID_ARG  # misaligned
+    assert _condense(lib, _lat(stride=577), ok_lat) == lca.LCA_ERR_INVALID_ARG
+    assert _condense(lib, _lat(dtype=7), ok_lat) == lca.LCA_ERR_INVALID_ARG
+    assert _condense(lib, ok_lat, ok_lat, sm=-1.0) == lca.LCA_ERR_INVALID_ARG
+    assert _condense(lib, ok_lat, ok_lat, sm=float("nan")) == lca.LCA_ERR_INVALID_ARG
+    assert _condense(lib, ok_lat, ok_lat, T=15) == lca.LCA_ERR_INVALID_ARG  # q rows out of range
+    assert "T = 15" in lca.lca_last_error()
+    assert _condense(lib, ok_lat, ok_lat, n=3, rs=16, T=40) == lca.LCA_ERR_INVALID_ARG
+    assert _condense(lib, ok_lat, ok_lat, anchor=None) == lca.LCA_ERR_INVALID_ARG
+    assert _condense(lib, ok_lat, ok_lat, ws=None) == lca.LCA_ERR_WORKSPACE
+    assert _condense(lib, ok_lat, ok_lat, wsb=100) == lca.LCA_ERR_WORKSPACE
+    assert _condense(lib, ok_lat, ok_lat, n=0) == lca.LCA_OK  # empty range: no launch
+
+
+def _decode(lib, reps, raw, **kw):
+    a = dict(q=64, qdt=0, qss=16 * 576, B=1, H=16, m=0, rb=0, re=8, sm=1.0, o=64, lse=None,
+             ws=None, wsb=0)
+    a.update(kw)
+    return lib.mla_latent_attn_decode(a["q"], a["qdt"], a["qss"], a["B"], a["H"],
+                                      None if reps is None else ctypes.byref(reps), a["m"],
+                                      None if raw is None else ctypes.byref(raw), a["rb"], a["re"],
+                                      a["sm"], a["o"], a["lse"], a["ws"], a["wsb"], None)
+
+
+def test_decode_argument_errors():
+    lib = lca.load()
+    lat = _lat()
+    assert _decode(lib, None, lat, H=24) == lca.LCA_ERR_UNSUPPORTED
+    assert _decode(lib, None, lat, re=0) == lca.LCA_ERR_INVALID_ARG  # nothing to attend
+    assert _decode(lib, None, None) == lca.LCA_ERR_INVALID_ARG       # raw rows but no raw
+    assert _decode(lib, None, lat, m=4) == lca.LCA_ERR_INVALID_ARG   # reps missing
+    assert _decode(lib, _lat(dtype=1), lat, m=4) == lca.LCA_ERR_UNSUPPORTED  # mixed dtypes
+    assert _decode(lib, None, lat, q=None) == lca.LCA_ERR_INVALID_ARG
+    assert _decode(lib, None, lat, o=None) == lca.LCA_ERR_INVALID_ARG
+    assert _decode(lib, None, lat, rb=5, re=4) == lca.LCA_ERR_INVALID_ARG
+    # a long single sequence needs split-K workspace
+    assert _decode(lib, None, lat, re=60000) == lca.LCA_ERR_WORKSPACE
+    assert "workspace needs" in lca.lca_last_error()
+
+
+def test_prefill_and_up_proj_argument_errors():
+    lib = lca.load()
+    lat = _lat()
+    pf = lib.mla_latent_attn_prefill_chunk
+    assert pf(64, 0, 9216, 10, 4, 16, None, 0, ctypes.byref(lat), 11, 1.0, 64, 0, None, None) == lca.LCA_ERR_INVALID_ARG
+    assert pf(64, 0, 9216, 10, 0, 16, None, 0, ctypes.byref(lat), 0, 1.0, 64, 0, None, None) == lca.LCA_ERR_INVALID_ARG
+    assert pf(64, 0, 9216, 10, 4, 8, None, 0, ctypes.byref(lat), 0, 1.0, 64, 0, None, None) == lca.LCA_ERR_UNSUPPORTED
+    assert pf(64, 0, 9216, 10, 4, 16, None, 0, ctypes.byref(lat), 0, 1.0, 64, 5, None, None) == lca.LCA_ERR_INVALID_ARG
+    up = lib.mla_up_proj
+    assert up(64, 0, 0, 16, 64, 0, 64, 0, None) == lca.LCA_OK  # T == 0
+    assert up(64, 0, -1, 16, 64, 0, 64, 0, None) == lca.LCA_ERR_INVALID_ARG
+    assert up(None, 0, 4, 16, 64, 0, 64, 0, None) == lca.LCA_ERR_INVALID_ARG
+    assert up(64, 3, 4, 16, 64, 0, 64, 0, None) == lca.LCA_ERR_INVALID_ARG

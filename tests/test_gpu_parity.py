@@ -1,0 +1,256 @@
+"""GPU parity: every kernel through the C ABI against the fp64 oracle.
+
+Inputs come from lca_inputs (seeded, bf16-rounded on the host); expected
+values come only from the oracle. Downstream stages are fed the GPU's own
+condensed cache, so a legitimate near-tie anchor cannot cascade.
+"""
+import numpy as np
+import pytest
+import torch
+
+import lca_inputs as li
+import mla_latent_kv_lca_amd as lca
+from oracle import lca_oracle as O
+from tests.gpu_util import TOL, anchors_agree, assert_close, dev, host, packed
+
+pytestmark = pytest.mark.gpu
+
+H = 16
+
+
+def _condense_gpu(cache_t, B, g, gb, n, q_t, r0, step, sm, m_cap, rep_dtype=None):
+    rep_dtype = rep_dtype or cache_t.dtype
+    reps = torch.zeros((B, m_cap, 576), dtype=rep_dtype, device="cuda")
+    anchor = torch.full((B, m_cap), -1, dtype=torch.int32, device="cuda")
+    alpha = torch.zeros((B, m_cap, g), dtype=torch.float32, device="cuda")
+    lca.lca_condense(lca.packed_latent(cache_t), B, g, gb, n, q_t, r0, step, sm,
+                     lca.packed_latent(reps), anchor, alpha)
+    return reps, anchor, alpha
+
+
+@pytest.mark.parametrize("dtype,rho", [(torch.bfloat16, 0.5), (torch.float32, 0.5), (torch.bfloat16, 0.0)])
+def test_condense_matches_oracle(dtype, rho):
+    B, L, g, w = 2, 2048, 16, 1024
+    bf = dtype == torch.bfloat16
+    c, kr = li.latent_cache(1, B, L, bf16=bf)
+    q = li.queries(1, B, 16, H, rho=rho, bf16=bf)
+    m = O.plan(L, w, g)["m"]
+    reps, anchor, alpha = _condense_gpu(packed(c, kr, dtype), B, g, 0, m, dev(q, dtype), 0, 0, 1.0, m)
+    torch.cuda.synchronize()
+    rc, rk, ra, ralpha, s = O.condense(c, kr, q, g, 0, m, 0, 0, 1.0)
+    r = host(reps)
+    assert_close(r[..., :512], rc, what="rep c_KV")
+    assert_close(host(alpha), ralpha, tol=1e-5, what="alpha")
+    np.testing.assert_allclose(host(alpha).sum(-1), 1.0, atol=1e-6)
+    n_sure = anchors_agree(host(anchor).astype(np.int64), ra, O.top2_margin(s))
+    assert n_sure > 0.5 * B * m
+    # the anchor's k_R is copied exactly from the cache row it names
+    ga = host(anchor).astype(np.int64)
+    for b in range(B):
+        np.testing.assert_array_equal(r[b, :, 512:], kr[b, ga[b]].astype(np.float64))
+
+
+def test_condense_per_group_summary_queries_prefill_style():
+    """Chunked-prefill addressing: group j uses the g queries after it."""
+    B, L, g = 1, 640, 16
+    c, kr = li.latent_cache(4, B, L)
+    q = li.queries(4, B, L, H, rho=0.5)
+    gb, n = 5, 20
+    reps, anchor, alpha = _condense_gpu(packed(c, kr), B, g, gb, n, dev(q), (gb + 1) * g, g, 0.7, gb + n)
+    torch.cuda.synchronize()
+    rc, rk, ra, ralpha, s = O.condense(c, kr, q, g, gb, n, (gb + 1) * g, g, 0.7)
+    r = host(reps)
+    assert not r[:, :gb].any(), "rows before group_begin must stay untouched"
+    assert_close(r[0, gb:, :512], rc[0], what="rep c_KV")
+    assert_close(host(alpha)[0, gb:], ralpha[0], tol=1e-5, what="alpha")
+    anchors_agree(host(anchor)[0, gb:].astype(np.int64), ra[0], O.top2_margin(s[0]))
+
+
+def test_condense_g1_copies_rows_exactly():
+    B, L = 2, 100
+    c, kr = li.latent_cache(5, B, L)
+    q = li.queries(5, B, 1, H)
+    reps, anchor, alpha = _condense_gpu(packed(c, kr), B, 1, 0, L, dev(q), 0, 0, 1.0, L)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(reps), np.concatenate([c, kr], -1).astype(np.float64))
+    np.testing.assert_array_equal(host(anchor), np.tile(np.arange(L), (B, 1)))
+    np.testing.assert_array_equal(host(alpha), 1.0)
+
+
+def test_condense_identical_rows_pool_to_the_row():
+    B, g = 1, 16
+    c, kr = li.latent_cache(6, B, 4 * g)
+    for j in range(4):  # every group is one row repeated
+        c[0, j * g:(j + 1) * g] = c[0, j * g]
+        kr[0, j * g:(j + 1) * g] = kr[0, j * g]
+    q = li.queries(6, B, g, H, rho=0.5)
+    reps, anchor, alpha = _condense_gpu(packed(c, kr), B, g, 0, 4, dev(q), 0, 0, 1.0, 4)
+    torch.cuda.synchronize()
+    want = np.concatenate([c[0, ::g], kr[0, ::g]], -1).astype(np.float64)
+    np.testing.assert_array_equal(host(reps)[0], want)
+    np.testing.assert_array_equal(host(anchor)[0], np.arange(4) * g)
+    np.testing.assert_array_equal(host(alpha), 1.0 / g)
+
+
+@pytest.mark.parametrize("g", [2, 4, 8, 32])
+def test_condense_other_group_sizes(g):
+    B, L = 1, 40 * g
+    c, kr = li.latent_cache(7, B, L)
+    q = li.queries(7, B, g, H, rho=0.5)
+    n = 37
+    reps, anchor, alpha = _condense_gpu(packed(c, kr), B, g, 1, n, dev(q), 0, 0, 1.3, n + 1)
+    torch.cuda.synchronize()
+    rc, rk, ra, ralpha, s = O.condense(c, kr, q, g, 1, n, 0, 0, 1.3)
+    assert_close(host(reps)[0, 1:, :512], rc[0], what=f"rep c_KV g={g}")
+    assert_close(host(alpha)[0, 1:], ralpha[0], tol=1e-5, what="alpha")
+    anchors_agree(host(anchor)[0, 1:].astype(np.int64), ra[0], O.top2_margin(s[0]))
+
+
+# ------------------------------------------------------------------ decode --
+def _decode_gpu(q_t, reps_t, m, cache_t, raw_begin, raw_end, sm):
+    B = q_t.shape[0]
+    o = torch.empty((B, q_t.shape[1], 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, q_t.shape[1]), dtype=torch.float32, device="cuda")
+    lca.mla_latent_attn_decode(q_t, None if m == 0 else lca.packed_latent(reps_t), m,
+                               lca.packed_latent(cache_t), raw_begin, raw_end, sm, o, lse)
+    return o, lse
+
+
+@pytest.mark.parametrize("dtype,L", [(torch.bfloat16, 2048), (torch.float32, 2048), (torch.bfloat16, 2077)])
+def test_decode_condensed_matches_oracle(dtype, L):
+    B, g, w = 2, 16, 1024
+    bf = dtype == torch.bfloat16
+    c, kr = li.latent_cache(1, B, L, bf16=bf)
+    li.plant_needles(1, c, kr, 3, 14.0, 0, L, bf16=bf)
+    qh = li.queries(1, B, 16, H, rho=0.5, bf16=bf)
+    qd = li.queries(1, B, 1, H, rho=0.5, bf16=bf, stream=1)[:, 0]
+    p = O.plan(L, w, g)
+    cache_t = packed(c, kr, dtype)
+    reps, anchor, _ = _condense_gpu(cache_t, B, g, 0, p["m"], dev(qh, dtype), 0, 0, 1.0, p["m"])
+    o, lse = _decode_gpu(dev(qd, dtype), reps, p["m"], cache_t, p["raw_begin"], L, 1.0)
+    torch.cuda.synchronize()
+    r = host(reps)
+    ro, rl = O.decode(qd, r[..., :512], r[..., 512:], p["m"], c, kr, p["raw_begin"], L, 1.0)
+    assert_close(host(o), ro, what="o_latent")
+    assert_close(host(lse), rl, tol=1e-3, what="lse")
+
+
+def test_decode_plain_mla_matches_oracle():
+    B, L = 2, 2048  # w = L: no groups, exact MLA over every row
+    c, kr = li.latent_cache(2, B, L)
+    li.plant_needles(2, c, kr, 2, 14.0, 0, L)
+    qd = li.queries(2, B, 1, H, rho=0.5, stream=1)[:, 0]
+    o, lse = _decode_gpu(dev(qd), None, 0, packed(c, kr), 0, L, 1.0)
+    torch.cuda.synchronize()
+    ro, rl = O.decode(qd, None, None, 0, c, kr, 0, L, 1.0)
+    assert_close(host(o), ro, what="o_latent")
+    assert_close(host(lse), rl, tol=1e-3, what="lse")
+
+
+def test_decode_singleton_groups_equal_plain_mla_bitwise():
+    """g = 1 representatives are exact row copies, so LCA decode over them
+    equals plain MLA decode bit for bit (same entries, same order)."""
+    B, L, w = 2, 1500, 300
+    c, kr = li.latent_cache(3, B, L)
+    qd = li.queries(3, B, 1, H, rho=0.5, stream=1)[:, 0]
+    cache_t = packed(c, kr)
+    m = L - w
+    reps, _, _ = _condense_gpu(cache_t, B, 1, 0, m, dev(li.queries(3, B, 1, H)), 0, 0, 1.0, m)
+    o1, l1 = _decode_gpu(dev(qd), reps, m, cache_t, m, L, 1.0)
+    o2, l2 = _decode_gpu(dev(qd), None, 0, cache_t, 0, L, 1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_decode_independent_of_split_count():
+    """The same sequence alone (many splits) and in a batch of 64 (few splits)."""
+    L = 9000
+    c, kr = li.latent_cache(8, 1, L)
+    li.plant_needles(8, c, kr, 2, 14.0, 0, L)
+    qd = li.queries(8, 1, 1, H, rho=0.5, stream=1)[:, 0]
+    cache1 = packed(c, kr)
+    o1, l1 = _decode_gpu(dev(qd), None, 0, cache1, 0, L, 1.0)
+    cacheB = cache1.expand(64, L, 576)
+    oB, lB = _decode_gpu(dev(qd).expand(64, H, 576), None, 0, cacheB, 0, L, 1.0)
+    torch.cuda.synchronize()
+    s1 = lca.mla_latent_attn_decode_workspace_size(1, H, L)
+    sB = lca.mla_latent_attn_decode_workspace_size(64, H, L)
+    assert s1 // (16 * 514 * 4) != sB // (64 * 16 * 514 * 4)  # different split counts
+    rel = (oB - o1).abs().max().item() / o1.abs().max().item()
+    assert rel <= 1e-5, rel
+    assert (lB - l1).abs().max().item() <= 1e-5
+    # every batch row identical (deterministic)
+    assert torch.equal(oB, oB[:1].expand_as(oB))
+
+
+def test_decode_tiny_and_ragged():
+    B, L = 3, 5
+    c, kr = li.latent_cache(9, B, L)
+    qd = li.queries(9, B, 1, 32, rho=0.5, stream=1)[:, 0]  # H = 32: two head blocks
+    o, lse = _decode_gpu(dev(qd), None, 0, packed(c, kr), 2, L, 0.8)
+    torch.cuda.synchronize()
+    ro, rl = O.decode(qd, None, None, 0, c, kr, 2, L, 0.8)
+    assert_close(host(o), ro, what="o_latent")
+    assert_close(host(lse), rl, tol=1e-3, what="lse")
+
+
+# ----------------------------------------------------------------- prefill --
+@pytest.mark.parametrize("L,C", [(320, 64), (301, 40)])
+def test_prefill_chunks_match_oracle(L, C):
+    w, g, sm = 64, 16, 1.0
+    c, kr = li.latent_cache(10, 1, L)
+    q = li.queries(10, 1, L, H, rho=0.5)[0]
+    cache_t = packed(c, kr)[0]
+    q_t = dev(q)
+    m_cap = O.prefill_plan(((L - 1) // C) * C, w, g)
+    reps = torch.zeros((max(m_cap, 1), 576), dtype=torch.bfloat16, device="cuda")
+    anchor = torch.zeros((1, max(m_cap, 1)), dtype=torch.int32, device="cuda")
+    out = torch.empty((L, H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((L, H), dtype=torch.float32, device="cuda")
+    m = 0
+    for s in range(0, L, C):
+        ms = O.prefill_plan(s, w, g)
+        if ms > m:
+            lca.lca_condense(lca.packed_latent(cache_t[None]), 1, g, m, ms - m, q_t[None],
+                             (m + 1) * g, g, sm, lca.packed_latent(reps[None]), anchor)
+            m = ms
+        e = min(L, s + C)
+        lca.mla_latent_attn_prefill_chunk(q_t[s:e], s, lca.packed_latent(reps) if m else None, m,
+                                          lca.packed_latent(cache_t), m * g, sm, out[s:e], lse[s:e])
+    torch.cuda.synchronize()
+    # oracle reps for the anchor check, GPU reps for the attention check
+    _, _, rep_c, rep_k = O.prefill(q, c[0], kr[0], w, g, C, sm)
+    r = host(reps)[:m_cap]
+    assert_close(r[:, :512], rep_c, what="prefill reps")
+    ro = np.zeros((L, H, 512))
+    rl = np.zeros((L, H))
+    for s in range(0, L, C):
+        ms = O.prefill_plan(s, w, g)
+        e = min(L, s + C)
+        ro[s:e], rl[s:e] = O.prefill_chunk(q[s:e], s, r[:, :512], r[:, 512:], ms, c[0], kr[0], ms * g, sm)
+    assert_close(host(out), ro, what="prefill o_latent")
+    assert_close(host(lse), rl, tol=1e-3, what="prefill lse")
+
+
+def test_prefill_bf16_output():
+    L, C = 96, 96
+    c, kr = li.latent_cache(11, 1, L)
+    q = li.queries(11, 1, L, H, rho=0.5)[0]
+    out = torch.empty((C, H, 512), dtype=torch.bfloat16, device="cuda")
+    lca.mla_latent_attn_prefill_chunk(dev(q), 0, None, 0, lca.packed_latent(packed(c, kr)[0]), 0, 1.0, out)
+    torch.cuda.synchronize()
+    ro, _ = O.prefill_chunk(q, 0, np.zeros((0, 512)), np.zeros((0, 64)), 0, c[0], kr[0], 0, 1.0)
+    assert_close(host(out), ro, what="prefill bf16 o_latent")
+
+
+# --------------------------------------------------------------- up-proj ----
+@pytest.mark.parametrize("xdt,ydt,T", [(torch.float32, torch.float32, 37), (torch.bfloat16, torch.bfloat16, 130),
+                                      (torch.float32, torch.bfloat16, 64)])
+def test_up_proj_matches_oracle(xdt, ydt, T):
+    rng = np.random.default_rng(12)
+    x = li.bf16_round(rng.standard_normal((T, H, 512)).astype(np.float32))
+    w = li.w_uv(12, H)
+    out = torch.empty((T, H, 128), dtype=ydt, device="cuda")
+    lca.mla_up_proj(dev(x, xdt), dev(w), out)
+    torch.cuda.synchronize()
+    assert_close(host(out), O.up_proj(x, w), tol=TOL, what="up_proj")
