@@ -71,8 +71,11 @@ __global__ __launch_bounds__(NT, 2) void decode_kernel(
       for (int ks = 0; ks < 4; ++ks)
         acc = mfma16x16x32(*reinterpret_cast<const uint4*>(rowp + 128 * w + 32 * ks + 8 * kg),
                            qa[ks], acc);
-      acc = mfma16x16x16(*reinterpret_cast<const uint2*>(rowp + D_C + 16 * w + 4 * kg), qr, acc);
-      *reinterpret_cast<f32x4_t*>(&sx[w][col][16 * eb + 4 * kg]) = acc;  // S[h=col][e]
+      // the RoPE columns go to their own accumulator: a 16x16x16 product that
+      // takes a 16x16x32 result as its accumulator lost that result here
+      const f32x4_t accr = mfma16x16x16(*reinterpret_cast<const uint2*>(rowp + D_C + 16 * w + 4 * kg),
+                                        qr, f32x4_t{0.f, 0.f, 0.f, 0.f});
+      *reinterpret_cast<f32x4_t*>(&sx[w][col][16 * eb + 4 * kg]) = acc + accr;  // S[h=col][e]
     }
     __syncthreads();
 

@@ -176,8 +176,10 @@ def decode(q, rep_c, rep_k, m: int, raw_c, raw_k, raw_begin: int, raw_end: int,
     o = np.zeros((B, H, D_C))
     lse = np.zeros((B, H))
     for b in range(B):
-        ec = np.concatenate([_f64(rep_c[b, :m]), _f64(raw_c[b, raw_begin:raw_end])])
-        ek = np.concatenate([_f64(rep_k[b, :m]), _f64(raw_k[b, raw_begin:raw_end])])
+        ec, ek = _f64(raw_c[b, raw_begin:raw_end]), _f64(raw_k[b, raw_begin:raw_end])
+        if m > 0:
+            ec = np.concatenate([_f64(rep_c[b, :m]), ec])
+            ek = np.concatenate([_f64(rep_k[b, :m]), ek])
         o[b], lse[b] = attend(q[b], ec, ek, sm_scale)
     return o, lse
 
@@ -195,7 +197,8 @@ def prefill_chunk(q, chunk_start: int, rep_c, rep_k, m: int, raw_c, raw_k, raw_b
     rows = np.arange(C) if rows is None else np.asarray(rows)
     o = np.zeros((len(rows), H, D_C))
     lse = np.zeros((len(rows), H))
-    rc, rk = _f64(rep_c[:m]), _f64(rep_k[:m])
+    rc = _f64(rep_c[:m]) if m > 0 else np.zeros((0, D_C))
+    rk = _f64(rep_k[:m]) if m > 0 else np.zeros((0, D_R))
     for n, i in enumerate(rows):
         t = chunk_start + int(i)
         ec = np.concatenate([rc, _f64(raw_c[raw_begin:t + 1])])
