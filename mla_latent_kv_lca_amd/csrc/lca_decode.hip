@@ -6,25 +6,332 @@
 // cached row and its value the row's 512-wide latent, so the H heads of one
 // sequence form a 16-row (per head block) by entries product, like MQA.
 //
-// decode_kernel: one workgroup of 4 wavefronts per (split, sequence, head
-// block). The split's entries stream through LDS in tiles of 32. Wave w owns
-// latent columns [128w, 128w + 128) and RoPE columns [16w, 16w + 16): it forms
-// the partial scores S^T = K Q^T over its columns on the matrix cores
-// (16x16x32 / 16x16x16 bf16), the four partials are summed through LDS in a
-// fixed order, every wave runs the same online softmax, and each wave
-// accumulates the value product for its own 128 columns (16x16x32 bf16,
-// fp32 accumulators). The cost per entry is 34,816 flop on 1,152 bytes,
-// above what the fp32 vector units could sustain at HBM rate, hence MFMA.
-// Partial (unnormalised output, running max, running sum) go to the
-// caller's workspace; merge_kernel combines the splits in split order.
+// Kernels:
+//  decode_kernel         bf16 rows packed as [c_KV ++ k_R]: HBM -> LDS ring by
+//                        direct loads, one workgroup per CU (details below).
+//  decode_kernel_staged  any strides / f32 rows: register-staged 32-entry tiles.
+//  merge_kernel          combines split-K partial results in split order.
 #include "lca_tile.h"
 
 namespace lca {
 
-constexpr int SX_ROW = 36;  // floats per head row of the score exchange (32 + pad)
+constexpr int SX_ROW = 36;                     // floats per head row of the staged score exchange
+constexpr int DNW = 4;                         // wavefronts per decode workgroup (2 x 2)
+constexpr int DNT = 64 * DNW;                  // threads per decode workgroup
+constexpr int DT = 32;                         // entries per tile: two 16-entry halves
+constexpr int DBUF = 4;                        // LDS ring depth (tiles)
+constexpr int DT_ELEMS = DT * D_ROW;           // dense tile, 36,864 bytes
+constexpr int DMA_PER_WAVE = DT * (D_ROW / 8) / 64 / DNW;  // 9 wave-instructions per tile per wave
 
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+}
+
+// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane.
+// Issued from asm so that the compiler does not drain the ring before every
+// LDS read; completion is tracked with explicit vmcnt waits. m0 is saved and
+// restored around the load, so the compiler's own use of m0 is untouched.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_block) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(lds_block)
+      : "memory");
+}
+// wait until at most `newer` tiles issued after the one wanted are in flight
+__device__ __forceinline__ void wait_dma_newer(int newer) {
+  static_assert(DMA_PER_WAVE == 9, "vmcnt immediates assume 9 loads per tile per wave");
+  if (newer >= 3) asm volatile("s_waitcnt vmcnt(27)" ::: "memory");
+  else if (newer == 2) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+  else if (newer == 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+__device__ __forceinline__ void barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// An empty asm that reads the four registers: the compiler must have waited
+// for the load that produced them before this point.
+__device__ __forceinline__ void retire(const uint4& v) {
+  asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w));
+}
+
+// Tile rows are dense (576 bf16); the 16-byte chunk c of row r sits at chunk
+// position c ^ (r & 7), which spreads the 16 rows read by one MFMA fragment
+// over distinct LDS banks.
+__device__ __forceinline__ int chunk_pos(int r, int c) { return r * (D_ROW / 8) + (c ^ (r & 7)); }
+
+// Packed rows (k_R right after c_KV, one token stride) of the two segments of
+// one sequence: entries [0, m) are representative rows, the rest raw rows.
+struct DmaSrc {
+  const char* rep;  // representative rows of sequence 0
+  const char* raw;  // raw rows of sequence 0, starting at raw_begin
+  int64_t tok;      // token stride in bytes, shared by both segments
+  int64_t m;
+};
+
+// LDS slot P = 64 j + lane (j = w + DNW i) of a tile holds 16-byte chunk
+// col = (P % 72) ^ (row & 7) of tile row row = P / 72; its byte offset from
+// the tile's first row is row * token stride + 16 col, fixed for every tile.
+__device__ __forceinline__ void slot_rowcol(int w, int i, int lane, int& row, int& col) {
+  const int P = 64 * (w + DNW * i) + lane;
+  row = P / 72;
+  col = (P - row * 72) ^ (row & 7);
+}
+
+// Issue the DMA of tile entries [e0, e0 + DT) into `buf`. Full tiles inside
+// one segment use uniform row bases plus per-lane offsets; the tile that
+// straddles the representative / raw boundary and the last, partial tile
+// compute each row, reloading the last valid row past e_end (those logits
+// are masked, so any finite row will do).
+__device__ __forceinline__ void tile_dma(const DmaSrc& src, int64_t e0, int64_t e_end,
+                                         const bf16_t* buf, int w, int lane,
+                                         const uint32_t (&off)[DMA_PER_WAVE]) {
+  const uint32_t base = lds_off(buf);
+  if (e0 + DT <= e_end && (e0 + DT <= src.m || e0 >= src.m)) {
+    const char* b0 = e0 < src.m ? src.rep + e0 * src.tok : src.raw + (e0 - src.m) * src.tok;
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i) dma16(b0 + off[i], base + 1024u * (w + DNW * i));
+  } else {
+    const int valid = (int)min((int64_t)DT, e_end - e0);
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+      int row, col;
+      slot_rowcol(w, i, lane, row, col);
+      const int64_t e = e0 + min(row, valid - 1);
+      const char* p = e < src.m ? src.rep + e * src.tok : src.raw + (e - src.m) * src.tok;
+      dma16(p + 16 * col, base + 1024u * (w + DNW * i));
+    }
+  }
+}
+
+// decode_kernel: one workgroup of 4 wavefronts per (split, sequence, head
+// block), one workgroup per CU. Entries stream from HBM straight into a
+// 4-deep LDS ring of 32-entry tiles (global_load_lds, 16 bytes per lane, no
+// register staging): three 36 KB tiles are in flight while one is used, which
+// is what the HBM latency needs per CU.
+// The waves form a 2 x 2 grid: wave w owns entry half eh = w & 1 (tile rows
+// [16 eh, 16 eh + 16)) and column half ch = w >> 1 (latent columns
+// [256 ch, 256 ch + 256) and RoPE columns [32 ch, 32 ch + 32)). Per tile it
+//   forms the partial scores S^T = K Q^T over its columns (9 MFMA 16x16x32,
+//   its queries in registers), adds the partner's half (wave w ^ 2, same
+//   entries) read through LDS in a fixed order, so both partners hold the
+//   same scores and the same online-softmax state, and
+//   accumulates O^T += V^T P^T for its own 256 columns over its 16 entries
+//   (16 MFMA 16x16x16; P comes straight from the score registers, V^T is built
+//   from row fragments with half-word shuffles).
+// The two entry halves are merged once, at the end. The cost per entry is
+// 34,816 flop on 1,152 bytes, more than the fp32 vector units sustain at HBM
+// rate, hence the matrix cores.
+// With S > 1 splits per sequence the workgroup writes its merged (O, max,
+// sum) to the workspace and merge_kernel combines the splits in split order.
+template <typename TQ>
+__global__ __launch_bounds__(DNT) void decode_kernel(
+    const TQ* __restrict__ q, int64_t q_seq, DmaSrc src0, int64_t rep_seq_b, int64_t raw_seq_b,
+    int64_t n_entries, int per_tiles, int S, float scale_log2, int H, float* __restrict__ part_o,
+    float* __restrict__ part_ml, float* __restrict__ o_final, float* __restrict__ lse_final) {
+  __shared__ __align__(16) bf16_t ring[DBUF][DT_ELEMS];
+  __shared__ __align__(16) float sx[DNW][HB][HB + 4];  // partial S^T: [wave][head][entry]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int eh = w & 1, ch = w >> 1;
+  const int kg = lane >> 4, col = lane & 15;
+  const int s = blockIdx.x, b = blockIdx.y, hg = blockIdx.z, HG = gridDim.z;
+
+  DmaSrc src = src0;
+  src.rep += (int64_t)b * rep_seq_b;
+  src.raw += (int64_t)b * raw_seq_b;
+  const int64_t e_begin = (int64_t)s * per_tiles * DT;
+  const int64_t e_end = min(n_entries, e_begin + (int64_t)per_tiles * DT);
+  const int n_tiles = e_end > e_begin ? (int)((e_end - e_begin + DT - 1) / DT) : 0;
+
+  uint32_t off[DMA_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < DMA_PER_WAVE; ++i) {
+    int row, col16;
+    slot_rowcol(w, i, lane, row, col16);
+    off[i] = (uint32_t)(row * src.tok) + 16u * col16;
+  }
+#pragma unroll
+  for (int t = 0; t < DBUF - 1; ++t)
+    if (t < n_tiles) tile_dma(src, e_begin + (int64_t)t * DT, e_end, ring[t], w, lane, off);
+
+  // query fragments of head col for this wave's columns: 8 latent k-steps of
+  // 32 columns and 1 RoPE k-step
+  const TQ* qh = q + (int64_t)b * q_seq + (int64_t)(hg * HB + col) * D_ROW;
+  uint4 qa[9];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) qa[ks] = load8_bf16(qh + 256 * ch + 32 * ks + 8 * kg);
+  qa[8] = load8_bf16(qh + D_C + 32 * ch + 8 * kg);
+  // Consume the query registers here so that the compiler waits for their
+  // loads once, before the loop. Otherwise it places those waits inside the
+  // loop, where (being unaware of the ring loads) its vmcnt counts would also
+  // drain every tile in flight.
+#pragma unroll
+  for (int ks = 0; ks < 9; ++ks) retire(qa[ks]);
+
+  // lane-constant element offsets of this lane's fragments inside a tile
+  int k_off[9], v_off[8];
+  const int krow = 16 * eh + col;  // score product: A = K rows
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) k_off[ks] = 8 * chunk_pos(krow, 32 * ch + 4 * ks + kg);
+  k_off[8] = 8 * chunk_pos(krow, 64 + 4 * ch + kg);
+#pragma unroll
+  for (int slab = 0; slab < 2; ++slab)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)  // value product: rows 16 eh + 4 kg + r, columns of slab
+      v_off[4 * slab + r] = 8 * chunk_pos(16 * eh + 4 * kg + r, 16 * (2 * ch + slab) + col);
+
+  f32x4_t o[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) o[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int64_t e0 = e_begin + (int64_t)t * DT;
+    wait_dma_newer(min(n_tiles - 1 - t, DBUF - 2));
+    barrier();  // tile t landed for every wave; tile t-1's slot and sx are free
+    if (t + DBUF - 1 < n_tiles)
+      tile_dma(src, e0 + (int64_t)(DBUF - 1) * DT, e_end, ring[(t + DBUF - 1) % DBUF], w, lane, off);
+    const bf16_t* tile = ring[t % DBUF];
+
+    // partial S^T over this wave's columns: two independent chains
+    f32x4_t sa = f32x4_t{0.f, 0.f, 0.f, 0.f}, sb = sa;
+#pragma unroll
+    for (int ks = 0; ks < 8; ks += 2) {
+      sa = mfma16x16x32(*reinterpret_cast<const uint4*>(tile + k_off[ks]), qa[ks], sa);
+      sb = mfma16x16x32(*reinterpret_cast<const uint4*>(tile + k_off[ks + 1]), qa[ks + 1], sb);
+    }
+    sa = mfma16x16x32(*reinterpret_cast<const uint4*>(tile + k_off[8]), qa[8], sa);
+    *reinterpret_cast<f32x4_t*>(&sx[w][col][4 * kg]) = sa + sb;  // S[h = col][16 eh + 4 kg + r]
+    barrier();
+    // both partners add the column halves in the same order (ch 0, then ch 1)
+    const f32x4_t sc = *reinterpret_cast<const f32x4_t*>(&sx[eh][col][4 * kg]) +
+                       *reinterpret_cast<const f32x4_t*>(&sx[eh + 2][col][4 * kg]);
+    float z[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) z[r] = sc[r] * scale_log2;
+    if (e0 + DT > e_end) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (e0 + 16 * eh + 4 * kg + r >= e_end) z[r] = -INFINITY;
+    }
+    // online softmax per head (lanes col, col+16, col+32, col+48), lazy rescale
+    float tmax = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    if (__builtin_amdgcn_ballot_w64(tmax > m_run + LAZY_LOG2) != 0) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float corr = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= corr;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) o[c] *= corr;
+      m_run = m_new;
+    }
+    // a wave with no visible entry yet keeps m_run = -inf: its p must be 0
+    const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(z[r] - m_ref);
+    float ps = (p[0] + p[1]) + (p[2] + p[3]);
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    l_run += ps;
+    const uint2 pb = make_uint2(pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3]));
+
+    // O^T += V^T P^T: per 128-column slab, 4 row fragments -> 8 MFMA 16x16x16
+#pragma unroll
+    for (int slab = 0; slab < 2; ++slab) {
+      uint4 R[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) R[r] = *reinterpret_cast<const uint4*>(tile + v_off[4 * slab + r]);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int wi = c >> 1;
+        uint2 a;
+        if (c & 1) {
+          a.x = hi_pair(u4_get(R[0], wi), u4_get(R[1], wi));
+          a.y = hi_pair(u4_get(R[2], wi), u4_get(R[3], wi));
+        } else {
+          a.x = lo_pair(u4_get(R[0], wi), u4_get(R[1], wi));
+          a.y = lo_pair(u4_get(R[2], wi), u4_get(R[3], wi));
+        }
+        // o[8 slab + c][r'] = O[head col][256 ch + 128 slab + 8 (4 kg + r') + c]
+        o[8 * slab + c] = mfma16x16x16(a, pb, o[8 * slab + c]);
+      }
+    }
+  }
+
+  // merge the two entry halves through LDS (the ring is free now)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  barrier();
+  float* ex = reinterpret_cast<float*>(&ring[0][0]);  // [w][head][256] then [w][head][2]
+  float* exml = ex + DNW * HB * 256;
+#pragma unroll
+  for (int slab = 0; slab < 2; ++slab)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float v[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) v[c] = o[8 * slab + c][r];
+      store8(ex + (w * HB + col) * 256 + 128 * slab + 32 * kg + 8 * r, v);
+    }
+  if (kg == 0) {
+    exml[(w * HB + col) * 2 + 0] = m_run;
+    exml[(w * HB + col) * 2 + 1] = l_run;
+  }
+  barrier();
+  // wave w finalises columns 256 ch + 128 eh + [0, 128) of every head: lane ->
+  // head col, 32 columns starting at 256 ch + 128 eh + 32 kg
+  const int wa = 2 * ch, wb = 2 * ch + 1;  // the two entry halves of this column half
+  const float ma = exml[(wa * HB + col) * 2], mb = exml[(wb * HB + col) * 2];
+  const float M = fmaxf(ma, mb);
+  const float wta = ma == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ma - M);
+  const float wtb = mb == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mb - M);
+  const float Lsum = fmaf(wtb, exml[(wb * HB + col) * 2 + 1], wta * exml[(wa * HB + col) * 2 + 1]);
+  const int cl = 128 * eh + 32 * kg;  // column within this column half
+  float acc[32];
+  const float4* pa = reinterpret_cast<const float4*>(ex + (wa * HB + col) * 256 + cl);
+  const float4* pbb = reinterpret_cast<const float4*>(ex + (wb * HB + col) * 256 + cl);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 va = pa[i], vb = pbb[i];
+    acc[4 * i + 0] = fmaf(wtb, vb.x, wta * va.x);
+    acc[4 * i + 1] = fmaf(wtb, vb.y, wta * va.y);
+    acc[4 * i + 2] = fmaf(wtb, vb.z, wta * va.z);
+    acc[4 * i + 3] = fmaf(wtb, vb.w, wta * va.w);
+  }
+  const int head = hg * HB + col;
+  const int d0 = 256 * ch + cl;
+  if (S == 1) {
+    const float inv = 1.0f / Lsum;
+    float* dst = o_final + ((int64_t)b * H + head) * D_C + d0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) v[c] = acc[8 * i + c] * inv;
+      store8(dst + 8 * i, v);
+    }
+    if (lse_final != nullptr && w == 0 && kg == 0)
+      lse_final[(int64_t)b * H + head] = (M + __log2f(Lsum)) * 0.69314718055994530942f;
+    return;
+  }
+  const int64_t slot = (((int64_t)b * HG + hg) * S + s) * HB + col;
+  float* dst = part_o + slot * D_C + d0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) store8(dst + 8 * i, acc + 8 * i);
+  if (w == 0 && kg == 0) {
+    part_ml[slot * 2 + 0] = M;
+    part_ml[slot * 2 + 1] = Lsum;
+  }
+}
+
+// Register-staged variant for f32 caches (rounded to bf16 as they are staged
+// into LDS); the bf16 path above copies rows into LDS without conversion.
 template <typename TQ, typename TC>
-__global__ __launch_bounds__(NT, 2) void decode_kernel(
+__global__ __launch_bounds__(NT) void decode_kernel_staged(
     const TQ* __restrict__ q, int64_t q_seq, Seg reps, int64_t m, Seg raw, int64_t raw_begin,
     int64_t n_entries, int per_tiles, int S, float scale_log2, int H, float* __restrict__ part_o,
     float* __restrict__ part_ml, float* __restrict__ o_final, float* __restrict__ lse_final) {
@@ -195,7 +502,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
 }
 
 DecodeSplit decode_split(int B, int HG, int64_t n_entries) {
-  const int64_t n_tiles = (n_entries + TILE - 1) / TILE;
+  const int64_t n_tiles = (n_entries + DT - 1) / DT;
   const int64_t seqs = (int64_t)B * HG;
   int64_t cap = (DEC_TARGET_BLOCKS + seqs - 1) / seqs;
   if (cap < 1) cap = 1;
@@ -207,18 +514,17 @@ DecodeSplit decode_split(int B, int HG, int64_t n_entries) {
   return DecodeSplit{(int)S, (int)(per > 0 ? per : 1)};
 }
 
+// workspace: [m, l: slots * 2][O: slots * 512], slots = B * HG * S * 16
 size_t decode_workspace_bytes(int B, int HG, int S) {
   if (S <= 1) return 0;
   const size_t slots = (size_t)B * HG * S * HB;
-  return slots * D_C * sizeof(float) + slots * 2 * sizeof(float);
+  return slots * 2 * sizeof(float) + slots * D_C * sizeof(float);
 }
 
-template <typename TQ, typename TC>
-static void launch_dec_t(dim3 grid, hipStream_t st, const void* q, int64_t q_seq, Seg reps,
-                         int64_t m, Seg raw, int64_t raw_begin, int64_t n, int per, int S,
-                         float sl2, int H, float* po, float* pml, float* of, float* lf) {
-  hipLaunchKernelGGL((decode_kernel<TQ, TC>), grid, dim3(NT), 0, st, (const TQ*)q, q_seq, reps, m,
-                     raw, raw_begin, n, per, S, sl2, H, po, pml, of, lf);
+static bool packed_rows(const lca_latent_t& t) {
+  return t.c != nullptr && t.dtype == LCA_BF16 &&
+         static_cast<const char*>(t.kr) == static_cast<const char*>(t.c) + 2 * D_C &&
+         t.kr_tok_stride == t.c_tok_stride && t.kr_seq_stride == t.c_seq_stride;
 }
 
 hipError_t launch_decode(const void* q, int q_dtype, int64_t q_seq_stride, int B, int H,
@@ -228,23 +534,49 @@ hipError_t launch_decode(const void* q, int q_dtype, int64_t q_seq_stride, int B
   const int HG = H / HB;
   const int64_t n = m + (raw_end - raw_begin);
   const DecodeSplit sp = decode_split(B, HG, n);
-  float* po = nullptr;
   float* pml = nullptr;
+  float* po = nullptr;
   if (sp.S > 1) {
     const size_t slots = (size_t)B * HG * sp.S * HB;
-    po = static_cast<float*>(workspace);
-    pml = po + slots * D_C;
+    pml = static_cast<float*>(workspace);
+    po = pml + slots * 2;
   }
   const float sl2 = sm_scale * 1.44269504088896340736f;
-  const Seg rs = to_seg(reps), ws = to_seg(raw);
-  const int cdt = (m > 0) ? reps.dtype : raw.dtype;
   dim3 grid((unsigned)sp.S, (unsigned)B, (unsigned)HG);
-  if (q_dtype == LCA_BF16) {
-    if (cdt == LCA_BF16) launch_dec_t<bf16_t, bf16_t>(grid, stream, q, q_seq_stride, rs, m, ws, raw_begin, n, sp.per_tiles, sp.S, sl2, H, po, pml, o_latent, lse);
-    else launch_dec_t<bf16_t, float>(grid, stream, q, q_seq_stride, rs, m, ws, raw_begin, n, sp.per_tiles, sp.S, sl2, H, po, pml, o_latent, lse);
+  const bool has_rep = m > 0, has_raw = raw_end > raw_begin;
+  const int64_t tok = has_rep ? reps.c_tok_stride : raw.c_tok_stride;
+  const bool fast = (!has_rep || packed_rows(reps)) && (!has_raw || packed_rows(raw)) &&
+                    (!has_rep || !has_raw || reps.c_tok_stride == raw.c_tok_stride) &&
+                    tok * 2 * DT < ((int64_t)1 << 31);
+  if (fast) {
+    DmaSrc src;
+    src.rep = has_rep ? static_cast<const char*>(reps.c) : nullptr;
+    src.raw = has_raw ? static_cast<const char*>(raw.c) + raw_begin * raw.c_tok_stride * 2 : nullptr;
+    src.tok = tok * 2;
+    src.m = m;
+    const int64_t rep_seq_b = m > 0 ? reps.c_seq_stride * 2 : 0;
+    const int64_t raw_seq_b = raw_end > raw_begin ? raw.c_seq_stride * 2 : 0;
+    if (q_dtype == LCA_BF16)
+      hipLaunchKernelGGL(decode_kernel<bf16_t>, grid, dim3(DNT), 0, stream, (const bf16_t*)q,
+                         q_seq_stride, src, rep_seq_b, raw_seq_b, n, sp.per_tiles, sp.S, sl2, H, po,
+                         pml, o_latent, lse);
+    else
+      hipLaunchKernelGGL(decode_kernel<float>, grid, dim3(DNT), 0, stream, (const float*)q,
+                         q_seq_stride, src, rep_seq_b, raw_seq_b, n, sp.per_tiles, sp.S, sl2, H, po,
+                         pml, o_latent, lse);
   } else {
-    if (cdt == LCA_BF16) launch_dec_t<float, bf16_t>(grid, stream, q, q_seq_stride, rs, m, ws, raw_begin, n, sp.per_tiles, sp.S, sl2, H, po, pml, o_latent, lse);
-    else launch_dec_t<float, float>(grid, stream, q, q_seq_stride, rs, m, ws, raw_begin, n, sp.per_tiles, sp.S, sl2, H, po, pml, o_latent, lse);
+    // general strides or f32 rows: register-staged kernel, 32-entry tiles
+    const Seg rs = to_seg(reps), ws = to_seg(raw);
+    const int cdt = (m > 0) ? reps.dtype : raw.dtype;
+#define LCA_STAGED(TQ, TC)                                                                       \
+  hipLaunchKernelGGL((decode_kernel_staged<TQ, TC>), grid, dim3(NT), 0, stream, (const TQ*)q,      \
+                     q_seq_stride, rs, m, ws, raw_begin, n, sp.per_tiles, sp.S, sl2, H, po,        \
+                     pml, o_latent, lse)
+    if (q_dtype == LCA_BF16 && cdt == LCA_BF16) LCA_STAGED(bf16_t, bf16_t);
+    else if (q_dtype == LCA_BF16) LCA_STAGED(bf16_t, float);
+    else if (cdt == LCA_BF16) LCA_STAGED(float, bf16_t);
+    else LCA_STAGED(float, float);
+#undef LCA_STAGED
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || sp.S == 1) return err;

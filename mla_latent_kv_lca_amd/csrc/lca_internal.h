@@ -27,8 +27,7 @@ hipError_t launch_condense(const lca_latent_t& cache, int B, int g, int64_t grou
                            hipStream_t stream);
 
 // ---- decode
-constexpr int DEC_TILE = 32;          // entries per tile
-constexpr int DEC_TARGET_BLOCKS = 512; // split-K aims for about this many workgroups
+constexpr int DEC_TARGET_BLOCKS = 256;   // split-K aims for about one workgroup per CU
 
 struct DecodeSplit {
   int S;         // splits per (sequence, head block)

@@ -77,16 +77,13 @@ __device__ __forceinline__ int pv_entry(int kg, int kk) {
   return kk < 4 ? 4 * kg + kk : 16 + 4 * kg + (kk - 4);
 }
 
-// Value product for one 128-column slab [d0, d0 + 128) of the tile:
+// Value product from row fragments: R[kk] holds 8 consecutive latent columns
+// (d = d0 + 8 col + 0..7) of tile entry pv_entry(kg, kk). Half-word shuffles
+// turn them into the k-major operands of V^T, then
 //   o[c] += V^T(d = d0 + 8 col + c) x P^T   for c = 0..7,
 // where pb holds P[head col][pv_entry(kg, kk)] as 8 packed bf16. Afterwards
 // o[c][r] accumulates O[head col][d0 + 32 kg + 8 r + c].
-__device__ __forceinline__ void pv_slab(const bf16_t* tile, int d0, int kg, int col, uint4 pb,
-                                        f32x4_t* o) {
-  uint4 R[8];
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk)
-    R[kk] = *reinterpret_cast<const uint4*>(tile + pv_entry(kg, kk) * LDS_ROW + d0 + 8 * col);
+__device__ __forceinline__ void pv_from_rows(const uint4 (&R)[8], uint4 pb, f32x4_t* o) {
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     const int w = c >> 1;
@@ -104,6 +101,17 @@ __device__ __forceinline__ void pv_slab(const bf16_t* tile, int d0, int kg, int 
     }
     o[c] = mfma16x16x32(a, pb, o[c]);
   }
+}
+
+// Value product for one 128-column slab [d0, d0 + 128) of a padded row-major
+// tile (LDS_ROW stride).
+__device__ __forceinline__ void pv_slab(const bf16_t* tile, int d0, int kg, int col, uint4 pb,
+                                        f32x4_t* o) {
+  uint4 R[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk)
+    R[kk] = *reinterpret_cast<const uint4*>(tile + pv_entry(kg, kk) * LDS_ROW + d0 + 8 * col);
+  pv_from_rows(R, pb, o);
 }
 
 // Online-softmax update for one tile. z[kk] are log2-domain logits of head
@@ -136,6 +144,40 @@ __device__ __forceinline__ float softmax_update(float (&z)[8], float& m_run, flo
   pb = make_uint4(pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3]), pack_bf2(p[4], p[5]),
                   pack_bf2(p[6], p[7]));
   return corr;
+}
+
+// Online softmax with a lazy reference point: the running max m_run (log2
+// domain) only moves when a logit exceeds it by more than LAZY_LOG2, and only
+// then are the running sum and the accumulators o rescaled. In between, p =
+// 2^(z - m_run) <= 2^LAZY_LOG2, which bf16 and fp32 hold easily; the final
+// normalisation by l_run is exact either way. The test is uniform across a
+// head's lanes, and skipping the rescale saves the 32 multiplies of o per tile.
+constexpr float LAZY_LOG2 = 8.0f;
+__device__ __forceinline__ void softmax_update_lazy(float (&z)[8], float& m_run, float& l_run,
+                                                    uint4& pb, f32x4_t* o) {
+  float tmax = z[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, z[i]);
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  if (__builtin_amdgcn_ballot_w64(tmax > m_run + LAZY_LOG2) != 0) {  // some head moves
+    const float m_new = fmaxf(m_run, tmax);
+    const float corr = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= corr;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[c] *= corr;
+    m_run = m_new;
+  }
+  const float m_ref = m_run == -INFINITY ? 0.f : m_run;  // nothing visible yet: p = 0
+  float p[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(z[i] - m_ref);
+  float ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  ps += __shfl_xor(ps, 16);
+  ps += __shfl_xor(ps, 32);
+  l_run += ps;
+  pb = make_uint4(pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3]), pack_bf2(p[4], p[5]),
+                  pack_bf2(p[6], p[7]));
 }
 
 }  // namespace lca
