@@ -24,8 +24,12 @@
 namespace lca {
 
 // ---------------------------------------------------------------- K0 -------
-constexpr int QBAR_THREADS = 288;  // 72 column chunks of 8 x 4 row phases
+constexpr int QBAR_PH = 14;                  // row phases
+constexpr int QBAR_THREADS = 72 * QBAR_PH;   // 72 column chunks of 8 x 14 row phases
 
+// One workgroup per summary query: thread (chunk c, phase p) sums rows
+// p, p + 14, ... of the g*H query rows, eight loads in flight at a time; the
+// 14 phase partials are then added in phase order.
 template <typename TQ>
 __global__ __launch_bounds__(QBAR_THREADS) void qbar_kernel(
     const TQ* __restrict__ q, int64_t q_seq, int64_t q_tok, int H, int g, int64_t row0,
@@ -35,20 +39,32 @@ __global__ __launch_bounds__(QBAR_THREADS) void qbar_kernel(
   const TQ* base = q + (int64_t)b * q_seq + (row0 + (int64_t)jq * step) * q_tok + ch * 8;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const int rows = g * H;
-  for (int r = ph; r < rows; r += 4) {
-    const int tok = r / H, h = r - tok * H;
-    float v[8];
-    load8_f32(base + (int64_t)tok * q_tok + h * D_ROW, v);
+  for (int r0 = ph; r0 < rows; r0 += 8 * QBAR_PH) {
+    float v[8][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    for (int u = 0; u < 8; ++u) {
+      const int r = r0 + u * QBAR_PH;
+      if (r < rows) {
+        const int tok = r / H, h = r - tok * H;
+        load8_f32(base + (int64_t)tok * q_tok + h * D_ROW, v[u]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[u][i] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[u][i];
   }
-  __shared__ float sh[4][D_ROW];
+  __shared__ float sh[QBAR_PH][D_ROW];
 #pragma unroll
   for (int i = 0; i < 8; ++i) sh[ph][ch * 8 + i] = acc[i];
   __syncthreads();
   const float inv = 1.0f / (float)rows;
   for (int c = t; c < D_ROW; c += QBAR_THREADS) {
-    const float s = ((sh[0][c] + sh[1][c]) + sh[2][c]) + sh[3][c];
+    float s = sh[0][c];
+    for (int p = 1; p < QBAR_PH; ++p) s += sh[p][c];
     qbar[((int64_t)b * n_q + jq) * D_ROW + c] = s * inv;
   }
 }

@@ -438,67 +438,88 @@ __global__ __launch_bounds__(NT) void decode_kernel_staged(
   }
 }
 
-// Combine S split partials of one (sequence, head) for 128 output columns:
-// o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, in split order.
+// Combine the S split partials of a (sequence, head):
+//   o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s,
+// always in split order. Few splits: one thread per 4 output columns.
+constexpr int MERGE_SMALL_S = 32;
+__global__ __launch_bounds__(256) void merge_small_kernel(const float* __restrict__ part_o,
+                                                          const float* __restrict__ part_ml, int S,
+                                                          int B, int H, float* __restrict__ o,
+                                                          float* __restrict__ lse) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= (int64_t)B * H * (D_C / 4)) return;
+  const int c4 = (int)(gid % (D_C / 4));
+  const int64_t bh = gid / (D_C / 4);
+  const int head = (int)(bh % H), b = (int)(bh / H);
+  const int HG = H / HB, hg = head / HB, hh = head % HB;
+  const int64_t slot0 = ((int64_t)b * HG + hg) * S;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, part_ml[((slot0 + s) * HB + hh) * 2]);
+  float L = 0.f;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < S; ++s) {
+    const int64_t slot = (slot0 + s) * HB + hh;
+    const float ms = part_ml[slot * 2];
+    const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - M);
+    L = fmaf(wgt, part_ml[slot * 2 + 1], L);
+    const float4 v = reinterpret_cast<const float4*>(part_o + slot * D_C)[c4];
+    a.x = fmaf(wgt, v.x, a.x); a.y = fmaf(wgt, v.y, a.y);
+    a.z = fmaf(wgt, v.z, a.z); a.w = fmaf(wgt, v.w, a.w);
+  }
+  const float inv = 1.0f / L;
+  reinterpret_cast<float4*>(o + ((int64_t)b * H + head) * D_C)[c4] =
+      make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
+  if (lse != nullptr && c4 == 0) lse[(int64_t)b * H + head] = (M + log2f(L)) * 0.69314718055994530942f;
+}
+
+// Many splits (one long sequence): workgroup per (32 columns, head, sequence),
+// 32 split phases x 8 threads of 4 columns; phase partials added in order.
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml, int S,
                                                     int H, float* __restrict__ o,
                                                     float* __restrict__ lse) {
   const int dchunk = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
   const int HG = H / HB, hg = head / HB, hh = head % HB;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, ph = t >> 3, c4 = t & 7;
   const int64_t slot0 = ((int64_t)b * HG + hg) * S;  // slot(s) = (slot0 + s) * HB + hh
-  __shared__ float red[256];
-  __shared__ float4 acc_sh[8][32];
+  __shared__ float red[2][32];
+  __shared__ float4 acc_sh[32][8];
 
   float mx = -INFINITY;
-  for (int s = t; s < S; s += 256) mx = fmaxf(mx, part_ml[((slot0 + s) * HB + hh) * 2]);
-  red[t] = mx;
+  for (int s = ph; s < S; s += 32) mx = fmaxf(mx, part_ml[((slot0 + s) * HB + hh) * 2]);
+  if (c4 == 0) red[0][ph] = mx;
   __syncthreads();
-  for (int k = 128; k > 0; k >>= 1) {
-    if (t < k) red[t] = fmaxf(red[t], red[t + k]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  __syncthreads();
+  float M = red[0][0];
+  for (int p = 1; p < 32; ++p) M = fmaxf(M, red[0][p]);
   float ls = 0.f;
-  for (int s = t; s < S; s += 256) {
-    const float* ml = part_ml + ((slot0 + s) * HB + hh) * 2;
-    ls += exp2f(ml[0] - M) * ml[1];
-  }
-  red[t] = ls;
-  __syncthreads();
-  for (int k = 128; k > 0; k >>= 1) {
-    if (t < k) red[t] += red[t + k];
-    __syncthreads();
-  }
-  const float Ltot = red[0];
-
-  const int ph = t >> 5, c4 = t & 31;
-  const int d = 128 * dchunk + 4 * c4;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = ph; s < S; s += 8) {
+  const int d = 32 * dchunk + 4 * c4;
+  for (int s = ph; s < S; s += 32) {
     const int64_t slot = (slot0 + s) * HB + hh;
-    const float wgt = exp2f(part_ml[slot * 2] - M);
+    const float ms = part_ml[slot * 2];
+    const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - M);
+    ls = fmaf(wgt, part_ml[slot * 2 + 1], ls);
     const float4 v = *reinterpret_cast<const float4*>(part_o + slot * D_C + d);
     a.x = fmaf(wgt, v.x, a.x); a.y = fmaf(wgt, v.y, a.y);
     a.z = fmaf(wgt, v.z, a.z); a.w = fmaf(wgt, v.w, a.w);
   }
+  if (c4 == 0) red[1][ph] = ls;
   acc_sh[ph][c4] = a;
   __syncthreads();
   if (ph == 0) {
+    float Lt = red[1][0];
     float4 r = acc_sh[0][c4];
-#pragma unroll
-    for (int p = 1; p < 8; ++p) {
+    for (int p = 1; p < 32; ++p) {
+      Lt += red[1][p];
       const float4 v = acc_sh[p][c4];
       r.x += v.x; r.y += v.y; r.z += v.z; r.w += v.w;
     }
-    const float inv = 1.0f / Ltot;
+    const float inv = 1.0f / Lt;
     *reinterpret_cast<float4*>(o + ((int64_t)b * H + head) * D_C + d) =
         make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv);
+    if (lse != nullptr && dchunk == 0 && c4 == 0)
+      lse[(int64_t)b * H + head] = (M + log2f(Lt)) * 0.69314718055994530942f;
   }
-  if (lse != nullptr && dchunk == 0 && t == 0)
-    lse[(int64_t)b * H + head] = (M + log2f(Ltot)) * 0.69314718055994530942f;
 }
 
 DecodeSplit decode_split(int B, int HG, int64_t n_entries) {
@@ -580,8 +601,14 @@ hipError_t launch_decode(const void* q, int q_dtype, int64_t q_seq_stride, int B
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || sp.S == 1) return err;
-  hipLaunchKernelGGL(merge_kernel, dim3(4, (unsigned)H, (unsigned)B), dim3(256), 0, stream, po, pml,
-                     sp.S, H, o_latent, lse);
+  if (sp.S <= MERGE_SMALL_S) {
+    const int64_t n = (int64_t)B * H * (D_C / 4);
+    hipLaunchKernelGGL(merge_small_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                       po, pml, sp.S, B, H, o_latent, lse);
+  } else {
+    hipLaunchKernelGGL(merge_kernel, dim3(D_C / 32, (unsigned)H, (unsigned)B), dim3(256), 0, stream,
+                       po, pml, sp.S, H, o_latent, lse);
+  }
   return hipGetLastError();
 }
 
