@@ -11,99 +11,16 @@
 //                        direct loads, one workgroup per CU (details below).
 //  decode_kernel_staged  any strides / f32 rows: register-staged 32-entry tiles.
 //  merge_kernel          combines split-K partial results in split order.
-#include "lca_tile.h"
+#include "lca_stream.h"
 
 namespace lca {
 
 constexpr int SX_ROW = 36;                     // floats per head row of the staged score exchange
-constexpr int DNW = 4;                         // wavefronts per decode workgroup (2 x 2)
+constexpr int DNW = SNW;                       // wavefronts per decode workgroup (2 x 2)
 constexpr int DNT = 64 * DNW;                  // threads per decode workgroup
-constexpr int DT = 32;                         // entries per tile: two 16-entry halves
+constexpr int DT = STILE;                      // entries per tile: two 16-entry halves
 constexpr int DBUF = 4;                        // LDS ring depth (tiles)
-constexpr int DT_ELEMS = DT * D_ROW;           // dense tile, 36,864 bytes
-constexpr int DMA_PER_WAVE = DT * (D_ROW / 8) / 64 / DNW;  // 9 wave-instructions per tile per wave
-
-__device__ __forceinline__ uint32_t lds_off(const void* p) {
-  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
-}
-
-// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane.
-// Issued from asm so that the compiler does not drain the ring before every
-// LDS read; completion is tracked with explicit vmcnt waits. m0 is saved and
-// restored around the load, so the compiler's own use of m0 is untouched.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_block) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(g), "s"(lds_block)
-      : "memory");
-}
-// wait until at most `newer` tiles issued after the one wanted are in flight
-__device__ __forceinline__ void wait_dma_newer(int newer) {
-  static_assert(DMA_PER_WAVE == 9, "vmcnt immediates assume 9 loads per tile per wave");
-  if (newer >= 3) asm volatile("s_waitcnt vmcnt(27)" ::: "memory");
-  else if (newer == 2) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-  else if (newer == 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-__device__ __forceinline__ void barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-// An empty asm that reads the four registers: the compiler must have waited
-// for the load that produced them before this point.
-__device__ __forceinline__ void retire(const uint4& v) {
-  asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w));
-}
-
-// Tile rows are dense (576 bf16); the 16-byte chunk c of row r sits at chunk
-// position c ^ (r & 7), which spreads the 16 rows read by one MFMA fragment
-// over distinct LDS banks.
-__device__ __forceinline__ int chunk_pos(int r, int c) { return r * (D_ROW / 8) + (c ^ (r & 7)); }
-
-// Packed rows (k_R right after c_KV, one token stride) of the two segments of
-// one sequence: entries [0, m) are representative rows, the rest raw rows.
-struct DmaSrc {
-  const char* rep;  // representative rows of sequence 0
-  const char* raw;  // raw rows of sequence 0, starting at raw_begin
-  int64_t tok;      // token stride in bytes, shared by both segments
-  int64_t m;
-};
-
-// LDS slot P = 64 j + lane (j = w + DNW i) of a tile holds 16-byte chunk
-// col = (P % 72) ^ (row & 7) of tile row row = P / 72; its byte offset from
-// the tile's first row is row * token stride + 16 col, fixed for every tile.
-__device__ __forceinline__ void slot_rowcol(int w, int i, int lane, int& row, int& col) {
-  const int P = 64 * (w + DNW * i) + lane;
-  row = P / 72;
-  col = (P - row * 72) ^ (row & 7);
-}
-
-// Issue the DMA of tile entries [e0, e0 + DT) into `buf`. Full tiles inside
-// one segment use uniform row bases plus per-lane offsets; the tile that
-// straddles the representative / raw boundary and the last, partial tile
-// compute each row, reloading the last valid row past e_end (those logits
-// are masked, so any finite row will do).
-__device__ __forceinline__ void tile_dma(const DmaSrc& src, int64_t e0, int64_t e_end,
-                                         const bf16_t* buf, int w, int lane,
-                                         const uint32_t (&off)[DMA_PER_WAVE]) {
-  const uint32_t base = lds_off(buf);
-  if (e0 + DT <= e_end && (e0 + DT <= src.m || e0 >= src.m)) {
-    const char* b0 = e0 < src.m ? src.rep + e0 * src.tok : src.raw + (e0 - src.m) * src.tok;
-#pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i) dma16(b0 + off[i], base + 1024u * (w + DNW * i));
-  } else {
-    const int valid = (int)min((int64_t)DT, e_end - e0);
-    for (int i = 0; i < DMA_PER_WAVE; ++i) {
-      int row, col;
-      slot_rowcol(w, i, lane, row, col);
-      const int64_t e = e0 + min(row, valid - 1);
-      const char* p = e < src.m ? src.rep + e * src.tok : src.raw + (e - src.m) * src.tok;
-      dma16(p + 16 * col, base + 1024u * (w + DNW * i));
-    }
-  }
-}
+constexpr int DT_ELEMS = STILE_ELEMS;          // dense tile, 36,864 bytes
 
 // decode_kernel: one workgroup of 4 wavefronts per (split, sequence, head
 // block), one workgroup per CU. Entries stream from HBM straight into a

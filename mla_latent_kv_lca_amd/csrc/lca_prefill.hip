@@ -14,14 +14,15 @@
 // registers), runs the online softmax in registers (four lanes per head) and
 // accumulates O for all 512 latent columns (32 MFMA 16x16x32 per tile).
 // Workgroups are issued heaviest (latest tokens) first.
-#include "lca_tile.h"
+#include "lca_stream.h"
 
 namespace lca {
 
 constexpr int PF_TOK = 4;  // query tokens per workgroup (one per wave)
 
+// Register-staged variant for strided or f32 rows, one token (16 rows) per wave.
 template <typename TQ, typename TC, typename TO>
-__global__ __launch_bounds__(NT) void prefill_kernel(
+__global__ __launch_bounds__(NT) void prefill_kernel_staged(
     const TQ* __restrict__ q, int64_t q_tok, int64_t chunk_start, int C, int H, Seg reps,
     int64_t m, Seg raw, int64_t raw_begin, float scale_log2, TO* __restrict__ o,
     float* __restrict__ lse) {
@@ -103,11 +104,159 @@ __global__ __launch_bounds__(NT) void prefill_kernel(
     lse[(int64_t)i_tok * H + head] = (m_run + log2f(l_run)) * 0.69314718055994530942f;
 }
 
+// prefill_kernel: the fast path for packed bf16 rows. Workgroup = 4
+// wavefronts = 2 pairs; pair p holds 2 query tokens x 16 heads = 32 query
+// rows, so every LDS fragment feeds a 32x32x16 MFMA. Entry tiles of 32 rows
+// stream HBM -> LDS by direct loads into a 3-slot ring (two tiles in flight).
+// Within a pair, wave k
+//   forms the partial S^T = K Q^T over query columns [288 k, 288 k + 288)
+//   (18 MFMA 32x32x16, those query columns in registers), adds its partner's
+//   partial read through LDS in a fixed order (columns 0..287 first), so both
+//   waves hold identical scores and run the same online softmax (two lanes per
+//   query row; the reference max only moves when a row's max grows by more
+//   than 2^8, so the accumulators are rarely rescaled), and
+//   accumulates O^T += V^T P^T for latent columns [256 k, 256 k + 256)
+//   (16 MFMA 32x32x16; P comes straight from the score registers, V^T from
+//   row fragments with half-word shuffles).
+constexpr int PF2_TOK = 4;  // query tokens per workgroup
+constexpr int PBUF = 3;     // LDS ring depth (tiles)
+
+template <typename TQ, typename TO>
+__global__ __launch_bounds__(256) void prefill_kernel(
+    const TQ* __restrict__ q, int64_t q_tok, int64_t chunk_start, int C, int H, DmaSrc src,
+    int64_t m, int64_t raw_begin, float scale_log2, TO* __restrict__ o, float* __restrict__ lse) {
+  __shared__ __align__(16) bf16_t ring[PBUF][STILE_ELEMS];
+  __shared__ __align__(16) float sx[4][16][64];  // partial scores [wave][r][lane]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pr = w >> 1, kh = w & 1;  // pair, column half
+  const int h32 = lane >> 5, r32 = lane & 31;
+  const int blk = (int)gridDim.x - 1 - (int)blockIdx.x;  // heavy workgroups first
+  const int hg = blockIdx.y;
+  const int tok0 = blk * PF2_TOK;
+  const int i_tok = tok0 + 2 * pr + (r32 >> 4);  // chunk row of this lane's query row
+  const bool active = i_tok < C;
+  const int i_ld = active ? i_tok : C - 1;
+  const int i_last = min(tok0 + PF2_TOK, C) - 1;
+  // entries visible to chunk row i: m + (chunk_start + i - raw_begin + 1)
+  const int64_t vis0 = m + (chunk_start - raw_begin + 1);
+  const int64_t n_blk = vis0 + i_last, n_min = vis0 + tok0, n_mine = vis0 + i_ld;
+  const int n_tiles = (int)((n_blk + STILE - 1) / STILE);
+
+  uint32_t off[DMA_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < DMA_PER_WAVE; ++i) {
+    int row, col16;
+    slot_rowcol(w, i, lane, row, col16);
+    off[i] = (uint32_t)(row * src.tok) + 16u * col16;
+  }
+#pragma unroll
+  for (int t = 0; t < PBUF - 1; ++t)
+    if (t < n_tiles) tile_dma(src, (int64_t)t * STILE, n_blk, ring[t], w, lane, off);
+
+  // Q^T operand: query row (token i_ld, head hg*16 + r32%16), k = 288 kh + 16 ks + 8 h32 ..
+  const TQ* qh = q + (int64_t)i_ld * q_tok + (int64_t)(hg * HB + (r32 & 15)) * D_ROW + 288 * kh + 8 * h32;
+  uint4 qf[18];
+#pragma unroll
+  for (int ks = 0; ks < 18; ++ks) qf[ks] = load8_bf16(qh + 16 * ks);
+#pragma unroll
+  for (int ks = 0; ks < 18; ++ks) retire(qf[ks]);  // wait here once, not inside the loop
+
+  f32x16_t oacc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[c][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int64_t e0 = (int64_t)t * STILE;
+    wait_dma_newer(min(n_tiles - 1 - t, PBUF - 2));
+    barrier();  // tile t landed for every wave; tile t-1's slot and sx are free
+    if (t + PBUF - 1 < n_tiles)
+      tile_dma(src, e0 + (int64_t)(PBUF - 1) * STILE, n_blk, ring[(t + PBUF - 1) % PBUF], w, lane, off);
+    const bf16_t* tile = ring[t % PBUF];
+
+    // partial S^T[entry 8(r/4) + 4 h32 + r%4][query row r32] over this half
+    f32x16_t sa, sb;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { sa[r] = 0.f; sb[r] = 0.f; }
+#pragma unroll
+    for (int ks = 0; ks < 18; ks += 2) {
+      sa = mfma32x32x16(*reinterpret_cast<const uint4*>(tile + 8 * chunk_pos(r32, 36 * kh + 2 * ks + h32)), qf[ks], sa);
+      sb = mfma32x32x16(*reinterpret_cast<const uint4*>(tile + 8 * chunk_pos(r32, 36 * kh + 2 * ks + 2 + h32)), qf[ks + 1], sb);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sx[w][r][lane] = sa[r] + sb[r];
+    barrier();
+    float z[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) z[r] = (sx[2 * pr][r][lane] + sx[2 * pr + 1][r][lane]) * scale_log2;
+    if (e0 + STILE > n_min) {  // causal boundary inside this tile
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (e0 + 8 * (r >> 2) + 4 * h32 + (r & 3) >= n_mine) z[r] = -INFINITY;
+    }
+    float tmax = z[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, z[r]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    if (__builtin_amdgcn_ballot_w64(tmax > m_run + LAZY_LOG2) != 0) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float corr = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= corr;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) oacc[c] *= corr;
+      m_run = m_new;
+    }
+    const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(z[r] - m_ref);
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ps += p[r];
+    ps += __shfl_xor(ps, 32);
+    l_run += ps;
+
+    // O^T += V^T P^T for columns [256 kh, 256 kh + 256): per entry k-step kap,
+    // slot (h32, j) <-> entry 16 kap + 8 (j/4) + 4 h32 + j%4 (the lane's p[8 kap + j])
+#pragma unroll
+    for (int kap = 0; kap < 2; ++kap) {
+      const uint4 pb = make_uint4(pack_bf2(p[8 * kap + 0], p[8 * kap + 1]), pack_bf2(p[8 * kap + 2], p[8 * kap + 3]),
+                                  pack_bf2(p[8 * kap + 4], p[8 * kap + 5]), pack_bf2(p[8 * kap + 6], p[8 * kap + 7]));
+      uint4 R[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int ent = 16 * kap + 8 * (j >> 2) + 4 * h32 + (j & 3);
+        R[j] = *reinterpret_cast<const uint4*>(tile + 8 * chunk_pos(ent, 32 * kh + r32));
+      }
+      pv_from_rows32(R, pb, oacc);
+    }
+  }
+
+  if (!active) return;
+  // oacc[c][r] = O[query row r32][256 kh + 8 (8(r/4) + 4 h32 + r%4) + c]
+  const int head = hg * HB + (r32 & 15);
+  const float inv = 1.0f / l_run;
+  TO* dst = o + ((int64_t)i_tok * H + head) * D_C + 256 * kh;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float v[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = oacc[c][r] * inv;
+    store8(dst + 8 * (8 * (r >> 2) + 4 * h32 + (r & 3)), v);
+  }
+  if (lse != nullptr && h32 == 0 && kh == 0)
+    lse[(int64_t)i_tok * H + head] = (m_run + __log2f(l_run)) * 0.69314718055994530942f;
+}
+
 template <typename TQ, typename TC, typename TO>
 static void launch_pf_t(dim3 grid, hipStream_t st, const void* q, int64_t q_tok, int64_t cs,
                         int C, int H, Seg reps, int64_t m, Seg raw, int64_t rb, float sl2, void* o,
                         float* lse) {
-  hipLaunchKernelGGL((prefill_kernel<TQ, TC, TO>), grid, dim3(NT), 0, st, (const TQ*)q, q_tok, cs,
+  hipLaunchKernelGGL((prefill_kernel_staged<TQ, TC, TO>), grid, dim3(NT), 0, st, (const TQ*)q, q_tok, cs,
                      C, H, reps, m, raw, rb, sl2, (TO*)o, lse);
 }
 
@@ -119,11 +268,40 @@ static void launch_pf_o(int o_dtype, dim3 grid, hipStream_t st, const void* q, i
   else launch_pf_t<TQ, TC, float>(grid, st, q, q_tok, cs, C, H, reps, m, raw, rb, sl2, o, lse);
 }
 
+static bool packed_rows_pf(const lca_latent_t& t) {
+  return t.c != nullptr && t.dtype == LCA_BF16 &&
+         static_cast<const char*>(t.kr) == static_cast<const char*>(t.c) + 2 * D_C &&
+         t.kr_tok_stride == t.c_tok_stride;
+}
+
+template <typename TQ>
+static void launch_pf2(int o_dtype, dim3 grid, hipStream_t st, const void* q, int64_t q_tok,
+                       int64_t cs, int C, int H, const DmaSrc& src, int64_t m, int64_t rb, float sl2,
+                       void* o, float* lse) {
+  if (o_dtype == LCA_BF16)
+    hipLaunchKernelGGL((prefill_kernel<TQ, bf16_t>), grid, dim3(256), 0, st, (const TQ*)q, q_tok, cs, C, H, src, m, rb, sl2, (bf16_t*)o, lse);
+  else
+    hipLaunchKernelGGL((prefill_kernel<TQ, float>), grid, dim3(256), 0, st, (const TQ*)q, q_tok, cs, C, H, src, m, rb, sl2, (float*)o, lse);
+}
+
 hipError_t launch_prefill(const void* q, int q_dtype, int64_t q_tok_stride, int64_t chunk_start,
                           int C, int H, const lca_latent_t& reps, int64_t m,
                           const lca_latent_t& raw, int64_t raw_begin, float sm_scale,
                           void* o_latent, int o_dtype, float* lse, hipStream_t stream) {
   const float sl2 = sm_scale * 1.44269504088896340736f;
+  const bool fast = packed_rows_pf(raw) && (m == 0 || (packed_rows_pf(reps) && reps.c_tok_stride == raw.c_tok_stride)) &&
+                    raw.c_tok_stride * 2 * STILE < ((int64_t)1 << 31);
+  if (fast) {
+    DmaSrc src;
+    src.rep = m > 0 ? static_cast<const char*>(reps.c) : nullptr;
+    src.raw = static_cast<const char*>(raw.c) + raw_begin * raw.c_tok_stride * 2;
+    src.tok = raw.c_tok_stride * 2;
+    src.m = m;
+    dim3 grid((unsigned)((C + PF2_TOK - 1) / PF2_TOK), (unsigned)(H / HB));
+    if (q_dtype == LCA_BF16) launch_pf2<bf16_t>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, src, m, raw_begin, sl2, o_latent, lse);
+    else launch_pf2<float>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, src, m, raw_begin, sl2, o_latent, lse);
+    return hipGetLastError();
+  }
   const Seg rs = to_seg(reps), ws = to_seg(raw);
   const int cdt = raw.dtype;
   dim3 grid((unsigned)((C + PF_TOK - 1) / PF_TOK), (unsigned)(H / HB));

@@ -103,6 +103,29 @@ __device__ __forceinline__ void pv_from_rows(const uint4 (&R)[8], uint4 pb, f32x
   }
 }
 
+// 32-row variant: R[j] holds latent columns d0 + 8 (l%32) + 0..7 of the entry
+// that k slot (l/32, j) stands for; o[c] += V^T(d = d0 + 8 (l%32) + c) x P^T
+// with 32x32x16 MFMAs, pb holding P[query row l%32][slot entries].
+__device__ __forceinline__ void pv_from_rows32(const uint4 (&R)[8], uint4 pb, f32x16_t* o) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int w = c >> 1;
+    uint4 a;
+    if (c & 1) {
+      a.x = hi_pair(u4_get(R[0], w), u4_get(R[1], w));
+      a.y = hi_pair(u4_get(R[2], w), u4_get(R[3], w));
+      a.z = hi_pair(u4_get(R[4], w), u4_get(R[5], w));
+      a.w = hi_pair(u4_get(R[6], w), u4_get(R[7], w));
+    } else {
+      a.x = lo_pair(u4_get(R[0], w), u4_get(R[1], w));
+      a.y = lo_pair(u4_get(R[2], w), u4_get(R[3], w));
+      a.z = lo_pair(u4_get(R[4], w), u4_get(R[5], w));
+      a.w = lo_pair(u4_get(R[6], w), u4_get(R[7], w));
+    }
+    o[c] = mfma32x32x16(a, pb, o[c]);
+  }
+}
+
 // Value product for one 128-column slab [d0, d0 + 128) of a padded row-major
 // tile (LDS_ROW stride).
 __device__ __forceinline__ void pv_slab(const bf16_t* tile, int d0, int kg, int col, uint4 pb,
