@@ -144,10 +144,12 @@ size_t mla_latent_attn_decode_workspace_size(int32_t B, int32_t H, int64_t max_e
  *  lse[b, h] = log(sum_e exp(z_e))    (fp32 [B, H], optional).
  *  The per-head value is o_latent[b, h] @ W_UV[h] (mla_up_proj).
  *  workspace >= mla_latent_attn_decode_workspace_size(B, H, m + raw_end -
- *  raw_begin) bytes, 16-byte aligned. It holds split-K partial results and
- *  one arrival counter per (sequence, 16-head block): zero-fill it once after
- *  allocating it (hipMemset); every call leaves the counters at zero again.
- *  Calls that run concurrently must not share a workspace. */
+ *  raw_begin) bytes, 16-byte aligned, owned by the caller. When the entries
+ *  are split across several workgroups it holds their partial results
+ *  (per split: running max and sum, then the unnormalised 512-wide output),
+ *  which a second kernel merges; every value read there was written by the
+ *  same call, so no initialisation is needed. Calls that run concurrently
+ *  must not share a workspace. */
 int mla_latent_attn_decode(const void* q, int32_t q_dtype, int64_t q_seq_stride, int32_t B,
                            int32_t H, const lca_latent_t* reps, int64_t m,
                            const lca_latent_t* raw, int64_t raw_begin, int64_t raw_end,

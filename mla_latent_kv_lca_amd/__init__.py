@@ -156,17 +156,17 @@ def mla_latent_attn_decode_workspace_size(B: int, H: int, max_entries: int) -> i
 
 
 def _workspace(nbytes: int, like: torch.Tensor, ws):
-    """Caller's workspace, or a fresh zero-filled one (decode's split-K
-    arrival counters must start at zero; the kernels leave them at zero)."""
+    """Caller's workspace, or a fresh one (no initialisation is needed)."""
     if ws is not None:
         return ws
-    return torch.zeros(max(16, (nbytes + 15) // 16 * 16), dtype=torch.uint8, device=like.device)
+    return torch.empty(max(16, (nbytes + 15) // 16 * 16), dtype=torch.uint8, device=like.device)
 
 
 def decode_workspace(B: int, H: int, max_entries: int, device="cuda") -> torch.Tensor:
-    """Zero-filled workspace for mla_latent_attn_decode, reusable across calls."""
+    """Workspace for mla_latent_attn_decode (any contents), reusable across
+    calls that do not overlap."""
     n = mla_latent_attn_decode_workspace_size(B, H, max_entries)
-    return torch.zeros(max(16, (n + 15) // 16 * 16), dtype=torch.uint8, device=device)
+    return torch.empty(max(16, (n + 15) // 16 * 16), dtype=torch.uint8, device=device)
 
 
 def lca_condense(cache: LatentT, B: int, g: int, group_begin: int, n_groups: int,

@@ -1,0 +1,187 @@
+"""GPU parity at the full workload sizes, in the launch configurations the
+benchmark uses, on outputs the oracle can compute one by one (sampled groups,
+sampled sequences, sampled query rows), plus the incremental decode loop of
+the million-token workload checked step by step at a small size.
+
+Inputs: lca_inputs (seeded, bf16-rounded on the host); expected values come
+only from the oracle, fed the GPU's own condensed rows where the attention is
+checked (so a legitimate near-tie anchor cannot cascade).
+"""
+import numpy as np
+import pytest
+import torch
+
+import lca_inputs as li
+import mla_latent_kv_lca_amd as lca
+from oracle import lca_oracle as O
+from tests.gpu_util import TOL, anchors_agree, assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+H, G, W = 16, 16, 1024
+
+
+def _packed(c, kr):
+    t = torch.empty(c.shape[:-1] + (576,), dtype=torch.bfloat16, device="cuda")
+    for b in range(c.shape[0]):  # upload sequence by sequence to bound host temporaries
+        t[b] = torch.from_numpy(np.concatenate([c[b], kr[b]], -1)).to("cuda", torch.bfloat16)
+    return t
+
+
+@pytest.mark.timeout(400)
+def test_batched_decode_32x32k_sampled():
+    """B = 32 sequences x L = 32,768: condense every group, one decode step."""
+    B, L = 32, 32768
+    c, kr = li.latent_cache(2, B, L)
+    li.plant_needles(2, c, kr, 4, 14.0, 0, L)
+    qh = li.queries(2, B, G, H, rho=0.5)
+    qd = li.queries(2, B, 1, H, rho=0.5, stream=1)[:, 0]
+    p = O.plan(L, W, G)
+    m = p["m"]
+    cache = _packed(c, kr)
+    reps = torch.empty((B, m, 576), dtype=torch.bfloat16, device="cuda")
+    anchor = torch.empty((B, m), dtype=torch.int32, device="cuda")
+    alpha = torch.empty((B, m, G), dtype=torch.float32, device="cuda")
+    lca.lca_condense(lca.packed_latent(cache), B, G, 0, m, dev(qh), 0, 0, 1.0,
+                     lca.packed_latent(reps), anchor, alpha)
+    o = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    ws = lca.decode_workspace(B, H, p["n_entries"])
+    lca.mla_latent_attn_decode(dev(qd), lca.packed_latent(reps), m, lca.packed_latent(cache),
+                               p["raw_begin"], L, 1.0, o, lse, ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    r = host(reps)
+    ga = host(anchor).astype(np.int64)
+    rng = np.random.default_rng(0)
+    for b, j in zip(rng.integers(0, B, 96), rng.integers(0, m, 96)):
+        rc, rk, ra, ralpha, s = O.condense(c[b:b + 1], kr[b:b + 1], qh[b:b + 1], G, int(j), 1, 0, 0, 1.0)
+        assert_close(r[b, j, :512], rc[0, 0], what=f"rep ({b},{j})")
+        assert_close(host(alpha[b, j]), ralpha[0, 0], tol=1e-5, what="alpha")
+        anchors_agree(ga[b, j:j + 1], ra[0], O.top2_margin(s[0]))
+        np.testing.assert_array_equal(r[b, j, 512:], kr[b, ga[b, j]])
+    for b in (0, 13, 31):
+        ro, rl = O.decode(qd[b:b + 1], r[b:b + 1, :, :512], r[b:b + 1, :, 512:], m,
+                          c[b:b + 1], kr[b:b + 1], p["raw_begin"], L, 1.0)
+        assert_close(host(o[b]), ro[0], what=f"o_latent seq {b}")
+        assert_close(host(lse[b]), rl[0], what=f"lse seq {b}")
+
+
+def test_incremental_decode_loop_matches_oracle():
+    """Decode steps that append a row each and condense every newly
+    completed group with the last g decode queries (frozen representatives)."""
+    L0, S, w, g = 1300, 40, 1024, 16
+    c0, k0 = li.latent_cache(5, 1, L0 + S)
+    li.plant_needles(5, c0, k0, 3, 14.0, 0, L0 + S)
+    qhist = li.queries(5, 1, g, H, rho=0.5)[0]
+    steps = li.queries(5, 1, S, H, rho=0.5, stream=2)[0]
+    ro, rl, _, _, m_ref = O.decode_loop(c0[0, :L0], k0[0, :L0], qhist, steps, c0[0, L0:], k0[0, L0:],
+                                        w, g, 1.0)
+    cache = _packed(c0, k0)           # rows are appended by advancing L
+    qall = dev(np.concatenate([qhist, steps])[None])  # [1, g + S, H, 576]
+    m_cap = O.plan(L0 + S, w, g)["m"]
+    reps = torch.empty((1, m_cap, 576), dtype=torch.bfloat16, device="cuda")
+    anchor = torch.empty((1, m_cap), dtype=torch.int32, device="cuda")
+    L = L0
+    m = O.plan(L, w, g)["m"]
+    lca.lca_condense(lca.packed_latent(cache), 1, g, 0, m, qall, 0, 0, 1.0,
+                     lca.packed_latent(reps), anchor)
+    o = torch.empty((1, H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((1, H), dtype=torch.float32, device="cuda")
+    ws = lca.decode_workspace(1, H, L0 + S)
+    outs, lses = [], []
+    for st in range(S):
+        lca.mla_latent_attn_decode(qall[:, g + st], lca.packed_latent(reps) if m else None, m,
+                                   lca.packed_latent(cache), m * g, L, 1.0, o, lse, ws)
+        outs.append(o.clone())
+        lses.append(lse.clone())
+        L += 1
+        if L - w >= (m + 1) * g:  # the row just appended completed group m
+            lca.lca_condense(lca.packed_latent(cache), 1, g, m, 1, qall, st + 1, 0, 1.0,
+                             lca.packed_latent(reps), anchor)
+            m += 1
+    torch.cuda.synchronize()
+    assert m == m_ref
+    got = np.stack([host(x)[0] for x in outs])
+    assert_close(got, ro, what="incremental decode o_latent")
+    assert_close(np.stack([host(x)[0] for x in lses]), rl, what="incremental decode lse")
+
+
+@pytest.mark.timeout(400)
+def test_million_token_decode_sampled():
+    """L = 1,048,576, one sequence: condense 65,472 groups, decode one step."""
+    L = 1 << 20
+    c, kr = li.latent_cache(6, 1, L)
+    li.plant_needles(6, c, kr, 4, 16.0, 0, L)
+    qh = li.queries(6, 1, G, H, rho=0.5)
+    qd = li.queries(6, 1, 1, H, rho=0.5, stream=1)[:, 0]
+    p = O.plan(L, W, G)
+    m = p["m"]
+    assert m == 65472
+    cache = _packed(c, kr)
+    reps = torch.empty((1, m, 576), dtype=torch.bfloat16, device="cuda")
+    anchor = torch.empty((1, m), dtype=torch.int32, device="cuda")
+    lca.lca_condense(lca.packed_latent(cache), 1, G, 0, m, dev(qh), 0, 0, 1.0,
+                     lca.packed_latent(reps), anchor)
+    o = torch.empty((1, H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((1, H), dtype=torch.float32, device="cuda")
+    ws = lca.decode_workspace(1, H, p["n_entries"])
+    lca.mla_latent_attn_decode(dev(qd), lca.packed_latent(reps), m, lca.packed_latent(cache),
+                               p["raw_begin"], L, 1.0, o, lse, ws)
+    torch.cuda.synchronize()
+    r = host(reps)
+    ga = host(anchor).astype(np.int64)
+    for j in np.random.default_rng(1).integers(0, m, 64):
+        rc, _, ra, _, s = O.condense(c, kr, qh, G, int(j), 1, 0, 0, 1.0)
+        assert_close(r[0, j, :512], rc[0, 0], what=f"rep {j}")
+        anchors_agree(ga[0, j:j + 1], ra[0], O.top2_margin(s[0]))
+    ro, rl = O.decode(qd, r[:, :, :512], r[:, :, 512:], m, c, kr, p["raw_begin"], L, 1.0)
+    assert_close(host(o), ro, what="o_latent")
+    assert_close(host(lse), rl, what="lse")
+
+
+@pytest.mark.timeout(400)
+def test_prefill_128k_sampled_rows():
+    """Chunked prefill of L = 131,072 in 4,096-token chunks: per chunk the
+    newly eligible groups are condensed with the 16 queries that follow each
+    group; sampled query rows of chunks 0, 1, 15 and 31 against the oracle."""
+    L, C = 131072, 4096
+    c, kr = li.latent_cache(7, 1, L)
+    q = li.queries(7, 1, L, H, rho=0.5)[0]
+    cache = _packed(c, kr)[0]
+    q_t = torch.empty((L, H, 576), dtype=torch.bfloat16, device="cuda")
+    for s0 in range(0, L, 16384):
+        q_t[s0:s0 + 16384] = torch.from_numpy(q[s0:s0 + 16384]).to("cuda", torch.bfloat16)
+    m_cap = O.prefill_plan(L - C, W, G)
+    reps = torch.empty((m_cap, 576), dtype=torch.bfloat16, device="cuda")
+    anchor = torch.empty((1, m_cap), dtype=torch.int32, device="cuda")
+    out = torch.empty((L, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((L, H), dtype=torch.float32, device="cuda")
+    m = 0
+    for s0 in range(0, L, C):
+        ms = O.prefill_plan(s0, W, G)
+        if ms > m:
+            lca.lca_condense(lca.packed_latent(cache[None]), 1, G, m, ms - m, q_t[None], (m + 1) * G, G,
+                             1.0, lca.packed_latent(reps[None]), anchor)
+            m = ms
+        lca.mla_latent_attn_prefill_chunk(q_t[s0:s0 + C], s0, lca.packed_latent(reps) if m else None, m,
+                                          lca.packed_latent(cache), m * G, 1.0, out[s0:s0 + C], lse[s0:s0 + C])
+    torch.cuda.synchronize()
+    r = host(reps)
+    rng = np.random.default_rng(2)
+    for j in rng.integers(0, m_cap, 32):  # representatives: per-group summary queries
+        rc, _, ra, _, s = O.condense(c, kr, q[None], G, int(j), 1, (int(j) + 1) * G, G, 1.0)
+        assert_close(r[j, :512], rc[0, 0], what=f"rep {j}")
+    for chunk in (0, 1, 15, 31):
+        s0 = chunk * C
+        ms = O.prefill_plan(s0, W, G)
+        rows = np.sort(rng.choice(C, 12, replace=False))
+        rows[-1] = C - 1  # the last row of a chunk sees the most entries
+        ro, rl = O.prefill_chunk(q[s0:s0 + C], s0, r[:, :512], r[:, 512:], ms, c[0], kr[0], ms * G, 1.0,
+                                 rows=rows)
+        # bf16 output: the arithmetic tolerance plus one bf16 rounding (2^-9 relative, doubled)
+        got = host(out[s0 + rows])
+        bound = TOL + 2.0 ** -8 * np.abs(ro)
+        assert np.all(np.abs(got - ro) <= bound), \
+            f"prefill chunk {chunk}: max excess {np.max(np.abs(got - ro) - bound):.3e}"
+        assert_close(host(lse[s0 + rows]), rl, what=f"prefill lse chunk {chunk}")

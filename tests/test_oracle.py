@@ -270,6 +270,26 @@ def test_no_condensation_is_exact_mla(L, w, g):
         assert list(anc[0]) == list(range(p["m"]))
 
 
+def test_mha_expanded_is_textbook_attention_and_equals_absorbed_form():
+    """The oracle's expanded-head MLA equals torch's float64 attention over
+    explicit W_UK / W_UV heads, and the absorbed decode + up-projection equals
+    it (the absorption identity q_nope . (W_UK^T c) = (W_UK q_nope) . c)."""
+    r = np.random.default_rng(33)
+    n, H = 29, 3
+    c = r.standard_normal((n, 512))
+    kr = r.standard_normal((n, 64))
+    wuk = r.standard_normal((H, 512, 128)) / math.sqrt(512)
+    wuv = r.standard_normal((H, 512, 128)) / math.sqrt(512)
+    q_nope, q_rope = r.standard_normal((H, 128)) * 0.4, r.standard_normal((H, 64)) * 0.4
+    got = O.mha_expanded(q_nope, q_rope, c, kr, wuk, wuv, 0.8)
+    kh, vh = _expanded_heads(c, kr, wuk, wuv)
+    ref = _sdpa(np.concatenate([q_nope, q_rope], 1)[:, None], kh, vh, 0.8)[:, 0]
+    np.testing.assert_allclose(got, ref, atol=1e-12)
+    o_lat, _ = O.decode(O.absorb_query(q_nope, q_rope, wuk)[None], None, None, 0, c[None], kr[None],
+                        0, n, 0.8)
+    np.testing.assert_allclose(O.up_proj(o_lat, wuv)[0], got, atol=1e-12)
+
+
 def test_condensed_decode_equals_textbook_attention_over_condensed_set():
     """Tiny-L brute force: the absorbed decode over [reps ++ window] equals
     textbook per-head attention whose keys/values are built from the same
