@@ -42,14 +42,16 @@ def parse():
     ap.add_argument("--roofline-reps", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-len", type=int, default=131072)
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch every kernel from Python instead of replaying a captured HIP graph")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB elementwise copy (counter calibration) and exit")
     return ap.parse_args()
 
 
-# HBM traffic of one mla_latent_attn_decode call on this workload, from two
-# rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE per dispatch, decode + merge
-# kernels summed) scaled by what the same counters read for a plain 1 GiB
+# HBM traffic of one mla_latent_attn_decode_up call on this workload, from
+# two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE per dispatch, the decode
+# and merge/up-projection kernels summed) scaled by what the same counters read for a plain 1 GiB
 # copy. Valid only for the decode sources it was measured on: the digest of
 # those files is checked at run time and the figure is dropped if it differs.
 TRAFFIC_SOURCES = ("mla_latent_kv_lca_amd/csrc/lca_decode.hip", "mla_latent_kv_lca_amd/csrc/lca_stream.h",
@@ -128,9 +130,8 @@ def main():
                          None, cws)
 
     def decode(i, st):
-        lca.mla_latent_attn_decode(qsteps[i][st], rep_lat[i], m, cache_lat[i], rb, L, 1.0, o_lat,
-                                   lse, dws)
-        lca.mla_up_proj(o_lat, wuv[i], out)
+        lca.mla_latent_attn_decode_up(qsteps[i][st], rep_lat[i], m, cache_lat[i], rb, L, 1.0, o_lat,
+                                      wuv[i], out, lse, dws)
 
     def step():
         for i in range(NL):
@@ -139,36 +140,52 @@ def main():
             for i in range(NL):
                 decode(i, st)
 
-    for _ in range(args.warmup):
+    run = step
+    if not args.no_graph:
+        # one step's ~520 launches captured once and replayed: the host no
+        # longer paces the GPU between the short decode kernels
         step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        run = graph.replay
+    for _ in range(args.warmup):
+        run()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        run()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     ctx_tokens = NL * B * L * DECODE_STEPS
     value = ctx_tokens / (ms_per_step / 1e3)
 
-    # per-kernel times with events on the launch stream, cycling the layers
+    # per-call times: `reps_` calls (cycling the layers) captured in one graph
+    # and replayed between two HIP events on the launch stream, so the
+    # average is the calls' own duration back to back, without host gaps
     stream = torch.cuda.current_stream()
 
     def timed(fn, reps_):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(reps_)]
-        for k in range(reps_):
-            ev[k][0].record(stream)
-            fn(k)
-            ev[k][1].record(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for k in range(reps_):
+                fn(k)
+        g.replay()
         torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in ev) / reps_ * 1e-3  # seconds
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps_ * 1e-3  # seconds
 
-    t_dec = timed(lambda k: lca.mla_latent_attn_decode(qsteps[k % NL][k % DECODE_STEPS],
-                                                       rep_lat[k % NL], m, cache_lat[k % NL], rb,
-                                                       L, 1.0, o_lat, lse, dws), args.roofline_reps)
+    t_dec = timed(lambda k: decode(k % NL, k % DECODE_STEPS), args.roofline_reps)
     t_con = timed(lambda k: condense(k % NL), max(4, args.roofline_reps // 4))
-    dec_bytes = B * n_ent * ROW_BYTES + B * H * 576 * 2 + B * H * (512 + 1) * 4
+    # entries read + queries + o_latent/lse written + W_UV read + up-projected output written
+    dec_bytes = (B * n_ent * ROW_BYTES + B * H * 576 * 2 + B * H * (512 + 1) * 4
+                 + H * 512 * 128 * 2 + B * H * 128 * 2)
     con_bytes = B * m * G * ROW_BYTES + B * G * H * 576 * 2 + B * m * (ROW_BYTES + 4)
     dec_gbs = dec_bytes / t_dec / 1e9
     con_gbs = con_bytes / t_con / 1e9
@@ -197,9 +214,11 @@ def main():
         "data": "synthetic (seeded N(0,1) latent cache with RoPE keys, N(0,1/576) queries)",
         "config": {"workload": f"batched LCA decode: B={B} x L={L}, H={H}, g={G}, w={W}, "
                                f"condense once + {DECODE_STEPS} decode steps (+W_UV), "
+                               f"{'eager launches' if args.no_graph else 'one HIP graph per step'}, "
                                f"{NL} rotating layer caches",
                    "global_batch": B, "seq_len": L, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "mla_latent_attn_decode (decode + split merge)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "mla_latent_attn_decode_up (decode_kernel + up_rows_kernel)",
                      "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": dec_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "bytes_per_launch": dec_bytes, "avg_launch_us": t_dec * 1e6},

@@ -156,6 +156,21 @@ int mla_latent_attn_decode(const void* q, int32_t q_dtype, int64_t q_seq_stride,
                            float sm_scale, float* o_latent, float* lse, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
 
+/* mla_latent_attn_decode followed by mla_up_proj of its output (the MLA
+ * page's projection back to each head's value space, 三.1), with the split
+ * merge and the projection fused into one kernel when B <= 64. Arguments as
+ * in the two calls: o_latent and lse receive the decode results,
+ * out[b, h, :] = o_latent[b, h, :] @ W_UV[h] (w_uv [H, 512, 128] contiguous,
+ * out [B, H, 128] contiguous, dtypes w_dtype / out_dtype). The results are
+ * bitwise equal to the two calls in sequence. workspace as for
+ * mla_latent_attn_decode (same size). */
+int mla_latent_attn_decode_up(const void* q, int32_t q_dtype, int64_t q_seq_stride, int32_t B,
+                              int32_t H, const lca_latent_t* reps, int64_t m,
+                              const lca_latent_t* raw, int64_t raw_begin, int64_t raw_end,
+                              float sm_scale, float* o_latent, float* lse, const void* w_uv,
+                              int32_t w_dtype, void* out, int32_t out_dtype, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
 /* Chunked prefill attention of one sequence over a condensed latent cache.
  * Query i of the chunk sits at absolute position t = chunk_start + i (its
  * absorbed query at q + i*q_tok_stride + h*576, H a multiple of 16) and

@@ -28,7 +28,7 @@ D_C, D_R, D_ROW, D_V = 512, 64, 576, 128
 # every symbol include/lca.h declares
 EXPORTS = ("lca_version", "lca_last_error", "lca_plan", "lca_condense_workspace_size",
            "lca_condense", "mla_latent_attn_decode_workspace_size", "mla_latent_attn_decode",
-           "mla_latent_attn_prefill_chunk", "mla_up_proj")
+           "mla_latent_attn_decode_up", "mla_latent_attn_prefill_chunk", "mla_up_proj")
 
 
 class LcaError(RuntimeError):
@@ -80,6 +80,11 @@ def load() -> ctypes.CDLL:
     lib.mla_latent_attn_decode.argtypes = [c_void_p, c_int32, c_int64, c_int32, c_int32, P(LatentT),
                                            c_int64, P(LatentT), c_int64, c_int64, c_float,
                                            c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.mla_latent_attn_decode_up.restype = c_int32
+    lib.mla_latent_attn_decode_up.argtypes = [c_void_p, c_int32, c_int64, c_int32, c_int32, P(LatentT),
+                                              c_int64, P(LatentT), c_int64, c_int64, c_float,
+                                              c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_int32,
+                                              c_void_p, c_size_t, c_void_p]
     lib.mla_latent_attn_prefill_chunk.restype = c_int32
     lib.mla_latent_attn_prefill_chunk.argtypes = [c_void_p, c_int32, c_int64, c_int64, c_int32,
                                                   c_int32, P(LatentT), c_int64, P(LatentT),
@@ -207,6 +212,33 @@ def mla_latent_attn_decode(q: torch.Tensor, reps: LatentT | None, m: int, raw: L
         None if raw is None else ctypes.byref(raw), raw_begin, raw_end, sm_scale,
         o_latent.data_ptr(), _ptr(lse), ws.data_ptr(), ws.numel() * ws.element_size(),
         _stream(stream)))
+
+
+def mla_latent_attn_decode_up(q: torch.Tensor, reps: LatentT | None, m: int, raw: LatentT | None,
+                              raw_begin: int, raw_end: int, sm_scale: float, o_latent: torch.Tensor,
+                              w_uv: torch.Tensor, out: torch.Tensor, lse: torch.Tensor | None = None,
+                              workspace: torch.Tensor | None = None, stream=None) -> None:
+    """Decode plus W_UV up-projection: q [B, H, 576]; o_latent fp32 [B, H, 512];
+    w_uv [H, 512, 128]; out [B, H, 128]; all contiguous."""
+    if q.dim() != 3 or q.shape[-1] != D_ROW or q.stride(-1) != 1 or q.stride(-2) != D_ROW:
+        raise ValueError("q must be [B, H, 576] with contiguous heads")
+    B, H = q.shape[0], q.shape[1]
+    if o_latent.dtype != torch.float32 or not o_latent.is_contiguous() or o_latent.shape != (B, H, D_C):
+        raise ValueError("o_latent must be a contiguous fp32 [B, H, 512] tensor")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous fp32 [B, H] tensor")
+    if not w_uv.is_contiguous() or tuple(w_uv.shape) != (H, D_C, D_V):
+        raise ValueError("w_uv must be a contiguous [H, 512, 128] tensor")
+    if not out.is_contiguous() or tuple(out.shape) != (B, H, D_V):
+        raise ValueError("out must be a contiguous [B, H, 128] tensor")
+    n = m + raw_end - raw_begin
+    ws = _workspace(mla_latent_attn_decode_workspace_size(B, H, max(n, 1)), q, workspace)
+    _check(load().mla_latent_attn_decode_up(
+        q.data_ptr(), dtype_code(q), q.stride(0), B, H,
+        None if reps is None else ctypes.byref(reps), m,
+        None if raw is None else ctypes.byref(raw), raw_begin, raw_end, sm_scale,
+        o_latent.data_ptr(), _ptr(lse), w_uv.data_ptr(), dtype_code(w_uv), out.data_ptr(),
+        dtype_code(out), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def mla_latent_attn_prefill_chunk(q: torch.Tensor, chunk_start: int, reps: LatentT | None, m: int,

@@ -161,6 +161,43 @@ int mla_latent_attn_decode(const void* q, int32_t q_dtype, int64_t q_seq_stride,
                     "mla_latent_attn_decode launch");
 }
 
+int mla_latent_attn_decode_up(const void* q, int32_t q_dtype, int64_t q_seq_stride, int32_t B,
+                              int32_t H, const lca_latent_t* reps, int64_t m,
+                              const lca_latent_t* raw, int64_t raw_begin, int64_t raw_end,
+                              float sm_scale, float* o_latent, float* lse, const void* w_uv,
+                              int32_t w_dtype, void* out, int32_t out_dtype, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  int rc;
+  if (q == nullptr || !aligned16(q)) return fail(LCA_ERR_INVALID_ARG, "q must be a non-null 16-byte aligned pointer");
+  if (!valid_dtype(q_dtype)) return fail(LCA_ERR_INVALID_ARG, "q_dtype %d is not LCA_BF16/LCA_F32", q_dtype);
+  if (!mult8(q_seq_stride) || q_seq_stride < 0) return fail(LCA_ERR_INVALID_ARG, "q_seq_stride must be a non-negative multiple of 8");
+  if (B < 1 || B > 65535) return fail(LCA_ERR_INVALID_ARG, "B must be in [1, 65535]");
+  if (H < 16 || H % 16 != 0 || H / 16 > 65535) return fail(LCA_ERR_UNSUPPORTED, "H = %d: the head count must be a positive multiple of 16", H);
+  if (m < 0 || raw_begin < 0 || raw_end < raw_begin) return fail(LCA_ERR_INVALID_ARG, "need m >= 0 and 0 <= raw_begin <= raw_end");
+  const int64_t n = m + (raw_end - raw_begin);
+  if (n < 1) return fail(LCA_ERR_INVALID_ARG, "nothing to attend: m + raw_end - raw_begin must be >= 1");
+  if (m > 0 && (rc = check_latent(reps, "reps", true, true)) != LCA_OK) return rc;
+  if (raw_end > raw_begin && (rc = check_latent(raw, "raw", true, true)) != LCA_OK) return rc;
+  if (m > 0 && raw_end > raw_begin && reps->dtype != raw->dtype)
+    return fail(LCA_ERR_UNSUPPORTED, "reps and raw must share one dtype");
+  if ((rc = check_scale(sm_scale)) != LCA_OK) return rc;
+  if (o_latent == nullptr || !aligned16(o_latent)) return fail(LCA_ERR_INVALID_ARG, "o_latent must be a non-null 16-byte aligned pointer");
+  if (!valid_dtype(w_dtype) || !valid_dtype(out_dtype)) return fail(LCA_ERR_INVALID_ARG, "w_dtype and out_dtype must be LCA_BF16 or LCA_F32");
+  if (w_uv == nullptr || !aligned16(w_uv) || out == nullptr || !aligned16(out))
+    return fail(LCA_ERR_INVALID_ARG, "w_uv and out must be non-null 16-byte aligned pointers");
+  const lca::DecodeSplit sp = lca::decode_split(B, H / 16, n);
+  const size_t need = lca::decode_workspace_bytes(B, H / 16, sp.S);
+  if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need))
+    return fail(LCA_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
+  const lca_latent_t none = {nullptr, nullptr, 0, 0, 0, 0, m > 0 ? reps->dtype : raw->dtype};
+  const lca_latent_t& rp = m > 0 ? *reps : none;
+  const lca_latent_t& rw = raw_end > raw_begin ? *raw : none;
+  return hip_status(lca::launch_decode_up(q, q_dtype, q_seq_stride, B, H, rp, m, rw, raw_begin, raw_end,
+                                          sm_scale, o_latent, lse, w_uv, w_dtype, out, out_dtype,
+                                          workspace, stream),
+                    "mla_latent_attn_decode_up launch");
+}
+
 int mla_latent_attn_prefill_chunk(const void* q, int32_t q_dtype, int64_t q_tok_stride,
                                   int64_t chunk_start, int32_t C, int32_t H,
                                   const lca_latent_t* reps, int64_t m,

@@ -12,6 +12,7 @@
 //  decode_kernel_staged  any strides / f32 rows: register-staged 32-entry tiles.
 //  merge_kernel          combines split-K partial results in split order.
 #include "lca_stream.h"
+#include "lca_up_rows.h"
 
 namespace lca {
 
@@ -63,6 +64,18 @@ __global__ __launch_bounds__(DNT) void decode_kernel(
   const int64_t e_end = min(n_entries, e_begin + (int64_t)per_tiles * DT);
   const int n_tiles = e_end > e_begin ? (int)((e_end - e_begin + DT - 1) / DT) : 0;
 
+  // The 16 queries of this head block are copied into the last ring slot
+  // (filled by the loop only at tile DBUF - 1) ahead of the first tiles, by
+  // the same direct loads, so waiting for them leaves those tiles in flight.
+  constexpr int QCH_W = HB * D_ROW * (int)sizeof(TQ) / 16 / DNW;  // 16-byte chunks per wave
+  constexpr int QI = (QCH_W + 63) / 64;                            // load instructions per wave
+  {
+    const char* qsrc = reinterpret_cast<const char*>(q + (int64_t)b * q_seq + (int64_t)hg * HB * D_ROW);
+    const uint32_t qlds = lds_off(&ring[DBUF - 1][0]);
+#pragma unroll
+    for (int i = 0; i < QI; ++i)
+      if (64 * i + lane < QCH_W) dma16(qsrc + 16 * (w * QCH_W + 64 * i + lane), qlds + 16u * (w * QCH_W + 64 * i));
+  }
   uint32_t off[DMA_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < DMA_PER_WAVE; ++i) {
@@ -73,20 +86,17 @@ __global__ __launch_bounds__(DNT) void decode_kernel(
 #pragma unroll
   for (int t = 0; t < DBUF - 1; ++t)
     if (t < n_tiles) tile_dma(src, e_begin + (int64_t)t * DT, e_end, ring[t], w, lane, off);
+  wait_dma_newer(min(n_tiles, DBUF - 1));  // the queries have landed
+  barrier();
 
   // query fragments of head col for this wave's columns: 8 latent k-steps of
   // 32 columns and 1 RoPE k-step
-  const TQ* qh = q + (int64_t)b * q_seq + (int64_t)(hg * HB + col) * D_ROW;
+  const TQ* qh = reinterpret_cast<const TQ*>(&ring[DBUF - 1][0]) + col * D_ROW;
   uint4 qa[9];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) qa[ks] = load8_bf16(qh + 256 * ch + 32 * ks + 8 * kg);
   qa[8] = load8_bf16(qh + D_C + 32 * ch + 8 * kg);
-  // Consume the query registers here so that the compiler waits for their
-  // loads once, before the loop. Otherwise it places those waits inside the
-  // loop, where (being unaware of the ring loads) its vmcnt counts would also
-  // drain every tile in flight.
-#pragma unroll
-  for (int ks = 0; ks < 9; ++ks) retire(qa[ks]);
+  // (the loop's first barrier orders these reads before tile DBUF - 1 lands in the slot)
 
   // lane-constant element offsets of this lane's fragments inside a tile
   int k_off[9], v_off[8];
@@ -358,7 +368,6 @@ __global__ __launch_bounds__(NT) void decode_kernel_staged(
 // Combine the S split partials of a (sequence, head):
 //   o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s,
 // always in split order. Few splits: one thread per 4 output columns.
-constexpr int MERGE_SMALL_S = 32;
 __global__ __launch_bounds__(256) void merge_small_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_ml, int S,
                                                           int B, int H, float* __restrict__ o,
@@ -369,23 +378,9 @@ __global__ __launch_bounds__(256) void merge_small_kernel(const float* __restric
   const int64_t bh = gid / (D_C / 4);
   const int head = (int)(bh % H), b = (int)(bh / H);
   const int HG = H / HB, hg = head / HB, hh = head % HB;
-  const int64_t slot0 = ((int64_t)b * HG + hg) * S;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, part_ml[((slot0 + s) * HB + hh) * 2]);
-  float L = 0.f;
-  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < S; ++s) {
-    const int64_t slot = (slot0 + s) * HB + hh;
-    const float ms = part_ml[slot * 2];
-    const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - M);
-    L = fmaf(wgt, part_ml[slot * 2 + 1], L);
-    const float4 v = reinterpret_cast<const float4*>(part_o + slot * D_C)[c4];
-    a.x = fmaf(wgt, v.x, a.x); a.y = fmaf(wgt, v.y, a.y);
-    a.z = fmaf(wgt, v.z, a.z); a.w = fmaf(wgt, v.w, a.w);
-  }
-  const float inv = 1.0f / L;
-  reinterpret_cast<float4*>(o + ((int64_t)b * H + head) * D_C)[c4] =
-      make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
+  float M, L;
+  const float4 v = merge_cols4(part_o, part_ml, S, ((int64_t)b * HG + hg) * S, hh, c4, M, L);
+  reinterpret_cast<float4*>(o + ((int64_t)b * H + head) * D_C)[c4] = v;
   if (lse != nullptr && c4 == 0) lse[(int64_t)b * H + head] = (M + log2f(L)) * 0.69314718055994530942f;
 }
 
@@ -465,20 +460,15 @@ static bool packed_rows(const lca_latent_t& t) {
          t.kr_tok_stride == t.c_tok_stride && t.kr_seq_stride == t.c_seq_stride;
 }
 
-hipError_t launch_decode(const void* q, int q_dtype, int64_t q_seq_stride, int B, int H,
-                         const lca_latent_t& reps, int64_t m, const lca_latent_t& raw,
-                         int64_t raw_begin, int64_t raw_end, float sm_scale, float* o_latent,
-                         float* lse, void* workspace, hipStream_t stream) {
+// The attention kernel of one decode call; with sp.S > 1 it leaves split
+// partials in the workspace (pml: [slots][2], po: [slots][512]).
+static hipError_t decode_attention(const void* q, int q_dtype, int64_t q_seq_stride, int B, int H,
+                                   const lca_latent_t& reps, int64_t m, const lca_latent_t& raw,
+                                   int64_t raw_begin, int64_t raw_end, float sm_scale,
+                                   float* o_latent, float* lse, const DecodeSplit& sp, float* po,
+                                   float* pml, hipStream_t stream) {
   const int HG = H / HB;
   const int64_t n = m + (raw_end - raw_begin);
-  const DecodeSplit sp = decode_split(B, HG, n);
-  float* pml = nullptr;
-  float* po = nullptr;
-  if (sp.S > 1) {
-    const size_t slots = (size_t)B * HG * sp.S * HB;
-    pml = static_cast<float*>(workspace);
-    po = pml + slots * 2;
-  }
   const float sl2 = sm_scale * 1.44269504088896340736f;
   dim3 grid((unsigned)sp.S, (unsigned)B, (unsigned)HG);
   const bool has_rep = m > 0, has_raw = raw_end > raw_begin;
@@ -516,8 +506,20 @@ hipError_t launch_decode(const void* q, int q_dtype, int64_t q_seq_stride, int B
     else LCA_STAGED(float, float);
 #undef LCA_STAGED
   }
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || sp.S == 1) return err;
+  return hipGetLastError();
+}
+
+static void split_buffers(void* workspace, int B, int HG, const DecodeSplit& sp, float*& po, float*& pml) {
+  po = pml = nullptr;
+  if (sp.S > 1) {
+    const size_t slots = (size_t)B * HG * sp.S * HB;
+    pml = static_cast<float*>(workspace);
+    po = pml + slots * 2;
+  }
+}
+
+static void launch_merge(const DecodeSplit& sp, int B, int H, const float* po, const float* pml,
+                         float* o_latent, float* lse, hipStream_t stream) {
   if (sp.S <= MERGE_SMALL_S) {
     const int64_t n = (int64_t)B * H * (D_C / 4);
     hipLaunchKernelGGL(merge_small_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
@@ -526,6 +528,41 @@ hipError_t launch_decode(const void* q, int q_dtype, int64_t q_seq_stride, int B
     hipLaunchKernelGGL(merge_kernel, dim3(D_C / 32, (unsigned)H, (unsigned)B), dim3(256), 0, stream,
                        po, pml, sp.S, H, o_latent, lse);
   }
+}
+
+hipError_t launch_decode(const void* q, int q_dtype, int64_t q_seq_stride, int B, int H,
+                         const lca_latent_t& reps, int64_t m, const lca_latent_t& raw,
+                         int64_t raw_begin, int64_t raw_end, float sm_scale, float* o_latent,
+                         float* lse, void* workspace, hipStream_t stream) {
+  const DecodeSplit sp = decode_split(B, H / HB, m + (raw_end - raw_begin));
+  float *po, *pml;
+  split_buffers(workspace, B, H / HB, sp, po, pml);
+  hipError_t err = decode_attention(q, q_dtype, q_seq_stride, B, H, reps, m, raw, raw_begin, raw_end,
+                                    sm_scale, o_latent, lse, sp, po, pml, stream);
+  if (err != hipSuccess || sp.S == 1) return err;
+  launch_merge(sp, B, H, po, pml, o_latent, lse, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_up(const void* q, int q_dtype, int64_t q_seq_stride, int B, int H,
+                            const lca_latent_t& reps, int64_t m, const lca_latent_t& raw,
+                            int64_t raw_begin, int64_t raw_end, float sm_scale, float* o_latent,
+                            float* lse, const void* w_uv, int w_dtype, void* out, int out_dtype,
+                            void* workspace, hipStream_t stream) {
+  const DecodeSplit sp = decode_split(B, H / HB, m + (raw_end - raw_begin));
+  float *po, *pml;
+  split_buffers(workspace, B, H / HB, sp, po, pml);
+  hipError_t err = decode_attention(q, q_dtype, q_seq_stride, B, H, reps, m, raw, raw_begin, raw_end,
+                                    sm_scale, o_latent, lse, sp, po, pml, stream);
+  if (err != hipSuccess) return err;
+  if (sp.S == 1 || sp.S > MERGE_SMALL_S || B > UP_SMALL_T) {
+    if (sp.S > 1) launch_merge(sp, B, H, po, pml, o_latent, lse, stream);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    return launch_up_proj(o_latent, LCA_F32, B, H, w_uv, w_dtype, out, out_dtype, stream);
+  }
+  const RowsFromSplits rows{po, pml, sp.S, o_latent, lse};
+  if (w_dtype == LCA_BF16) launch_up_rows<RowsFromSplits, bf16_t>(rows, B, H, w_uv, out, out_dtype, stream);
+  else launch_up_rows<RowsFromSplits, float>(rows, B, H, w_uv, out, out_dtype, stream);
   return hipGetLastError();
 }
 

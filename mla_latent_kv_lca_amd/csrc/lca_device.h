@@ -58,6 +58,27 @@ __device__ __forceinline__ void load8_f32(const float* p, float* o) {
   o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
 }
 
+// 8 consecutive elements kept in their stored type until converted, so that
+// a batch of loads can be issued before any of them is used.
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16_t> { uint4 v; };
+template <> struct Raw8<float> { float4 a, b; };
+__device__ __forceinline__ Raw8<bf16_t> raw8_load(const bf16_t* p) {
+  return Raw8<bf16_t>{*reinterpret_cast<const uint4*>(p)};
+}
+__device__ __forceinline__ Raw8<float> raw8_load(const float* p) {
+  return Raw8<float>{reinterpret_cast<const float4*>(p)[0], reinterpret_cast<const float4*>(p)[1]};
+}
+template <typename T> __device__ __forceinline__ Raw8<T> raw8_zero();
+template <> __device__ __forceinline__ Raw8<bf16_t> raw8_zero<bf16_t>() { return Raw8<bf16_t>{make_uint4(0u, 0u, 0u, 0u)}; }
+template <> __device__ __forceinline__ Raw8<float> raw8_zero<float>() {
+  return Raw8<float>{make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+}
+__device__ __forceinline__ uint4 raw8_bf16(const Raw8<bf16_t>& r) { return r.v; }
+__device__ __forceinline__ uint4 raw8_bf16(const Raw8<float>& r) {
+  return make_uint4(pack_bf2(r.a.x, r.a.y), pack_bf2(r.a.z, r.a.w), pack_bf2(r.b.x, r.b.y), pack_bf2(r.b.z, r.b.w));
+}
+
 __device__ __forceinline__ float to_f32(bf16_t x) { return bf2f(x); }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 

@@ -41,6 +41,14 @@ hipError_t launch_decode(const void* q, int q_dtype, int64_t q_seq_stride, int B
                          int64_t raw_begin, int64_t raw_end, float sm_scale, float* o_latent,
                          float* lse, void* workspace, hipStream_t stream);
 
+// decode followed by the W_UV up-projection of its output; the split merge
+// and the projection share one kernel when B <= UP_SMALL_T.
+hipError_t launch_decode_up(const void* q, int q_dtype, int64_t q_seq_stride, int B, int H,
+                            const lca_latent_t& reps, int64_t m, const lca_latent_t& raw,
+                            int64_t raw_begin, int64_t raw_end, float sm_scale, float* o_latent,
+                            float* lse, const void* w_uv, int w_dtype, void* out, int out_dtype,
+                            void* workspace, hipStream_t stream);
+
 // ---- prefill
 hipError_t launch_prefill(const void* q, int q_dtype, int64_t q_tok_stride, int64_t chunk_start,
                           int C, int H, const lca_latent_t& reps, int64_t m,
@@ -48,6 +56,7 @@ hipError_t launch_prefill(const void* q, int q_dtype, int64_t q_tok_stride, int6
                           void* o_latent, int o_dtype, float* lse, hipStream_t stream);
 
 // ---- up-projection
+constexpr int UP_SMALL_T = 64;  // token counts up to this use the small-T kernel
 hipError_t launch_up_proj(const void* o_latent, int o_dtype, int64_t T, int H, const void* w_uv,
                           int w_dtype, void* out, int out_dtype, hipStream_t stream);
 

@@ -11,6 +11,7 @@
 // product of attention. o_latent fragments come straight from global memory.
 #include "lca_device.h"
 #include "lca_internal.h"
+#include "lca_up_rows.h"
 
 namespace lca {
 
@@ -87,67 +88,11 @@ __global__ __launch_bounds__(256) void up_proj_kernel(const TO* __restrict__ x, 
   }
 }
 
-// Small token counts (decode: T = batch): W_UV[h] is the only sizeable input,
-// so spread it. Workgroup (n-block of 16 outputs, head) with 4 wavefronts,
-// wave w covering k in [128 w, 128 w + 128): its 4 B-operand fragments are
-// gathered once from global memory (8 k-rows per lane, 16 outputs per wave),
-// every 16-token tile is one chain of 4 MFMA 16x16x32, and the 4 k-partials
-// are added through LDS in wave order. T <= UP_SMALL_T.
-constexpr int UP_SMALL_T = 64;
-
-template <typename TO, typename TW, typename TY>
-__global__ __launch_bounds__(256) void up_proj_small_kernel(const TO* __restrict__ x, int64_t T,
-                                                            int H, const TW* __restrict__ wuv,
-                                                            TY* __restrict__ y) {
-  __shared__ float red[4][UP_SMALL_T / 16][16][17];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int kg = lane >> 4, col = lane & 15;
-  const int n0 = 16 * blockIdx.x, h = blockIdx.y;
-  const TW* wh = wuv + (int64_t)h * D_C * D_V + n0 + col;
-  uint4 bf[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    float v[8];
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) v[kk] = to_f32(wh[(int64_t)(128 * w + 32 * ks + 8 * kg + kk) * D_V]);
-    bf[ks] = make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]),
-                        pack_bf2(v[6], v[7]));
-  }
-  const int n_mt = (int)((T + 15) / 16);
-#pragma unroll
-  for (int mt = 0; mt < UP_SMALL_T / 16; ++mt) {
-    if (mt >= n_mt) break;
-    const int64_t t = 16 * mt + col;
-    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint4 a = t < T ? load8_bf16(x + (t * H + h) * D_C + 128 * w + 32 * ks + 8 * kg)
-                            : make_uint4(0u, 0u, 0u, 0u);
-      acc = mfma16x16x32(a, bf[ks], acc);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) red[w][mt][4 * kg + r][col] = acc[r];  // [token][output]
-  }
-  __syncthreads();
-  for (int i = tid; i < n_mt * 256; i += 256) {
-    const int mt = i >> 8, row = (i >> 4) & 15, c = i & 15;
-    const int64_t t = 16 * mt + row;
-    if (t < T) {
-      const float v = ((red[0][mt][row][c] + red[1][mt][row][c]) + red[2][mt][row][c]) + red[3][mt][row][c];
-      y[(t * H + h) * D_V + n0 + c] = from_f32<TY>(v);
-    }
-  }
-}
-
 template <typename TO, typename TW>
 static void launch_up_w(int y_dtype, dim3 grid, hipStream_t st, const void* x, int64_t T, int H,
                         const void* w, void* y) {
-  if (T <= UP_SMALL_T) {
-    dim3 g2(D_V / 16, (unsigned)H);
-    if (y_dtype == LCA_BF16)
-      hipLaunchKernelGGL((up_proj_small_kernel<TO, TW, bf16_t>), g2, dim3(256), 0, st, (const TO*)x, T, H, (const TW*)w, (bf16_t*)y);
-    else
-      hipLaunchKernelGGL((up_proj_small_kernel<TO, TW, float>), g2, dim3(256), 0, st, (const TO*)x, T, H, (const TW*)w, (float*)y);
+  if (T <= UP_SMALL_T) {  // few rows (decode): W_UV streamed once per XCD, see lca_up_rows.h
+    launch_up_rows<RowsFromLatent<TO>, TW>(RowsFromLatent<TO>{(const TO*)x}, T, H, w, y, y_dtype, st);
     return;
   }
   if (y_dtype == LCA_BF16)

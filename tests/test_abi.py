@@ -123,6 +123,27 @@ def test_decode_argument_errors():
     assert "workspace needs" in lca.lca_last_error()
 
 
+def _decode_up(lib, raw, **kw):
+    a = dict(q=64, qdt=0, qss=16 * 576, B=1, H=16, m=0, rb=0, re=8, sm=1.0, o=64, lse=None,
+             w=64, wdt=0, out=64, odt=0, ws=None, wsb=0)
+    a.update(kw)
+    return lib.mla_latent_attn_decode_up(a["q"], a["qdt"], a["qss"], a["B"], a["H"], None, a["m"],
+                                         None if raw is None else ctypes.byref(raw), a["rb"], a["re"],
+                                         a["sm"], a["o"], a["lse"], a["w"], a["wdt"], a["out"],
+                                         a["odt"], a["ws"], a["wsb"], None)
+
+
+def test_decode_up_argument_errors():
+    lib = lca.load()
+    lat = _lat()
+    assert _decode_up(lib, lat, w=None) == lca.LCA_ERR_INVALID_ARG
+    assert _decode_up(lib, lat, out=None) == lca.LCA_ERR_INVALID_ARG
+    assert _decode_up(lib, lat, w=72) == lca.LCA_ERR_INVALID_ARG   # misaligned
+    assert _decode_up(lib, lat, odt=7) == lca.LCA_ERR_INVALID_ARG
+    assert _decode_up(lib, lat, H=8) == lca.LCA_ERR_UNSUPPORTED
+    assert _decode_up(lib, lat, re=60000) == lca.LCA_ERR_WORKSPACE
+
+
 def test_prefill_and_up_proj_argument_errors():
     lib = lca.load()
     lat = _lat()

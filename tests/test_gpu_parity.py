@@ -197,6 +197,33 @@ def test_decode_tiny_and_ragged():
 
 
 # ----------------------------------------------------------------- prefill --
+@pytest.mark.parametrize("B,L,wdt,odt", [(32, 3008, torch.bfloat16, torch.bfloat16),  # fused merge
+                                         (5, 1000, torch.float32, torch.float32),    # fused, 32 splits, ragged B
+                                         (3, 30, torch.bfloat16, torch.float32),     # one split
+                                         (1, 40000, torch.bfloat16, torch.bfloat16),  # many splits
+                                         (70, 600, torch.bfloat16, torch.bfloat16)])  # B > 64
+def test_decode_up_equals_decode_then_up_proj(B, L, wdt, odt):
+    """The fused decode + up-projection entry point gives bitwise the results
+    of mla_latent_attn_decode followed by mla_up_proj, and the up-projected
+    output matches the oracle."""
+    c, kr = li.latent_cache(13, B, L)
+    li.plant_needles(13, c, kr, 2, 12.0, 0, L)
+    q = li.queries(13, B, 1, H, rho=0.5)[:, 0]
+    w = li.w_uv(13, H)
+    cache_t, q_t, w_t = packed(c, kr), dev(q), dev(w, wdt)
+    o1, l1 = _decode_gpu(q_t, None, 0, cache_t, 0, L, 1.0)
+    y1 = torch.empty((B, H, 128), dtype=odt, device="cuda")
+    lca.mla_up_proj(o1, w_t, y1)
+    o2 = torch.empty_like(o1)
+    l2 = torch.empty_like(l1)
+    y2 = torch.empty_like(y1)
+    lca.mla_latent_attn_decode_up(q_t, None, 0, lca.packed_latent(cache_t), 0, L, 1.0, o2, w_t, y2, l2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(y1, y2)
+    ro, _ = O.decode(q, None, None, 0, c, kr, 0, L, 1.0)
+    assert_close(host(y2), O.up_proj(ro, w), what="decode_up out")
+
+
 @pytest.mark.parametrize("L,C", [(320, 64), (301, 40)])
 def test_prefill_chunks_match_oracle(L, C):
     w, g, sm = 64, 16, 1.0
@@ -257,3 +284,45 @@ def test_up_proj_matches_oracle(xdt, ydt, T):
     lca.mla_up_proj(dev(x, xdt), dev(w), out)
     torch.cuda.synchronize()
     assert_close(host(out), O.up_proj(x, w), tol=TOL, what="up_proj")
+
+
+# ------------------------------------------------------------- HIP graphs --
+def test_graph_replay_matches_eager():
+    """Condense + fused decode captured in a HIP graph: every replay, with
+    eager work and synchronisations in between, equals the eager results."""
+    B, L, g, w = 4, 2500, 16, 1024
+    c, kr = li.latent_cache(14, B, L)
+    qh = li.queries(14, B, 16, H, rho=0.5)
+    qd = li.queries(14, B, 1, H, rho=0.5, stream=1)[:, 0]
+    p = O.plan(L, w, g)
+    m = p["m"]
+    cache_t, qh_t, qd_t, w_t = packed(c, kr), dev(qh), dev(qd), dev(li.w_uv(14, H))
+    reps = torch.zeros((B, m, 576), dtype=torch.bfloat16, device="cuda")
+    anchor = torch.zeros((B, m), dtype=torch.int32, device="cuda")
+    o = torch.zeros((B, H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.zeros((B, H), dtype=torch.float32, device="cuda")
+    y = torch.zeros((B, H, 128), dtype=torch.bfloat16, device="cuda")
+    cws = torch.empty(lca.lca_condense_workspace_size(B, m, 0), dtype=torch.uint8, device="cuda")
+    dws = lca.decode_workspace(B, H, p["n_entries"])
+
+    def work():
+        lca.lca_condense(lca.packed_latent(cache_t), B, g, 0, m, qh_t, 0, 0, 1.0,
+                         lca.packed_latent(reps), anchor, None, cws)
+        lca.mla_latent_attn_decode_up(qd_t, lca.packed_latent(reps), m, lca.packed_latent(cache_t),
+                                      p["raw_begin"], L, 1.0, o, w_t, y, lse, dws)
+
+    work()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (reps, anchor, o, lse, y)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work()
+    for rep in range(3):
+        for t in (reps, o, lse, y):
+            t.fill_(float("nan"))
+        anchor.fill_(-1)
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((reps, anchor, o, lse, y), want):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager run"
+        _ = (qd_t.float() * 2).sum().item()  # eager work between replays
