@@ -26,30 +26,93 @@ constexpr int DT_ELEMS = STILE_ELEMS;          // dense tile, 36,864 bytes
 // decode_kernel: one workgroup of 4 wavefronts per (split, sequence, head
 // block), one workgroup per CU. Entries stream from HBM straight into a
 // 4-deep LDS ring of 32-entry tiles (global_load_lds, 16 bytes per lane, no
-// register staging): three 36 KB tiles are in flight while one is used, which
-// is what the HBM latency needs per CU.
+// register staging).
 // The waves form a 2 x 2 grid: wave w owns entry half eh = w & 1 (tile rows
 // [16 eh, 16 eh + 16)) and column half ch = w >> 1 (latent columns
-// [256 ch, 256 ch + 256) and RoPE columns [32 ch, 32 ch + 32)). Per tile it
+// [256 ch, 256 ch + 256) and RoPE columns [32 ch, 32 ch + 32)). That block of
+// a tile is all the wave ever reads, so each wave streams its own quarter of
+// every tile and waits for it with its own vmcnt: there is no workgroup-wide
+// wait per tile, and a slot is refilled as soon as its owner is done with it,
+// which keeps all four tiles of the ring in flight. Per tile the wave
 //   forms the partial scores S^T = K Q^T over its columns (9 MFMA 16x16x32,
 //   its queries in registers), adds the partner's half (wave w ^ 2, same
 //   entries) read through LDS in a fixed order, so both partners hold the
-//   same scores and the same online-softmax state, and
-//   accumulates O^T += V^T P^T for its own 256 columns over its 16 entries
-//   (16 MFMA 16x16x16; P comes straight from the score registers, V^T is built
-//   from row fragments with half-word shuffles).
+//   same scores and the same online-softmax state (the one barrier per tile),
+//   and accumulates O^T += V^T P^T for its own 256 columns over its 16
+//   entries (16 MFMA 16x16x16; P comes straight from the score registers,
+//   V^T is built from row fragments with half-word shuffles).
 // The two entry halves are merged once, at the end. The cost per entry is
 // 34,816 flop on 1,152 bytes, more than the fp32 vector units sustain at HBM
 // rate, hence the matrix cores.
 // With S > 1 splits per sequence the workgroup writes its merged (O, max,
-// sum) to the workspace and merge_kernel combines the splits in split order.
+// sum) to the workspace and a second kernel combines the splits in split order.
+//
+// Quarter layout: 16 rows x 36 chunks of 16 bytes (32 latent + 4 RoPE chunks
+// of the wave's columns), 9,216 bytes. Latent chunk j of row r sits at
+// j ^ (r & 7), RoPE chunk 32 + j at 32 + (j ^ ((r >> 1) & 3)): every group of
+// 8 lanes of a fragment read then covers 8 distinct 16-byte bank groups.
+// Reductions over the four 16-lane rows holding one head (lanes col + 16 k):
+// v_permlane16_swap / v_permlane32_swap exchange lane halves in registers;
+// both results of a swap are combined, so every lane gets the same value.
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+constexpr int QROW = 36;                        // chunks per quarter row
+constexpr int QUARTER = 16 * QROW * 8;          // bf16 elements per quarter
+__device__ __forceinline__ int qchunk(int r, int j) {
+  return r * QROW + (j < 32 ? (j ^ (r & 7)) : 32 + ((j - 32) ^ ((r >> 1) & 3)));
+}
+// global 16-byte chunk (of the 72 in a row) and quarter row of LDS position
+// P = 64 i + lane of wave (eh, ch)'s quarter
+__device__ __forceinline__ void quarter_slot(int ch, int i, int lane, int& r, int& gchunk) {
+  const int P = 64 * i + lane;
+  r = P / QROW;
+  const int jp = P - r * QROW;
+  const int j = jp < 32 ? (jp ^ (r & 7)) : 32 + ((jp - 32) ^ ((r >> 1) & 3));
+  gchunk = j < 32 ? 32 * ch + j : 64 + 4 * ch + (j - 32);
+}
+// DMA of wave (eh, ch)'s quarter of tile entries [e0, e0 + 32) into `qbuf`
+__device__ __forceinline__ void quarter_dma(const DmaSrc& src, int64_t e0, int64_t e_end,
+                                            const bf16_t* qbuf, int eh, int ch, int lane,
+                                            const uint32_t (&off)[DMA_PER_WAVE]) {
+  const uint32_t base = lds_off(qbuf);
+  if (e0 + STILE <= e_end && (e0 + STILE <= src.m || e0 >= src.m)) {
+    const char* b0 = e0 < src.m ? src.rep + e0 * src.tok : src.raw + (e0 - src.m) * src.tok;
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i) dma16(b0 + off[i], base + 1024u * i);
+  } else {
+    const int valid = (int)min((int64_t)STILE, e_end - e0);
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+      int r, gc;
+      quarter_slot(ch, i, lane, r, gc);
+      const int64_t e = e0 + min(16 * eh + r, valid - 1);
+      const char* p = e < src.m ? src.rep + e * src.tok : src.raw + (e - src.m) * src.tok;
+      dma16(p + 16 * gc, base + 1024u * i);
+    }
+  }
+}
+
 template <typename TQ>
 __global__ __launch_bounds__(DNT) void decode_kernel(
     const TQ* __restrict__ q, int64_t q_seq, DmaSrc src0, int64_t rep_seq_b, int64_t raw_seq_b,
     int64_t n_entries, int per_tiles, int S, float scale_log2, int H, float* __restrict__ part_o,
     float* __restrict__ part_ml, float* __restrict__ o_final, float* __restrict__ lse_final) {
   __shared__ __align__(16) bf16_t ring[DBUF][DT_ELEMS];
-  __shared__ __align__(16) float sx[DNW][HB][HB + 4];  // partial S^T: [wave][head][entry]
+  __shared__ __align__(16) float sx[2][DNW][HB][HB + 4];  // partial S^T by tile parity: [wave][head][entry]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -64,65 +127,52 @@ __global__ __launch_bounds__(DNT) void decode_kernel(
   const int64_t e_end = min(n_entries, e_begin + (int64_t)per_tiles * DT);
   const int n_tiles = e_end > e_begin ? (int)((e_end - e_begin + DT - 1) / DT) : 0;
 
-  // The 16 queries of this head block are copied into the last ring slot
-  // (filled by the loop only at tile DBUF - 1) ahead of the first tiles, by
-  // the same direct loads, so waiting for them leaves those tiles in flight.
-  constexpr int QCH_W = HB * D_ROW * (int)sizeof(TQ) / 16 / DNW;  // 16-byte chunks per wave
-  constexpr int QI = (QCH_W + 63) / 64;                            // load instructions per wave
-  {
-    const char* qsrc = reinterpret_cast<const char*>(q + (int64_t)b * q_seq + (int64_t)hg * HB * D_ROW);
-    const uint32_t qlds = lds_off(&ring[DBUF - 1][0]);
-#pragma unroll
-    for (int i = 0; i < QI; ++i)
-      if (64 * i + lane < QCH_W) dma16(qsrc + 16 * (w * QCH_W + 64 * i + lane), qlds + 16u * (w * QCH_W + 64 * i));
-  }
-  uint32_t off[DMA_PER_WAVE];
-#pragma unroll
-  for (int i = 0; i < DMA_PER_WAVE; ++i) {
-    int row, col16;
-    slot_rowcol(w, i, lane, row, col16);
-    off[i] = (uint32_t)(row * src.tok) + 16u * col16;
-  }
-#pragma unroll
-  for (int t = 0; t < DBUF - 1; ++t)
-    if (t < n_tiles) tile_dma(src, e_begin + (int64_t)t * DT, e_end, ring[t], w, lane, off);
-  wait_dma_newer(min(n_tiles, DBUF - 1));  // the queries have landed
-  barrier();
-
-  // query fragments of head col for this wave's columns: 8 latent k-steps of
-  // 32 columns and 1 RoPE k-step
-  const TQ* qh = reinterpret_cast<const TQ*>(&ring[DBUF - 1][0]) + col * D_ROW;
+  // Queries first, alone: all four tiles of the ring are then issued at once
+  // and stay in flight. (Loading the queries behind the first tiles makes the
+  // wait for them drain the ring: the memory system serves them no earlier
+  // than the tiles.) 8 latent k-steps of 32 columns and 1 RoPE k-step of head
+  // col for this wave's columns.
+  const TQ* qh = q + (int64_t)b * q_seq + (int64_t)(hg * HB + col) * D_ROW;
   uint4 qa[9];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) qa[ks] = load8_bf16(qh + 256 * ch + 32 * ks + 8 * kg);
   qa[8] = load8_bf16(qh + D_C + 32 * ch + 8 * kg);
-  // (the loop's first barrier orders these reads before tile DBUF - 1 lands in the slot)
-
-  // lane-constant element offsets of this lane's fragments inside a tile
-  int k_off[9], v_off[8];
-  const int krow = 16 * eh + col;  // score product: A = K rows
+  uint32_t off[DMA_PER_WAVE];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) k_off[ks] = 8 * chunk_pos(krow, 32 * ch + 4 * ks + kg);
-  k_off[8] = 8 * chunk_pos(krow, 64 + 4 * ch + kg);
+  for (int i = 0; i < DMA_PER_WAVE; ++i) {
+    int r, gc;
+    quarter_slot(ch, i, lane, r, gc);
+    off[i] = (uint32_t)((16 * eh + r) * src.tok) + 16u * gc;
+  }
+  // the compiler waits for the query loads here, before any tile is in flight
+#pragma unroll
+  for (int ks = 0; ks < 9; ++ks) retire(qa[ks]);
+#pragma unroll
+  for (int t = 0; t < DBUF; ++t)
+    if (t < n_tiles) quarter_dma(src, e_begin + (int64_t)t * DT, e_end, ring[t] + w * QUARTER, eh, ch, lane, off);
+
+  // lane-constant element offsets of this lane's fragments inside its quarter
+  int k_off[9], v_off[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) k_off[ks] = 8 * qchunk(col, 4 * ks + kg);  // score product: A = K rows
+  k_off[8] = 8 * qchunk(col, 32 + kg);
 #pragma unroll
   for (int slab = 0; slab < 2; ++slab)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)  // value product: rows 16 eh + 4 kg + r, columns of slab
-      v_off[4 * slab + r] = 8 * chunk_pos(16 * eh + 4 * kg + r, 16 * (2 * ch + slab) + col);
+    for (int r = 0; r < 4; ++r)  // value product: rows 4 kg + r, latent chunk 16 slab + col
+      v_off[4 * slab + r] = 8 * qchunk(4 * kg + r, 16 * slab + col);
 
   f32x4_t o[16];
 #pragma unroll
   for (int c = 0; c < 16; ++c) o[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int t = 0; t < n_tiles; ++t) {
+  // Scores of tile t for this wave's 16 entries (log2 units, masked past
+  // e_end); returns their per-head maximum.
+  auto scores = [&](int t, float (&z)[4]) -> float {
     const int64_t e0 = e_begin + (int64_t)t * DT;
-    wait_dma_newer(min(n_tiles - 1 - t, DBUF - 2));
-    barrier();  // tile t landed for every wave; tile t-1's slot and sx are free
-    if (t + DBUF - 1 < n_tiles)
-      tile_dma(src, e0 + (int64_t)(DBUF - 1) * DT, e_end, ring[(t + DBUF - 1) % DBUF], w, lane, off);
-    const bf16_t* tile = ring[t % DBUF];
-
+    wait_dma_newer(min(n_tiles - 1 - t, DBUF - 1));  // this wave's quarter of tile t has landed
+    const bf16_t* tile = ring[t % DBUF] + w * QUARTER;
     // partial S^T over this wave's columns: two independent chains
     f32x4_t sa = f32x4_t{0.f, 0.f, 0.f, 0.f}, sb = sa;
 #pragma unroll
@@ -131,12 +181,12 @@ __global__ __launch_bounds__(DNT) void decode_kernel(
       sb = mfma16x16x32(*reinterpret_cast<const uint4*>(tile + k_off[ks + 1]), qa[ks + 1], sb);
     }
     sa = mfma16x16x32(*reinterpret_cast<const uint4*>(tile + k_off[8]), qa[8], sa);
-    *reinterpret_cast<f32x4_t*>(&sx[w][col][4 * kg]) = sa + sb;  // S[h = col][16 eh + 4 kg + r]
+    float(*sxt)[HB][HB + 4] = sx[t & 1];
+    *reinterpret_cast<f32x4_t*>(&sxt[w][col][4 * kg]) = sa + sb;  // S[h = col][16 eh + 4 kg + r]
     barrier();
     // both partners add the column halves in the same order (ch 0, then ch 1)
-    const f32x4_t sc = *reinterpret_cast<const f32x4_t*>(&sx[eh][col][4 * kg]) +
-                       *reinterpret_cast<const f32x4_t*>(&sx[eh + 2][col][4 * kg]);
-    float z[4];
+    const f32x4_t sc = *reinterpret_cast<const f32x4_t*>(&sxt[eh][col][4 * kg]) +
+                       *reinterpret_cast<const f32x4_t*>(&sxt[eh + 2][col][4 * kg]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) z[r] = sc[r] * scale_log2;
     if (e0 + DT > e_end) {
@@ -144,30 +194,21 @@ __global__ __launch_bounds__(DNT) void decode_kernel(
       for (int r = 0; r < 4; ++r)
         if (e0 + 16 * eh + 4 * kg + r >= e_end) z[r] = -INFINITY;
     }
-    // online softmax per head (lanes col, col+16, col+32, col+48), lazy rescale
-    float tmax = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    if (__builtin_amdgcn_ballot_w64(tmax > m_run + LAZY_LOG2) != 0) {
-      const float m_new = fmaxf(m_run, tmax);
-      const float corr = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= corr;
-#pragma unroll
-      for (int c = 0; c < 16; ++c) o[c] *= corr;
-      m_run = m_new;
-    }
+    // per head: lanes col, col + 16, col + 32, col + 48
+    return xor32_max(xor16_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]))));
+  };
+  // Probabilities relative to the running max, their sum, and the value
+  // product O^T += V^T P^T (per 128-column slab, 4 row fragments -> 8 MFMA
+  // 16x16x16); then this wave's quarter of the slot takes tile t + DBUF.
+  auto accumulate = [&](int t, const float (&z)[4]) {
+    const bf16_t* tile = ring[t % DBUF] + w * QUARTER;
     // a wave with no visible entry yet keeps m_run = -inf: its p must be 0
     const float m_ref = m_run == -INFINITY ? 0.f : m_run;
     float p[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(z[r] - m_ref);
-    float ps = (p[0] + p[1]) + (p[2] + p[3]);
-    ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
-    l_run += ps;
+    l_run += xor32_sum(xor16_sum((p[0] + p[1]) + (p[2] + p[3])));
     const uint2 pb = make_uint2(pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3]));
-
-    // O^T += V^T P^T: per 128-column slab, 4 row fragments -> 8 MFMA 16x16x16
 #pragma unroll
     for (int slab = 0; slab < 2; ++slab) {
       uint4 R[4];
@@ -188,6 +229,33 @@ __global__ __launch_bounds__(DNT) void decode_kernel(
         o[8 * slab + c] = mfma16x16x16(a, pb, o[8 * slab + c]);
       }
     }
+    if (t + DBUF < n_tiles) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      quarter_dma(src, e_begin + (int64_t)(t + DBUF) * DT, e_end, ring[t % DBUF] + w * QUARTER, eh, ch,
+                  lane, off);
+    }
+  };
+  // Online softmax with a lazy rescale: the inner loop runs while the running
+  // max stays within LAZY_LOG2 of every new score, so the accumulators are
+  // touched only by the MFMA there; a tile that raises it leaves the loop,
+  // rescales, and the loop resumes after it.
+  int t = 0;
+  while (t < n_tiles) {
+    float z[4], tmax = 0.f;
+    for (; t < n_tiles; ++t) {
+      tmax = scores(t, z);
+      if (__builtin_amdgcn_ballot_w64(tmax > m_run + LAZY_LOG2) != 0) break;
+      accumulate(t, z);
+    }
+    if (t >= n_tiles) break;
+    const float m_new = fmaxf(m_run, tmax);
+    const float corr = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= corr;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) o[c] *= corr;
+    m_run = m_new;
+    accumulate(t, z);
+    ++t;
   }
 
   // merge the two entry halves through LDS (the ring is free now)
