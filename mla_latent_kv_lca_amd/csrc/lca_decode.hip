@@ -128,10 +128,9 @@ __global__ __launch_bounds__(DNT) void decode_kernel(
   const int n_tiles = e_end > e_begin ? (int)((e_end - e_begin + DT - 1) / DT) : 0;
 
   // Queries first, alone: all four tiles of the ring are then issued at once
-  // and stay in flight. (Loading the queries behind the first tiles makes the
-  // wait for them drain the ring: the memory system serves them no earlier
-  // than the tiles.) 8 latent k-steps of 32 columns and 1 RoPE k-step of head
-  // col for this wave's columns.
+  // and stay in flight. (Requested behind the tiles, the queries would only
+  // arrive with them.) 8 latent k-steps of 32 columns and 1 RoPE k-step of
+  // head col for this wave's columns.
   const TQ* qh = q + (int64_t)b * q_seq + (int64_t)(hg * HB + col) * D_ROW;
   uint4 qa[9];
 #pragma unroll
@@ -152,15 +151,20 @@ __global__ __launch_bounds__(DNT) void decode_kernel(
     if (t < n_tiles) quarter_dma(src, e_begin + (int64_t)t * DT, e_end, ring[t] + w * QUARTER, eh, ch, lane, off);
 
   // lane-constant element offsets of this lane's fragments inside its quarter
-  int k_off[9], v_off[8];
+  int k_off[9], v_off[16];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) k_off[ks] = 8 * qchunk(col, 4 * ks + kg);  // score product: A = K rows
   k_off[8] = 8 * qchunk(col, 32 + kg);
+  // value product, column tile ct (latent columns 16 ct .. 16 ct + 15 of this
+  // wave's 256): a transposed LDS read (ds_read_b64_tr_b16) gives lane
+  // (kg, col) the values of rows 4 kg .. 4 kg + 3 in column 16 ct + col -- the
+  // MFMA A operand of V^T -- when the 16 lanes of row group kg point at rows
+  // 4 kg + col / 4, columns 16 ct + 4 (col % 4) .. + 3.
 #pragma unroll
-  for (int slab = 0; slab < 2; ++slab)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)  // value product: rows 4 kg + r, latent chunk 16 slab + col
-      v_off[4 * slab + r] = 8 * qchunk(4 * kg + r, 16 * slab + col);
+  for (int ct = 0; ct < 16; ++ct) {
+    const int c = 16 * ct + 4 * (col & 3);
+    v_off[ct] = 8 * qchunk(4 * kg + (col >> 2), c >> 3) + (c & 7);
+  }
 
   f32x4_t o[16];
 #pragma unroll
@@ -198,8 +202,8 @@ __global__ __launch_bounds__(DNT) void decode_kernel(
     return xor32_max(xor16_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]))));
   };
   // Probabilities relative to the running max, their sum, and the value
-  // product O^T += V^T P^T (per 128-column slab, 4 row fragments -> 8 MFMA
-  // 16x16x16); then this wave's quarter of the slot takes tile t + DBUF.
+  // product O^T += V^T P^T (16 column tiles, one MFMA 16x16x16 each); then
+  // this wave's quarter of the slot takes tile t + DBUF.
   auto accumulate = [&](int t, const float (&z)[4]) {
     const bf16_t* tile = ring[t % DBUF] + w * QUARTER;
     // a wave with no visible entry yet keeps m_run = -inf: its p must be 0
@@ -210,24 +214,9 @@ __global__ __launch_bounds__(DNT) void decode_kernel(
     l_run += xor32_sum(xor16_sum((p[0] + p[1]) + (p[2] + p[3])));
     const uint2 pb = make_uint2(pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3]));
 #pragma unroll
-    for (int slab = 0; slab < 2; ++slab) {
-      uint4 R[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) R[r] = *reinterpret_cast<const uint4*>(tile + v_off[4 * slab + r]);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int wi = c >> 1;
-        uint2 a;
-        if (c & 1) {
-          a.x = hi_pair(u4_get(R[0], wi), u4_get(R[1], wi));
-          a.y = hi_pair(u4_get(R[2], wi), u4_get(R[3], wi));
-        } else {
-          a.x = lo_pair(u4_get(R[0], wi), u4_get(R[1], wi));
-          a.y = lo_pair(u4_get(R[2], wi), u4_get(R[3], wi));
-        }
-        // o[8 slab + c][r'] = O[head col][256 ch + 128 slab + 8 (4 kg + r') + c]
-        o[8 * slab + c] = mfma16x16x16(a, pb, o[8 * slab + c]);
-      }
+    for (int ct = 0; ct < 16; ++ct) {
+      // o[ct][r] = O[head col][256 ch + 16 ct + 4 kg + r]
+      o[ct] = mfma16x16x16(lds_read_tr4(tile + v_off[ct]), pb, o[ct]);
     }
     if (t + DBUF < n_tiles) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -261,17 +250,14 @@ __global__ __launch_bounds__(DNT) void decode_kernel(
   // merge the two entry halves through LDS (the ring is free now)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   barrier();
-  float* ex = reinterpret_cast<float*>(&ring[0][0]);  // [w][head][256] then [w][head][2]
-  float* exml = ex + DNW * HB * 256;
+  // [w][head][EXR] then [w][head][2]; rows padded by 4 floats so that the
+  // 16 heads of one access fall on different LDS banks
+  constexpr int EXR = 256 + 4;
+  float* ex = reinterpret_cast<float*>(&ring[0][0]);
+  float* exml = ex + DNW * HB * EXR;
 #pragma unroll
-  for (int slab = 0; slab < 2; ++slab)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float v[8];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) v[c] = o[8 * slab + c][r];
-      store8(ex + (w * HB + col) * 256 + 128 * slab + 32 * kg + 8 * r, v);
-    }
+  for (int ct = 0; ct < 16; ++ct)
+    *reinterpret_cast<f32x4_t*>(ex + (w * HB + col) * EXR + 16 * ct + 4 * kg) = o[ct];
   if (kg == 0) {
     exml[(w * HB + col) * 2 + 0] = m_run;
     exml[(w * HB + col) * 2 + 1] = l_run;
@@ -287,8 +273,8 @@ __global__ __launch_bounds__(DNT) void decode_kernel(
   const float Lsum = fmaf(wtb, exml[(wb * HB + col) * 2 + 1], wta * exml[(wa * HB + col) * 2 + 1]);
   const int cl = 128 * eh + 32 * kg;  // column within this column half
   float acc[32];
-  const float4* pa = reinterpret_cast<const float4*>(ex + (wa * HB + col) * 256 + cl);
-  const float4* pbb = reinterpret_cast<const float4*>(ex + (wb * HB + col) * 256 + cl);
+  const float4* pa = reinterpret_cast<const float4*>(ex + (wa * HB + col) * EXR + cl);
+  const float4* pbb = reinterpret_cast<const float4*>(ex + (wb * HB + col) * EXR + cl);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float4 va = pa[i], vb = pbb[i];

@@ -117,6 +117,17 @@ __device__ __forceinline__ f32x4_t mfma16x16x16(uint2 a, uint2 b, f32x4_t c) {
                                                    __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
 }
 
+// Transposed LDS read (gfx950 ds_read_b64_tr_b16). The 16 lanes of each
+// row group g (lanes 16 g .. 16 g + 15) each point at 4 consecutive 16-bit
+// elements (8 bytes); lane 16 g + i receives element i % 4 of the rows
+// pointed at by lanes i / 4, i / 4 + 4, i / 4 + 8 and i / 4 + 12 of its group.
+__device__ __forceinline__ uint2 lds_read_tr4(const bf16_t* p) {
+  typedef short s16x4_lds __attribute__((ext_vector_type(4)));
+  const s16x4_lds v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_lds*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
 // Low / high bf16 halves of two words combined into one word: (lo(x), lo(y))
 // or (hi(x), hi(y)). Used to turn row-major fragments into k-major operands.
 __device__ __forceinline__ uint32_t lo_pair(uint32_t x, uint32_t y) { return (x & 0xffffu) | (y << 16); }
