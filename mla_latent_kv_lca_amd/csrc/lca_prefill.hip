@@ -170,14 +170,28 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     for (int r = 0; r < 16; ++r) oacc[c][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int t = 0; t < n_tiles; ++t) {
+  // Value-product operands come from transposed LDS reads
+  // (ds_read_b64_tr_b16): for column tile ct (32 latent columns) and entry
+  // k-step kap, lane l (row group g = l / 16: h32 = g / 2, column half
+  // rh = g % 2) needs V[entry][256 kh + 32 ct + 16 rh + l % 16] for the 8
+  // entries that its P operand holds (16 kap + 4 h32 + 0..3, then + 8). Read a
+  // gives the four entries 16 kap + 8 a + 4 h32 + 0..3 when the 16 lanes of
+  // the group point at entry rows (l % 16) / 4 of that run, columns
+  // 4 ((l % 16) % 4) .. + 3 of the 16-column half: the offsets below are
+  // those addresses for ct = 0, kap = 0.
+  const int tr_row0 = 4 * h32 + ((lane & 15) >> 2);     // + 16 kap + 8 a
+  const int tr_col0 = 256 * kh + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // + 32 ct
+
+  // Scores of tile t: this lane's query row r32 against entries
+  // 8 (r / 4) + 4 h32 + r % 4 (log2 units, causally masked); returns the row
+  // max over the tile (the two lanes of a query row combined).
+  auto scores = [&](int t, float (&z)[16]) -> float {
     const int64_t e0 = (int64_t)t * STILE;
     wait_dma_newer(min(n_tiles - 1 - t, PBUF - 2));
     barrier();  // tile t landed for every wave; tile t-1's slot and sx are free
     if (t + PBUF - 1 < n_tiles)
       tile_dma(src, e0 + (int64_t)(PBUF - 1) * STILE, n_blk, ring[(t + PBUF - 1) % PBUF], w, lane, off);
     const bf16_t* tile = ring[t % PBUF];
-
     // partial S^T[entry 8(r/4) + 4 h32 + r%4][query row r32] over this half
     f32x16_t sa, sb;
 #pragma unroll
@@ -190,7 +204,6 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) sx[w][r][lane] = sa[r] + sb[r];
     barrier();
-    float z[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) z[r] = (sx[2 * pr][r][lane] + sx[2 * pr + 1][r][lane]) * scale_log2;
     if (e0 + STILE > n_min) {  // causal boundary inside this tile
@@ -201,15 +214,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     float tmax = z[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, z[r]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    if (__builtin_amdgcn_ballot_w64(tmax > m_run + LAZY_LOG2) != 0) {
-      const float m_new = fmaxf(m_run, tmax);
-      const float corr = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= corr;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) oacc[c] *= corr;
-      m_run = m_new;
-    }
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  };
+  // P relative to the running max, its row sum, and O^T += V^T P^T for
+  // latent columns [256 kh, 256 kh + 256) (8 column tiles x 2 entry k-steps
+  // of MFMA 32x32x16).
+  auto accumulate = [&](int t, const float (&z)[16]) {
+    const bf16_t* tile = ring[t % PBUF];
     const float m_ref = m_run == -INFINITY ? 0.f : m_run;
     float p[16];
 #pragma unroll
@@ -217,37 +229,58 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     float ps = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) ps += p[r];
-    ps += __shfl_xor(ps, 32);
-    l_run += ps;
-
-    // O^T += V^T P^T for columns [256 kh, 256 kh + 256): per entry k-step kap,
-    // slot (h32, j) <-> entry 16 kap + 8 (j/4) + 4 h32 + j%4 (the lane's p[8 kap + j])
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps), __float_as_uint(ps), false, false);
+    l_run += __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 #pragma unroll
     for (int kap = 0; kap < 2; ++kap) {
       const uint4 pb = make_uint4(pack_bf2(p[8 * kap + 0], p[8 * kap + 1]), pack_bf2(p[8 * kap + 2], p[8 * kap + 3]),
                                   pack_bf2(p[8 * kap + 4], p[8 * kap + 5]), pack_bf2(p[8 * kap + 6], p[8 * kap + 7]));
-      uint4 R[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int ent = 16 * kap + 8 * (j >> 2) + 4 * h32 + (j & 3);
-        R[j] = *reinterpret_cast<const uint4*>(tile + 8 * chunk_pos(ent, 32 * kh + r32));
+      for (int ct = 0; ct < 8; ++ct) {
+        const int c = tr_col0 + 32 * ct;
+        const int e_a = 16 * kap + tr_row0, e_b = e_a + 8;
+        const uint2 lo = lds_read_tr4(tile + 8 * chunk_pos(e_a, c >> 3) + (c & 7));
+        const uint2 hi = lds_read_tr4(tile + 8 * chunk_pos(e_b, c >> 3) + (c & 7));
+        // oacc[ct][r] = O[query row r32][256 kh + 32 ct + 8 (r / 4) + 4 h32 + r % 4]
+        oacc[ct] = mfma32x32x16(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, oacc[ct]);
       }
-      pv_from_rows32(R, pb, oacc);
     }
+  };
+  // Online softmax with a lazy rescale; the accumulators are touched only by
+  // the MFMA inside the inner loop (see the decode kernel).
+  int t = 0;
+  while (t < n_tiles) {
+    float z[16], tmax = 0.f;
+    for (; t < n_tiles; ++t) {
+      tmax = scores(t, z);
+      if (__builtin_amdgcn_ballot_w64(tmax > m_run + LAZY_LOG2) != 0) break;
+      accumulate(t, z);
+    }
+    if (t >= n_tiles) break;
+    const float m_new = fmaxf(m_run, tmax);
+    const float corr = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= corr;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) oacc[c] *= corr;
+    m_run = m_new;
+    accumulate(t, z);
+    ++t;
   }
 
   if (!active) return;
-  // oacc[c][r] = O[query row r32][256 kh + 8 (8(r/4) + 4 h32 + r%4) + c]
+  // oacc[ct][r] = O[query row r32][256 kh + 32 ct + 8 (r / 4) + 4 h32 + r % 4]
   const int head = hg * HB + (r32 & 15);
   const float inv = 1.0f / l_run;
-  TO* dst = o + ((int64_t)i_tok * H + head) * D_C + 256 * kh;
+  TO* dst = o + ((int64_t)i_tok * H + head) * D_C + 256 * kh + 4 * h32;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    float v[8];
+  for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-    for (int c = 0; c < 8; ++c) v[c] = oacc[c][r] * inv;
-    store8(dst + 8 * (8 * (r >> 2) + 4 * h32 + (r & 3)), v);
-  }
+    for (int r4 = 0; r4 < 4; ++r4) {
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = oacc[ct][4 * r4 + j] * inv;
+      store4(dst + 32 * ct + 8 * r4, v);
+    }
   if (lse != nullptr && h32 == 0 && kh == 0)
     lse[(int64_t)i_tok * H + head] = (m_run + __log2f(l_run)) * 0.69314718055994530942f;
 }
