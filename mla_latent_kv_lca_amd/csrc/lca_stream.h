@@ -3,7 +3,7 @@
 //
 // A tile is 32 consecutive attended entries (representative rows first, then
 // raw cache rows), stored densely in LDS (576 bf16 per row) with the 16-byte
-// chunk c of row r at chunk position c ^ (r & 7): the 16 or 32 rows read by
+// chunk c of row r at chunk position c ^ swz(r) (swz below): the rows read by
 // one MFMA fragment then fall on distinct LDS banks. A workgroup of 4
 // wavefronts fills a tile with 36 global_load_lds_dwordx4 wave instructions
 // (16 bytes per lane straight into LDS, no register staging), 9 per wave.
@@ -52,9 +52,12 @@ __device__ __forceinline__ void retire(const uint4& v) {
 }
 
 // Tile rows are dense (576 bf16); the 16-byte chunk c of row r sits at chunk
-// position c ^ (r & 7), which spreads the 16 rows read by one MFMA fragment
-// over distinct LDS banks.
-__device__ __forceinline__ int chunk_pos(int r, int c) { return r * (D_ROW / 8) + (c ^ (r & 7)); }
+// position c ^ swz(r). swz permutes 0..7 over any 8 consecutive rows (so the
+// rows of a K fragment, one chunk each, use 8 different bank groups) and gives
+// the 4 rows of an aligned group distinct values in bits 1-2 (so a transposed
+// read of 4 rows x 2 adjacent chunks touches 8 different bank groups).
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+__device__ __forceinline__ int chunk_pos(int r, int c) { return r * (D_ROW / 8) + (c ^ swz(r)); }
 
 // Packed rows (k_R right after c_KV, one token stride) of the two segments of
 // one sequence: entries [0, m) are representative rows, the rest raw rows.
@@ -66,12 +69,12 @@ struct DmaSrc {
 };
 
 // LDS slot P = 64 j + lane (j = w + SNW i) of a tile holds 16-byte chunk
-// col = (P % 72) ^ (row & 7) of tile row row = P / 72; its byte offset from
+// col = (P % 72) ^ swz(row) of tile row row = P / 72; its byte offset from
 // the tile's first row is row * token stride + 16 col, fixed for every tile.
 __device__ __forceinline__ void slot_rowcol(int w, int i, int lane, int& row, int& col) {
   const int P = 64 * (w + SNW * i) + lane;
   row = P / 72;
-  col = (P - row * 72) ^ (row & 7);
+  col = (P - row * 72) ^ swz(row);
 }
 
 // Issue the DMA of tile entries [e0, e0 + STILE) into `buf`. Full tiles inside
