@@ -20,6 +20,7 @@
 // The work is HBM streaming (about 2 flop per byte): no matrix cores.
 #include "lca_device.h"
 #include "lca_internal.h"
+#include "lca_stream.h"
 
 namespace lca {
 
@@ -70,6 +71,15 @@ __global__ __launch_bounds__(QBAR_THREADS) void qbar_kernel(
 }
 
 // ---------------------------------------------------------------- K1 -------
+// v_cndmask with the lane mask in an SGPR pair, kept opaque: written as a C
+// select, the compiler turns "upper ? v[i] : v[i + half]" into a variable
+// index into v, which it then expands into a compare-and-select per element.
+__device__ __forceinline__ float lane_select(uint64_t take_b, float a, float b) {
+  float r;
+  asm("v_cndmask_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(take_b));
+  return r;
+}
+
 // Reduce v[0..G) over all 64 lanes; afterwards every lane holds the total of
 // row (lane >> (6 - LG)).
 template <int LG>
@@ -79,11 +89,11 @@ __device__ __forceinline__ float reduce_rows(float (&v)[1 << LG], int lane) {
   for (int st = 0; st < LG; ++st) {
     const int mask = 32 >> st;
     const int half = G >> (st + 1);
-    const bool upper = (lane & mask) != 0;
+    const uint64_t upper = __builtin_amdgcn_ballot_w64((lane & mask) != 0);
 #pragma unroll
     for (int i = 0; i < half; ++i) {
-      const float send = upper ? v[i] : v[i + half];
-      const float keep = upper ? v[i + half] : v[i];
+      const float send = lane_select(upper, v[i + half], v[i]);  // upper lanes send v[i]
+      const float keep = lane_select(upper, v[i], v[i + half]);
       v[i] = keep + __shfl_xor(send, mask);
     }
   }
@@ -107,6 +117,67 @@ template <> struct RowChunk<float> {
   __device__ void load(const float* p) { load8_f32(p, v); }
   __device__ float get(int i) const { return v[i]; }
 };
+
+// Scores, weights and pooled row of one group held by a wavefront (lane owns
+// latent columns 8 lane .. 8 lane + 7 and RoPE column lane of every row).
+// wsh: 32 floats of this wave's LDS, for the weights broadcast.
+template <typename TC, int LG>
+struct GroupResult {
+  float acc[8];   // pooled latent columns of this lane
+  int arg;        // anchor row within the group (wave-uniform)
+  float a_mine;   // weight of row my_row
+  int my_row;
+  TC ksel;        // anchor row's RoPE column of this lane
+};
+template <typename TC, int LG>
+__device__ __forceinline__ GroupResult<TC, LG> condense_group(const RowChunk<TC> (&rows)[1 << LG],
+                                                             const TC (&krv)[1 << LG], const float (&qc)[8],
+                                                             float qr, float sm_scale, int lane, float* wsh) {
+  constexpr int G = 1 << LG;
+  GroupResult<TC, LG> out;
+  // partial scores of this lane's columns, same operation order for every row
+  float s[G];
+#pragma unroll
+  for (int r = 0; r < G; ++r) {
+    float a = rows[r].get(0) * qc[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) a = fmaf(rows[r].get(i), qc[i], a);
+    s[r] = fmaf(to_f32(krv[r]), qr, a);
+  }
+  const float score = reduce_rows<LG>(s, lane);
+  out.my_row = lane >> (6 - LG);
+  // group max and first argmax over rows (rows sit in the top LG lane bits)
+  float mx = score;
+  int arg = out.my_row;
+#pragma unroll
+  for (int st = 0; st < LG; ++st) {
+    const int mask = 32 >> st;
+    const float om = __shfl_xor(mx, mask);
+    const int oa = __shfl_xor(arg, mask);
+    if (om > mx || (om == mx && oa < arg)) { mx = om; arg = oa; }
+  }
+  out.arg = __builtin_amdgcn_readfirstlane(arg);
+  const float e = __expf(sm_scale * (score - mx));
+  float tot = e;
+#pragma unroll
+  for (int st = 0; st < LG; ++st) tot += __shfl_xor(tot, 32 >> st);
+  out.a_mine = e / tot;
+  // every lane needs all G weights: one lane per row publishes its weight
+  if ((lane & ((64 >> LG) - 1)) == 0) wsh[out.my_row] = out.a_mine;
+  float al[G];
+#pragma unroll
+  for (int r = 0; r < G; ++r) al[r] = wsh[r];
+  // pooled latent: sum_r alpha_r c_r in row order
+#pragma unroll
+  for (int r = 0; r < G; ++r)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out.acc[i] = (r == 0) ? al[r] * rows[r].get(i) : fmaf(al[r], rows[r].get(i), out.acc[i]);
+  out.ksel = krv[0];
+#pragma unroll
+  for (int r = 1; r < G; ++r)
+    if (r == out.arg) out.ksel = krv[r];  // arg is uniform: a scalar branch per row
+  return out;
+}
 
 template <typename TC, typename TR, int LG>
 __global__ __launch_bounds__(256) void condense_kernel(
@@ -137,53 +208,151 @@ __global__ __launch_bounds__(256) void condense_kernel(
     rows[r].load(cg + r * c_tok);
     krv[r] = kg[r * kr_tok];
   }
-
-  // partial scores of this lane's columns, same operation order for every row
-  float s[G];
-#pragma unroll
-  for (int r = 0; r < G; ++r) {
-    float a = rows[r].get(0) * qc[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) a = fmaf(rows[r].get(i), qc[i], a);
-    s[r] = fmaf(to_f32(krv[r]), qr, a);
-  }
-  const float score = reduce_rows<LG>(s, lane);
-  const int my_row = lane >> (6 - LG);
-
-  // group max and first argmax over rows (rows sit in the top LG lane bits)
-  float mx = score;
-  int arg = my_row;
-#pragma unroll
-  for (int st = 0; st < LG; ++st) {
-    const int mask = 32 >> st;
-    const float om = __shfl_xor(mx, mask);
-    const int oa = __shfl_xor(arg, mask);
-    if (om > mx || (om == mx && oa < arg)) { mx = om; arg = oa; }
-  }
-  const float e = __expf(sm_scale * (score - mx));
-  float tot = e;
-#pragma unroll
-  for (int st = 0; st < LG; ++st) tot += __shfl_xor(tot, 32 >> st);
-  const float a_mine = e / tot;
-
-  // pooled latent: sum_r alpha_r c_r in row order
-  float acc[8];
-#pragma unroll
-  for (int r = 0; r < G; ++r) {
-    const float ar = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a_mine), r << (6 - LG)));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = (r == 0) ? ar * rows[r].get(i) : fmaf(ar, rows[r].get(i), acc[i]);
-  }
-  store8(rc + (int64_t)b * rc_seq + j * rc_tok + 8 * lane, acc);
-
-  // anchor row's k_R (arg is uniform across the wave)
-  TC ksel = krv[0];
-#pragma unroll
-  for (int r = 1; r < G; ++r) ksel = (r == arg) ? krv[r] : ksel;
-  rk[(int64_t)b * rk_seq + j * rk_tok + lane] = from_f32<TR>(to_f32(ksel));
-  if (lane == 0) anchor[(int64_t)b * anchor_seq + j] = (int32_t)(j * G + arg);
+  __shared__ float wsh[4][32];
+  const GroupResult<TC, LG> gr = condense_group<TC, LG>(rows, krv, qc, qr, sm_scale, lane, wsh[threadIdx.x >> 6]);
+  store8(rc + (int64_t)b * rc_seq + j * rc_tok + 8 * lane, gr.acc);
+  rk[(int64_t)b * rk_seq + j * rk_tok + lane] = from_f32<TR>(to_f32(gr.ksel));
+  if (lane == 0) anchor[(int64_t)b * anchor_seq + j] = (int32_t)(j * G + gr.arg);
   if (alpha != nullptr && (lane & ((64 >> LG) - 1)) == 0)
-    alpha[(int64_t)b * alpha_seq + j * G + my_row] = a_mine;
+    alpha[(int64_t)b * alpha_seq + j * G + gr.my_row] = gr.a_mine;
+}
+
+// ---------------------------------------------------------------- K1r ------
+// Streaming variant for packed bf16 rows and one summary query per sequence
+// (decode-time condensation), g = 8 or 16. Each wavefront walks a contiguous
+// run of groups of one sequence; group tiles (g rows x 1,152 bytes) stream
+// from HBM straight into a wave-private LDS ring by direct loads, so the
+// next groups are in flight while one is scored and pooled, and the
+// workgroups stay resident instead of being re-dispatched per group.
+// The arithmetic per group is exactly that of condense_kernel (same operand
+// order), so both kernels give bitwise equal results.
+// Completion of a tile is tracked with vmcnt, which also counts this wave's
+// stores: every group issues exactly NST stores (pooled row, anchor k_R,
+// anchor index, and the weights when requested), after the loads of the tile
+// that reuses its slot.
+template <int LG>
+struct RingCfg {
+  static constexpr int G = 1 << LG;
+  static constexpr int TILE = G * D_ROW;                      // bf16 elements per group tile
+  static constexpr int NS = LG == 3 ? 4 : 2;                  // slots per wave
+  static constexpr int NI = G * (D_ROW / 8) / 64;             // load instructions per tile
+};
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+// Wait until the tile issued before `stores_after` groups' stores and
+// `tiles_after` later tiles has landed (vmcnt counts loads and stores in
+// issue order).
+template <int LG, bool ALPHA>
+__device__ __forceinline__ void wait_tile(int stores_after, int tiles_after) {
+  constexpr int NI = RingCfg<LG>::NI, NS = RingCfg<LG>::NS, NST = ALPHA ? 4 : 3;
+  // stores_after in [0, NS], tiles_after in [0, NS - 1]
+  if constexpr (NS == 2) {
+    switch (stores_after * 2 + tiles_after) {
+      case 0: wait_vm<0>(); break;
+      case 1: wait_vm<NI>(); break;
+      case 2: wait_vm<NST>(); break;
+      case 3: wait_vm<NST + NI>(); break;
+      case 4: wait_vm<2 * NST>(); break;
+      default: wait_vm<2 * NST + NI>(); break;
+    }
+  } else {
+    static_assert(NS == 4 && 4 * NST + 3 * NI <= 63, "vmcnt immediates");
+    switch (stores_after * 4 + tiles_after) {
+      case 0: wait_vm<0>(); break;
+      case 1: wait_vm<NI>(); break;
+      case 2: wait_vm<2 * NI>(); break;
+      case 3: wait_vm<3 * NI>(); break;
+      case 4: wait_vm<NST>(); break;
+      case 5: wait_vm<NST + NI>(); break;
+      case 6: wait_vm<NST + 2 * NI>(); break;
+      case 7: wait_vm<NST + 3 * NI>(); break;
+      case 8: wait_vm<2 * NST>(); break;
+      case 9: wait_vm<2 * NST + NI>(); break;
+      case 10: wait_vm<2 * NST + 2 * NI>(); break;
+      case 11: wait_vm<2 * NST + 3 * NI>(); break;
+      case 12: wait_vm<3 * NST>(); break;
+      case 13: wait_vm<3 * NST + NI>(); break;
+      case 14: wait_vm<3 * NST + 2 * NI>(); break;
+      case 15: wait_vm<3 * NST + 3 * NI>(); break;
+      case 16: wait_vm<4 * NST>(); break;
+      case 17: wait_vm<4 * NST + NI>(); break;
+      case 18: wait_vm<4 * NST + 2 * NI>(); break;
+      default: wait_vm<4 * NST + 3 * NI>(); break;
+    }
+  }
+}
+
+template <int LG, bool ALPHA>
+__global__ __launch_bounds__(256) void condense_ring_kernel(
+    const char* __restrict__ cache, int64_t seq_b, int64_t tok_b, const float* __restrict__ qbar,
+    int64_t group_begin, int64_t n_groups, int64_t per_wave, float sm_scale,
+    bf16_t* __restrict__ rc, bf16_t* __restrict__ rk, int64_t rc_seq, int64_t rc_tok,
+    int64_t rk_seq, int64_t rk_tok, int32_t* __restrict__ anchor, int64_t anchor_seq,
+    float* __restrict__ alpha, int64_t alpha_seq) {
+  using Cfg = RingCfg<LG>;
+  constexpr int G = Cfg::G, NS = Cfg::NS, NI = Cfg::NI;
+  __shared__ __align__(16) bf16_t ring[4][NS][Cfg::TILE];
+  __shared__ float wsh[4][32];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int b = blockIdx.y;
+  const int64_t first = ((int64_t)blockIdx.x * 4 + w) * per_wave;
+  const int64_t last = min(n_groups, first + per_wave);
+  if (first >= last) return;  // wave-uniform; the kernel has no barriers
+
+  const float* qb = qbar + (int64_t)b * D_ROW;
+  float qc[8];
+  load8_f32(qb + 8 * lane, qc);
+  const float qr = qb[D_C + lane];
+  // the compiler waits for these loads here, before any tile is in flight
+  asm volatile("" ::"v"(qc[0]), "v"(qc[1]), "v"(qc[2]), "v"(qc[3]), "v"(qc[4]), "v"(qc[5]), "v"(qc[6]),
+               "v"(qc[7]), "v"(qr));
+
+  // tile load: LDS position P = 64 i + lane holds bytes [16 P, 16 P + 16) of
+  // the group's rows laid end to end (row P / 72, chunk P % 72)
+  uint32_t off[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int P = 64 * i + lane, row = P / (D_ROW / 8), c16 = P - row * (D_ROW / 8);
+    off[i] = (uint32_t)(row * tok_b) + 16u * c16;
+  }
+  const char* seq = cache + (int64_t)b * seq_b;
+  auto issue = [&](int64_t n) {
+    const char* g0 = seq + (group_begin + n) * G * tok_b;
+    const uint32_t base = lds_off(&ring[w][n % NS][0]);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dma16(g0 + off[i], base + 1024u * i);
+  };
+#pragma unroll
+  for (int k = 0; k < NS; ++k)
+    if (first + k < last) issue(first + k);
+
+  for (int64_t n = first; n < last; ++n) {
+    // after tile n was issued: the stores of groups max(first, n - NS) .. n - 1
+    // and the tiles n + 1 .. n + NS - 1
+    wait_tile<LG, ALPHA>((int)min(n - first, (int64_t)NS), (int)min(last - 1 - n, (int64_t)NS - 1));
+    const bf16_t* tile = &ring[w][n % NS][0];
+    RowChunk<bf16_t> rows[G];
+    bf16_t krv[G];
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+      rows[r].v = *reinterpret_cast<const uint4*>(tile + r * D_ROW + 8 * lane);
+      krv[r] = tile[r * D_ROW + D_C + lane];
+    }
+    // the rows are in registers: the slot takes group n + NS right away
+    if (n + NS < last) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue(n + NS);
+    }
+    const int64_t j = group_begin + n;
+    const GroupResult<bf16_t, LG> gr = condense_group<bf16_t, LG>(rows, krv, qc, qr, sm_scale, lane, wsh[w]);
+    // exactly NST vector stores per group (counted by wait_tile)
+    store8(rc + (int64_t)b * rc_seq + j * rc_tok + 8 * lane, gr.acc);
+    rk[(int64_t)b * rk_seq + j * rk_tok + lane] = gr.ksel;
+    if (lane == 0) anchor[(int64_t)b * anchor_seq + j] = (int32_t)(j * G + gr.arg);
+    if (ALPHA && (lane & ((64 >> LG) - 1)) == 0) alpha[(int64_t)b * alpha_seq + j * G + gr.my_row] = gr.a_mine;
+  }
 }
 
 template <typename TC, typename TR, int LG>
@@ -234,6 +403,27 @@ hipError_t launch_condense(const lca_latent_t& cache, int B, int g, int64_t grou
 
   int lg = 0;
   while ((1 << lg) < g) ++lg;
+  const bool packed = cache.dtype == LCA_BF16 && reps.dtype == LCA_BF16 &&
+                      static_cast<const char*>(cache.kr) == static_cast<const char*>(cache.c) + 2 * D_C &&
+                      cache.kr_tok_stride == cache.c_tok_stride && cache.kr_seq_stride == cache.c_seq_stride &&
+                      cache.c_tok_stride * 2 * 32 < ((int64_t)1 << 31);
+  if (!per_group_q && packed && (lg == 3 || lg == 4) && n_groups > 0) {
+    // one resident workgroup per CU: 4 waves x contiguous runs of groups
+    const int64_t wpb = B >= 256 ? 1 : (256 + B - 1) / B;  // workgroups per sequence
+    const int64_t per_wave = (n_groups + 4 * wpb - 1) / (4 * wpb);
+    const int64_t nblk = (n_groups + 4 * per_wave - 1) / (4 * per_wave);
+    dim3 gr((unsigned)nblk, (unsigned)B);
+#define LCA_RING(LGV, AL)                                                                          \
+  hipLaunchKernelGGL((condense_ring_kernel<LGV, AL>), gr, dim3(256), 0, stream,                    \
+                     static_cast<const char*>(cache.c), cache.c_seq_stride * 2, cache.c_tok_stride * 2, \
+                     qbar_ws, group_begin, n_groups, per_wave, sm_scale, (bf16_t*)reps.c,           \
+                     (bf16_t*)reps.kr, reps.c_seq_stride, reps.c_tok_stride, reps.kr_seq_stride,     \
+                     reps.kr_tok_stride, anchor, anchor_seq, alpha, alpha_seq)
+    if (lg == 3) { if (alpha) LCA_RING(3, true); else LCA_RING(3, false); }
+    else { if (alpha) LCA_RING(4, true); else LCA_RING(4, false); }
+#undef LCA_RING
+    return hipGetLastError();
+  }
   dim3 g1((unsigned)((n_groups + 3) / 4), (unsigned)B);
   const bool cb = cache.dtype == LCA_BF16, rb = reps.dtype == LCA_BF16;
   if (cb && rb)

@@ -66,6 +66,39 @@ def test_condense_per_group_summary_queries_prefill_style():
     anchors_agree(host(anchor)[0, gb:].astype(np.int64), ra[0], O.top2_margin(s[0]))
 
 
+@pytest.mark.parametrize("B,L,g,with_alpha", [(3, 5000, 16, True), (2, 4100, 8, False), (1, 70000, 16, False)])
+def test_condense_streaming_kernel_equals_general_kernel(B, L, g, with_alpha):
+    """Packed bf16 rows with one summary query per sequence take the streaming
+    kernel; the same rows given as separate c_KV / k_R tensors take the general
+    kernel. Both must agree bit for bit (same arithmetic order), and with the
+    oracle on sampled groups."""
+    c, kr = li.latent_cache(15, B, L)
+    li.plant_needles(15, c, kr, 3, 12.0, 0, L)
+    q = li.queries(15, B, g, H, rho=0.5)
+    m = (L - 64) // g
+    cache_t = packed(c, kr)
+    q_t = dev(q)
+    outs = []
+    for split in (False, True):
+        reps = torch.zeros((B, m, 576), dtype=torch.bfloat16, device="cuda")
+        anchor = torch.full((B, m), -1, dtype=torch.int32, device="cuda")
+        alpha = torch.zeros((B, m, g), dtype=torch.float32, device="cuda") if with_alpha else None
+        src = lca.latent(cache_t[..., :512].contiguous(), cache_t[..., 512:].contiguous()) if split \
+            else lca.packed_latent(cache_t)
+        lca.lca_condense(src, B, g, 0, m, q_t, 0, 0, 1.0, lca.packed_latent(reps), anchor, alpha)
+        outs.append((reps, anchor, alpha))
+    torch.cuda.synchronize()
+    (r0, a0, al0), (r1, a1, al1) = outs
+    assert torch.equal(r0, r1) and torch.equal(a0, a1)
+    if with_alpha:
+        assert torch.equal(al0, al1)
+    r = host(r0)
+    for b, j in zip(np.random.default_rng(3).integers(0, B, 24), np.random.default_rng(4).integers(0, m, 24)):
+        rc, _, ra, _, sc = O.condense(c[b:b + 1], kr[b:b + 1], q[b:b + 1], g, int(j), 1, 0, 0, 1.0)
+        assert_close(r[b, j, :512], rc[0, 0], what=f"rep ({b},{j})")
+        anchors_agree(host(a0)[b, j:j + 1].astype(np.int64), ra[0], O.top2_margin(sc[0]))
+
+
 def test_condense_g1_copies_rows_exactly():
     B, L = 2, 100
     c, kr = li.latent_cache(5, B, L)
