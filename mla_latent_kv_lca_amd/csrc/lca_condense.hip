@@ -15,9 +15,14 @@
 //                   sequence of operations (identical rows give bitwise equal
 //                   scores). The g partial dot products are reduced across
 //                   the 64 lanes with a halving butterfly (g/2 + g/4 + ...
-//                   shuffles instead of 6 g), the g-way softmax / argmax uses
-//                   shuffles, and the pooled row is accumulated in fp32.
+//                   exchanges instead of 6 g), all exchanges stay in
+//                   registers (lane-half swaps and DPP), the anchor is the
+//                   lowest lane of a ballot at the group max, the weights
+//                   reach every lane as scalars, and the pooled row is
+//                   accumulated in fp32.
 // The work is HBM streaming (about 2 flop per byte): no matrix cores.
+#include <algorithm>
+
 #include "lca_device.h"
 #include "lca_internal.h"
 #include "lca_stream.h"
@@ -80,33 +85,96 @@ __device__ __forceinline__ float lane_select(uint64_t take_b, float a, float b) 
   return r;
 }
 
-// Reduce v[0..G) over all 64 lanes; afterwards every lane holds the total of
-// row (lane >> (6 - LG)).
-template <int LG>
-__device__ __forceinline__ float reduce_rows(float (&v)[1 << LG], int lane) {
-  constexpr int G = 1 << LG;
-#pragma unroll
-  for (int st = 0; st < LG; ++st) {
-    const int mask = 32 >> st;
-    const int half = G >> (st + 1);
-    const uint64_t upper = __builtin_amdgcn_ballot_w64((lane & mask) != 0);
-#pragma unroll
-    for (int i = 0; i < half; ++i) {
-      const float send = lane_select(upper, v[i + half], v[i]);  // upper lanes send v[i]
-      const float keep = lane_select(upper, v[i], v[i + half]);
-      v[i] = keep + __shfl_xor(send, mask);
-    }
-  }
-  float x = v[0];
-#pragma unroll
-  for (int mask = 32 >> LG; mask >= 1; mask >>= 1) x += __shfl_xor(x, mask);
-  return x;
+// Cross-lane exchanges of the group reductions, all in registers. Lane bits
+// 5 and 4: v_permlane32_swap / v_permlane16_swap swap register halves in one
+// instruction. Bit 3: DPP rotate of each 16-lane row by 8 (lane xor 8).
+// Bit 2: DPP half-row mirror (lane l <-> 7 - l within each 8 lanes, which
+// pairs every lane that has bit 2 clear with one that has it set). Bits 1
+// and 0: DPP quad permutations (lane xor 2, lane xor 1). Every pairing is an
+// involution, so both lanes of a pair combine the same two values.
+template <int MASK>
+__device__ __forceinline__ float dpp_partner(float v) {
+  static_assert(MASK == 8 || MASK == 4 || MASK == 2 || MASK == 1, "DPP exchange");
+  constexpr int ctrl = MASK == 8 ? 0x128 : MASK == 4 ? 0x141 : MASK == 2 ? 0x4e : 0xb1;
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xf, 0xf, false));
+}
+// lanes whose bit MASK is set
+template <int MASK>
+constexpr uint64_t lanes_with_bit() {
+  uint64_t m = 0;
+  for (int l = 0; l < 64; ++l)
+    if (l & MASK) m |= uint64_t(1) << l;
+  return m;
 }
 
+// Sum (or max) of v over the two lanes of a pair differing in bit MASK.
+template <int MASK, bool MAX>
+__device__ __forceinline__ float pair_op(float v) {
+  float a, b;
+  if constexpr (MASK == 32 || MASK == 16) {
+    const auto r = MASK == 32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false)
+                              : __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else {
+    a = v;
+    b = dpp_partner<MASK>(v);
+  }
+  return MAX ? fmaxf(a, b) : a + b;
+}
+// Fold v over lane bits MASK, MASK / 2, ..., STOP (MASK >= STOP, powers of 2).
+template <int MASK, int STOP, bool MAX>
+__device__ __forceinline__ float fold_lanes(float v) {
+  if constexpr (MASK >= STOP && MASK >= 1) return fold_lanes<MASK / 2, STOP, MAX>(pair_op<MASK, MAX>(v));
+  else return v;
+}
+
+// One halving step on lane bit MASK: the lanes with the bit clear end with
+// lo summed over the pair, the lanes with it set with hi.
+template <int MASK>
+__device__ __forceinline__ float halve(float lo, float hi) {
+  if constexpr (MASK == 32 || MASK == 16) {
+    // lanes below the half boundary get (lo, lo of the partner), the others
+    // (hi of the partner, hi)
+    const auto r = MASK == 32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(hi), false, false)
+                              : __builtin_amdgcn_permlane16_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    constexpr uint64_t upper = lanes_with_bit<MASK>();
+    const float send = lane_select(upper, hi, lo);  // lanes with the bit set send lo
+    const float keep = lane_select(upper, lo, hi);
+    return keep + dpp_partner<MASK>(send);
+  }
+}
+template <int LG, int ST>
+__device__ __forceinline__ void halving_stages(float (&v)[1 << LG]) {
+  if constexpr (ST < LG) {
+    constexpr int MASK = 32 >> ST, HALF = (1 << LG) >> (ST + 1);
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) v[i] = halve<MASK>(v[i], v[i + HALF]);
+    halving_stages<LG, ST + 1>(v);
+  }
+}
+
+// Reduce v[0..G) over all 64 lanes; afterwards every lane holds the total of
+// row (lane >> (6 - LG)), bitwise the same in all lanes of the row, and every
+// row's total is formed by the same tree of additions.
+template <int LG>
+__device__ __forceinline__ float reduce_rows(float (&v)[1 << LG]) {
+  halving_stages<LG, 0>(v);
+  return fold_lanes<(32 >> LG), 1, false>(v[0]);
+}
+
+// Group rows are read exactly once: non-temporal (streaming) loads.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
 template <typename TC> struct RowChunk;  // 8 latent elements of one row held by a lane
 template <> struct RowChunk<bf16_t> {
   uint4 v;
-  __device__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ void load(const bf16_t* p) {
+    const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    v = make_uint4(t.x, t.y, t.z, t.w);
+  }
   __device__ float get(int i) const {
     const uint32_t w = u4_get(v, i >> 1);
     return (i & 1) ? bf_hi(w) : bf_lo(w);
@@ -114,13 +182,16 @@ template <> struct RowChunk<bf16_t> {
 };
 template <> struct RowChunk<float> {
   float v[8];
-  __device__ void load(const float* p) { load8_f32(p, v); }
+  __device__ void load(const float* p) {
+    const f32x4v_t a = __builtin_nontemporal_load(reinterpret_cast<const f32x4v_t*>(p));
+    const f32x4v_t b = __builtin_nontemporal_load(reinterpret_cast<const f32x4v_t*>(p) + 1);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
   __device__ float get(int i) const { return v[i]; }
 };
 
 // Scores, weights and pooled row of one group held by a wavefront (lane owns
 // latent columns 8 lane .. 8 lane + 7 and RoPE column lane of every row).
-// wsh: 32 floats of this wave's LDS, for the weights broadcast.
 template <typename TC, int LG>
 struct GroupResult {
   float acc[8];   // pooled latent columns of this lane
@@ -132,8 +203,8 @@ struct GroupResult {
 template <typename TC, int LG>
 __device__ __forceinline__ GroupResult<TC, LG> condense_group(const RowChunk<TC> (&rows)[1 << LG],
                                                              const TC (&krv)[1 << LG], const float (&qc)[8],
-                                                             float qr, float sm_scale, int lane, float* wsh) {
-  constexpr int G = 1 << LG;
+                                                             float qr, float sm_scale, int lane) {
+  constexpr int G = 1 << LG, SH = 6 - LG;  // a row's total sits in lanes [r << SH, (r + 1) << SH)
   GroupResult<TC, LG> out;
   // partial scores of this lane's columns, same operation order for every row
   float s[G];
@@ -144,30 +215,21 @@ __device__ __forceinline__ GroupResult<TC, LG> condense_group(const RowChunk<TC>
     for (int i = 1; i < 8; ++i) a = fmaf(rows[r].get(i), qc[i], a);
     s[r] = fmaf(to_f32(krv[r]), qr, a);
   }
-  const float score = reduce_rows<LG>(s, lane);
-  out.my_row = lane >> (6 - LG);
-  // group max and first argmax over rows (rows sit in the top LG lane bits)
-  float mx = score;
-  int arg = out.my_row;
-#pragma unroll
-  for (int st = 0; st < LG; ++st) {
-    const int mask = 32 >> st;
-    const float om = __shfl_xor(mx, mask);
-    const int oa = __shfl_xor(arg, mask);
-    if (om > mx || (om == mx && oa < arg)) { mx = om; arg = oa; }
-  }
-  out.arg = __builtin_amdgcn_readfirstlane(arg);
+  const float score = reduce_rows<LG>(s);
+  out.my_row = lane >> SH;
+  // group max over the row bits; the anchor is the first row that attains it
+  const float mx = fold_lanes<32, (64 >> LG), true>(score);
+  const uint64_t at_max = __builtin_amdgcn_ballot_w64(score == mx);
+  out.arg = at_max ? (int)(__builtin_ctzll(at_max) >> SH) : 0;
   const float e = __expf(sm_scale * (score - mx));
-  float tot = e;
-#pragma unroll
-  for (int st = 0; st < LG; ++st) tot += __shfl_xor(tot, 32 >> st);
+  const float tot = fold_lanes<32, (64 >> LG), false>(e);
   out.a_mine = e / tot;
-  // every lane needs all G weights: one lane per row publishes its weight
-  if ((lane & ((64 >> LG) - 1)) == 0) wsh[out.my_row] = out.a_mine;
+  // pooled latent: sum_r alpha_r c_r in row order, alpha_r read from the
+  // first lane of row r (wave-uniform, so it lives in a scalar register)
   float al[G];
 #pragma unroll
-  for (int r = 0; r < G; ++r) al[r] = wsh[r];
-  // pooled latent: sum_r alpha_r c_r in row order
+  for (int r = 0; r < G; ++r)
+    al[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(out.a_mine), r << SH));
 #pragma unroll
   for (int r = 0; r < G; ++r)
 #pragma unroll
@@ -206,10 +268,9 @@ __global__ __launch_bounds__(256) void condense_kernel(
 #pragma unroll
   for (int r = 0; r < G; ++r) {
     rows[r].load(cg + r * c_tok);
-    krv[r] = kg[r * kr_tok];
+    krv[r] = __builtin_nontemporal_load(kg + r * kr_tok);
   }
-  __shared__ float wsh[4][32];
-  const GroupResult<TC, LG> gr = condense_group<TC, LG>(rows, krv, qc, qr, sm_scale, lane, wsh[threadIdx.x >> 6]);
+  const GroupResult<TC, LG> gr = condense_group<TC, LG>(rows, krv, qc, qr, sm_scale, lane);
   store8(rc + (int64_t)b * rc_seq + j * rc_tok + 8 * lane, gr.acc);
   rk[(int64_t)b * rk_seq + j * rk_tok + lane] = from_f32<TR>(to_f32(gr.ksel));
   if (lane == 0) anchor[(int64_t)b * anchor_seq + j] = (int32_t)(j * G + gr.arg);
@@ -219,17 +280,22 @@ __global__ __launch_bounds__(256) void condense_kernel(
 
 // ---------------------------------------------------------------- K1r ------
 // Streaming variant for packed bf16 rows and one summary query per sequence
-// (decode-time condensation), g = 8 or 16. Each wavefront walks a contiguous
-// run of groups of one sequence; group tiles (g rows x 1,152 bytes) stream
-// from HBM straight into a wave-private LDS ring by direct loads, so the
-// next groups are in flight while one is scored and pooled, and the
-// workgroups stay resident instead of being re-dispatched per group.
+// (decode-time condensation), g = 8 or 16. The wavefronts of a sequence take
+// its groups round robin (wave w of W: groups w, w + W, ...), so at any time
+// the loads and the output writes of all waves fall in one narrow window of
+// memory. Group tiles (g rows x 1,152 bytes) stream from HBM straight into a
+// wave-private LDS ring by direct non-temporal loads, so the next groups are
+// in flight while one is scored and pooled, and the workgroups stay resident
+// instead of being re-dispatched per group. Outputs are written through to
+// memory (device-scope stores): a steady trickle of writes costs the read
+// stream less than bursts of write-backs from L2.
 // The arithmetic per group is exactly that of condense_kernel (same operand
 // order), so both kernels give bitwise equal results.
 // Completion of a tile is tracked with vmcnt, which also counts this wave's
 // stores: every group issues exactly NST stores (pooled row, anchor k_R,
 // anchor index, and the weights when requested), after the loads of the tile
-// that reuses its slot.
+// that reuses its slot; the stores are written in asm so that their number
+// is exact.
 template <int LG>
 struct RingCfg {
   static constexpr int G = 1 << LG;
@@ -239,6 +305,19 @@ struct RingCfg {
 };
 template <int N>
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+// device-scope (write-through) vector stores, one instruction each
+// (a VALU write to the data registers of a 16-byte store must wait one cycle)
+__device__ __forceinline__ void st_wt16(void* p, uint4 v) {
+  const u32x4_t d = {v.x, v.y, v.z, v.w};
+  asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 0" ::"v"(p), "v"(d) : "memory");
+}
+__device__ __forceinline__ void st_wt4(void* p, uint32_t v) {
+  asm volatile("global_store_dword %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void st_wt2(void* p, uint32_t v) {
+  asm volatile("global_store_short %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
 
 // Wait until the tile issued before `stores_after` groups' stores and
 // `tiles_after` later tiles has landed (vmcnt counts loads and stores in
@@ -286,20 +365,20 @@ __device__ __forceinline__ void wait_tile(int stores_after, int tiles_after) {
 template <int LG, bool ALPHA>
 __global__ __launch_bounds__(256) void condense_ring_kernel(
     const char* __restrict__ cache, int64_t seq_b, int64_t tok_b, const float* __restrict__ qbar,
-    int64_t group_begin, int64_t n_groups, int64_t per_wave, float sm_scale,
+    int64_t group_begin, int64_t n_groups, float sm_scale,
     bf16_t* __restrict__ rc, bf16_t* __restrict__ rk, int64_t rc_seq, int64_t rc_tok,
     int64_t rk_seq, int64_t rk_tok, int32_t* __restrict__ anchor, int64_t anchor_seq,
     float* __restrict__ alpha, int64_t alpha_seq) {
   using Cfg = RingCfg<LG>;
   constexpr int G = Cfg::G, NS = Cfg::NS, NI = Cfg::NI;
   __shared__ __align__(16) bf16_t ring[4][NS][Cfg::TILE];
-  __shared__ float wsh[4][32];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.y;
-  const int64_t first = ((int64_t)blockIdx.x * 4 + w) * per_wave;
-  const int64_t last = min(n_groups, first + per_wave);
-  if (first >= last) return;  // wave-uniform; the kernel has no barriers
+  // this wave's groups: wg + k nw, k = 0 .. count - 1
+  const int64_t wg = (int64_t)blockIdx.x * 4 + w, nw = (int64_t)gridDim.x * 4;
+  const int64_t count = wg < n_groups ? (n_groups - 1 - wg) / nw + 1 : 0;
+  if (count == 0) return;  // wave-uniform; the kernel has no barriers
 
   const float* qb = qbar + (int64_t)b * D_ROW;
   float qc[8];
@@ -318,21 +397,21 @@ __global__ __launch_bounds__(256) void condense_ring_kernel(
     off[i] = (uint32_t)(row * tok_b) + 16u * c16;
   }
   const char* seq = cache + (int64_t)b * seq_b;
-  auto issue = [&](int64_t n) {
-    const char* g0 = seq + (group_begin + n) * G * tok_b;
-    const uint32_t base = lds_off(&ring[w][n % NS][0]);
+  auto issue = [&](int64_t k) {
+    const char* g0 = seq + (group_begin + wg + k * nw) * G * tok_b;
+    const uint32_t base = lds_off(&ring[w][k % NS][0]);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dma16(g0 + off[i], base + 1024u * i);
+    for (int i = 0; i < NI; ++i) dma16_nt(g0 + off[i], base + 1024u * i);
   };
 #pragma unroll
   for (int k = 0; k < NS; ++k)
-    if (first + k < last) issue(first + k);
+    if (k < count) issue(k);
 
-  for (int64_t n = first; n < last; ++n) {
-    // after tile n was issued: the stores of groups max(first, n - NS) .. n - 1
-    // and the tiles n + 1 .. n + NS - 1
-    wait_tile<LG, ALPHA>((int)min(n - first, (int64_t)NS), (int)min(last - 1 - n, (int64_t)NS - 1));
-    const bf16_t* tile = &ring[w][n % NS][0];
+  for (int64_t k = 0; k < count; ++k) {
+    // after tile k was issued: the stores of groups max(0, k - NS) .. k - 1
+    // and the tiles k + 1 .. k + NS - 1
+    wait_tile<LG, ALPHA>((int)min(k, (int64_t)NS), (int)min(count - 1 - k, (int64_t)NS - 1));
+    const bf16_t* tile = &ring[w][k % NS][0];
     RowChunk<bf16_t> rows[G];
     bf16_t krv[G];
 #pragma unroll
@@ -340,18 +419,21 @@ __global__ __launch_bounds__(256) void condense_ring_kernel(
       rows[r].v = *reinterpret_cast<const uint4*>(tile + r * D_ROW + 8 * lane);
       krv[r] = tile[r * D_ROW + D_C + lane];
     }
-    // the rows are in registers: the slot takes group n + NS right away
-    if (n + NS < last) {
+    // the rows are in registers: the slot takes group k + NS right away
+    if (k + NS < count) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      issue(n + NS);
+      issue(k + NS);
     }
-    const int64_t j = group_begin + n;
-    const GroupResult<bf16_t, LG> gr = condense_group<bf16_t, LG>(rows, krv, qc, qr, sm_scale, lane, wsh[w]);
+    const int64_t j = group_begin + wg + k * nw;
+    const GroupResult<bf16_t, LG> gr = condense_group<bf16_t, LG>(rows, krv, qc, qr, sm_scale, lane);
     // exactly NST vector stores per group (counted by wait_tile)
-    store8(rc + (int64_t)b * rc_seq + j * rc_tok + 8 * lane, gr.acc);
-    rk[(int64_t)b * rk_seq + j * rk_tok + lane] = gr.ksel;
-    if (lane == 0) anchor[(int64_t)b * anchor_seq + j] = (int32_t)(j * G + gr.arg);
-    if (ALPHA && (lane & ((64 >> LG) - 1)) == 0) alpha[(int64_t)b * alpha_seq + j * G + gr.my_row] = gr.a_mine;
+    st_wt16(rc + (int64_t)b * rc_seq + j * rc_tok + 8 * lane,
+            make_uint4(pack_bf2(gr.acc[0], gr.acc[1]), pack_bf2(gr.acc[2], gr.acc[3]),
+                       pack_bf2(gr.acc[4], gr.acc[5]), pack_bf2(gr.acc[6], gr.acc[7])));
+    st_wt2(rk + (int64_t)b * rk_seq + j * rk_tok + lane, (uint32_t)gr.ksel);
+    if (lane == 0) st_wt4(anchor + (int64_t)b * anchor_seq + j, (uint32_t)(j * G + gr.arg));
+    if (ALPHA && (lane & ((64 >> LG) - 1)) == 0)
+      st_wt4(alpha + (int64_t)b * alpha_seq + j * G + gr.my_row, __float_as_uint(gr.a_mine));
   }
 }
 
@@ -408,15 +490,14 @@ hipError_t launch_condense(const lca_latent_t& cache, int B, int g, int64_t grou
                       cache.kr_tok_stride == cache.c_tok_stride && cache.kr_seq_stride == cache.c_seq_stride &&
                       cache.c_tok_stride * 2 * 32 < ((int64_t)1 << 31);
   if (!per_group_q && packed && (lg == 3 || lg == 4) && n_groups > 0) {
-    // one resident workgroup per CU: 4 waves x contiguous runs of groups
+    // one resident workgroup per CU; the waves of a sequence share its groups
     const int64_t wpb = B >= 256 ? 1 : (256 + B - 1) / B;  // workgroups per sequence
-    const int64_t per_wave = (n_groups + 4 * wpb - 1) / (4 * wpb);
-    const int64_t nblk = (n_groups + 4 * per_wave - 1) / (4 * per_wave);
+    const int64_t nblk = std::min(wpb, (n_groups + 3) / 4);
     dim3 gr((unsigned)nblk, (unsigned)B);
 #define LCA_RING(LGV, AL)                                                                          \
   hipLaunchKernelGGL((condense_ring_kernel<LGV, AL>), gr, dim3(256), 0, stream,                    \
                      static_cast<const char*>(cache.c), cache.c_seq_stride * 2, cache.c_tok_stride * 2, \
-                     qbar_ws, group_begin, n_groups, per_wave, sm_scale, (bf16_t*)reps.c,           \
+                     qbar_ws, group_begin, n_groups, sm_scale, (bf16_t*)reps.c,           \
                      (bf16_t*)reps.kr, reps.c_seq_stride, reps.c_tok_stride, reps.kr_seq_stride,     \
                      reps.kr_tok_stride, anchor, anchor_seq, alpha, alpha_seq)
     if (lg == 3) { if (alpha) LCA_RING(3, true); else LCA_RING(3, false); }

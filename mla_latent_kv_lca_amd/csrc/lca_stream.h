@@ -36,6 +36,19 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_block) {
       : "v"(g), "s"(lds_block)
       : "memory");
 }
+// The same load marked non-temporal (streaming): for rows read exactly once,
+// so they do not displace data that is read again.
+__device__ __forceinline__ void dma16_nt(const void* g, uint32_t lds_block) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off nt\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(lds_block)
+      : "memory");
+}
 // wait until at most `newer` tiles issued after the one wanted are in flight
 __device__ __forceinline__ void wait_dma_newer(int newer) {
   static_assert(DMA_PER_WAVE == 9, "vmcnt immediates assume 9 loads per tile per wave");
