@@ -17,40 +17,37 @@
 namespace lca {
 
 constexpr int SX_ROW = 36;                     // floats per head row of the staged score exchange
-constexpr int DNW = SNW;                       // wavefronts per decode workgroup (2 x 2)
+constexpr int DNW = 4;                         // wavefronts per decode workgroup
 constexpr int DNT = 64 * DNW;                  // threads per decode workgroup
-constexpr int DT = STILE;                      // entries per tile: two 16-entry halves
-constexpr int DBUF = 4;                        // LDS ring depth (tiles)
-constexpr int DT_ELEMS = STILE_ELEMS;          // dense tile, 36,864 bytes
+constexpr int DT = STILE;                      // entries per split-planning tile
+constexpr int WT = 16;                         // entries per wave tile
+constexpr int WSLOT = 2;                       // LDS slots per wavefront
+constexpr int WT_ELEMS = WT * D_ROW;           // 9,216 bf16 = 18,432 bytes
+constexpr int WT_DMA = WT * (D_ROW / 8) / 64;  // 18 direct loads per wave tile
 
 // decode_kernel: one workgroup of 4 wavefronts per (split, sequence, head
-// block), one workgroup per CU. Entries stream from HBM straight into a
-// 4-deep LDS ring of 32-entry tiles (global_load_lds, 16 bytes per lane, no
-// register staging).
-// The waves form a 2 x 2 grid: wave w owns entry half eh = w & 1 (tile rows
-// [16 eh, 16 eh + 16)) and column half ch = w >> 1 (latent columns
-// [256 ch, 256 ch + 256) and RoPE columns [32 ch, 32 ch + 32)). That block of
-// a tile is all the wave ever reads, so each wave streams its own quarter of
-// every tile and waits for it with its own vmcnt: there is no workgroup-wide
-// wait per tile, and a slot is refilled as soon as its owner is done with it,
-// which keeps all four tiles of the ring in flight. Per tile the wave
-//   forms the partial scores S^T = K Q^T over its columns (9 MFMA 16x16x32,
-//   its queries in registers), adds the partner's half (wave w ^ 2, same
-//   entries) read through LDS in a fixed order, so both partners hold the
-//   same scores and the same online-softmax state (the one barrier per tile),
-//   and accumulates O^T += V^T P^T for its own 256 columns over its 16
-//   entries (16 MFMA 16x16x16; P comes straight from the score registers,
-//   V^T is built from row fragments with half-word shuffles).
-// The two entry halves are merged once, at the end. The cost per entry is
-// 34,816 flop on 1,152 bytes, more than the fp32 vector units sustain at HBM
-// rate, hence the matrix cores.
+// block), one workgroup per CU. A sequence's entries are cut into 16-entry
+// wave tiles, dealt round robin over the 4 S wavefronts of its S splits
+// (wave w of split s takes tiles 4 s + w + 4 S k); each wavefront runs its own online softmax over its own entries for all 16
+// heads and all 576 columns, so there is no cross-wave exchange (and no
+// barrier) per tile. Its tiles stream from HBM straight into its own two LDS
+// slots (global_load_lds, 16 bytes per lane, 18 loads per tile, completion
+// tracked with its own vmcnt); a slot is refilled as soon as its tile's value
+// product is done. Per tile the wavefront
+//   forms S^T = K Q^T for its 16 entries (18 MFMA 16x16x32 in two chains,
+//   the 16 heads' queries in registers as the B operand), and
+//   accumulates O^T += V^T P^T over all 512 latent columns (32 MFMA
+//   16x16x16; P comes straight from the score registers, V^T from transposed
+//   LDS reads, ds_read_b64_tr_b16).
+// The four wavefronts' states are merged once, at the end, in wave order.
+// The cost per entry is 34,816 flop on 1,152 bytes, more than the fp32
+// vector units sustain at HBM rate, hence the matrix cores.
 // With S > 1 splits per sequence the workgroup writes its merged (O, max,
 // sum) to the workspace and a second kernel combines the splits in split order.
 //
-// Quarter layout: 16 rows x 36 chunks of 16 bytes (32 latent + 4 RoPE chunks
-// of the wave's columns), 9,216 bytes. Latent chunk j of row r sits at
-// j ^ (r & 7), RoPE chunk 32 + j at 32 + (j ^ ((r >> 1) & 3)): every group of
-// 8 lanes of a fragment read then covers 8 distinct 16-byte bank groups.
+// Tile layout: the dense rows of lca_stream.h (chunk c of row r at c ^ swz(r)),
+// so the 16 rows x 1 chunk of a K fragment and the 4 rows x 2 chunks of a
+// transposed V^T read both touch distinct LDS bank groups.
 // Reductions over the four 16-lane rows holding one head (lanes col + 16 k):
 // v_permlane16_swap / v_permlane32_swap exchange lane halves in registers;
 // both results of a swap are combined, so every lane gets the same value.
@@ -71,39 +68,36 @@ __device__ __forceinline__ float xor32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-constexpr int QROW = 36;                        // chunks per quarter row
-constexpr int QUARTER = 16 * QROW * 8;          // bf16 elements per quarter
-__device__ __forceinline__ int qchunk(int r, int j) {
-  return r * QROW + (j < 32 ? (j ^ (r & 7)) : 32 + ((j - 32) ^ ((r >> 1) & 3)));
-}
-// global 16-byte chunk (of the 72 in a row) and quarter row of LDS position
-// P = 64 i + lane of wave (eh, ch)'s quarter
-__device__ __forceinline__ void quarter_slot(int ch, int i, int lane, int& r, int& gchunk) {
-  const int P = 64 * i + lane;
-  r = P / QROW;
-  const int jp = P - r * QROW;
-  const int j = jp < 32 ? (jp ^ (r & 7)) : 32 + ((jp - 32) ^ ((r >> 1) & 3));
-  gchunk = j < 32 ? 32 * ch + j : 64 + 4 * ch + (j - 32);
-}
-// DMA of wave (eh, ch)'s quarter of tile entries [e0, e0 + 32) into `qbuf`
-__device__ __forceinline__ void quarter_dma(const DmaSrc& src, int64_t e0, int64_t e_end,
-                                            const bf16_t* qbuf, int eh, int ch, int lane,
-                                            const uint32_t (&off)[DMA_PER_WAVE]) {
-  const uint32_t base = lds_off(qbuf);
-  if (e0 + STILE <= e_end && (e0 + STILE <= src.m || e0 >= src.m)) {
+// Direct loads of wave tile entries [e0, e0 + WT) into `slot`: LDS position
+// P = 64 i + lane holds chunk (P % 72) ^ swz(row) of tile row row = P / 72.
+// Full tiles inside one segment use a uniform row base plus per-lane
+// offsets; the tile that straddles the representative / raw boundary and the
+// last, partial tile compute each row, reloading the last valid row past
+// e_end (those logits are masked, so any finite row will do).
+__device__ __forceinline__ void wave_tile_dma(const DmaSrc& src, int64_t e0, int64_t e_end,
+                                              const bf16_t* slot, int lane,
+                                              const uint32_t (&off)[WT_DMA]) {
+  const uint32_t base = lds_off(slot);
+  if (e0 + WT <= e_end && (e0 + WT <= src.m || e0 >= src.m)) {
     const char* b0 = e0 < src.m ? src.rep + e0 * src.tok : src.raw + (e0 - src.m) * src.tok;
 #pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i) dma16(b0 + off[i], base + 1024u * i);
+    for (int i = 0; i < WT_DMA; ++i) dma16(b0 + off[i], base + 1024u * i);
   } else {
-    const int valid = (int)min((int64_t)STILE, e_end - e0);
-    for (int i = 0; i < DMA_PER_WAVE; ++i) {
-      int r, gc;
-      quarter_slot(ch, i, lane, r, gc);
-      const int64_t e = e0 + min(16 * eh + r, valid - 1);
+    const int valid = (int)min((int64_t)WT, e_end - e0);
+    for (int i = 0; i < WT_DMA; ++i) {
+      const int P = 64 * i + lane, row = P / (D_ROW / 8);
+      const int c = (P - row * (D_ROW / 8)) ^ swz(row);
+      const int64_t e = e0 + min(row, valid - 1);
       const char* p = e < src.m ? src.rep + e * src.tok : src.raw + (e - src.m) * src.tok;
-      dma16(p + 16 * gc, base + 1024u * i);
+      dma16(p + 16 * c, base + 1024u * i);
     }
   }
+}
+// wait until at most `newer` wave tiles issued after the one wanted are in flight
+__device__ __forceinline__ void wait_wave_tile(int newer) {
+  static_assert(WSLOT == 2 && WT_DMA == 18, "vmcnt immediates assume 2 slots of 18 loads");
+  if (newer >= 1) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 template <typename TQ>
@@ -111,101 +105,113 @@ __global__ __launch_bounds__(DNT) void decode_kernel(
     const TQ* __restrict__ q, int64_t q_seq, DmaSrc src0, int64_t rep_seq_b, int64_t raw_seq_b,
     int64_t n_entries, int per_tiles, int S, float scale_log2, int H, float* __restrict__ part_o,
     float* __restrict__ part_ml, float* __restrict__ o_final, float* __restrict__ lse_final) {
-  __shared__ __align__(16) bf16_t ring[DBUF][DT_ELEMS];
-  __shared__ __align__(16) float sx[2][DNW][HB][HB + 4];  // partial S^T by tile parity: [wave][head][entry]
+  __shared__ __align__(16) bf16_t ring[DNW][WSLOT][WT_ELEMS];  // 147,456 bytes
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int eh = w & 1, ch = w >> 1;
   const int kg = lane >> 4, col = lane & 15;
   const int s = blockIdx.x, b = blockIdx.y, hg = blockIdx.z, HG = gridDim.z;
 
   DmaSrc src = src0;
   src.rep += (int64_t)b * rep_seq_b;
   src.raw += (int64_t)b * raw_seq_b;
-  const int64_t e_begin = (int64_t)s * per_tiles * DT;
-  const int64_t e_end = min(n_entries, e_begin + (int64_t)per_tiles * DT);
-  const int n_tiles = e_end > e_begin ? (int)((e_end - e_begin + DT - 1) / DT) : 0;
+  // the sequence's wave tiles are dealt round robin over the S x 4
+  // wavefronts of its splits: this wave takes u0 + ustep k, k < n_mine, so at
+  // any time the sequence's wavefronts read one narrow window of its entries
+  const int64_t e_end = n_entries;
+  const int64_t n_wt = (n_entries + WT - 1) / WT;
+  const int64_t u0 = w + (int64_t)DNW * s, ustep = (int64_t)DNW * S;
+  const int n_mine = n_wt > u0 ? (int)((n_wt - 1 - u0) / ustep + 1) : 0;
 
-  // Queries first, alone: all four tiles of the ring are then issued at once
-  // and stay in flight. (Requested behind the tiles, the queries would only
-  // arrive with them.) 8 latent k-steps of 32 columns and 1 RoPE k-step of
-  // head col for this wave's columns.
-  const TQ* qh = q + (int64_t)b * q_seq + (int64_t)(hg * HB + col) * D_ROW;
-  uint4 qa[9];
+  uint32_t off[WT_DMA];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) qa[ks] = load8_bf16(qh + 256 * ch + 32 * ks + 8 * kg);
-  qa[8] = load8_bf16(qh + D_C + 32 * ch + 8 * kg);
-  uint32_t off[DMA_PER_WAVE];
-#pragma unroll
-  for (int i = 0; i < DMA_PER_WAVE; ++i) {
-    int r, gc;
-    quarter_slot(ch, i, lane, r, gc);
-    off[i] = (uint32_t)((16 * eh + r) * src.tok) + 16u * gc;
+  for (int i = 0; i < WT_DMA; ++i) {
+    const int P = 64 * i + lane, row = P / (D_ROW / 8);
+    off[i] = (uint32_t)(row * src.tok) + 16u * ((P - row * (D_ROW / 8)) ^ swz(row));
   }
-  // the compiler waits for the query loads here, before any tile is in flight
-#pragma unroll
-  for (int ks = 0; ks < 9; ++ks) retire(qa[ks]);
-#pragma unroll
-  for (int t = 0; t < DBUF; ++t)
-    if (t < n_tiles) quarter_dma(src, e_begin + (int64_t)t * DT, e_end, ring[t] + w * QUARTER, eh, ch, lane, off);
+  auto issue = [&](int k) {
+    wave_tile_dma(src, (u0 + ustep * k) * WT, e_end, &ring[w][k % WSLOT][0], lane, off);
+  };
+  // lane-constant element offsets inside a wave tile.
+  // Score product, k-step ks: lane (kg, col) reads row col, chunk 4 ks + kg,
+  // at kb[ks & 1] + 64 (ks >> 1) (swz only flips the low three chunk bits).
+  const int swc = swz(col);
+  const int kb[2] = {8 * (col * (D_ROW / 8) + (kg ^ swc)), 8 * (col * (D_ROW / 8) + ((4 + kg) ^ swc))};
 
-  // lane-constant element offsets of this lane's fragments inside its quarter
-  int k_off[9], v_off[16];
+  // The queries (B operand of head col, 18 k-steps of 32 columns). bf16: the
+  // 16 query rows travel like a tile, by direct loads into slot 1 right
+  // behind tile 0, so both are in flight together; one wait covers them, the
+  // wave copies the queries into registers, and slot 1 then takes tile 1.
+  // f32: register loads (rounded to bf16), waited for before any tile is in
+  // flight (requested behind the tiles, they would only arrive with them).
+  uint4 qa[18];
+  const TQ* qh = q + (int64_t)b * q_seq + (int64_t)(hg * HB) * D_ROW;
+  if constexpr (sizeof(TQ) == 2) {
+    if (n_mine > 0) issue(0);
+    const uint32_t qbase = lds_off(&ring[w][1][0]);
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) k_off[ks] = 8 * qchunk(col, 4 * ks + kg);  // score product: A = K rows
-  k_off[8] = 8 * qchunk(col, 32 + kg);
-  // value product, column tile ct (latent columns 16 ct .. 16 ct + 15 of this
-  // wave's 256): a transposed LDS read (ds_read_b64_tr_b16) gives lane
-  // (kg, col) the values of rows 4 kg .. 4 kg + 3 in column 16 ct + col -- the
-  // MFMA A operand of V^T -- when the 16 lanes of row group kg point at rows
-  // 4 kg + col / 4, columns 16 ct + 4 (col % 4) .. + 3.
+    for (int i = 0; i < WT_DMA; ++i) {
+      const int P = 64 * i + lane, row = P / (D_ROW / 8);
+      dma16(qh + row * D_ROW + 8 * ((P - row * (D_ROW / 8)) ^ swz(row)), qbase + 1024u * i);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const bf16_t* qt = &ring[w][1][0];
 #pragma unroll
-  for (int ct = 0; ct < 16; ++ct) {
-    const int c = 16 * ct + 4 * (col & 3);
-    v_off[ct] = 8 * qchunk(4 * kg + (col >> 2), c >> 3) + (c & 7);
+    for (int ks = 0; ks < 18; ++ks) qa[ks] = *reinterpret_cast<const uint4*>(qt + kb[ks & 1] + 64 * (ks >> 1));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (n_mine > 1) issue(1);
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) qa[ks] = load8_bf16(qh + col * D_ROW + 32 * ks + 8 * kg);
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) retire(qa[ks]);
+#pragma unroll
+    for (int k = 0; k < WSLOT; ++k)
+      if (k < n_mine) issue(k);
   }
-
-  f32x4_t o[16];
+  // Value product, column tile ct (latent columns 16 ct .. 16 ct + 15): a
+  // transposed read gives lane (kg, col) the values of rows 4 kg .. 4 kg + 3
+  // in column 16 ct + col -- the A operand of V^T -- when the 16 lanes of row
+  // group kg point at rows 4 kg + col / 4, columns 16 ct + 4 (col % 4) .. + 3;
+  // that address is vb[ct & 3] + 64 (ct >> 2).
+  const int vr = 4 * kg + (col >> 2), swv = swz(vr);
+  int vb[4];
 #pragma unroll
-  for (int c = 0; c < 16; ++c) o[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 4; ++j) vb[j] = 8 * (vr * (D_ROW / 8) + ((2 * j + ((col >> 1) & 1)) ^ swv)) + 4 * (col & 1);
+
+  f32x4_t o[32];
+#pragma unroll
+  for (int c = 0; c < 32; ++c) o[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Scores of tile t for this wave's 16 entries (log2 units, masked past
-  // e_end); returns their per-head maximum.
-  auto scores = [&](int t, float (&z)[4]) -> float {
-    const int64_t e0 = e_begin + (int64_t)t * DT;
-    wait_dma_newer(min(n_tiles - 1 - t, DBUF - 1));  // this wave's quarter of tile t has landed
-    const bf16_t* tile = ring[t % DBUF] + w * QUARTER;
-    // partial S^T over this wave's columns: two independent chains
+  // Scores of wave tile k (log2 units, masked past e_end); returns their
+  // per-head maximum.
+  auto scores = [&](int k, float (&z)[4]) -> float {
+    const int64_t e0 = (u0 + ustep * k) * WT;
+    wait_wave_tile(min(n_mine - 1 - k, WSLOT - 1));
+    const bf16_t* tile = &ring[w][k % WSLOT][0];
     f32x4_t sa = f32x4_t{0.f, 0.f, 0.f, 0.f}, sb = sa;
 #pragma unroll
-    for (int ks = 0; ks < 8; ks += 2) {
-      sa = mfma16x16x32(*reinterpret_cast<const uint4*>(tile + k_off[ks]), qa[ks], sa);
-      sb = mfma16x16x32(*reinterpret_cast<const uint4*>(tile + k_off[ks + 1]), qa[ks + 1], sb);
+    for (int ks = 0; ks < 18; ks += 2) {
+      sa = mfma16x16x32(*reinterpret_cast<const uint4*>(tile + kb[0] + 64 * (ks >> 1)), qa[ks], sa);
+      sb = mfma16x16x32(*reinterpret_cast<const uint4*>(tile + kb[1] + 64 * (ks >> 1)), qa[ks + 1], sb);
     }
-    sa = mfma16x16x32(*reinterpret_cast<const uint4*>(tile + k_off[8]), qa[8], sa);
-    float(*sxt)[HB][HB + 4] = sx[t & 1];
-    *reinterpret_cast<f32x4_t*>(&sxt[w][col][4 * kg]) = sa + sb;  // S[h = col][16 eh + 4 kg + r]
-    barrier();
-    // both partners add the column halves in the same order (ch 0, then ch 1)
-    const f32x4_t sc = *reinterpret_cast<const f32x4_t*>(&sxt[eh][col][4 * kg]) +
-                       *reinterpret_cast<const f32x4_t*>(&sxt[eh + 2][col][4 * kg]);
+    const f32x4_t sc = sa + sb;  // S[entry 4 kg + r][head col]
 #pragma unroll
     for (int r = 0; r < 4; ++r) z[r] = sc[r] * scale_log2;
-    if (e0 + DT > e_end) {
+    if (e0 + WT > e_end) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (e0 + 16 * eh + 4 * kg + r >= e_end) z[r] = -INFINITY;
+        if (e0 + 4 * kg + r >= e_end) z[r] = -INFINITY;
     }
     // per head: lanes col, col + 16, col + 32, col + 48
     return xor32_max(xor16_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]))));
   };
   // Probabilities relative to the running max, their sum, and the value
-  // product O^T += V^T P^T (16 column tiles, one MFMA 16x16x16 each); then
-  // this wave's quarter of the slot takes tile t + DBUF.
-  auto accumulate = [&](int t, const float (&z)[4]) {
-    const bf16_t* tile = ring[t % DBUF] + w * QUARTER;
+  // product O^T += V^T P^T (32 column tiles); then the slot takes wave tile
+  // k + WSLOT.
+  auto accumulate = [&](int k, const float (&z)[4]) {
+    const bf16_t* tile = &ring[w][k % WSLOT][0];
     // a wave with no visible entry yet keeps m_run = -inf: its p must be 0
     const float m_ref = m_run == -INFINITY ? 0.f : m_run;
     float p[4];
@@ -214,77 +220,80 @@ __global__ __launch_bounds__(DNT) void decode_kernel(
     l_run += xor32_sum(xor16_sum((p[0] + p[1]) + (p[2] + p[3])));
     const uint2 pb = make_uint2(pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3]));
 #pragma unroll
-    for (int ct = 0; ct < 16; ++ct) {
-      // o[ct][r] = O[head col][256 ch + 16 ct + 4 kg + r]
-      o[ct] = mfma16x16x16(lds_read_tr4(tile + v_off[ct]), pb, o[ct]);
+    for (int ct = 0; ct < 32; ++ct) {
+      // o[ct][r] = O[head col][16 ct + 4 kg + r]
+      o[ct] = mfma16x16x16(lds_read_tr4(tile + vb[ct & 3] + 64 * (ct >> 2)), pb, o[ct]);
     }
-    if (t + DBUF < n_tiles) {
+    if (k + WSLOT < n_mine) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      quarter_dma(src, e_begin + (int64_t)(t + DBUF) * DT, e_end, ring[t % DBUF] + w * QUARTER, eh, ch,
-                  lane, off);
+      issue(k + WSLOT);
     }
   };
   // Online softmax with a lazy rescale: the inner loop runs while the running
   // max stays within LAZY_LOG2 of every new score, so the accumulators are
   // touched only by the MFMA there; a tile that raises it leaves the loop,
   // rescales, and the loop resumes after it.
-  int t = 0;
-  while (t < n_tiles) {
+  int k = 0;
+  while (k < n_mine) {
     float z[4], tmax = 0.f;
-    for (; t < n_tiles; ++t) {
-      tmax = scores(t, z);
+    for (; k < n_mine; ++k) {
+      tmax = scores(k, z);
       if (__builtin_amdgcn_ballot_w64(tmax > m_run + LAZY_LOG2) != 0) break;
-      accumulate(t, z);
+      accumulate(k, z);
     }
-    if (t >= n_tiles) break;
+    if (k >= n_mine) break;
     const float m_new = fmaxf(m_run, tmax);
     const float corr = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
     l_run *= corr;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) o[c] *= corr;
+    for (int c = 0; c < 32; ++c) o[c] *= corr;
     m_run = m_new;
-    accumulate(t, z);
-    ++t;
+    accumulate(k, z);
+    ++k;
   }
 
-  // merge the two entry halves through LDS (the ring is free now)
+  // merge the four wavefronts through LDS (the ring is free now):
+  // [w][head][EXR] then [w][head][2]; rows padded by 4 floats so that the
+  // heads of one access fall on different LDS banks
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   barrier();
-  // [w][head][EXR] then [w][head][2]; rows padded by 4 floats so that the
-  // 16 heads of one access fall on different LDS banks
-  constexpr int EXR = 256 + 4;
-  float* ex = reinterpret_cast<float*>(&ring[0][0]);
+  constexpr int EXR = D_C + 4;
+  float* ex = reinterpret_cast<float*>(&ring[0][0][0]);
   float* exml = ex + DNW * HB * EXR;
 #pragma unroll
-  for (int ct = 0; ct < 16; ++ct)
+  for (int ct = 0; ct < 32; ++ct)
     *reinterpret_cast<f32x4_t*>(ex + (w * HB + col) * EXR + 16 * ct + 4 * kg) = o[ct];
   if (kg == 0) {
     exml[(w * HB + col) * 2 + 0] = m_run;
     exml[(w * HB + col) * 2 + 1] = l_run;
   }
   barrier();
-  // wave w finalises columns 256 ch + 128 eh + [0, 128) of every head: lane ->
-  // head col, 32 columns starting at 256 ch + 128 eh + 32 kg
-  const int wa = 2 * ch, wb = 2 * ch + 1;  // the two entry halves of this column half
-  const float ma = exml[(wa * HB + col) * 2], mb = exml[(wb * HB + col) * 2];
-  const float M = fmaxf(ma, mb);
-  const float wta = ma == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ma - M);
-  const float wtb = mb == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mb - M);
-  const float Lsum = fmaf(wtb, exml[(wb * HB + col) * 2 + 1], wta * exml[(wa * HB + col) * 2 + 1]);
-  const int cl = 128 * eh + 32 * kg;  // column within this column half
-  float acc[32];
-  const float4* pa = reinterpret_cast<const float4*>(ex + (wa * HB + col) * EXR + cl);
-  const float4* pbb = reinterpret_cast<const float4*>(ex + (wb * HB + col) * EXR + cl);
+  // wave w finalises latent columns [128 w, 128 w + 128) of every head: lane
+  // -> head col, 32 columns starting at 128 w + 32 kg; the four states are
+  // added in wave order
+  float mw[DNW], M = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float4 va = pa[i], vb = pbb[i];
-    acc[4 * i + 0] = fmaf(wtb, vb.x, wta * va.x);
-    acc[4 * i + 1] = fmaf(wtb, vb.y, wta * va.y);
-    acc[4 * i + 2] = fmaf(wtb, vb.z, wta * va.z);
-    acc[4 * i + 3] = fmaf(wtb, vb.w, wta * va.w);
+  for (int i = 0; i < DNW; ++i) {
+    mw[i] = exml[(i * HB + col) * 2];
+    M = fmaxf(M, mw[i]);
+  }
+  float Lsum = 0.f, acc[32];
+  const int d0 = 128 * w + 32 * kg;
+#pragma unroll
+  for (int i = 0; i < DNW; ++i) {
+    const float wt = mw[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[i] - M);
+    Lsum = i == 0 ? wt * exml[(i * HB + col) * 2 + 1] : fmaf(wt, exml[(i * HB + col) * 2 + 1], Lsum);
+    const float4* pi = reinterpret_cast<const float4*>(ex + (i * HB + col) * EXR + d0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float4 v = pi[j];
+      acc[4 * j + 0] = i == 0 ? wt * v.x : fmaf(wt, v.x, acc[4 * j + 0]);
+      acc[4 * j + 1] = i == 0 ? wt * v.y : fmaf(wt, v.y, acc[4 * j + 1]);
+      acc[4 * j + 2] = i == 0 ? wt * v.z : fmaf(wt, v.z, acc[4 * j + 2]);
+      acc[4 * j + 3] = i == 0 ? wt * v.w : fmaf(wt, v.w, acc[4 * j + 3]);
+    }
   }
   const int head = hg * HB + col;
-  const int d0 = 256 * ch + cl;
   if (S == 1) {
     const float inv = 1.0f / Lsum;
     float* dst = o_final + ((int64_t)b * H + head) * D_C + d0;
