@@ -89,7 +89,8 @@ const char* lca_last_error(void);
 int lca_plan(int64_t L, int64_t w, int32_t g, lca_plan_t* out);
 
 /* Workspace bytes lca_condense needs: one fp32 summary query per sequence
- * (q_row_step == 0) or per sequence and group (q_row_step > 0). */
+ * and group (q_row_step > 0), or per sequence plus 8 fp32 partial sums of
+ * its query rows (q_row_step == 0). */
 size_t lca_condense_workspace_size(int32_t B, int64_t n_groups, int64_t q_row_step);
 
 /* Condense groups [group_begin, group_begin + n_groups) of every sequence

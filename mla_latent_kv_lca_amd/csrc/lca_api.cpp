@@ -81,7 +81,8 @@ int lca_plan(int64_t L, int64_t w, int32_t g, lca_plan_t* out) {
 
 size_t lca_condense_workspace_size(int32_t B, int64_t n_groups, int64_t q_row_step) {
   if (B < 1 || n_groups < 0) return 0;
-  const int64_t nq = q_row_step != 0 ? n_groups : (n_groups > 0 ? 1 : 0);
+  // per-group summary queries, or one per sequence plus its partial sums
+  const int64_t nq = q_row_step != 0 ? n_groups : (n_groups > 0 ? 1 + lca::QBAR_PARTS : 0);
   return (size_t)B * (size_t)nq * LCA_D_ROW * sizeof(float);
 }
 

@@ -5,9 +5,11 @@
 // importance, softmax weights, weighted pooling of c_KV) and 关键设计 2 (the
 // group's k_R is the k_R of its most important token).
 //
-// Two kernels:
+// Kernels:
 //  qbar_kernel      one workgroup per summary query: mean over g query tokens
 //                   and H heads of 576-wide absorbed queries -> fp32 workspace.
+//  qbar_part_kernel / qbar_final_kernel: the same mean for one summary query
+//                   per sequence, in 8 part sums over 8 workgroups, then added.
 //  condense_kernel  one wavefront per group. Lane l owns latent columns
 //                   [8l, 8l+8) and RoPE column l of all g rows, so each row
 //                   load is one fully coalesced 1 KB (c_KV) + 128 B (k_R)
@@ -33,9 +35,9 @@ namespace lca {
 constexpr int QBAR_PH = 14;                  // row phases
 constexpr int QBAR_THREADS = 72 * QBAR_PH;   // 72 column chunks of 8 x 14 row phases
 
-// One workgroup per summary query: thread (chunk c, phase p) sums rows
-// p, p + 14, ... of the g*H query rows, eight loads in flight at a time; the
-// 14 phase partials are then added in phase order.
+// Per-group summary queries: one workgroup per summary query; thread (chunk
+// c, phase p) sums rows p, p + 14, ... of the g*H query rows, eight loads in
+// flight at a time; the 14 phase partials are then added in phase order.
 template <typename TQ>
 __global__ __launch_bounds__(QBAR_THREADS) void qbar_kernel(
     const TQ* __restrict__ q, int64_t q_seq, int64_t q_tok, int H, int g, int64_t row0,
@@ -73,6 +75,62 @@ __global__ __launch_bounds__(QBAR_THREADS) void qbar_kernel(
     for (int p = 1; p < QBAR_PH; ++p) s += sh[p][c];
     qbar[((int64_t)b * n_q + jq) * D_ROW + c] = s * inv;
   }
+}
+
+// One summary query per sequence (decode): its g*H rows are cut into
+// QBAR_PARTS contiguous parts summed by separate workgroups (so a handful of
+// sequences still spread over many CUs), then qbar_final_kernel adds the part
+// sums in part order. Part workgroup: thread (chunk c, phase p) sums rows
+// p, p + 4, ... of its part, all its loads in flight at once, and the four
+// phase sums are added in phase order.
+constexpr int QP_PH = 4;
+constexpr int QP_THREADS = 72 * QP_PH;
+template <typename TQ>
+__global__ __launch_bounds__(QP_THREADS) void qbar_part_kernel(
+    const TQ* __restrict__ q, int64_t q_seq, int64_t q_tok, int H, int g, int64_t row0,
+    float* __restrict__ part) {
+  const int p = blockIdx.x, b = blockIdx.y;
+  const int t = threadIdx.x, ch = t % 72, ph = t / 72;
+  const int rows = g * H, per = (rows + QBAR_PARTS - 1) / QBAR_PARTS;
+  const int r_begin = p * per, r_end = min(rows, r_begin + per);
+  const TQ* base = q + (int64_t)b * q_seq + row0 * q_tok + ch * 8;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int r0 = r_begin + ph; r0 < r_end; r0 += 8 * QP_PH) {
+    float v[8][8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = r0 + u * QP_PH;
+      if (r < r_end) {
+        const int tok = r / H, h = r - tok * H;
+        load8_f32(base + (int64_t)tok * q_tok + h * D_ROW, v[u]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[u][i] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[u][i];
+  }
+  __shared__ float sh[QP_PH][D_ROW];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sh[ph][ch * 8 + i] = acc[i];
+  __syncthreads();
+  for (int c = t; c < D_ROW; c += QP_THREADS) {
+    float s = sh[0][c];
+    for (int k = 1; k < QP_PH; ++k) s += sh[k][c];
+    part[((int64_t)b * QBAR_PARTS + p) * D_ROW + c] = s;
+  }
+}
+__global__ __launch_bounds__(D_ROW) void qbar_final_kernel(const float* __restrict__ part, int rows,
+                                                           float* __restrict__ qbar) {
+  const int b = blockIdx.x, c = threadIdx.x;
+  const float* pp = part + (int64_t)b * QBAR_PARTS * D_ROW + c;
+  float s = pp[0];
+#pragma unroll
+  for (int k = 1; k < QBAR_PARTS; ++k) s += pp[k * D_ROW];
+  qbar[(int64_t)b * D_ROW + c] = s * (1.0f / (float)rows);
 }
 
 // ---------------------------------------------------------------- K1 -------
@@ -473,13 +531,26 @@ hipError_t launch_condense(const lca_latent_t& cache, int B, int g, int64_t grou
                            hipStream_t stream) {
   const int per_group_q = q_row_step != 0;
   const int64_t n_q = per_group_q ? n_groups : 1;
-  dim3 g0((unsigned)n_q, (unsigned)B);
-  if (q_dtype == LCA_BF16)
-    hipLaunchKernelGGL(qbar_kernel<bf16_t>, g0, dim3(QBAR_THREADS), 0, stream, (const bf16_t*)q,
-                       q_seq_stride, q_tok_stride, H, g, q_row0, q_row_step, (int)n_q, qbar_ws);
-  else
-    hipLaunchKernelGGL(qbar_kernel<float>, g0, dim3(QBAR_THREADS), 0, stream, (const float*)q,
-                       q_seq_stride, q_tok_stride, H, g, q_row0, q_row_step, (int)n_q, qbar_ws);
+  if (per_group_q) {
+    dim3 g0((unsigned)n_q, (unsigned)B);
+    if (q_dtype == LCA_BF16)
+      hipLaunchKernelGGL(qbar_kernel<bf16_t>, g0, dim3(QBAR_THREADS), 0, stream, (const bf16_t*)q,
+                         q_seq_stride, q_tok_stride, H, g, q_row0, q_row_step, (int)n_q, qbar_ws);
+    else
+      hipLaunchKernelGGL(qbar_kernel<float>, g0, dim3(QBAR_THREADS), 0, stream, (const float*)q,
+                         q_seq_stride, q_tok_stride, H, g, q_row0, q_row_step, (int)n_q, qbar_ws);
+  } else {
+    // workspace: [B][576] summary queries, then [B][QBAR_PARTS][576] part sums
+    float* part = qbar_ws + (int64_t)B * D_ROW;
+    dim3 gp((unsigned)QBAR_PARTS, (unsigned)B);
+    if (q_dtype == LCA_BF16)
+      hipLaunchKernelGGL(qbar_part_kernel<bf16_t>, gp, dim3(QP_THREADS), 0, stream, (const bf16_t*)q,
+                         q_seq_stride, q_tok_stride, H, g, q_row0, part);
+    else
+      hipLaunchKernelGGL(qbar_part_kernel<float>, gp, dim3(QP_THREADS), 0, stream, (const float*)q,
+                         q_seq_stride, q_tok_stride, H, g, q_row0, part);
+    hipLaunchKernelGGL(qbar_final_kernel, dim3((unsigned)B), dim3(D_ROW), 0, stream, part, g * H, qbar_ws);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 

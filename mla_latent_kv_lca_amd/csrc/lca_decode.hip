@@ -68,7 +68,9 @@ __device__ __forceinline__ float xor32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Direct loads of wave tile entries [e0, e0 + WT) into `slot`: LDS position
+// Direct loads (non-temporal: a decode step reads each row once, and a
+// model's cache over all layers far exceeds the Infinity Cache) of wave tile
+// entries [e0, e0 + WT) into `slot`: LDS position
 // P = 64 i + lane holds chunk (P % 72) ^ swz(row) of tile row row = P / 72.
 // Full tiles inside one segment use a uniform row base plus per-lane
 // offsets; the tile that straddles the representative / raw boundary and the
@@ -81,7 +83,7 @@ __device__ __forceinline__ void wave_tile_dma(const DmaSrc& src, int64_t e0, int
   if (e0 + WT <= e_end && (e0 + WT <= src.m || e0 >= src.m)) {
     const char* b0 = e0 < src.m ? src.rep + e0 * src.tok : src.raw + (e0 - src.m) * src.tok;
 #pragma unroll
-    for (int i = 0; i < WT_DMA; ++i) dma16(b0 + off[i], base + 1024u * i);
+    for (int i = 0; i < WT_DMA; ++i) dma16_nt(b0 + off[i], base + 1024u * i);
   } else {
     const int valid = (int)min((int64_t)WT, e_end - e0);
     for (int i = 0; i < WT_DMA; ++i) {
@@ -89,7 +91,7 @@ __device__ __forceinline__ void wave_tile_dma(const DmaSrc& src, int64_t e0, int
       const int c = (P - row * (D_ROW / 8)) ^ swz(row);
       const int64_t e = e0 + min(row, valid - 1);
       const char* p = e < src.m ? src.rep + e * src.tok : src.raw + (e - src.m) * src.tok;
-      dma16(p + 16 * c, base + 1024u * i);
+      dma16_nt(p + 16 * c, base + 1024u * i);
     }
   }
 }

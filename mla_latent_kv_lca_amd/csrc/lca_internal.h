@@ -27,6 +27,7 @@ hipError_t launch_condense(const lca_latent_t& cache, int B, int g, int64_t grou
                            hipStream_t stream);
 
 // ---- decode
+constexpr int QBAR_PARTS = 8;            // partial sums per shared summary query
 constexpr int DEC_TARGET_BLOCKS = 256;   // split-K aims for about one workgroup per CU
 
 struct DecodeSplit {

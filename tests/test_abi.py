@@ -51,7 +51,7 @@ def test_plan_rejects_bad_args():
 
 
 def test_workspace_sizes():
-    assert lca.lca_condense_workspace_size(32, 1984, 0) == 32 * 576 * 4
+    assert lca.lca_condense_workspace_size(32, 1984, 0) == 32 * 9 * 576 * 4  # summary query + 8 partial sums
     assert lca.lca_condense_workspace_size(1, 256, 16) == 256 * 576 * 4
     assert lca.lca_condense_workspace_size(0, 1, 0) == 0
     # one split needs no workspace; more splits need partials of 16 x 514 floats
