@@ -188,6 +188,16 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   const int tr_base = 8 * (tr_row0 * (D_ROW / 8) + ((tr_col0 >> 3) ^ (tr_sw & 3))) + (tr_col0 & 7);
   const int tr_bb = 32 * (tr_sw >> 2);
   const int tr_off[2] = {tr_base + tr_bb, tr_base - tr_bb};  // + 32 ct + 576 (16 kap + 8 a)
+  // Score-product operand, k-step f (query columns 288 kh + 16 f + 8 h32 ..):
+  // chunk c = 36 kh + 2 f + h32 of row r32, at kq[f & 3] + 64 (f >> 2) (swz
+  // only flips the low three chunk bits, so four per-lane bases cover all f).
+  const int sw32 = swz(r32);
+  int kq[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int F = jj + 2 * kh;
+    kq[jj] = 8 * (r32 * (D_ROW / 8)) + 256 * kh + 64 * (F >> 2) + 8 * ((2 * (F & 3) + h32) ^ sw32);
+  }
 
   // Scores of tile t: this lane's query row r32 against entries
   // 8 (r / 4) + 4 h32 + r % 4 (log2 units, causally masked); returns the row
@@ -199,14 +209,21 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     if (t + PBUF - 1 < n_tiles)
       tile_dma(src, e0 + (int64_t)(PBUF - 1) * STILE, n_blk, ring[(t + PBUF - 1) % PBUF], w, lane, off);
     const bf16_t* tile = ring[t % PBUF];
-    // partial S^T[entry 8(r/4) + 4 h32 + r%4][query row r32] over this half
+    // partial S^T[entry 8(r/4) + 4 h32 + r%4][query row r32] over this half;
+    // fragments are read four k-steps ahead of their MFMA
+    auto frag = [&](int f) { return *reinterpret_cast<const uint4*>(tile + kq[f & 3] + 64 * (f >> 2)); };
     f32x16_t sa, sb;
 #pragma unroll
     for (int r = 0; r < 16; ++r) { sa[r] = 0.f; sb[r] = 0.f; }
+    uint4 kf[18];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) kf[f] = frag(f);
 #pragma unroll
     for (int ks = 0; ks < 18; ks += 2) {
-      sa = mfma32x32x16(*reinterpret_cast<const uint4*>(tile + 8 * chunk_pos(r32, 36 * kh + 2 * ks + h32)), qf[ks], sa);
-      sb = mfma32x32x16(*reinterpret_cast<const uint4*>(tile + 8 * chunk_pos(r32, 36 * kh + 2 * ks + 2 + h32)), qf[ks + 1], sb);
+      if (ks + 4 < 18) kf[ks + 4] = frag(ks + 4);
+      if (ks + 5 < 18) kf[ks + 5] = frag(ks + 5);
+      sa = mfma32x32x16(kf[ks], qf[ks], sa);
+      sb = mfma32x32x16(kf[ks + 1], qf[ks + 1], sb);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) sx[w][r][lane] = sa[r] + sb[r];
