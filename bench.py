@@ -51,13 +51,14 @@ def parse():
 
 # HBM traffic of one mla_latent_attn_decode_up call on this workload, from
 # two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE per dispatch, the decode
-# and merge/up-projection kernels summed) scaled by what the same counters read for a plain 1 GiB
+# attention and merge/up-projection kernels summed) scaled by what the same counters read for a plain 1 GiB
 # copy. Valid only for the decode sources it was measured on: the digest of
 # those files is checked at run time and the figure is dropped if it differs.
 TRAFFIC_SOURCES = ("mla_latent_kv_lca_amd/csrc/lca_decode.hip", "mla_latent_kv_lca_amd/csrc/lca_stream.h",
-                   "mla_latent_kv_lca_amd/csrc/lca_tile.h", "mla_latent_kv_lca_amd/csrc/lca_device.h")
-TRAFFIC = {"sha256": "ff195f4b3f45b285b9058ed8a0edcfcd5dfc6eddf92a5539ef32f48e6ae59b38",
-           "fetch_bytes": 124_526_448, "write_bytes": 9_478_147}
+                   "mla_latent_kv_lca_amd/csrc/lca_tile.h", "mla_latent_kv_lca_amd/csrc/lca_device.h",
+                   "mla_latent_kv_lca_amd/csrc/lca_up_rows.h")
+TRAFFIC = {"sha256": "0c399d3220c3296929ff84bcc21fd589e55a348f7826767079d7d80892dfbcb4",
+           "fetch_bytes": 126_799_495, "write_bytes": 9_617_408}
 
 
 def decode_sources_digest() -> str:
