@@ -23,6 +23,10 @@ with no blocking, fusion or reordering beyond the plain definition:
          - 关键设计 2: the position key of a group is the k_R of its most
            important token I_j (the displayed anchor equation).
          - 关键设计 3: the last w tokens are never compressed.
+         - 消融实验 (ablation table): two variants beside full LCA (semantic
+           pooling + position anchor): "pure pooling including position" (the
+           position keys pooled with the same weights as the latents) and "pure
+           sparse" (the group keeps only its most important token).
   [MLA]  "新一代开源大模型架构演进与注意力机制深度对比解析" (cloud.baidu.com),
          三、核心差异分析 1: MLA caches a low-rank latent per token and projects
          it back up at compute time.
@@ -52,6 +56,11 @@ import numpy as np
 D_C = 512
 D_R = 64
 D_ROW = D_C + D_R
+
+# condensation modes: full LCA and the two ablation variants of 消融实验
+MODE_LCA = 0          # c_rep = sum alpha_i c_i, k_rep = k_R of the anchor
+MODE_POOL_ROPE = 1    # c_rep = sum alpha_i c_i, k_rep = sum alpha_i k_R,i
+MODE_ANCHOR = 2       # c_rep = c of the anchor, k_rep = k_R of the anchor
 
 
 def _f64(x) -> np.ndarray:
@@ -96,30 +105,34 @@ def softmax(x) -> np.ndarray:
     return e / e.sum(axis=-1, keepdims=True)
 
 
-def condense_group(c_rows, k_rows, qbar, sm_scale: float):
-    """One group [LCT 关键设计 1 pooling equation, 关键设计 2 anchor equation].
+def condense_group(c_rows, k_rows, qbar, sm_scale: float, mode: int = MODE_LCA):
+    """One group [LCT 关键设计 1 pooling equation, 关键设计 2 anchor equation;
+    消融实验 for the other modes].
 
     Returns (c_rep [512], k_rep [64], alpha [g], anchor (index within the
-    group), scores [g]). alpha = softmax(sm_scale * s) (R4); c_rep = sum_i
-    alpha_i c_i; anchor = first argmax of s (R3); k_rep = k_R of the anchor.
+    group), scores [g]). alpha = softmax(sm_scale * s) (R4); anchor = first
+    argmax of s (R3). MODE_LCA: c_rep = sum_i alpha_i c_i, k_rep = k_R of the
+    anchor. MODE_POOL_ROPE: k_rep = sum_i alpha_i k_R,i as well. MODE_ANCHOR:
+    c_rep and k_rep are the anchor's own row.
     """
     s = importance_scores(qbar, c_rows, k_rows)
     alpha = softmax(sm_scale * s)
-    c_rep = alpha @ _f64(c_rows)
     anchor = int(np.flatnonzero(s == s.max())[0])
-    k_rep = _f64(k_rows)[anchor]
+    c_rep = _f64(c_rows)[anchor] if mode == MODE_ANCHOR else alpha @ _f64(c_rows)
+    k_rep = alpha @ _f64(k_rows) if mode == MODE_POOL_ROPE else _f64(k_rows)[anchor]
     return c_rep, k_rep, alpha, anchor, s
 
 
 def condense(c, kr, q, g: int, group_begin: int, n_groups: int, q_row0: int,
-             q_row_step: int, sm_scale: float):
+             q_row_step: int, sm_scale: float, mode: int = MODE_LCA):
     """Condense groups [group_begin, group_begin + n_groups) of every sequence.
 
     c [B, L, 512], kr [B, L, 64], q [B, T, H, 576]. Group j (token rows
     [j g, (j+1) g)) takes its summary query from query tokens
     [q_row0 + (j - group_begin) q_row_step, ... + g) (R2, R6, R7).
     Returns rep_c [B, n, 512], rep_k [B, n, 64], anchor [B, n] (absolute token
-    index I_j), alpha [B, n, g], scores [B, n, g].
+    index I_j), alpha [B, n, g], scores [B, n, g]. `mode` selects full LCA or
+    one of the ablation variants (condense_group).
     """
     c, kr = np.asarray(c), np.asarray(kr)
     B = c.shape[0]
@@ -134,7 +147,7 @@ def condense(c, kr, q, g: int, group_begin: int, n_groups: int, q_row0: int,
             r0 = q_row0 + n * q_row_step
             qbar = summary_query(q[b, r0:r0 + g])
             cr, kk, a, i, s = condense_group(c[b, j * g:(j + 1) * g], kr[b, j * g:(j + 1) * g],
-                                             qbar, sm_scale)
+                                             qbar, sm_scale, mode)
             rep_c[b, n], rep_k[b, n], alpha[b, n], scores[b, n] = cr, kk, a, s
             anchor[b, n] = j * g + i
     return rep_c, rep_k, anchor, alpha, scores

@@ -103,6 +103,76 @@ def test_condense_worked_example_golden():
     np.testing.assert_allclose(a2[0, 0], np.array([e, e, 1, 1]) / (2 * e + 2), atol=1e-12)
 
 
+def test_condense_modes_worked_example_golden():
+    """The 消融实验 variants on the hand-derived group (golden values)."""
+    gold = _load("condense_worked_example.json")
+    g, H = gold["g"], gold["H"]
+    c, k = _worked_rows(g)
+    qbar = np.zeros(576)
+    qbar[:4] = [_num(x) for x in gold["qbar_latent_head"]]
+    q = _queries_with_mean(qbar, g, H)
+    for mode, key in ((O.MODE_POOL_ROPE, "pool_rope"), (O.MODE_ANCHOR, "anchor")):
+        rc, rk, anc, alpha, _ = O.condense(c[None], k[None], q[None], g, 0, 1, 0, 0, gold["sm_scale"], mode)
+        ex = gold["modes"][key]
+        want_c = np.zeros(512)
+        want_c[:4] = [_num(x) for x in ex["c_rep_head"]]
+        np.testing.assert_allclose(rc[0, 0], want_c, atol=1e-12)
+        want_k = np.zeros(64)
+        want_k[0] = _num(ex["k_rep_head"][0])
+        np.testing.assert_allclose(rk[0, 0], want_k, atol=1e-12)
+        assert anc[0, 0] == gold["expected"]["anchor"]
+        np.testing.assert_allclose(alpha[0, 0], [_num(x) for x in gold["expected"]["alpha"]], atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_pool_rope_mode_is_weighted_mean_with_limits(seed):
+    """Pooled RoPE key: the alpha-weighted mean (sum_i alpha_i (k_i - k_rep) = 0);
+    sm_scale -> 0 gives the plain mean, sm_scale -> inf the anchor's key."""
+    c, k, qb = _rand_group(seed, scale=0.5)
+    cr, kk, a, anc, _ = O.condense_group(c, k, qb, 1.0, O.MODE_POOL_ROPE)
+    np.testing.assert_allclose((a[:, None] * (k - kk)).sum(axis=0), 0.0, atol=1e-12)
+    cr_lca, kk_lca, _, anc_lca, _ = O.condense_group(c, k, qb, 1.0, O.MODE_LCA)
+    np.testing.assert_array_equal(cr, cr_lca)  # the latent pool is unchanged
+    assert anc == anc_lca
+    # with spread-out weights the pooled key really differs from the anchor's
+    _, kk_s, _, _, _ = O.condense_group(c, k, qb, 0.05, O.MODE_POOL_ROPE)
+    _, kk_a, _, _, _ = O.condense_group(c, k, qb, 0.05, O.MODE_LCA)
+    assert np.max(np.abs(kk_s - kk_a)) > 0.1
+    _, k0, _, _, _ = O.condense_group(c, k, qb, 1e-12, O.MODE_POOL_ROPE)
+    np.testing.assert_allclose(k0, k.mean(axis=0), atol=1e-10)
+    _, kinf, _, ainf, _ = O.condense_group(c, k, qb, 1e4, O.MODE_POOL_ROPE)
+    np.testing.assert_allclose(kinf, k[ainf], atol=1e-9)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_anchor_mode_keeps_the_anchor_row(seed):
+    """Pure sparse: the representative is the most important token's own row,
+    whatever the softmax scale."""
+    c, k, qb = _rand_group(seed, scale=0.5)
+    s = np.concatenate([c, k], axis=1) @ qb
+    i = int(np.argmax(s))
+    for sm in (1e-6, 1.0, 30.0):
+        cr, kk, a, anc, _ = O.condense_group(c, k, qb, sm, O.MODE_ANCHOR)
+        assert anc == i
+        np.testing.assert_array_equal(cr, c[i])
+        np.testing.assert_array_equal(kk, k[i])
+        assert abs(a.sum() - 1.0) <= 1e-12
+
+
+def test_all_modes_agree_on_singletons_and_identical_rows():
+    r = np.random.default_rng(11)
+    c1, k1, qb = r.standard_normal((1, 512)), r.standard_normal((1, 64)), r.standard_normal(576)
+    row_c, row_k = r.standard_normal(512), r.standard_normal(64)
+    for mode in (O.MODE_LCA, O.MODE_POOL_ROPE, O.MODE_ANCHOR):
+        cr, kk, a, anc, _ = O.condense_group(c1, k1, qb, 1.0, mode)
+        np.testing.assert_array_equal(cr, c1[0])
+        np.testing.assert_array_equal(kk, k1[0])
+        cr, kk, _, anc, _ = O.condense_group(np.tile(row_c, (16, 1)), np.tile(row_k, (16, 1)), qb, 1.0, mode)
+        np.testing.assert_allclose(cr, row_c, rtol=1e-14, atol=1e-14)
+        np.testing.assert_allclose(kk, row_k, rtol=1e-14, atol=1e-14)
+        assert anc == 0
+
+
 def _rand_group(seed, g=16, scale=1.0):
     r = np.random.default_rng(seed)
     return r.standard_normal((g, 512)), r.standard_normal((g, 64)), r.standard_normal(576) * scale
