@@ -46,6 +46,9 @@ def parse():
                     help="launch every kernel from Python instead of replaying a captured HIP graph")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB elementwise copy (counter calibration) and exit")
+    ap.add_argument("--ablation-study", action="store_true",
+                    help="only run the condensation-mode error-versus-length study and exit")
+    ap.add_argument("--study-lengths", type=str, default="2048,4096,8192,16384,32768,65536,131072")
     return ap.parse_args()
 
 
@@ -90,6 +93,107 @@ def calib_copy():
     print(json.dumps({"calib_copy_bytes_read": 2 * n, "calib_copy_bytes_written": 2 * n, "dispatches": 3}))
 
 
+def ablation_study(lengths, B=2, steps=4):
+    """Approximation error of condensed decode against exact MLA as the context
+    grows, for the method and the two variants of the pages' ablation table
+    (pooled RoPE keys; anchor row only), plus attending the window alone.
+
+    Per length L: a seeded latent cache of B sequences (bf16), summary query
+    from 16 rho = 0.5 history queries, `steps` fresh decode queries. Two input
+    regimes: "needles" (4 rows per sequence planted in the condensed history
+    with a logit of about 12, a retrieval-like structure), "diffuse" (no
+    needles: attention spread over the whole context) and "positional" (no
+    needles; every k_R is one per-sequence vector rotated to its position and
+    the queries' RoPE parts are that vector rotated to the query position, so
+    the RoPE logits carry relative position: the structure that pooling the
+    RoPE keys blurs). The reference is the
+    decode kernel over all L raw rows (m = 0), itself checked against the
+    oracle by the parity tests. Error = |o - o_ref| / |o_ref| per (sequence,
+    step, head), over the 512 latent columns; mean and max reported, then the
+    mean absolute error |o - o_ref| (unit-scale rows have norm ~22, so
+    where the exact output averages many random rows and its own norm
+    shrinks, the relative figure grows while the absolute one does not).
+    "lca_log_g" repeats every LCA representative g times in the entry list,
+    which is the same as adding log g to its logit (a representative stands
+    for g tokens); the pages give representatives no such offset (reading R4),
+    so this row is a probe of that reading, not the method.
+    Prints one JSON line."""
+    import numpy as np
+    import torch
+
+    import lca_inputs as li
+    import mla_latent_kv_lca_amd as lca
+
+    torch.cuda.set_device(0)
+    modes = (("lca", lca.LCA_MODE_LCA), ("pool_rope", lca.LCA_MODE_POOL_ROPE),
+             ("anchor", lca.LCA_MODE_ANCHOR))
+    rows = []
+    for regime in ("needles", "diffuse", "positional"):
+        for L in lengths:
+            cfg = 700 + L.bit_length() + {"needles": 0, "diffuse": 50, "positional": 100}[regime]
+            c, kr = li.latent_cache(cfg, B, L)
+            plan = lca.lca_plan(L, W, G)
+            m, rb = plan["m"], plan["raw_begin"]
+            if regime == "needles" and m > 0:
+                li.plant_needles(cfg, c, kr, 4, 12.0, 0, m * G)
+            qh_np = li.queries(cfg, B, G, H, rho=0.5)
+            qd_np = li.queries(cfg, B, steps, H, rho=0.5, stream=1)
+            if regime == "positional":
+                # RoPE logit of gain * |v|^2 ~ 6 at distance 0; history queries sit at
+                # positions L - 16 .. L - 1, decode queries at L
+                kr = li.positional_keys(cfg, B, L)
+                gain = 6.0 / 64.0
+                for t in range(G):
+                    qh_np[:, t, :, 512:] = li.positional_query_rope(cfg, B, L - G + t, gain)[:, None]
+                qd_np[:, :, :, 512:] = li.positional_query_rope(cfg, B, L, gain)[:, None, None]
+            qh = torch.from_numpy(qh_np).to("cuda", torch.bfloat16)
+            qd = torch.from_numpy(qd_np).to("cuda", torch.bfloat16)
+            cache = torch.empty((B, L, 576), dtype=torch.bfloat16, device="cuda")
+            for b in range(B):
+                cache[b] = torch.from_numpy(np.concatenate([c[b], kr[b]], -1)).to("cuda", torch.bfloat16)
+            del c, kr
+            cl = lca.packed_latent(cache)
+            ws = lca.decode_workspace(B, H, L)
+            o = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
+
+            def run(reps_lat, mm, begin):
+                outs = []
+                for st in range(steps):
+                    lca.mla_latent_attn_decode(qd[:, st].contiguous(), reps_lat, mm, cl, begin, L, 1.0, o, None, ws)
+                    outs.append(o.clone())
+                return torch.stack(outs)  # [steps, B, H, 512]
+
+            ref = run(None, 0, 0)
+            ref_n = ref.norm(dim=-1)
+
+            def err(x):
+                d = (x - ref).norm(dim=-1).flatten()
+                e = d / ref_n.flatten()
+                return [float(e.mean()), float(e.max()), float(d.mean())]
+
+            rec = {"regime": regime, "L": L, "m": m, "kept_fraction": (m + L - rb) / L,
+                   "ref_norm_mean": float(ref_n.mean()), "rel_err": {}}
+            for name, mode in modes:
+                reps = torch.empty((B, max(m, 1), 576), dtype=torch.bfloat16, device="cuda")
+                anchor = torch.empty((B, max(m, 1)), dtype=torch.int32, device="cuda")
+                if m > 0:
+                    lca.lca_condense(cl, B, G, 0, m, qh, 0, 0, 1.0, lca.packed_latent(reps), anchor, mode=mode)
+                rec["rel_err"][name] = err(run(lca.packed_latent(reps) if m > 0 else None, m, rb))
+                if mode == lca.LCA_MODE_LCA and m > 0:
+                    # each representative repeated g times = a log g offset on its logit
+                    # (the alternative to reading R4, which gives representatives none)
+                    rep_g = reps.repeat_interleave(G, dim=1).contiguous()
+                    rec["rel_err"]["lca_log_g"] = err(run(lca.packed_latent(rep_g), m * G, rb))
+                    del rep_g
+            rec["rel_err"]["window_only"] = err(run(None, 0, rb))
+            torch.cuda.synchronize()
+            rows.append(rec)
+            print(json.dumps(rec), file=sys.stderr, flush=True)
+            del cache, ws
+            torch.cuda.empty_cache()
+    print(json.dumps({"ablation_study": rows, "B": B, "steps": steps, "H": H, "g": G, "w": W}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -98,6 +202,9 @@ def main():
         sys.exit(2)
     if args.calib_copy:
         calib_copy()
+        return
+    if args.ablation_study:
+        ablation_study([int(x) for x in args.study_lengths.split(",")])
         return
     import numpy as np
     import torch

@@ -126,6 +126,27 @@ int lca_condense(const lca_latent_t* cache, int32_t B, int32_t g, int64_t group_
                  int64_t alpha_seq_stride, void* workspace, size_t workspace_bytes,
                  hipStream_t stream);
 
+/* Condensation modes. LCA_MODE_LCA is the method (关键设计 1 and 2: latent
+ * rows pooled with the softmax weights, RoPE key of the most important
+ * token). The other two are the variants of the ablation table (消融实验):
+ * LCA_MODE_POOL_ROPE pools the RoPE keys with the same weights as the
+ * latents ("pure pooling including position"); LCA_MODE_ANCHOR keeps the
+ * most important token's whole row ("pure sparse"). */
+typedef enum { LCA_MODE_LCA = 0, LCA_MODE_POOL_ROPE = 1, LCA_MODE_ANCHOR = 2 } lca_mode_t;
+
+/* lca_condense with an explicit mode (lca_condense is mode LCA_MODE_LCA).
+ * Same arguments, layouts, ownership and errors; a mode outside lca_mode_t
+ * returns LCA_ERR_INVALID_ARG. alpha and the anchor index are the same in
+ * every mode; in LCA_MODE_ANCHOR the representative is a bit-exact copy of
+ * the anchor row (converted to the representatives' dtype). */
+int lca_condense_mode(const lca_latent_t* cache, int32_t B, int32_t g, int64_t group_begin,
+                      int64_t n_groups, const void* q, int32_t q_dtype, int64_t q_seq_stride,
+                      int64_t q_tok_stride, int64_t T, int32_t H, int64_t q_row0,
+                      int64_t q_row_step, float sm_scale, const lca_latent_t* reps,
+                      int32_t* anchor_idx, int64_t anchor_seq_stride, float* alpha,
+                      int64_t alpha_seq_stride, void* workspace, size_t workspace_bytes,
+                      int32_t mode, hipStream_t stream);
+
 /* Workspace bytes mla_latent_attn_decode needs for up to max_entries
  * attended rows per sequence (split-K partial results). */
 size_t mla_latent_attn_decode_workspace_size(int32_t B, int32_t H, int64_t max_entries);

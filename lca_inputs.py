@@ -16,6 +16,11 @@ Recipe (one generator per tensor, numpy PCG64 seeded with 1000*cfg + id):
   id 4  W_UV                        N(0, 1/512)         [H, 512, 128]
   id 5  W_UK                        N(0, 1/512)         [H, 512, 128]
   id 6  needle rows (planted rows aligned with u, for unit-scale outputs)
+  id 7  one pre-rotation position vector per sequence, N(0, 1) [B, 64], for
+        inputs where position carries signal: every token's k_R is that
+        vector rotated to the token's position, and a query's RoPE part is
+        it rotated to the query's position (so the RoPE logit depends on the
+        distance only).
 Values are drawn in float32 and, for bf16 runs, rounded once on the host, so
 the oracle and the GPU read identical numbers.
 """
@@ -28,7 +33,7 @@ D_R = 64    # decoupled RoPE key width
 D_ROW = D_C + D_R
 D_V = 128   # per-head value width after the up-projection
 
-ID_C, ID_K, ID_Q, ID_WUV, ID_WUK, ID_NEEDLE = 1, 2, 3, 4, 5, 6
+ID_C, ID_K, ID_Q, ID_WUV, ID_WUK, ID_NEEDLE, ID_POS = 1, 2, 3, 4, 5, 6, 7
 
 
 def rng(cfg: int, tensor_id: int) -> np.random.Generator:
@@ -67,6 +72,21 @@ def latent_cache(cfg: int, B: int, L: int, bf16: bool = True, pos0: int = 0):
     if bf16:
         c, k = bf16_round(c), bf16_round(k)
     return c, k
+
+
+def positional_keys(cfg: int, B: int, L: int, bf16: bool = True) -> np.ndarray:
+    """k_R [B, L, 64]: the sequence's position vector rotated to each token position."""
+    v = rng(cfg, ID_POS).standard_normal((B, D_R), dtype=np.float32)
+    pos = np.arange(L)
+    k = np.stack([rope(np.broadcast_to(v[b], (L, D_R)), pos) for b in range(B)])
+    return bf16_round(k) if bf16 else k
+
+
+def positional_query_rope(cfg: int, B: int, pos: int, gain: float, bf16: bool = True) -> np.ndarray:
+    """[B, 64]: gain times the sequence's position vector rotated to position pos."""
+    v = rng(cfg, ID_POS).standard_normal((B, D_R), dtype=np.float32) * np.float32(gain)
+    q = np.stack([rope(v[b][None], np.array([pos]))[0] for b in range(B)])
+    return bf16_round(q) if bf16 else q
 
 
 def shared_direction(cfg: int, B: int) -> np.ndarray:

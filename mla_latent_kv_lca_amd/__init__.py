@@ -6,7 +6,7 @@ the current stream. There is no fallback: if the library is not built, every
 call raises.
 
 Entry points (same names as the C ABI):
-  lca_plan, lca_condense, mla_latent_attn_decode,
+  lca_plan, lca_condense (and lca_condense_mode), mla_latent_attn_decode,
   mla_latent_attn_prefill_chunk, mla_up_proj,
   lca_condense_workspace_size, mla_latent_attn_decode_workspace_size,
   lca_version, lca_last_error
@@ -23,11 +23,14 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblca.so")
 
 LCA_OK, LCA_ERR_INVALID_ARG, LCA_ERR_UNSUPPORTED, LCA_ERR_WORKSPACE, LCA_ERR_HIP = 0, -1, -2, -3, -4
 LCA_BF16, LCA_F32 = 0, 1
+# condensation modes: the method, and the two variants of the pages' ablation table
+LCA_MODE_LCA, LCA_MODE_POOL_ROPE, LCA_MODE_ANCHOR = 0, 1, 2
 D_C, D_R, D_ROW, D_V = 512, 64, 576, 128
 
 # every symbol include/lca.h declares
 EXPORTS = ("lca_version", "lca_last_error", "lca_plan", "lca_condense_workspace_size",
-           "lca_condense", "mla_latent_attn_decode_workspace_size", "mla_latent_attn_decode",
+           "lca_condense", "lca_condense_mode", "mla_latent_attn_decode_workspace_size",
+           "mla_latent_attn_decode",
            "mla_latent_attn_decode_up", "mla_latent_attn_prefill_chunk", "mla_up_proj")
 
 
@@ -74,6 +77,11 @@ def load() -> ctypes.CDLL:
                                  c_int64, c_int64, c_int64, c_int32, c_int64, c_int64, c_float,
                                  P(LatentT), c_void_p, c_int64, c_void_p, c_int64, c_void_p,
                                  c_size_t, c_void_p]
+    lib.lca_condense_mode.restype = c_int32
+    lib.lca_condense_mode.argtypes = [P(LatentT), c_int32, c_int32, c_int64, c_int64, c_void_p, c_int32,
+                                      c_int64, c_int64, c_int64, c_int32, c_int64, c_int64, c_float,
+                                      P(LatentT), c_void_p, c_int64, c_void_p, c_int64, c_void_p,
+                                      c_size_t, c_int32, c_void_p]
     lib.mla_latent_attn_decode_workspace_size.restype = c_size_t
     lib.mla_latent_attn_decode_workspace_size.argtypes = [c_int32, c_int32, c_int64]
     lib.mla_latent_attn_decode.restype = c_int32
@@ -177,19 +185,23 @@ def decode_workspace(B: int, H: int, max_entries: int, device="cuda") -> torch.T
 def lca_condense(cache: LatentT, B: int, g: int, group_begin: int, n_groups: int,
                  q: torch.Tensor, q_row0: int, q_row_step: int, sm_scale: float,
                  reps: LatentT, anchor: torch.Tensor, alpha: torch.Tensor | None = None,
-                 workspace: torch.Tensor | None = None, stream=None) -> None:
+                 workspace: torch.Tensor | None = None, stream=None, mode: int = LCA_MODE_LCA) -> None:
     """Condense groups [group_begin, group_begin + n_groups) (q: [B, T, H, 576];
-    anchor: int32 [B, *]; alpha: fp32 [B, *, g] or None)."""
+    anchor: int32 [B, *]; alpha: fp32 [B, *, g] or None). mode != LCA_MODE_LCA
+    calls lca_condense_mode (the ablation variants)."""
     if q.dim() != 4 or q.shape[-1] != D_ROW or q.stride(-1) != 1 or q.stride(-2) != D_ROW:
         raise ValueError("q must be [B, T, H, 576] with contiguous heads")
     if anchor.dtype != torch.int32:
         raise TypeError("anchor must be int32")
     ws = _workspace(lca_condense_workspace_size(B, n_groups, q_row_step), q, workspace)
-    _check(load().lca_condense(
-        ctypes.byref(cache), B, g, group_begin, n_groups, q.data_ptr(), dtype_code(q), q.stride(0),
-        q.stride(1), q.shape[1], q.shape[2], q_row0, q_row_step, sm_scale, ctypes.byref(reps),
-        anchor.data_ptr(), anchor.stride(0), _ptr(alpha), 0 if alpha is None else alpha.stride(0),
-        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
+    args = (ctypes.byref(cache), B, g, group_begin, n_groups, q.data_ptr(), dtype_code(q), q.stride(0),
+            q.stride(1), q.shape[1], q.shape[2], q_row0, q_row_step, sm_scale, ctypes.byref(reps),
+            anchor.data_ptr(), anchor.stride(0), _ptr(alpha), 0 if alpha is None else alpha.stride(0),
+            ws.data_ptr(), ws.numel() * ws.element_size())
+    if mode == LCA_MODE_LCA:
+        _check(load().lca_condense(*args, _stream(stream)))
+    else:
+        _check(load().lca_condense_mode(*args, mode, _stream(stream)))
 
 
 def mla_latent_attn_decode(q: torch.Tensor, reps: LatentT | None, m: int, raw: LatentT | None,

@@ -93,7 +93,21 @@ int lca_condense(const lca_latent_t* cache, int32_t B, int32_t g, int64_t group_
                  int32_t* anchor_idx, int64_t anchor_seq_stride, float* alpha,
                  int64_t alpha_seq_stride, void* workspace, size_t workspace_bytes,
                  hipStream_t stream) {
+  return lca_condense_mode(cache, B, g, group_begin, n_groups, q, q_dtype, q_seq_stride, q_tok_stride, T,
+                           H, q_row0, q_row_step, sm_scale, reps, anchor_idx, anchor_seq_stride, alpha,
+                           alpha_seq_stride, workspace, workspace_bytes, LCA_MODE_LCA, stream);
+}
+
+int lca_condense_mode(const lca_latent_t* cache, int32_t B, int32_t g, int64_t group_begin,
+                      int64_t n_groups, const void* q, int32_t q_dtype, int64_t q_seq_stride,
+                      int64_t q_tok_stride, int64_t T, int32_t H, int64_t q_row0,
+                      int64_t q_row_step, float sm_scale, const lca_latent_t* reps,
+                      int32_t* anchor_idx, int64_t anchor_seq_stride, float* alpha,
+                      int64_t alpha_seq_stride, void* workspace, size_t workspace_bytes,
+                      int32_t mode, hipStream_t stream) {
   int rc;
+  if (mode != LCA_MODE_LCA && mode != LCA_MODE_POOL_ROPE && mode != LCA_MODE_ANCHOR)
+    return fail(LCA_ERR_INVALID_ARG, "mode %d is not an lca_mode_t", mode);
   if ((rc = check_latent(cache, "cache", true, true)) != LCA_OK) return rc;
   if ((rc = check_latent(reps, "reps", true, true)) != LCA_OK) return rc;
   if (B < 1 || B > 65535) return fail(LCA_ERR_INVALID_ARG, "B must be in [1, 65535]");
@@ -120,7 +134,7 @@ int lca_condense(const lca_latent_t* cache, int32_t B, int32_t g, int64_t group_
   return hip_status(lca::launch_condense(*cache, B, g, group_begin, n_groups, q, q_dtype, q_seq_stride,
                                          q_tok_stride, H, q_row0, q_row_step, sm_scale, *reps,
                                          anchor_idx, anchor_seq_stride, alpha, alpha_seq_stride,
-                                         static_cast<float*>(workspace), stream),
+                                         static_cast<float*>(workspace), mode, stream),
                     "lca_condense launch");
 }
 

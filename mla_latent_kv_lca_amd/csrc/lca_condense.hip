@@ -248,20 +248,23 @@ template <> struct RowChunk<float> {
   __device__ float get(int i) const { return v[i]; }
 };
 
-// Scores, weights and pooled row of one group held by a wavefront (lane owns
-// latent columns 8 lane .. 8 lane + 7 and RoPE column lane of every row).
+// Scores, weights and representative of one group held by a wavefront (lane
+// owns latent columns 8 lane .. 8 lane + 7 and RoPE column lane of every row).
+// mode (wave-uniform): LCA_MODE_LCA pools the latents and takes the anchor's
+// RoPE key; LCA_MODE_POOL_ROPE pools the RoPE keys too; LCA_MODE_ANCHOR
+// keeps the anchor's row (the ablation variants of 消融实验).
 template <typename TC, int LG>
 struct GroupResult {
-  float acc[8];   // pooled latent columns of this lane
+  float acc[8];   // representative latent columns of this lane
   int arg;        // anchor row within the group (wave-uniform)
   float a_mine;   // weight of row my_row
   int my_row;
-  TC ksel;        // anchor row's RoPE column of this lane
+  float kval;     // representative RoPE column of this lane
 };
 template <typename TC, int LG>
 __device__ __forceinline__ GroupResult<TC, LG> condense_group(const RowChunk<TC> (&rows)[1 << LG],
                                                              const TC (&krv)[1 << LG], const float (&qc)[8],
-                                                             float qr, float sm_scale, int lane) {
+                                                             float qr, float sm_scale, int lane, int mode) {
   constexpr int G = 1 << LG, SH = 6 - LG;  // a row's total sits in lanes [r << SH, (r + 1) << SH)
   GroupResult<TC, LG> out;
   // partial scores of this lane's columns, same operation order for every row
@@ -282,20 +285,43 @@ __device__ __forceinline__ GroupResult<TC, LG> condense_group(const RowChunk<TC>
   const float e = __expf(sm_scale * (score - mx));
   const float tot = fold_lanes<32, (64 >> LG), false>(e);
   out.a_mine = e / tot;
-  // pooled latent: sum_r alpha_r c_r in row order, alpha_r read from the
-  // first lane of row r (wave-uniform, so it lives in a scalar register)
+  // alpha_r read from the first lane of row r (wave-uniform, so it lives in
+  // a scalar register)
   float al[G];
 #pragma unroll
   for (int r = 0; r < G; ++r)
     al[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(out.a_mine), r << SH));
-#pragma unroll
-  for (int r = 0; r < G; ++r)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) out.acc[i] = (r == 0) ? al[r] * rows[r].get(i) : fmaf(al[r], rows[r].get(i), out.acc[i]);
-  out.ksel = krv[0];
+  // the anchor's own row (arg is uniform: a scalar branch per row)
+  int ka = 0;
 #pragma unroll
   for (int r = 1; r < G; ++r)
-    if (r == out.arg) out.ksel = krv[r];  // arg is uniform: a scalar branch per row
+    if (r == out.arg) ka = r;
+  if (mode == LCA_MODE_ANCHOR) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out.acc[i] = rows[0].get(i);
+#pragma unroll
+    for (int r = 1; r < G; ++r)
+      if (r == ka) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out.acc[i] = rows[r].get(i);
+      }
+  } else {
+    // pooled latent: sum_r alpha_r c_r in row order
+#pragma unroll
+    for (int r = 0; r < G; ++r)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) out.acc[i] = (r == 0) ? al[r] * rows[r].get(i) : fmaf(al[r], rows[r].get(i), out.acc[i]);
+  }
+  if (mode == LCA_MODE_POOL_ROPE) {
+    out.kval = al[0] * to_f32(krv[0]);
+#pragma unroll
+    for (int r = 1; r < G; ++r) out.kval = fmaf(al[r], to_f32(krv[r]), out.kval);
+  } else {
+    out.kval = to_f32(krv[0]);
+#pragma unroll
+    for (int r = 1; r < G; ++r)
+      if (r == ka) out.kval = to_f32(krv[r]);
+  }
   return out;
 }
 
@@ -306,7 +332,7 @@ __global__ __launch_bounds__(256) void condense_kernel(
     int64_t n_q, int64_t group_begin, int64_t n_groups, float sm_scale, TR* __restrict__ rc,
     TR* __restrict__ rk, int64_t rc_seq, int64_t rc_tok, int64_t rk_seq, int64_t rk_tok,
     int32_t* __restrict__ anchor, int64_t anchor_seq, float* __restrict__ alpha,
-    int64_t alpha_seq) {
+    int64_t alpha_seq, int mode) {
   constexpr int G = 1 << LG;
   const int lane = threadIdx.x & 63;
   const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -328,9 +354,9 @@ __global__ __launch_bounds__(256) void condense_kernel(
     rows[r].load(cg + r * c_tok);
     krv[r] = __builtin_nontemporal_load(kg + r * kr_tok);
   }
-  const GroupResult<TC, LG> gr = condense_group<TC, LG>(rows, krv, qc, qr, sm_scale, lane);
+  const GroupResult<TC, LG> gr = condense_group<TC, LG>(rows, krv, qc, qr, sm_scale, lane, mode);
   store8(rc + (int64_t)b * rc_seq + j * rc_tok + 8 * lane, gr.acc);
-  rk[(int64_t)b * rk_seq + j * rk_tok + lane] = from_f32<TR>(to_f32(gr.ksel));
+  rk[(int64_t)b * rk_seq + j * rk_tok + lane] = from_f32<TR>(gr.kval);
   if (lane == 0) anchor[(int64_t)b * anchor_seq + j] = (int32_t)(j * G + gr.arg);
   if (alpha != nullptr && (lane & ((64 >> LG) - 1)) == 0)
     alpha[(int64_t)b * alpha_seq + j * G + gr.my_row] = gr.a_mine;
@@ -483,12 +509,12 @@ __global__ __launch_bounds__(256) void condense_ring_kernel(
       issue(k + NS);
     }
     const int64_t j = group_begin + wg + k * nw;
-    const GroupResult<bf16_t, LG> gr = condense_group<bf16_t, LG>(rows, krv, qc, qr, sm_scale, lane);
+    const GroupResult<bf16_t, LG> gr = condense_group<bf16_t, LG>(rows, krv, qc, qr, sm_scale, lane, LCA_MODE_LCA);
     // exactly NST vector stores per group (counted by wait_tile)
     st_wt16(rc + (int64_t)b * rc_seq + j * rc_tok + 8 * lane,
             make_uint4(pack_bf2(gr.acc[0], gr.acc[1]), pack_bf2(gr.acc[2], gr.acc[3]),
                        pack_bf2(gr.acc[4], gr.acc[5]), pack_bf2(gr.acc[6], gr.acc[7])));
-    st_wt2(rk + (int64_t)b * rk_seq + j * rk_tok + lane, (uint32_t)gr.ksel);
+    st_wt2(rk + (int64_t)b * rk_seq + j * rk_tok + lane, f2bf(gr.kval));
     if (lane == 0) st_wt4(anchor + (int64_t)b * anchor_seq + j, (uint32_t)(j * G + gr.arg));
     if (ALPHA && (lane & ((64 >> LG) - 1)) == 0)
       st_wt4(alpha + (int64_t)b * alpha_seq + j * G + gr.my_row, __float_as_uint(gr.a_mine));
@@ -499,27 +525,27 @@ template <typename TC, typename TR, int LG>
 static void launch_k1(dim3 grid, hipStream_t st, const lca_latent_t& cache, const float* qbar,
                       int per_group_q, int64_t n_q, int64_t gb, int64_t ng, float sm,
                       const lca_latent_t& reps, int32_t* anchor, int64_t anchor_seq,
-                      float* alpha, int64_t alpha_seq) {
+                      float* alpha, int64_t alpha_seq, int mode) {
   hipLaunchKernelGGL((condense_kernel<TC, TR, LG>), grid, dim3(256), 0, st,
                      (const TC*)cache.c, (const TC*)cache.kr, cache.c_seq_stride,
                      cache.c_tok_stride, cache.kr_seq_stride, cache.kr_tok_stride, qbar,
                      per_group_q, n_q, gb, ng, sm, (TR*)reps.c, (TR*)reps.kr, reps.c_seq_stride,
                      reps.c_tok_stride, reps.kr_seq_stride, reps.kr_tok_stride, anchor,
-                     anchor_seq, alpha, alpha_seq);
+                     anchor_seq, alpha, alpha_seq, mode);
 }
 
 template <typename TC, typename TR>
 static void dispatch_g(int lg, dim3 grid, hipStream_t st, const lca_latent_t& cache,
                        const float* qbar, int pg, int64_t n_q, int64_t gb, int64_t ng, float sm,
                        const lca_latent_t& reps, int32_t* anchor, int64_t as, float* alpha,
-                       int64_t als) {
+                       int64_t als, int mode) {
   switch (lg) {
-    case 0: launch_k1<TC, TR, 0>(grid, st, cache, qbar, pg, n_q, gb, ng, sm, reps, anchor, as, alpha, als); break;
-    case 1: launch_k1<TC, TR, 1>(grid, st, cache, qbar, pg, n_q, gb, ng, sm, reps, anchor, as, alpha, als); break;
-    case 2: launch_k1<TC, TR, 2>(grid, st, cache, qbar, pg, n_q, gb, ng, sm, reps, anchor, as, alpha, als); break;
-    case 3: launch_k1<TC, TR, 3>(grid, st, cache, qbar, pg, n_q, gb, ng, sm, reps, anchor, as, alpha, als); break;
-    case 4: launch_k1<TC, TR, 4>(grid, st, cache, qbar, pg, n_q, gb, ng, sm, reps, anchor, as, alpha, als); break;
-    default: launch_k1<TC, TR, 5>(grid, st, cache, qbar, pg, n_q, gb, ng, sm, reps, anchor, as, alpha, als); break;
+    case 0: launch_k1<TC, TR, 0>(grid, st, cache, qbar, pg, n_q, gb, ng, sm, reps, anchor, as, alpha, als, mode); break;
+    case 1: launch_k1<TC, TR, 1>(grid, st, cache, qbar, pg, n_q, gb, ng, sm, reps, anchor, as, alpha, als, mode); break;
+    case 2: launch_k1<TC, TR, 2>(grid, st, cache, qbar, pg, n_q, gb, ng, sm, reps, anchor, as, alpha, als, mode); break;
+    case 3: launch_k1<TC, TR, 3>(grid, st, cache, qbar, pg, n_q, gb, ng, sm, reps, anchor, as, alpha, als, mode); break;
+    case 4: launch_k1<TC, TR, 4>(grid, st, cache, qbar, pg, n_q, gb, ng, sm, reps, anchor, as, alpha, als, mode); break;
+    default: launch_k1<TC, TR, 5>(grid, st, cache, qbar, pg, n_q, gb, ng, sm, reps, anchor, as, alpha, als, mode); break;
   }
 }
 
@@ -528,7 +554,7 @@ hipError_t launch_condense(const lca_latent_t& cache, int B, int g, int64_t grou
                            int64_t q_tok_stride, int H, int64_t q_row0, int64_t q_row_step,
                            float sm_scale, const lca_latent_t& reps, int32_t* anchor,
                            int64_t anchor_seq, float* alpha, int64_t alpha_seq, float* qbar_ws,
-                           hipStream_t stream) {
+                           int mode, hipStream_t stream) {
   const int per_group_q = q_row_step != 0;
   const int64_t n_q = per_group_q ? n_groups : 1;
   if (per_group_q) {
@@ -560,7 +586,7 @@ hipError_t launch_condense(const lca_latent_t& cache, int B, int g, int64_t grou
                       static_cast<const char*>(cache.kr) == static_cast<const char*>(cache.c) + 2 * D_C &&
                       cache.kr_tok_stride == cache.c_tok_stride && cache.kr_seq_stride == cache.c_seq_stride &&
                       cache.c_tok_stride * 2 * 32 < ((int64_t)1 << 31);
-  if (!per_group_q && packed && (lg == 3 || lg == 4) && n_groups > 0) {
+  if (mode == LCA_MODE_LCA && !per_group_q && packed && (lg == 3 || lg == 4) && n_groups > 0) {
     // one resident workgroup per CU; the waves of a sequence share its groups
     const int64_t wpb = B >= 256 ? 1 : (256 + B - 1) / B;  // workgroups per sequence
     const int64_t nblk = std::min(wpb, (n_groups + 3) / 4);
@@ -579,13 +605,13 @@ hipError_t launch_condense(const lca_latent_t& cache, int B, int g, int64_t grou
   dim3 g1((unsigned)((n_groups + 3) / 4), (unsigned)B);
   const bool cb = cache.dtype == LCA_BF16, rb = reps.dtype == LCA_BF16;
   if (cb && rb)
-    dispatch_g<bf16_t, bf16_t>(lg, g1, stream, cache, qbar_ws, per_group_q, n_q, group_begin, n_groups, sm_scale, reps, anchor, anchor_seq, alpha, alpha_seq);
+    dispatch_g<bf16_t, bf16_t>(lg, g1, stream, cache, qbar_ws, per_group_q, n_q, group_begin, n_groups, sm_scale, reps, anchor, anchor_seq, alpha, alpha_seq, mode);
   else if (cb)
-    dispatch_g<bf16_t, float>(lg, g1, stream, cache, qbar_ws, per_group_q, n_q, group_begin, n_groups, sm_scale, reps, anchor, anchor_seq, alpha, alpha_seq);
+    dispatch_g<bf16_t, float>(lg, g1, stream, cache, qbar_ws, per_group_q, n_q, group_begin, n_groups, sm_scale, reps, anchor, anchor_seq, alpha, alpha_seq, mode);
   else if (rb)
-    dispatch_g<float, bf16_t>(lg, g1, stream, cache, qbar_ws, per_group_q, n_q, group_begin, n_groups, sm_scale, reps, anchor, anchor_seq, alpha, alpha_seq);
+    dispatch_g<float, bf16_t>(lg, g1, stream, cache, qbar_ws, per_group_q, n_q, group_begin, n_groups, sm_scale, reps, anchor, anchor_seq, alpha, alpha_seq, mode);
   else
-    dispatch_g<float, float>(lg, g1, stream, cache, qbar_ws, per_group_q, n_q, group_begin, n_groups, sm_scale, reps, anchor, anchor_seq, alpha, alpha_seq);
+    dispatch_g<float, float>(lg, g1, stream, cache, qbar_ws, per_group_q, n_q, group_begin, n_groups, sm_scale, reps, anchor, anchor_seq, alpha, alpha_seq, mode);
   return hipGetLastError();
 }
 

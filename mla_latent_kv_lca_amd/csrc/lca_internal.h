@@ -24,7 +24,7 @@ hipError_t launch_condense(const lca_latent_t& cache, int B, int g, int64_t grou
                            int64_t q_tok_stride, int H, int64_t q_row0, int64_t q_row_step,
                            float sm_scale, const lca_latent_t& reps, int32_t* anchor,
                            int64_t anchor_seq, float* alpha, int64_t alpha_seq, float* qbar_ws,
-                           hipStream_t stream);
+                           int mode, hipStream_t stream);
 
 // ---- decode
 constexpr int QBAR_PARTS = 8;            // partial sums per shared summary query

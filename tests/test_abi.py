@@ -97,6 +97,25 @@ def test_condense_argument_errors():
     assert _condense(lib, ok_lat, ok_lat, n=0) == lca.LCA_OK  # empty range: no launch
 
 
+def test_condense_mode_argument_errors():
+    """lca_condense_mode: the mode is checked first, then the same checks as lca_condense."""
+    lib = lca.load()
+    ok_lat = _lat()
+    a = dict(B=1, g=16, gb=0, n=1, q=64, qdt=0, qss=0, qts=576 * 16, T=16, H=16, r0=0, rs=0)
+
+    def call(mode, **kw):
+        b = dict(a, **kw)
+        return lib.lca_condense_mode(ctypes.byref(ok_lat), b["B"], b["g"], b["gb"], b["n"], b["q"], b["qdt"],
+                                     b["qss"], b["qts"], b["T"], b["H"], b["r0"], b["rs"], 1.0,
+                                     ctypes.byref(ok_lat), 64, 0, None, 0, 64, 4096, mode, None)
+    for bad in (-1, 3, 99):
+        assert call(bad) == lca.LCA_ERR_INVALID_ARG
+        assert "mode" in lca.lca_last_error()
+    assert call(lca.LCA_MODE_POOL_ROPE, g=12) == lca.LCA_ERR_UNSUPPORTED
+    assert call(lca.LCA_MODE_ANCHOR, T=15) == lca.LCA_ERR_INVALID_ARG
+    assert call(lca.LCA_MODE_ANCHOR, n=0) == lca.LCA_OK  # empty range: no launch
+
+
 def _decode(lib, reps, raw, **kw):
     a = dict(q=64, qdt=0, qss=16 * 576, B=1, H=16, m=0, rb=0, re=8, sm=1.0, o=64, lse=None,
              ws=None, wsb=0)

@@ -18,14 +18,45 @@ pytestmark = pytest.mark.gpu
 H = 16
 
 
-def _condense_gpu(cache_t, B, g, gb, n, q_t, r0, step, sm, m_cap, rep_dtype=None):
+def _condense_gpu(cache_t, B, g, gb, n, q_t, r0, step, sm, m_cap, rep_dtype=None, mode=lca.LCA_MODE_LCA):
     rep_dtype = rep_dtype or cache_t.dtype
     reps = torch.zeros((B, m_cap, 576), dtype=rep_dtype, device="cuda")
     anchor = torch.full((B, m_cap), -1, dtype=torch.int32, device="cuda")
     alpha = torch.zeros((B, m_cap, g), dtype=torch.float32, device="cuda")
     lca.lca_condense(lca.packed_latent(cache_t), B, g, gb, n, q_t, r0, step, sm,
-                     lca.packed_latent(reps), anchor, alpha)
+                     lca.packed_latent(reps), anchor, alpha, mode=mode)
     return reps, anchor, alpha
+
+
+@pytest.mark.parametrize("mode,dtype,g,step", [(lca.LCA_MODE_POOL_ROPE, torch.bfloat16, 16, 0),
+                                               (lca.LCA_MODE_POOL_ROPE, torch.float32, 8, 8),
+                                               (lca.LCA_MODE_ANCHOR, torch.bfloat16, 16, 0),
+                                               (lca.LCA_MODE_ANCHOR, torch.float32, 4, 4)])
+def test_condense_ablation_modes_match_oracle(mode, dtype, g, step):
+    """The ablation variants (pooled RoPE keys; anchor row only) against the oracle's modes."""
+    B, L, w = 2, 2600, 1024
+    bf = dtype == torch.bfloat16
+    c, kr = li.latent_cache(4, B, L, bf16=bf)
+    m = O.plan(L, w, g)["m"]
+    T = (m - 1) * step + g
+    q = li.queries(4, B, T, H, rho=0.5, bf16=bf)
+    reps, anchor, alpha = _condense_gpu(packed(c, kr, dtype), B, g, 0, m, dev(q, dtype), 0, step, 1.0, m,
+                                        mode=mode)
+    torch.cuda.synchronize()
+    rc, rk, ra, ralpha, s = O.condense(c, kr, q, g, 0, m, 0, step, 1.0, mode)
+    r = host(reps)
+    assert_close(host(alpha), ralpha, tol=1e-5, what="alpha")
+    ga = host(anchor).astype(np.int64)
+    n_sure = anchors_agree(ga, ra, O.top2_margin(s))
+    assert n_sure > 0.5 * B * m
+    if mode == lca.LCA_MODE_ANCHOR:
+        # the representative is the anchor row itself, bit for bit
+        for b in range(B):
+            np.testing.assert_array_equal(r[b, :, :512], c[b, ga[b]].astype(np.float64))
+            np.testing.assert_array_equal(r[b, :, 512:], kr[b, ga[b]].astype(np.float64))
+    else:
+        assert_close(r[..., :512], rc, what="rep c_KV")
+        assert_close(r[..., 512:], rk, what="pooled rep k_R")
 
 
 @pytest.mark.parametrize("dtype,rho", [(torch.bfloat16, 0.5), (torch.float32, 0.5), (torch.bfloat16, 0.0)])
