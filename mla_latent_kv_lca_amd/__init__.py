@@ -160,6 +160,21 @@ def lca_plan(L: int, w: int, g: int) -> dict:
             "n_entries": out.n_entries}
 
 
+def gqa_sequences(q: torch.Tensor, n_kv: int) -> torch.Tensor:
+    """GQA as independent sequences (the reading that the pages' "extends to
+    GQA" leaves open: n_kv latent caches, the H query heads in n_kv groups of
+    Hg = H / n_kv consecutive heads, group k attending and condensing cache
+    k). With caches and representatives laid out [B, n_kv, L, 576] (used as
+    [B * n_kv, L, 576]) every entry point runs GQA unchanged on B * n_kv
+    sequences of Hg heads. This reorders queries [B, T, H, 576] kv-major into
+    [B * n_kv, T, Hg, 576]; decode queries [B, H, 576] are already kv-major
+    and only need .view(B * n_kv, Hg, 576)."""
+    B, T, H, D = q.shape
+    if H % n_kv:
+        raise ValueError("H must be a multiple of n_kv")
+    return q.view(B, T, n_kv, H // n_kv, D).transpose(1, 2).contiguous().view(B * n_kv, T, H // n_kv, D)
+
+
 def lca_condense_workspace_size(B: int, n_groups: int, q_row_step: int) -> int:
     return load().lca_condense_workspace_size(B, n_groups, q_row_step)
 

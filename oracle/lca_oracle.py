@@ -47,7 +47,11 @@ Readings where the pages are silent (each is restated where it is used):
      [m_s g, t];
   R7 in decode, representatives are computed once when a group leaves the
      window and are frozen afterwards; the g most recent decode queries give
-     the summary query of the group being condensed.
+     the summary query of the group being condensed;
+  R8 GQA (关键发现 says the design extends to GQA, with no mapping): n_kv
+     independent latent caches; the H query heads form n_kv groups of
+     Hg = H / n_kv consecutive heads, group k attends cache k, and cache k is
+     condensed with the summary query of its own Hg heads.
 """
 from __future__ import annotations
 
@@ -324,3 +328,29 @@ def absorb_query(q_nope, q_rope, w_uk) -> np.ndarray:
     """Absorbed query [W_UK[h] q_nope_h ; q_rope_h] ([H, 576])."""
     qa = np.einsum("hkd,hd->hk", _f64(w_uk), _f64(q_nope))
     return np.concatenate([qa, _f64(q_rope)], axis=-1)
+
+
+def condense_gqa(c, kr, q, n_kv: int, g: int, group_begin: int, n_groups: int, q_row0: int,
+                 q_row_step: int, sm_scale: float, mode: int = MODE_LCA):
+    """GQA condensation (R8): c [B, n_kv, L, 512], kr [B, n_kv, L, 64],
+    q [B, T, H, 576]; kv group k is condensed on its own cache with its own
+    heads' queries. Returns condense()'s outputs with a kv axis after B."""
+    Hg = q.shape[2] // n_kv
+    per = [condense(c[:, k], kr[:, k], q[:, :, k * Hg:(k + 1) * Hg], g, group_begin, n_groups,
+                    q_row0, q_row_step, sm_scale, mode) for k in range(n_kv)]
+    return tuple(np.stack([o[i] for o in per], axis=1) for i in range(5))
+
+
+def decode_gqa(q, rep_c, rep_k, m: int, raw_c, raw_k, raw_begin: int, raw_end: int, n_kv: int,
+               sm_scale: float):
+    """GQA decode (R8): q [B, H, 576]; rep_* [B, n_kv, m, *]; raw_* [B, n_kv, L, *];
+    head h attends kv group h // (H / n_kv). Returns (o [B, H, 512], lse [B, H])."""
+    Hg = q.shape[1] // n_kv
+    os_, ls_ = [], []
+    for k in range(n_kv):
+        o, l = decode(q[:, k * Hg:(k + 1) * Hg], None if rep_c is None else rep_c[:, k],
+                      None if rep_k is None else rep_k[:, k], m, raw_c[:, k], raw_k[:, k], raw_begin,
+                      raw_end, sm_scale)
+        os_.append(o)
+        ls_.append(l)
+    return np.concatenate(os_, axis=1), np.concatenate(ls_, axis=1)

@@ -97,6 +97,36 @@ def test_condense_per_group_summary_queries_prefill_style():
     anchors_agree(host(anchor)[0, gb:].astype(np.int64), ra[0], O.top2_margin(s[0]))
 
 
+def test_gqa_condense_and_decode_match_oracle():
+    """GQA reading (n_kv latent caches, heads grouped per cache) through the
+    existing entry points on B * n_kv sequences, against the oracle's GQA
+    condensation and decode."""
+    B, n_kv, Hq, L, g, w = 2, 2, 32, 2600, 16, 1024
+    Hg = Hq // n_kv
+    c, kr = li.latent_cache(8, B * n_kv, L)
+    li.plant_needles(8, c, kr, 2, 14.0, 0, L)
+    q = li.queries(8, B, g, Hq, rho=0.5)
+    qd = li.queries(8, B, 1, Hq, rho=0.5, stream=1)[:, 0]
+    m = O.plan(L, w, g)["m"]
+    cache = packed(c, kr, torch.bfloat16)                      # [B * n_kv, L, 576]
+    reps, anchor, alpha = _condense_gpu(cache, B * n_kv, g, 0, m, lca.gqa_sequences(dev(q), n_kv), 0, 0, 1.0, m)
+    o = torch.empty((B * n_kv, Hg, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B * n_kv, Hg), dtype=torch.float32, device="cuda")
+    lca.mla_latent_attn_decode(dev(qd).view(B * n_kv, Hg, 576), lca.packed_latent(reps), m,
+                               lca.packed_latent(cache), m * g, L, 1.0, o, lse)
+    torch.cuda.synchronize()
+    c4, k4 = c.reshape(B, n_kv, L, 512), kr.reshape(B, n_kv, L, 64)
+    rc, rk, ra, ralpha, s = O.condense_gqa(c4, k4, q, n_kv, g, 0, m, 0, 0, 1.0)
+    r = host(reps).reshape(B, n_kv, m, 576)
+    assert_close(r[..., :512], rc, what="GQA rep c_KV")
+    assert_close(host(alpha).reshape(B, n_kv, m, g), ralpha, tol=1e-5, what="GQA alpha")
+    ga = host(anchor).astype(np.int64).reshape(B, n_kv, m)
+    assert anchors_agree(ga.reshape(-1, m), ra.reshape(-1, m), O.top2_margin(s.reshape(-1, m, g))) > 0.5 * B * n_kv * m
+    ro, rl = O.decode_gqa(qd, r[..., :512], r[..., 512:], m, c4, k4, m * g, L, n_kv, 1.0)
+    assert_close(host(o).reshape(B, Hq, 512), ro, what="GQA o_latent")
+    assert_close(host(lse).reshape(B, Hq), rl, what="GQA lse")
+
+
 @pytest.mark.parametrize("B,L,g,with_alpha", [(3, 5000, 16, True), (2, 4100, 8, False), (1, 70000, 16, False)])
 def test_condense_streaming_kernel_equals_general_kernel(B, L, g, with_alpha):
     """Packed bf16 rows with one summary query per sequence take the streaming

@@ -529,3 +529,59 @@ def test_input_recipe_moments():
     q = li.queries(9, 2, 64, 16, rho=0.5)
     assert abs(q.var() * 576 - 1) < 0.1
     np.testing.assert_array_equal(li.latent_cache(9, 2, 256)[0], c)  # seeded
+
+
+def test_gqa_decode_is_textbook_grouped_attention():
+    """R8: with nothing condensed, GQA decode + up-projection equals torch's
+    float64 attention with grouped key/value heads (enable_gqa), keys and
+    values built explicitly per head through W_UK / W_UV from its group's
+    latent rows."""
+    r = np.random.default_rng(44)
+    B, n_kv, Hg, L = 2, 2, 3, 21
+    H = n_kv * Hg
+    c = r.standard_normal((B, n_kv, L, 512))
+    kr = r.standard_normal((B, n_kv, L, 64))
+    wuk = r.standard_normal((H, 512, 128)) / math.sqrt(512)
+    wuv = r.standard_normal((H, 512, 128)) / math.sqrt(512)
+    q_nope, q_rope = r.standard_normal((B, H, 128)) * 0.4, r.standard_normal((B, H, 64)) * 0.4
+    qa = np.stack([O.absorb_query(q_nope[b], q_rope[b], wuk) for b in range(B)])
+    o_lat, _ = O.decode_gqa(qa, None, None, 0, c, kr, 0, L, n_kv, 0.9)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))  # noqa: E731
+    for b in range(B):
+        # head h's key/value from group h // Hg through its own W_UK[h] / W_UV[h]:
+        # with grouped SDPA the per-head key must be shared by the group, so
+        # compare head by head against single-head attention over that group
+        for h in range(H):
+            k = h // Hg
+            kh = np.concatenate([c[b, k] @ wuk[h], kr[b, k]], axis=1)[None]
+            vh = (c[b, k] @ wuv[h])[None]
+            qh = np.concatenate([q_nope[b, h], q_rope[b, h]])[None, None]
+            ref = F.scaled_dot_product_attention(t(qh)[None], t(kh)[None], t(vh)[None], scale=0.9)[0, 0, 0]
+            np.testing.assert_allclose(O.up_proj(o_lat[b:b + 1, h:h + 1], wuv[h:h + 1])[0, 0], ref.numpy(),
+                                       atol=1e-12)
+    # grouped SDPA over the latent rows themselves (keys [c ; k_R], values c):
+    # query heads h of group k share kv head k
+    kk = t(np.concatenate([c, kr], axis=-1))            # [B, n_kv, L, 576]
+    vv = t(c)                                            # [B, n_kv, L, 512]
+    ref = F.scaled_dot_product_attention(t(qa)[:, :, None], kk, vv, scale=0.9, enable_gqa=True)[:, :, 0]
+    np.testing.assert_allclose(o_lat, ref.numpy(), atol=1e-12)
+
+
+def test_gqa_condense_uses_each_groups_own_heads_and_cache():
+    """R8: group k's representative equals condensing cache k with the mean of
+    heads [k Hg, (k+1) Hg) only (the other groups' queries do not leak in)."""
+    r = np.random.default_rng(45)
+    B, n_kv, Hg, g, L = 1, 3, 2, 4, 16
+    c = r.standard_normal((B, n_kv, L, 512))
+    kr = r.standard_normal((B, n_kv, L, 64))
+    q = r.standard_normal((B, g, n_kv * Hg, 576)) * 0.2
+    rc, rk, anc, al, s = O.condense_gqa(c, kr, q, n_kv, g, 0, 4, 0, 0, 1.0)
+    for k in range(n_kv):
+        qbar = q[0, :, k * Hg:(k + 1) * Hg].reshape(-1, 576).mean(axis=0)
+        for j in range(4):
+            rows = np.concatenate([c[0, k, j * g:(j + 1) * g], kr[0, k, j * g:(j + 1) * g]], axis=1)
+            sc = rows @ qbar
+            np.testing.assert_allclose(s[0, k, j], sc, atol=1e-12)
+            a = np.exp(sc - sc.max()) / np.exp(sc - sc.max()).sum()
+            np.testing.assert_allclose(rc[0, k, j], a @ c[0, k, j * g:(j + 1) * g], atol=1e-12)
+            assert anc[0, k, j] == j * g + int(np.argmax(sc))
