@@ -147,6 +147,19 @@ int lca_condense_mode(const lca_latent_t* cache, int32_t B, int32_t g, int64_t g
                       int64_t alpha_seq_stride, void* workspace, size_t workspace_bytes,
                       int32_t mode, hipStream_t stream);
 
+/* A paged latent cache for ragged batches: packed bf16 rows [c_KV (512) ++
+ * k_R (64)] stored in fixed-size pages of a shared pool. Token t of sequence
+ * b is row t % page_rows of page block_table[b * table_stride + t / page_rows],
+ * at pages + (page * page_rows + t % page_rows) * row_stride (elements).
+ * page_rows is a multiple of 16; block_table is a device int32 array. */
+typedef struct {
+  const void* pages;
+  int64_t row_stride;            /* elements between rows, >= 576, multiple of 8 */
+  int32_t page_rows;
+  const int32_t* block_table;
+  int64_t table_stride;          /* block_table entries per sequence */
+} lca_paged_t;
+
 /* Workspace bytes mla_latent_attn_decode needs for up to max_entries
  * attended rows per sequence (split-K partial results). */
 size_t mla_latent_attn_decode_workspace_size(int32_t B, int32_t H, int64_t max_entries);
@@ -177,6 +190,28 @@ int mla_latent_attn_decode(const void* q, int32_t q_dtype, int64_t q_seq_stride,
                            const lca_latent_t* raw, int64_t raw_begin, int64_t raw_end,
                            float sm_scale, float* o_latent, float* lse, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
+
+/* Decode over a ragged batch with a paged cache (a serving layout; the
+ * attention is that of mla_latent_attn_decode, 整体框架 flowchart E -> F).
+ * Sequence b attends representative rows [0, seq_m[b]) of reps (dense,
+ * packed bf16, row b at reps->c + b * reps->c_seq_stride) followed by its
+ * cache tokens [seq_raw_begin[b], seq_raw_end[b]) read through the block
+ * table. seq_m, seq_raw_begin, seq_raw_end are device int32 [B] arrays,
+ * read only by the kernel; the caller guarantees for every b: 0 <=
+ * seq_raw_begin <= seq_raw_end, seq_m + (seq_raw_end - seq_raw_begin) in
+ * [1, max_entries], the representative rows exist, and the block table maps
+ * every token in the raw range to a page of the pool (out-of-range values
+ * are not detected and read arbitrary memory). reps->c_tok_stride must equal
+ * cache->row_stride. q, o_latent, lse as in mla_latent_attn_decode;
+ * workspace >= mla_latent_attn_decode_workspace_size(B, H, max_entries).
+ * Outputs are not bitwise equal to the dense entry point's (tiles are
+ * formed differently), only within rounding. */
+int mla_latent_attn_decode_paged(const void* q, int32_t q_dtype, int64_t q_seq_stride, int32_t B,
+                                 int32_t H, const lca_latent_t* reps, const int32_t* seq_m,
+                                 const lca_paged_t* cache, const int32_t* seq_raw_begin,
+                                 const int32_t* seq_raw_end, int64_t max_entries, float sm_scale,
+                                 float* o_latent, float* lse, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
 
 /* mla_latent_attn_decode followed by mla_up_proj of its output (the MLA
  * page's projection back to each head's value space, 三.1), with the split

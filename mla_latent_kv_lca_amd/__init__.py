@@ -30,7 +30,7 @@ D_C, D_R, D_ROW, D_V = 512, 64, 576, 128
 # every symbol include/lca.h declares
 EXPORTS = ("lca_version", "lca_last_error", "lca_plan", "lca_condense_workspace_size",
            "lca_condense", "lca_condense_mode", "mla_latent_attn_decode_workspace_size",
-           "mla_latent_attn_decode",
+           "mla_latent_attn_decode", "mla_latent_attn_decode_paged",
            "mla_latent_attn_decode_up", "mla_latent_attn_prefill_chunk", "mla_up_proj")
 
 
@@ -44,6 +44,11 @@ class LatentT(ctypes.Structure):
     _fields_ = [("c", c_void_p), ("kr", c_void_p), ("c_seq_stride", c_int64),
                 ("c_tok_stride", c_int64), ("kr_seq_stride", c_int64),
                 ("kr_tok_stride", c_int64), ("dtype", c_int32)]
+
+
+class PagedT(ctypes.Structure):
+    _fields_ = [("pages", c_void_p), ("row_stride", c_int64), ("page_rows", c_int32),
+                ("block_table", c_void_p), ("table_stride", c_int64)]
 
 
 class PlanT(ctypes.Structure):
@@ -88,6 +93,10 @@ def load() -> ctypes.CDLL:
     lib.mla_latent_attn_decode.argtypes = [c_void_p, c_int32, c_int64, c_int32, c_int32, P(LatentT),
                                            c_int64, P(LatentT), c_int64, c_int64, c_float,
                                            c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.mla_latent_attn_decode_paged.restype = c_int32
+    lib.mla_latent_attn_decode_paged.argtypes = [c_void_p, c_int32, c_int64, c_int32, c_int32, P(LatentT),
+                                                 c_void_p, P(PagedT), c_void_p, c_void_p, c_int64, c_float,
+                                                 c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.mla_latent_attn_decode_up.restype = c_int32
     lib.mla_latent_attn_decode_up.argtypes = [c_void_p, c_int32, c_int64, c_int32, c_int32, P(LatentT),
                                               c_int64, P(LatentT), c_int64, c_int64, c_float,
@@ -142,6 +151,19 @@ def latent(c: torch.Tensor, kr: torch.Tensor) -> LatentT:
 def packed_latent(cache: torch.Tensor) -> LatentT:
     """Describe a packed [B, L, 576] (or [L, 576]) cache: c = [..., :512], kr = [..., 512:]."""
     return latent(cache[..., :D_C], cache[..., D_C:])
+
+
+def paged_latent(pool: torch.Tensor, block_table: torch.Tensor) -> PagedT:
+    """Describe a paged cache: pool [n_pages, page_rows, 576] bf16 (packed rows),
+    block_table int32 [B, pages per sequence] on the device. The tensors must
+    outlive the calls that use the description."""
+    if pool.dim() != 3 or pool.shape[-1] != D_ROW or pool.stride(-1) != 1:
+        raise ValueError("pool must be [n_pages, page_rows, 576] with contiguous rows")
+    if pool.stride(0) != pool.shape[1] * pool.stride(1):
+        raise ValueError("pages must be contiguous in the pool")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be an int32 [B, n] tensor with contiguous rows")
+    return PagedT(pool.data_ptr(), pool.stride(1), pool.shape[1], block_table.data_ptr(), block_table.stride(0))
 
 
 # ----------------------------------------------------------------- calls ---
@@ -217,6 +239,27 @@ def lca_condense(cache: LatentT, B: int, g: int, group_begin: int, n_groups: int
         _check(load().lca_condense(*args, _stream(stream)))
     else:
         _check(load().lca_condense_mode(*args, mode, _stream(stream)))
+
+
+def mla_latent_attn_decode_paged(q: torch.Tensor, reps: LatentT, seq_m: torch.Tensor, cache: PagedT,
+                                 seq_raw_begin: torch.Tensor, seq_raw_end: torch.Tensor, max_entries: int,
+                                 sm_scale: float, o_latent: torch.Tensor, lse: torch.Tensor | None = None,
+                                 workspace: torch.Tensor | None = None, stream=None) -> None:
+    """Ragged batch over a paged cache: q [B, H, 576]; seq_m, seq_raw_begin,
+    seq_raw_end int32 [B] device tensors; o_latent fp32 [B, H, 512]."""
+    if q.dim() != 3 or q.shape[-1] != D_ROW or q.stride(-1) != 1 or q.stride(-2) != D_ROW:
+        raise ValueError("q must be [B, H, 576] with contiguous heads")
+    B, H = q.shape[0], q.shape[1]
+    if o_latent.dtype != torch.float32 or not o_latent.is_contiguous() or o_latent.shape != (B, H, D_C):
+        raise ValueError("o_latent must be a contiguous fp32 [B, H, 512] tensor")
+    for t in (seq_m, seq_raw_begin, seq_raw_end):
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() != B:
+            raise ValueError("per-sequence arrays must be contiguous int32 [B] tensors")
+    ws = _workspace(mla_latent_attn_decode_workspace_size(B, H, max_entries), q, workspace)
+    _check(load().mla_latent_attn_decode_paged(
+        q.data_ptr(), dtype_code(q), q.stride(0), B, H, ctypes.byref(reps), seq_m.data_ptr(),
+        ctypes.byref(cache), seq_raw_begin.data_ptr(), seq_raw_end.data_ptr(), max_entries, sm_scale,
+        o_latent.data_ptr(), _ptr(lse), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def mla_latent_attn_decode(q: torch.Tensor, reps: LatentT | None, m: int, raw: LatentT | None,

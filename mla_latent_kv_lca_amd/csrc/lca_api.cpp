@@ -176,6 +176,47 @@ int mla_latent_attn_decode(const void* q, int32_t q_dtype, int64_t q_seq_stride,
                     "mla_latent_attn_decode launch");
 }
 
+int mla_latent_attn_decode_paged(const void* q, int32_t q_dtype, int64_t q_seq_stride, int32_t B,
+                                 int32_t H, const lca_latent_t* reps, const int32_t* seq_m,
+                                 const lca_paged_t* cache, const int32_t* seq_raw_begin,
+                                 const int32_t* seq_raw_end, int64_t max_entries, float sm_scale,
+                                 float* o_latent, float* lse, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  int rc;
+  if (q == nullptr || !aligned16(q)) return fail(LCA_ERR_INVALID_ARG, "q must be a non-null 16-byte aligned pointer");
+  if (!valid_dtype(q_dtype)) return fail(LCA_ERR_INVALID_ARG, "q_dtype %d is not LCA_BF16/LCA_F32", q_dtype);
+  if (!mult8(q_seq_stride) || q_seq_stride < 0) return fail(LCA_ERR_INVALID_ARG, "q_seq_stride must be a non-negative multiple of 8");
+  if (B < 1 || B > 65535) return fail(LCA_ERR_INVALID_ARG, "B must be in [1, 65535]");
+  if (H < 16 || H % 16 != 0 || H / 16 > 65535) return fail(LCA_ERR_UNSUPPORTED, "H = %d: the head count must be a positive multiple of 16", H);
+  if (cache == nullptr || cache->pages == nullptr || !aligned16(cache->pages))
+    return fail(LCA_ERR_INVALID_ARG, "cache pages must be a non-null 16-byte aligned pointer");
+  if (cache->row_stride < LCA_D_ROW || !mult8(cache->row_stride))
+    return fail(LCA_ERR_INVALID_ARG, "cache row_stride must be >= 576 and a multiple of 8");
+  if (cache->page_rows < 16 || cache->page_rows % 16 != 0)
+    return fail(LCA_ERR_UNSUPPORTED, "page_rows = %d: must be a positive multiple of 16", cache->page_rows);
+  if (cache->block_table == nullptr || cache->table_stride < 1)
+    return fail(LCA_ERR_INVALID_ARG, "block_table must be non-null with table_stride >= 1");
+  if (seq_m == nullptr || seq_raw_begin == nullptr || seq_raw_end == nullptr)
+    return fail(LCA_ERR_INVALID_ARG, "seq_m, seq_raw_begin and seq_raw_end must be non-null device arrays");
+  if (max_entries < 1 || max_entries > ((int64_t)1 << 31)) return fail(LCA_ERR_INVALID_ARG, "max_entries must be in [1, 2^31]");
+  if ((rc = check_latent(reps, "reps", true, true)) != LCA_OK) return rc;
+  if (reps->dtype != LCA_BF16 || static_cast<const char*>(reps->kr) != static_cast<const char*>(reps->c) + 2 * LCA_D_C ||
+      reps->kr_tok_stride != reps->c_tok_stride || reps->kr_seq_stride != reps->c_seq_stride)
+    return fail(LCA_ERR_UNSUPPORTED, "paged decode needs packed bf16 representatives (k_R right after c_KV)");
+  if (reps->c_tok_stride != cache->row_stride)
+    return fail(LCA_ERR_UNSUPPORTED, "representatives and cache pages must share one row stride");
+  if (cache->row_stride * 2 * 16 >= ((int64_t)1 << 31)) return fail(LCA_ERR_UNSUPPORTED, "row stride too large");
+  if ((rc = check_scale(sm_scale)) != LCA_OK) return rc;
+  if (o_latent == nullptr || !aligned16(o_latent)) return fail(LCA_ERR_INVALID_ARG, "o_latent must be a non-null 16-byte aligned pointer");
+  const lca::DecodeSplit sp = lca::decode_split(B, H / 16, max_entries);
+  const size_t need = lca::decode_workspace_bytes(B, H / 16, sp.S);
+  if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need))
+    return fail(LCA_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
+  return hip_status(lca::launch_decode_paged(q, q_dtype, q_seq_stride, B, H, *reps, seq_m, *cache, seq_raw_begin,
+                                             seq_raw_end, max_entries, sm_scale, o_latent, lse, workspace, stream),
+                    "mla_latent_attn_decode_paged launch");
+}
+
 int mla_latent_attn_decode_up(const void* q, int32_t q_dtype, int64_t q_seq_stride, int32_t B,
                               int32_t H, const lca_latent_t* reps, int64_t m,
                               const lca_latent_t* raw, int64_t raw_begin, int64_t raw_end,

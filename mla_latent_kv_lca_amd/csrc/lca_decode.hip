@@ -102,26 +102,84 @@ __device__ __forceinline__ void wait_wave_tile(int newer) {
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <typename TQ>
-__global__ __launch_bounds__(DNT) void decode_kernel(
-    const TQ* __restrict__ q, int64_t q_seq, DmaSrc src0, int64_t rep_seq_b, int64_t raw_seq_b,
-    int64_t n_entries, int per_tiles, int S, float scale_log2, int H, float* __restrict__ part_o,
-    float* __restrict__ part_ml, float* __restrict__ o_final, float* __restrict__ lse_final) {
-  __shared__ __align__(16) bf16_t ring[DNW][WSLOT][WT_ELEMS];  // 147,456 bytes
+// A sequence's attended entries as 16-entry wave tiles. DenseTiles: entries
+// [0, n) = representative rows [0, m) ++ raw rows, in one token stride.
+struct DenseTiles {
+  DmaSrc src;
+  int64_t n;
+  __device__ __forceinline__ int64_t count() const { return (n + WT - 1) / WT; }
+  __device__ __forceinline__ int valid(int64_t u) const { return (int)min((int64_t)WT, n - u * WT); }
+  __device__ __forceinline__ void dma(int64_t u, const bf16_t* slot, int lane, const uint32_t (&off)[WT_DMA]) const {
+    wave_tile_dma(src, u * WT, n, slot, lane, off);
+  }
+};
 
+// PagedTiles: ceil(m / 16) tiles of dense representative rows, then the raw
+// rows [raw_begin, raw_end) of a paged cache (rows of token t in page
+// table[t / P], row t % P), 16 tokens per tile from raw_begin on. A tile
+// touches at most two pages (P is a multiple of 16); its page indices are
+// wave-uniform loads. Rows past the valid ones reload the last valid row
+// (their logits are masked).
+struct PagedTiles {
+  const char* rep;        // this sequence's representative rows
+  const char* pages;      // page pool
+  const int32_t* table;   // this sequence's block table
+  int64_t tok;            // row stride in bytes (representatives and pages)
+  int64_t m, raw_begin, raw_end, R;  // R = representative tiles
+  int P;                  // rows per page
+  __device__ __forceinline__ int64_t count() const { return R + (raw_end - raw_begin + WT - 1) / WT; }
+  __device__ __forceinline__ int valid(int64_t u) const {
+    return u < R ? (int)min((int64_t)WT, m - u * WT) : (int)min((int64_t)WT, raw_end - raw_begin - (u - R) * WT);
+  }
+  __device__ __forceinline__ void dma(int64_t u, const bf16_t* slot, int lane, const uint32_t (&off)[WT_DMA]) const {
+    const uint32_t base = lds_off(slot);
+    const int v = valid(u);
+    if (u < R) {
+      const char* b0 = rep + u * WT * tok;
+      if (v == WT) {
+#pragma unroll
+        for (int i = 0; i < WT_DMA; ++i) dma16_nt(b0 + off[i], base + 1024u * i);
+      } else {
+        for (int i = 0; i < WT_DMA; ++i) {
+          const int Q = 64 * i + lane, row = Q / (D_ROW / 8), c = (Q - row * (D_ROW / 8)) ^ swz(row);
+          dma16_nt(b0 + min(row, v - 1) * tok + 16 * c, base + 1024u * i);
+        }
+      }
+      return;
+    }
+    const int64_t t0 = raw_begin + (u - R) * WT, pg0 = t0 / P, pg1 = (t0 + v - 1) / P;
+    const int64_t p0 = table[__builtin_amdgcn_readfirstlane((int)pg0)];
+    const int64_t p1 = table[__builtin_amdgcn_readfirstlane((int)pg1)];
+    if (v == WT && pg0 == pg1) {
+      const char* b0 = pages + (p0 * P + (t0 - pg0 * P)) * tok;
+#pragma unroll
+      for (int i = 0; i < WT_DMA; ++i) dma16_nt(b0 + off[i], base + 1024u * i);
+    } else {
+      for (int i = 0; i < WT_DMA; ++i) {
+        const int Q = 64 * i + lane, row = Q / (D_ROW / 8), c = (Q - row * (D_ROW / 8)) ^ swz(row);
+        const int64_t t = t0 + min(row, v - 1), pg = t / P;
+        const int64_t page = pg == pg0 ? p0 : p1;
+        dma16_nt(pages + (page * P + (t - pg * P)) * tok + 16 * c, base + 1024u * i);
+      }
+    }
+  }
+};
+
+template <typename TQ, class Tiles>
+__device__ __forceinline__ void decode_body(bf16_t (&ring)[DNW][WSLOT][WT_ELEMS], const TQ* __restrict__ q,
+                                            int64_t q_seq, const Tiles& tiles, int64_t tok_b, int S,
+                                            float scale_log2, int H, float* __restrict__ part_o,
+                                            float* __restrict__ part_ml, float* __restrict__ o_final,
+                                            float* __restrict__ lse_final) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = lane >> 4, col = lane & 15;
   const int s = blockIdx.x, b = blockIdx.y, hg = blockIdx.z, HG = gridDim.z;
 
-  DmaSrc src = src0;
-  src.rep += (int64_t)b * rep_seq_b;
-  src.raw += (int64_t)b * raw_seq_b;
   // the sequence's wave tiles are dealt round robin over the S x 4
   // wavefronts of its splits: this wave takes u0 + ustep k, k < n_mine, so at
   // any time the sequence's wavefronts read one narrow window of its entries
-  const int64_t e_end = n_entries;
-  const int64_t n_wt = (n_entries + WT - 1) / WT;
+  const int64_t n_wt = tiles.count();
   const int64_t u0 = w + (int64_t)DNW * s, ustep = (int64_t)DNW * S;
   const int n_mine = n_wt > u0 ? (int)((n_wt - 1 - u0) / ustep + 1) : 0;
 
@@ -129,11 +187,9 @@ __global__ __launch_bounds__(DNT) void decode_kernel(
 #pragma unroll
   for (int i = 0; i < WT_DMA; ++i) {
     const int P = 64 * i + lane, row = P / (D_ROW / 8);
-    off[i] = (uint32_t)(row * src.tok) + 16u * ((P - row * (D_ROW / 8)) ^ swz(row));
+    off[i] = (uint32_t)(row * tok_b) + 16u * ((P - row * (D_ROW / 8)) ^ swz(row));
   }
-  auto issue = [&](int k) {
-    wave_tile_dma(src, (u0 + ustep * k) * WT, e_end, &ring[w][k % WSLOT][0], lane, off);
-  };
+  auto issue = [&](int k) { tiles.dma(u0 + ustep * k, &ring[w][k % WSLOT][0], lane, off); };
   // lane-constant element offsets inside a wave tile.
   // Score product, k-step ks: lane (kg, col) reads row col, chunk 4 ks + kg,
   // at kb[ks & 1] + 64 (ks >> 1) (swz only flips the low three chunk bits).
@@ -186,10 +242,10 @@ __global__ __launch_bounds__(DNT) void decode_kernel(
   for (int c = 0; c < 32; ++c) o[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Scores of wave tile k (log2 units, masked past e_end); returns their
+  // Scores of wave tile k (log2 units, rows past the tile's valid ones masked); returns their
   // per-head maximum.
   auto scores = [&](int k, float (&z)[4]) -> float {
-    const int64_t e0 = (u0 + ustep * k) * WT;
+    const int valid = tiles.valid(u0 + ustep * k);
     wait_wave_tile(min(n_mine - 1 - k, WSLOT - 1));
     const bf16_t* tile = &ring[w][k % WSLOT][0];
     f32x4_t sa = f32x4_t{0.f, 0.f, 0.f, 0.f}, sb = sa;
@@ -201,10 +257,10 @@ __global__ __launch_bounds__(DNT) void decode_kernel(
     const f32x4_t sc = sa + sb;  // S[entry 4 kg + r][head col]
 #pragma unroll
     for (int r = 0; r < 4; ++r) z[r] = sc[r] * scale_log2;
-    if (e0 + WT > e_end) {
+    if (valid < WT) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (e0 + 4 * kg + r >= e_end) z[r] = -INFINITY;
+        if (4 * kg + r >= valid) z[r] = -INFINITY;
     }
     // per head: lanes col, col + 16, col + 32, col + 48
     return xor32_max(xor16_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]))));
@@ -318,6 +374,45 @@ __global__ __launch_bounds__(DNT) void decode_kernel(
     part_ml[slot * 2 + 0] = M;
     part_ml[slot * 2 + 1] = Lsum;
   }
+}
+
+template <typename TQ>
+__global__ __launch_bounds__(DNT) void decode_kernel(
+    const TQ* __restrict__ q, int64_t q_seq, DmaSrc src0, int64_t rep_seq_b, int64_t raw_seq_b,
+    int64_t n_entries, int S, float scale_log2, int H, float* __restrict__ part_o,
+    float* __restrict__ part_ml, float* __restrict__ o_final, float* __restrict__ lse_final) {
+  __shared__ __align__(16) bf16_t ring[DNW][WSLOT][WT_ELEMS];  // 147,456 bytes
+  DenseTiles tiles;
+  tiles.src = src0;
+  tiles.src.rep += (int64_t)blockIdx.y * rep_seq_b;
+  tiles.src.raw += (int64_t)blockIdx.y * raw_seq_b;
+  tiles.n = n_entries;
+  decode_body<TQ>(ring, q, q_seq, tiles, src0.tok, S, scale_log2, H, part_o, part_ml, o_final, lse_final);
+}
+
+// Ragged batch over a paged cache: per-sequence representative count and raw
+// range from device arrays.
+template <typename TQ>
+__global__ __launch_bounds__(DNT) void decode_paged_kernel(
+    const TQ* __restrict__ q, int64_t q_seq, const char* __restrict__ rep, int64_t rep_seq_b,
+    const int32_t* __restrict__ seq_m, const char* __restrict__ pages, const int32_t* __restrict__ table,
+    int64_t table_stride, int page_rows, const int32_t* __restrict__ seq_raw_begin,
+    const int32_t* __restrict__ seq_raw_end, int64_t tok_b, int S, float scale_log2, int H,
+    float* __restrict__ part_o, float* __restrict__ part_ml, float* __restrict__ o_final,
+    float* __restrict__ lse_final) {
+  __shared__ __align__(16) bf16_t ring[DNW][WSLOT][WT_ELEMS];  // 147,456 bytes
+  const int b = blockIdx.y;
+  PagedTiles tiles;
+  tiles.rep = rep + (int64_t)b * rep_seq_b;
+  tiles.pages = pages;
+  tiles.table = table + (int64_t)b * table_stride;
+  tiles.tok = tok_b;
+  tiles.P = page_rows;
+  tiles.m = seq_m[b];
+  tiles.raw_begin = seq_raw_begin[b];
+  tiles.raw_end = seq_raw_end[b];
+  tiles.R = (tiles.m + WT - 1) / WT;
+  decode_body<TQ>(ring, q, q_seq, tiles, tok_b, S, scale_log2, H, part_o, part_ml, o_final, lse_final);
 }
 
 // Register-staged variant for f32 caches (rounded to bf16 as they are staged
@@ -551,12 +646,10 @@ static hipError_t decode_attention(const void* q, int q_dtype, int64_t q_seq_str
     const int64_t raw_seq_b = raw_end > raw_begin ? raw.c_seq_stride * 2 : 0;
     if (q_dtype == LCA_BF16)
       hipLaunchKernelGGL(decode_kernel<bf16_t>, grid, dim3(DNT), 0, stream, (const bf16_t*)q,
-                         q_seq_stride, src, rep_seq_b, raw_seq_b, n, sp.per_tiles, sp.S, sl2, H, po,
-                         pml, o_latent, lse);
+                         q_seq_stride, src, rep_seq_b, raw_seq_b, n, sp.S, sl2, H, po, pml, o_latent, lse);
     else
       hipLaunchKernelGGL(decode_kernel<float>, grid, dim3(DNT), 0, stream, (const float*)q,
-                         q_seq_stride, src, rep_seq_b, raw_seq_b, n, sp.per_tiles, sp.S, sl2, H, po,
-                         pml, o_latent, lse);
+                         q_seq_stride, src, rep_seq_b, raw_seq_b, n, sp.S, sl2, H, po, pml, o_latent, lse);
   } else {
     // general strides or f32 rows: register-staged kernel, 32-entry tiles
     const Seg rs = to_seg(reps), ws = to_seg(raw);
@@ -604,6 +697,34 @@ hipError_t launch_decode(const void* q, int q_dtype, int64_t q_seq_stride, int B
   split_buffers(workspace, B, H / HB, sp, po, pml);
   hipError_t err = decode_attention(q, q_dtype, q_seq_stride, B, H, reps, m, raw, raw_begin, raw_end,
                                     sm_scale, o_latent, lse, sp, po, pml, stream);
+  if (err != hipSuccess || sp.S == 1) return err;
+  launch_merge(sp, B, H, po, pml, o_latent, lse, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_paged(const void* q, int q_dtype, int64_t q_seq_stride, int B, int H,
+                               const lca_latent_t& reps, const int32_t* seq_m, const lca_paged_t& cache,
+                               const int32_t* seq_raw_begin, const int32_t* seq_raw_end,
+                               int64_t max_entries, float sm_scale, float* o_latent, float* lse,
+                               void* workspace, hipStream_t stream) {
+  const int HG = H / HB;
+  const DecodeSplit sp = decode_split(B, HG, max_entries);
+  float *po, *pml;
+  split_buffers(workspace, B, HG, sp, po, pml);
+  const float sl2 = sm_scale * 1.44269504088896340736f;
+  dim3 grid((unsigned)sp.S, (unsigned)B, (unsigned)HG);
+  const char* rep = static_cast<const char*>(reps.c);
+  const int64_t rep_seq_b = reps.c_seq_stride * 2, tok_b = cache.row_stride * 2;
+  const char* pages = static_cast<const char*>(cache.pages);
+  if (q_dtype == LCA_BF16)
+    hipLaunchKernelGGL(decode_paged_kernel<bf16_t>, grid, dim3(DNT), 0, stream, (const bf16_t*)q, q_seq_stride,
+                       rep, rep_seq_b, seq_m, pages, cache.block_table, cache.table_stride, cache.page_rows,
+                       seq_raw_begin, seq_raw_end, tok_b, sp.S, sl2, H, po, pml, o_latent, lse);
+  else
+    hipLaunchKernelGGL(decode_paged_kernel<float>, grid, dim3(DNT), 0, stream, (const float*)q, q_seq_stride,
+                       rep, rep_seq_b, seq_m, pages, cache.block_table, cache.table_stride, cache.page_rows,
+                       seq_raw_begin, seq_raw_end, tok_b, sp.S, sl2, H, po, pml, o_latent, lse);
+  hipError_t err = hipGetLastError();
   if (err != hipSuccess || sp.S == 1) return err;
   launch_merge(sp, B, H, po, pml, o_latent, lse, stream);
   return hipGetLastError();

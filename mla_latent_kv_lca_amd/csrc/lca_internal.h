@@ -44,6 +44,11 @@ hipError_t launch_decode(const void* q, int q_dtype, int64_t q_seq_stride, int B
 
 // decode followed by the W_UV up-projection of its output; the split merge
 // and the projection share one kernel when B <= UP_SMALL_T.
+hipError_t launch_decode_paged(const void* q, int q_dtype, int64_t q_seq_stride, int B, int H,
+                               const lca_latent_t& reps, const int32_t* seq_m, const lca_paged_t& cache,
+                               const int32_t* seq_raw_begin, const int32_t* seq_raw_end,
+                               int64_t max_entries, float sm_scale, float* o_latent, float* lse,
+                               void* workspace, hipStream_t stream);
 hipError_t launch_decode_up(const void* q, int q_dtype, int64_t q_seq_stride, int B, int H,
                             const lca_latent_t& reps, int64_t m, const lca_latent_t& raw,
                             int64_t raw_begin, int64_t raw_end, float sm_scale, float* o_latent,

@@ -116,6 +116,30 @@ def test_condense_mode_argument_errors():
     assert call(lca.LCA_MODE_ANCHOR, n=0) == lca.LCA_OK  # empty range: no launch
 
 
+def test_decode_paged_argument_errors():
+    lib = lca.load()
+    reps = lca.LatentT(64, 64 + 1024, 0, 576, 0, 576, 0)
+
+    def call(pages=64, row_stride=576, page_rows=64, table=128, table_stride=4, seq=256, max_entries=100,
+             H=16, reps_=reps):
+        cache = lca.PagedT(pages, row_stride, page_rows, table, table_stride)
+        return lib.mla_latent_attn_decode_paged(64, 0, 16 * 576, 1, H, ctypes.byref(reps_), seq,
+                                                ctypes.byref(cache), seq, seq, max_entries, 1.0, 64, None,
+                                                64, 1 << 20, None)
+    assert call(page_rows=8) == lca.LCA_ERR_UNSUPPORTED
+    assert call(page_rows=40) == lca.LCA_ERR_UNSUPPORTED
+    assert call(pages=None) == lca.LCA_ERR_INVALID_ARG
+    assert call(pages=72) == lca.LCA_ERR_INVALID_ARG  # misaligned
+    assert call(row_stride=570) == lca.LCA_ERR_INVALID_ARG
+    assert call(table=None) == lca.LCA_ERR_INVALID_ARG
+    assert call(table_stride=0) == lca.LCA_ERR_INVALID_ARG
+    assert call(seq=None) == lca.LCA_ERR_INVALID_ARG
+    assert call(max_entries=0) == lca.LCA_ERR_INVALID_ARG
+    assert call(H=24) == lca.LCA_ERR_UNSUPPORTED
+    assert call(row_stride=584) == lca.LCA_ERR_UNSUPPORTED  # reps stride differs from the pages'
+    assert call(reps_=lca.LatentT(64, 64 + 1024, 0, 576, 0, 576, 1)) == lca.LCA_ERR_UNSUPPORTED  # f32 reps
+
+
 def _decode(lib, reps, raw, **kw):
     a = dict(q=64, qdt=0, qss=16 * 576, B=1, H=16, m=0, rb=0, re=8, sm=1.0, o=64, lse=None,
              ws=None, wsb=0)

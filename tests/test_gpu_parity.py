@@ -127,6 +127,68 @@ def test_gqa_condense_and_decode_match_oracle():
     assert_close(host(lse).reshape(B, Hq), rl, what="GQA lse")
 
 
+def _page_pool(seqs, page_rows, seed):
+    """Scatter each sequence's packed rows [L_b, 576] over shuffled pages of a
+    pool; returns (pool [n_pages, page_rows, 576], block table int32 [B, n])."""
+    r = np.random.default_rng(seed)
+    need = [-(-len(x) // page_rows) for x in seqs]
+    order = r.permutation(sum(need))
+    pool = np.zeros((sum(need), page_rows, 576), dtype=np.float32)
+    table = np.zeros((len(seqs), max(need)), dtype=np.int32)
+    k = 0
+    for b, x in enumerate(seqs):
+        for j in range(need[b]):
+            pg = order[k]
+            k += 1
+            table[b, j] = pg
+            rows = x[j * page_rows:(j + 1) * page_rows]
+            pool[pg, :len(rows)] = rows
+    return pool, table
+
+
+@pytest.mark.parametrize("page_rows,g", [(64, 16), (16, 8)])
+def test_decode_paged_ragged_matches_oracle(page_rows, g):
+    """Ragged batch (different lengths, one shorter than the window) over a
+    shuffled paged cache against the oracle on each sequence's logical rows.
+    With g = 8 the raw ranges start off a 16-row boundary, so tiles straddle
+    pages."""
+    Ls, w = [1500, 2077, 3000, 1040, 777], 1024
+    B = len(Ls)
+    seqs, reps, ms, rbs = [], [], [], []
+    for b, L in enumerate(Ls):
+        c, kr = li.latent_cache(20 + b, 1, L)
+        li.plant_needles(20 + b, c, kr, 2, 14.0, 0, L)
+        seqs.append(np.concatenate([c[0], kr[0]], -1))
+        p = O.plan(L, w, g)
+        ms.append(p["m"])
+        rbs.append(p["raw_begin"])
+        rc, rk = li.latent_cache(40 + b, 1, max(p["m"], 1))
+        reps.append(np.concatenate([rc[0], rk[0]], -1)[:p["m"]])
+    pool, table = _page_pool(seqs, page_rows, 7)
+    m_cap = max(max(ms), 1)
+    reps_t = torch.zeros((B, m_cap, 576), dtype=torch.bfloat16, device="cuda")
+    for b in range(B):
+        if ms[b]:
+            reps_t[b, :ms[b]] = dev(reps[b])
+    q = li.queries(9, B, 1, H, rho=0.5)[:, 0]
+    pool_t = dev(pool)
+    table_t = torch.from_numpy(table).cuda()
+    i32 = lambda x: torch.tensor(x, dtype=torch.int32, device="cuda")  # noqa: E731
+    o = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    max_entries = max(m + L - rb for m, L, rb in zip(ms, Ls, rbs))
+    lca.mla_latent_attn_decode_paged(dev(q), lca.packed_latent(reps_t), i32(ms), lca.paged_latent(pool_t, table_t),
+                                     i32(rbs), i32(Ls), max_entries, 1.0, o, lse)
+    torch.cuda.synchronize()
+    for b in range(B):
+        x = seqs[b][None]
+        rep = reps[b][None] if ms[b] else None
+        ro, rl = O.decode(q[b:b + 1], None if rep is None else rep[..., :512], None if rep is None else rep[..., 512:],
+                          ms[b], x[..., :512], x[..., 512:], rbs[b], Ls[b], 1.0)
+        assert_close(host(o[b:b + 1]), ro, what=f"paged o_latent seq {b}")
+        assert_close(host(lse[b:b + 1]), rl, what=f"paged lse seq {b}")
+
+
 @pytest.mark.parametrize("B,L,g,with_alpha", [(3, 5000, 16, True), (2, 4100, 8, False), (1, 70000, 16, False)])
 def test_condense_streaming_kernel_equals_general_kernel(B, L, g, with_alpha):
     """Packed bf16 rows with one summary query per sequence take the streaming
