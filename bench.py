@@ -41,6 +41,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--roofline-reps", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-paged", action="store_true")
     ap.add_argument("--prefill-len", type=int, default=131072)
     ap.add_argument("--no-graph", action="store_true",
                     help="launch every kernel from Python instead of replaying a captured HIP graph")
@@ -303,6 +304,10 @@ def main():
     if not args.no_prefill:
         prefill = prefill_leg(args.prefill_len)
 
+    paged = None
+    if not args.no_paged:
+        paged = paged_leg()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cache0, qhist[0], qsteps0, args.cpu_seconds)
@@ -334,6 +339,7 @@ def main():
                      "bytes_per_launch": con_bytes, "avg_launch_us": t_con * 1e6},
         "decode_context_tokens_per_s": B * L / t_dec,
         "prefill": prefill,
+        "paged": paged,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec))
@@ -411,6 +417,82 @@ def prefill_leg(Lp):
             "mfma_frac": attn_flop / (attn_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS,
             "up_proj_tflop": up_flop / 1e12,
             "context": "pages: 128K prefill 10.78 s MLA vs 4.40 s LCA, whole model on 8xH200"}
+
+
+def paged_leg(B=32, page_rows=64, reps_=20):
+    """Ragged batch over a paged cache: B sequences with lengths drawn
+    uniformly from [16,384, 49,152] (seeded), rows on shuffled pages of 64;
+    condense every group once, then time lca_condense_paged and
+    mla_latent_attn_decode_paged calls (captured in graphs, HIP events on the
+    launch stream) against their algorithmic bytes."""
+    import numpy as np
+    import torch
+
+    import mla_latent_kv_lca_amd as lca
+    r = np.random.default_rng(900)
+    Ls = [int(x) for x in r.integers(16384, 49153, B)]
+    need = [-(-L // page_rows) for L in Ls]
+    n_pages = sum(need)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(901)
+    pool = torch.randn((n_pages, page_rows, 576), generator=g, device="cuda").to(torch.bfloat16)
+    perm = torch.from_numpy(r.permutation(n_pages).astype(np.int32))
+    table = torch.zeros((B, max(need)), dtype=torch.int32)
+    k = 0
+    for b in range(B):
+        table[b, :need[b]] = perm[k:k + need[b]]
+        k += need[b]
+    table = table.cuda()
+    plans = [lca.lca_plan(L, W, G) for L in Ls]
+    ms = [p["m"] for p in plans]
+    m_cap = max(ms)
+    i32 = lambda x: torch.tensor(x, dtype=torch.int32, device="cuda")  # noqa: E731
+    seq_m, seq_rb, seq_re, seq_gb = i32(ms), i32([p["raw_begin"] for p in plans]), i32(Ls), i32([0] * B)
+    max_e = max(p["n_entries"] for p in plans)
+    cache = lca.paged_latent(pool, table)
+    qh = torch.randn((B, G, H, 576), generator=g, device="cuda").mul_(576 ** -0.5).to(torch.bfloat16)
+    qd = torch.randn((B, H, 576), generator=g, device="cuda").mul_(576 ** -0.5).to(torch.bfloat16)
+    reps = torch.empty((B, m_cap, 576), dtype=torch.bfloat16, device="cuda")
+    anchor = torch.empty((B, m_cap), dtype=torch.int32, device="cuda")
+    o = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    cws = torch.empty(lca.lca_condense_workspace_size(B, m_cap, 0), dtype=torch.uint8, device="cuda")
+    dws = lca.decode_workspace(B, H, max_e)
+    rl = lca.packed_latent(reps)
+
+    def condense():
+        lca.lca_condense_paged(cache, B, G, seq_gb, seq_m, m_cap, qh, 0, 1.0, rl, anchor, None, cws)
+
+    def decode():
+        lca.mla_latent_attn_decode_paged(qd, rl, seq_m, cache, seq_rb, seq_re, max_e, 1.0, o, lse, dws)
+
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for _ in range(n):
+                fn()
+        gr.replay()
+        torch.cuda.synchronize()
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        gr.replay()
+        b_.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b_) / n * 1e-3
+
+    t_con = timed(condense, max(2, reps_ // 4))
+    t_dec = timed(decode, reps_)
+    dec_bytes = sum(p["n_entries"] for p in plans) * 1152 + B * H * 576 * 2 + B * H * 513 * 4
+    con_bytes = sum(ms) * (G * 1152 + 1152 + 4) + B * G * H * 576 * 2
+    return {"B": B, "lengths": "uniform [16384, 49152], seeded", "total_tokens": sum(Ls),
+            "page_rows": page_rows, "entries": sum(p["n_entries"] for p in plans),
+            "decode_us": t_dec * 1e6, "decode_gbs": dec_bytes / t_dec / 1e9,
+            "decode_context_tokens_per_s": sum(Ls) / t_dec,
+            "condense_us": t_con * 1e6, "condense_gbs": con_bytes / t_con / 1e9}
 
 
 def cpu_baseline(cache, qhist, qsteps, budget_s):

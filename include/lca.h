@@ -160,6 +160,26 @@ typedef struct {
   int64_t table_stride;          /* block_table entries per sequence */
 } lca_paged_t;
 
+/* lca_condense over a ragged batch with a paged cache (lca_paged_t
+ * above): for every sequence b, groups j in [seq_group_begin[b],
+ * seq_group_begin[b] + seq_n_groups[b]) (tokens [j g, (j+1) g) read through
+ * the block table) are condensed as in lca_condense with one summary query
+ * per sequence, the mean over query rows [q_row0, q_row0 + g) and the H
+ * heads of that sequence. Representative j is written to row j of reps
+ * (packed bf16, dense, row b at reps->c + b * reps->c_seq_stride); anchors
+ * are absolute token indices; alpha optional as in lca_condense.
+ * seq_group_begin and seq_n_groups are device int32 [B] arrays read only by
+ * the kernel; the caller guarantees 0 <= seq_n_groups[b] <= max_groups, that
+ * the representative rows exist and that the block table maps every token
+ * of the groups. page_rows must be a multiple of g (a group never straddles
+ * pages). workspace >= lca_condense_workspace_size(B, max_groups, 0). */
+int lca_condense_paged(const lca_paged_t* cache, int32_t B, int32_t g, const int32_t* seq_group_begin,
+                       const int32_t* seq_n_groups, int64_t max_groups, const void* q, int32_t q_dtype,
+                       int64_t q_seq_stride, int64_t q_tok_stride, int64_t T, int32_t H, int64_t q_row0,
+                       float sm_scale, const lca_latent_t* reps, int32_t* anchor_idx,
+                       int64_t anchor_seq_stride, float* alpha, int64_t alpha_seq_stride,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace bytes mla_latent_attn_decode needs for up to max_entries
  * attended rows per sequence (split-K partial results). */
 size_t mla_latent_attn_decode_workspace_size(int32_t B, int32_t H, int64_t max_entries);

@@ -29,7 +29,7 @@ D_C, D_R, D_ROW, D_V = 512, 64, 576, 128
 
 # every symbol include/lca.h declares
 EXPORTS = ("lca_version", "lca_last_error", "lca_plan", "lca_condense_workspace_size",
-           "lca_condense", "lca_condense_mode", "mla_latent_attn_decode_workspace_size",
+           "lca_condense", "lca_condense_mode", "lca_condense_paged", "mla_latent_attn_decode_workspace_size",
            "mla_latent_attn_decode", "mla_latent_attn_decode_paged",
            "mla_latent_attn_decode_up", "mla_latent_attn_prefill_chunk", "mla_up_proj")
 
@@ -93,6 +93,10 @@ def load() -> ctypes.CDLL:
     lib.mla_latent_attn_decode.argtypes = [c_void_p, c_int32, c_int64, c_int32, c_int32, P(LatentT),
                                            c_int64, P(LatentT), c_int64, c_int64, c_float,
                                            c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.lca_condense_paged.restype = c_int32
+    lib.lca_condense_paged.argtypes = [P(PagedT), c_int32, c_int32, c_void_p, c_void_p, c_int64, c_void_p, c_int32,
+                                       c_int64, c_int64, c_int64, c_int32, c_int64, c_float, P(LatentT), c_void_p,
+                                       c_int64, c_void_p, c_int64, c_void_p, c_size_t, c_void_p]
     lib.mla_latent_attn_decode_paged.restype = c_int32
     lib.mla_latent_attn_decode_paged.argtypes = [c_void_p, c_int32, c_int64, c_int32, c_int32, P(LatentT),
                                                  c_void_p, P(PagedT), c_void_p, c_void_p, c_int64, c_float,
@@ -239,6 +243,27 @@ def lca_condense(cache: LatentT, B: int, g: int, group_begin: int, n_groups: int
         _check(load().lca_condense(*args, _stream(stream)))
     else:
         _check(load().lca_condense_mode(*args, mode, _stream(stream)))
+
+
+def lca_condense_paged(cache: PagedT, B: int, g: int, seq_group_begin: torch.Tensor, seq_n_groups: torch.Tensor,
+                       max_groups: int, q: torch.Tensor, q_row0: int, sm_scale: float, reps: LatentT,
+                       anchor: torch.Tensor, alpha: torch.Tensor | None = None,
+                       workspace: torch.Tensor | None = None, stream=None) -> None:
+    """Ragged condensation over a paged cache; q [B, T, H, 576]; per-sequence
+    int32 [B] device arrays; one summary query per sequence (rows [q_row0, + g))."""
+    if q.dim() != 4 or q.shape[-1] != D_ROW or q.stride(-1) != 1 or q.stride(-2) != D_ROW:
+        raise ValueError("q must be [B, T, H, 576] with contiguous heads")
+    if anchor.dtype != torch.int32:
+        raise TypeError("anchor must be int32")
+    for t in (seq_group_begin, seq_n_groups):
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() != B:
+            raise ValueError("per-sequence arrays must be contiguous int32 [B] tensors")
+    ws = _workspace(lca_condense_workspace_size(B, max_groups, 0), q, workspace)
+    _check(load().lca_condense_paged(
+        ctypes.byref(cache), B, g, seq_group_begin.data_ptr(), seq_n_groups.data_ptr(), max_groups, q.data_ptr(),
+        dtype_code(q), q.stride(0), q.stride(1), q.shape[1], q.shape[2], q_row0, sm_scale, ctypes.byref(reps),
+        anchor.data_ptr(), anchor.stride(0), _ptr(alpha), 0 if alpha is None else alpha.stride(0),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def mla_latent_attn_decode_paged(q: torch.Tensor, reps: LatentT, seq_m: torch.Tensor, cache: PagedT,

@@ -138,6 +138,51 @@ int lca_condense_mode(const lca_latent_t* cache, int32_t B, int32_t g, int64_t g
                     "lca_condense launch");
 }
 
+int lca_condense_paged(const lca_paged_t* cache, int32_t B, int32_t g, const int32_t* seq_group_begin,
+                       const int32_t* seq_n_groups, int64_t max_groups, const void* q, int32_t q_dtype,
+                       int64_t q_seq_stride, int64_t q_tok_stride, int64_t T, int32_t H, int64_t q_row0,
+                       float sm_scale, const lca_latent_t* reps, int32_t* anchor_idx,
+                       int64_t anchor_seq_stride, float* alpha, int64_t alpha_seq_stride,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int rc;
+  if (cache == nullptr || cache->pages == nullptr || !aligned16(cache->pages))
+    return fail(LCA_ERR_INVALID_ARG, "cache pages must be a non-null 16-byte aligned pointer");
+  if (cache->row_stride < LCA_D_ROW || !mult8(cache->row_stride))
+    return fail(LCA_ERR_INVALID_ARG, "cache row_stride must be >= 576 and a multiple of 8");
+  if (cache->block_table == nullptr || cache->table_stride < 1)
+    return fail(LCA_ERR_INVALID_ARG, "block_table must be non-null with table_stride >= 1");
+  if (B < 1 || B > 65535) return fail(LCA_ERR_INVALID_ARG, "B must be in [1, 65535]");
+  if (g < 1 || g > LCA_MAX_G || (g & (g - 1)) != 0)
+    return fail(LCA_ERR_UNSUPPORTED, "g = %d: supported group sizes are powers of two up to %d", g, LCA_MAX_G);
+  if (cache->page_rows < 1 || cache->page_rows % g != 0)
+    return fail(LCA_ERR_UNSUPPORTED, "page_rows = %d must be a positive multiple of g = %d", cache->page_rows, g);
+  if (seq_group_begin == nullptr || seq_n_groups == nullptr)
+    return fail(LCA_ERR_INVALID_ARG, "seq_group_begin and seq_n_groups must be non-null device arrays");
+  if (max_groups < 0 || max_groups > ((int64_t)1 << 31)) return fail(LCA_ERR_INVALID_ARG, "max_groups must be in [0, 2^31]");
+  if (H < 1) return fail(LCA_ERR_INVALID_ARG, "H must be >= 1");
+  if (q == nullptr || !aligned16(q)) return fail(LCA_ERR_INVALID_ARG, "q must be a non-null 16-byte aligned pointer");
+  if (!valid_dtype(q_dtype)) return fail(LCA_ERR_INVALID_ARG, "q_dtype %d is not LCA_BF16/LCA_F32", q_dtype);
+  if (!mult8(q_seq_stride) || !mult8(q_tok_stride) || q_seq_stride < 0 || q_tok_stride < 0)
+    return fail(LCA_ERR_INVALID_ARG, "q strides must be non-negative multiples of 8 elements");
+  if (q_row0 < 0 || q_row0 + g > T) return fail(LCA_ERR_INVALID_ARG, "summary-query rows [q_row0, q_row0 + g) must lie in [0, T)");
+  if ((rc = check_latent(reps, "reps", true, true)) != LCA_OK) return rc;
+  if (reps->dtype != LCA_BF16 || static_cast<const char*>(reps->kr) != static_cast<const char*>(reps->c) + 2 * LCA_D_C ||
+      reps->kr_tok_stride != reps->c_tok_stride || reps->kr_seq_stride != reps->c_seq_stride)
+    return fail(LCA_ERR_UNSUPPORTED, "paged condensation writes packed bf16 representatives (k_R right after c_KV)");
+  if (anchor_idx == nullptr) return fail(LCA_ERR_INVALID_ARG, "anchor_idx is null");
+  if (anchor_seq_stride < 0 || alpha_seq_stride < 0) return fail(LCA_ERR_INVALID_ARG, "negative output stride");
+  if ((rc = check_scale(sm_scale)) != LCA_OK) return rc;
+  if (max_groups == 0) return ok();
+  const size_t need = lca_condense_workspace_size(B, max_groups, 0);
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need)
+    return fail(LCA_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
+  return hip_status(lca::launch_condense_paged(*cache, B, g, seq_group_begin, seq_n_groups, max_groups, q, q_dtype,
+                                               q_seq_stride, q_tok_stride, H, q_row0, sm_scale, *reps, anchor_idx,
+                                               anchor_seq_stride, alpha, alpha_seq_stride,
+                                               static_cast<float*>(workspace), stream),
+                    "lca_condense_paged launch");
+}
+
 size_t mla_latent_attn_decode_workspace_size(int32_t B, int32_t H, int64_t max_entries) {
   if (B < 1 || H < 16 || H % 16 != 0 || max_entries < 1) return 0;
   const lca::DecodeSplit sp = lca::decode_split(B, H / 16, max_entries);

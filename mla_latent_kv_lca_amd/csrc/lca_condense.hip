@@ -521,6 +521,46 @@ __global__ __launch_bounds__(256) void condense_ring_kernel(
   }
 }
 
+// ---------------------------------------------------------------- K1p ------
+// Ragged batch over a paged cache (packed bf16 rows and representatives,
+// one summary query per sequence): wavefront n of sequence b condenses group
+// seq_group_begin[b] + n when n < seq_n_groups[b]. A group lies inside one
+// page (page_rows is a multiple of g), found with one scalar table load.
+template <int LG>
+__global__ __launch_bounds__(256) void condense_paged_kernel(
+    const bf16_t* __restrict__ pages, int64_t row_stride, int page_rows, const int32_t* __restrict__ table,
+    int64_t table_stride, const int32_t* __restrict__ seq_group_begin, const int32_t* __restrict__ seq_n_groups,
+    const float* __restrict__ qbar, float sm_scale, bf16_t* __restrict__ rc, int64_t rc_seq, int64_t rc_tok,
+    int32_t* __restrict__ anchor, int64_t anchor_seq, float* __restrict__ alpha, int64_t alpha_seq) {
+  constexpr int G = 1 << LG;
+  const int lane = threadIdx.x & 63;
+  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int b = blockIdx.y;
+  if (n >= seq_n_groups[b]) return;  // wave-uniform
+  const int64_t j = seq_group_begin[b] + n, t0 = j * G;
+  const int64_t page = table[(int64_t)b * table_stride + t0 / page_rows];
+  const bf16_t* rows0 = pages + (page * page_rows + t0 % page_rows) * row_stride;
+
+  const float* qb = qbar + (int64_t)b * D_ROW;
+  float qc[8];
+  load8_f32(qb + 8 * lane, qc);
+  const float qr = qb[D_C + lane];
+  RowChunk<bf16_t> rows[G];
+  bf16_t krv[G];
+#pragma unroll
+  for (int r = 0; r < G; ++r) {
+    rows[r].load(rows0 + r * row_stride + 8 * lane);
+    krv[r] = __builtin_nontemporal_load(rows0 + r * row_stride + D_C + lane);
+  }
+  const GroupResult<bf16_t, LG> gr = condense_group<bf16_t, LG>(rows, krv, qc, qr, sm_scale, lane, LCA_MODE_LCA);
+  bf16_t* dst = rc + (int64_t)b * rc_seq + j * rc_tok;
+  store8(dst + 8 * lane, gr.acc);
+  dst[D_C + lane] = (bf16_t)f2bf(gr.kval);
+  if (lane == 0) anchor[(int64_t)b * anchor_seq + j] = (int32_t)(t0 + gr.arg);
+  if (alpha != nullptr && (lane & ((64 >> LG) - 1)) == 0)
+    alpha[(int64_t)b * alpha_seq + j * G + gr.my_row] = gr.a_mine;
+}
+
 template <typename TC, typename TR, int LG>
 static void launch_k1(dim3 grid, hipStream_t st, const lca_latent_t& cache, const float* qbar,
                       int per_group_q, int64_t n_q, int64_t gb, int64_t ng, float sm,
@@ -549,6 +589,48 @@ static void dispatch_g(int lg, dim3 grid, hipStream_t st, const lca_latent_t& ca
   }
 }
 
+static void launch_qbar_shared(int B, int g, const void* q, int q_dtype, int64_t q_seq_stride,
+                               int64_t q_tok_stride, int H, int64_t q_row0, float* qbar_ws, hipStream_t stream) {
+  // workspace: [B][576] summary queries, then [B][QBAR_PARTS][576] part sums
+  float* part = qbar_ws + (int64_t)B * D_ROW;
+  dim3 gp((unsigned)QBAR_PARTS, (unsigned)B);
+  if (q_dtype == LCA_BF16)
+    hipLaunchKernelGGL(qbar_part_kernel<bf16_t>, gp, dim3(QP_THREADS), 0, stream, (const bf16_t*)q,
+                       q_seq_stride, q_tok_stride, H, g, q_row0, part);
+  else
+    hipLaunchKernelGGL(qbar_part_kernel<float>, gp, dim3(QP_THREADS), 0, stream, (const float*)q,
+                       q_seq_stride, q_tok_stride, H, g, q_row0, part);
+  hipLaunchKernelGGL(qbar_final_kernel, dim3((unsigned)B), dim3(D_ROW), 0, stream, part, g * H, qbar_ws);
+}
+
+hipError_t launch_condense_paged(const lca_paged_t& cache, int B, int g, const int32_t* seq_group_begin,
+                                 const int32_t* seq_n_groups, int64_t max_groups, const void* q, int q_dtype,
+                                 int64_t q_seq_stride, int64_t q_tok_stride, int H, int64_t q_row0,
+                                 float sm_scale, const lca_latent_t& reps, int32_t* anchor, int64_t anchor_seq,
+                                 float* alpha, int64_t alpha_seq, float* qbar_ws, hipStream_t stream) {
+  launch_qbar_shared(B, g, q, q_dtype, q_seq_stride, q_tok_stride, H, q_row0, qbar_ws, stream);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  int lg = 0;
+  while ((1 << lg) < g) ++lg;
+  dim3 grid((unsigned)((max_groups + 3) / 4), (unsigned)B);
+#define LCA_PAGED(LGV)                                                                                     \
+  hipLaunchKernelGGL((condense_paged_kernel<LGV>), grid, dim3(256), 0, stream, (const bf16_t*)cache.pages,   \
+                     cache.row_stride, cache.page_rows, cache.block_table, cache.table_stride, seq_group_begin, \
+                     seq_n_groups, qbar_ws, sm_scale, (bf16_t*)reps.c, reps.c_seq_stride, reps.c_tok_stride,  \
+                     anchor, anchor_seq, alpha, alpha_seq)
+  switch (lg) {
+    case 0: LCA_PAGED(0); break;
+    case 1: LCA_PAGED(1); break;
+    case 2: LCA_PAGED(2); break;
+    case 3: LCA_PAGED(3); break;
+    case 4: LCA_PAGED(4); break;
+    default: LCA_PAGED(5); break;
+  }
+#undef LCA_PAGED
+  return hipGetLastError();
+}
+
 hipError_t launch_condense(const lca_latent_t& cache, int B, int g, int64_t group_begin,
                            int64_t n_groups, const void* q, int q_dtype, int64_t q_seq_stride,
                            int64_t q_tok_stride, int H, int64_t q_row0, int64_t q_row_step,
@@ -566,16 +648,7 @@ hipError_t launch_condense(const lca_latent_t& cache, int B, int g, int64_t grou
       hipLaunchKernelGGL(qbar_kernel<float>, g0, dim3(QBAR_THREADS), 0, stream, (const float*)q,
                          q_seq_stride, q_tok_stride, H, g, q_row0, q_row_step, (int)n_q, qbar_ws);
   } else {
-    // workspace: [B][576] summary queries, then [B][QBAR_PARTS][576] part sums
-    float* part = qbar_ws + (int64_t)B * D_ROW;
-    dim3 gp((unsigned)QBAR_PARTS, (unsigned)B);
-    if (q_dtype == LCA_BF16)
-      hipLaunchKernelGGL(qbar_part_kernel<bf16_t>, gp, dim3(QP_THREADS), 0, stream, (const bf16_t*)q,
-                         q_seq_stride, q_tok_stride, H, g, q_row0, part);
-    else
-      hipLaunchKernelGGL(qbar_part_kernel<float>, gp, dim3(QP_THREADS), 0, stream, (const float*)q,
-                         q_seq_stride, q_tok_stride, H, g, q_row0, part);
-    hipLaunchKernelGGL(qbar_final_kernel, dim3((unsigned)B), dim3(D_ROW), 0, stream, part, g * H, qbar_ws);
+    launch_qbar_shared(B, g, q, q_dtype, q_seq_stride, q_tok_stride, H, q_row0, qbar_ws, stream);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

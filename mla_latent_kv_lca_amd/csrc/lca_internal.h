@@ -19,6 +19,11 @@ inline Seg to_seg(const lca_latent_t& t) {
 }
 
 // ---- condensation
+hipError_t launch_condense_paged(const lca_paged_t& cache, int B, int g, const int32_t* seq_group_begin,
+                                 const int32_t* seq_n_groups, int64_t max_groups, const void* q, int q_dtype,
+                                 int64_t q_seq_stride, int64_t q_tok_stride, int H, int64_t q_row0,
+                                 float sm_scale, const lca_latent_t& reps, int32_t* anchor, int64_t anchor_seq,
+                                 float* alpha, int64_t alpha_seq, float* qbar_ws, hipStream_t stream);
 hipError_t launch_condense(const lca_latent_t& cache, int B, int g, int64_t group_begin,
                            int64_t n_groups, const void* q, int q_dtype, int64_t q_seq_stride,
                            int64_t q_tok_stride, int H, int64_t q_row0, int64_t q_row_step,

@@ -140,6 +140,24 @@ def test_decode_paged_argument_errors():
     assert call(reps_=lca.LatentT(64, 64 + 1024, 0, 576, 0, 576, 1)) == lca.LCA_ERR_UNSUPPORTED  # f32 reps
 
 
+def test_condense_paged_argument_errors():
+    lib = lca.load()
+    reps = lca.LatentT(64, 64 + 1024, 0, 576, 0, 576, 0)
+
+    def call(page_rows=64, g=16, table=128, seq=256, max_groups=4, T=16, reps_=reps):
+        cache = lca.PagedT(64, 576, page_rows, table, 4)
+        return lib.lca_condense_paged(ctypes.byref(cache), 1, g, seq, seq, max_groups, 64, 0, 0, 16 * 576, T, 16,
+                                      0, 1.0, ctypes.byref(reps_), 64, 0, None, 0, 64, 1 << 20, None)
+    assert call(page_rows=40) == lca.LCA_ERR_UNSUPPORTED  # not a multiple of g
+    assert call(g=12) == lca.LCA_ERR_UNSUPPORTED
+    assert call(table=None) == lca.LCA_ERR_INVALID_ARG
+    assert call(seq=None) == lca.LCA_ERR_INVALID_ARG
+    assert call(T=15) == lca.LCA_ERR_INVALID_ARG
+    assert call(max_groups=-1) == lca.LCA_ERR_INVALID_ARG
+    assert call(reps_=lca.LatentT(64, 64 + 1024, 0, 576, 0, 576, 1)) == lca.LCA_ERR_UNSUPPORTED
+    assert call(max_groups=0) == lca.LCA_OK  # nothing to condense: no launch
+
+
 def _decode(lib, reps, raw, **kw):
     a = dict(q=64, qdt=0, qss=16 * 576, B=1, H=16, m=0, rb=0, re=8, sm=1.0, o=64, lse=None,
              ws=None, wsb=0)

@@ -189,6 +189,53 @@ def test_decode_paged_ragged_matches_oracle(page_rows, g):
         assert_close(host(lse[b:b + 1]), rl, what=f"paged lse seq {b}")
 
 
+def test_condense_and_decode_paged_ragged_end_to_end():
+    """Ragged batch over shuffled pages: lca_condense_paged against the oracle
+    per sequence, then mla_latent_attn_decode_paged over the GPU's own
+    representatives against the oracle's decode."""
+    Ls, g, w, P = [1500, 2077, 3000, 1040, 777, 2600], 16, 1024, 64
+    B = len(Ls)
+    cs, ks = [], []
+    for b, L in enumerate(Ls):
+        c, kr = li.latent_cache(60 + b, 1, L)
+        li.plant_needles(60 + b, c, kr, 2, 14.0, 0, L)
+        cs.append(c[0])
+        ks.append(kr[0])
+    pool, table = _page_pool([np.concatenate([c, k], -1) for c, k in zip(cs, ks)], P, 11)
+    plans = [O.plan(L, w, g) for L in Ls]
+    ms = [p["m"] for p in plans]
+    m_cap = max(ms)
+    qh = li.queries(61, B, g, H, rho=0.5)
+    qd = li.queries(61, B, 1, H, rho=0.5, stream=1)[:, 0]
+    pool_t, table_t = dev(pool), torch.from_numpy(table).cuda()
+    cache = lca.paged_latent(pool_t, table_t)
+    i32 = lambda x: torch.tensor(x, dtype=torch.int32, device="cuda")  # noqa: E731
+    reps = torch.zeros((B, m_cap, 576), dtype=torch.bfloat16, device="cuda")
+    anchor = torch.full((B, m_cap), -1, dtype=torch.int32, device="cuda")
+    alpha = torch.zeros((B, m_cap, g), dtype=torch.float32, device="cuda")
+    lca.lca_condense_paged(cache, B, g, i32([0] * B), i32(ms), m_cap, dev(qh), 0, 1.0,
+                           lca.packed_latent(reps), anchor, alpha)
+    o = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    rbs = [p["raw_begin"] for p in plans]
+    lca.mla_latent_attn_decode_paged(dev(qd), lca.packed_latent(reps), i32(ms), cache, i32(rbs), i32(Ls),
+                                     max(p["n_entries"] for p in plans), 1.0, o, lse)
+    torch.cuda.synchronize()
+    r, ga = host(reps), host(anchor).astype(np.int64)
+    for b in range(B):
+        m = ms[b]
+        if m:
+            rc, rk, ra, ralpha, s = O.condense(cs[b][None], ks[b][None], qh[b:b + 1], g, 0, m, 0, 0, 1.0)
+            assert_close(r[b, :m, :512], rc[0], what=f"paged rep c_KV seq {b}")
+            assert_close(host(alpha[b, :m]), ralpha[0], tol=1e-5, what=f"paged alpha seq {b}")
+            anchors_agree(ga[b, :m], ra[0], O.top2_margin(s[0]))
+            np.testing.assert_array_equal(r[b, :m, 512:], ks[b][ga[b, :m]].astype(np.float64))
+        ro, rl = O.decode(qd[b:b + 1], r[b:b + 1, :m, :512] if m else None, r[b:b + 1, :m, 512:] if m else None, m,
+                          cs[b][None], ks[b][None], rbs[b], Ls[b], 1.0)
+        assert_close(host(o[b:b + 1]), ro, what=f"paged decode seq {b}")
+        assert_close(host(lse[b:b + 1]), rl, what=f"paged lse seq {b}")
+
+
 @pytest.mark.parametrize("B,L,g,with_alpha", [(3, 5000, 16, True), (2, 4100, 8, False), (1, 70000, 16, False)])
 def test_condense_streaming_kernel_equals_general_kernel(B, L, g, with_alpha):
     """Packed bf16 rows with one summary query per sequence take the streaming
