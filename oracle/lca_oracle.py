@@ -51,7 +51,16 @@ Readings where the pages are silent (each is restated where it is used):
   R8 GQA (关键发现 says the design extends to GQA, with no mapping): n_kv
      independent latent caches; the H query heads form n_kv groups of
      Hg = H / n_kv consecutive heads, group k attends cache k, and cache k is
-     condensed with the summary query of its own Hg heads.
+     condensed with the summary query of its own Hg heads;
+  R9 the step before the path ([MLA] 三.1: per-token latent down-projection,
+     and RoPE needs its own handling under MLA; [LCT] 研究背景与动机 / 核心矛盾:
+     the position key K^R carries RoPE beside the latent): for hidden state x_t
+     at position p_t, c_t = x_t W_DKV, k^R_t = RoPE(x_t W_KR, p_t) and per head
+     [q^nope_h ; q^rope_h] = x_t W_Q[h], q^rope rotated by RoPE(p_t); the
+     absorbed query is [W_UK[h] q^nope_h ; RoPE(q^rope_h, p_t)]. RoPE is the
+     rotate-half convention on 64 dims (pairs (i, i + 32), angle p theta_i,
+     theta_i = base^(-2i/64)). The pages give no widths beyond d_c, d_R and H:
+     per-head no-RoPE query width 128 as W_UK's shape implies.
 """
 from __future__ import annotations
 
@@ -354,3 +363,30 @@ def decode_gqa(q, rep_c, rep_k, m: int, raw_c, raw_k, raw_begin: int, raw_end: i
         os_.append(o)
         ls_.append(l)
     return np.concatenate(os_, axis=1), np.concatenate(ls_, axis=1)
+
+
+def rope_rotate(x, pos, base: float = 10000.0) -> np.ndarray:
+    """Rotate-half RoPE of the last axis (64 wide) at positions pos (R9):
+    out[i] = x[i] cos(p t_i) - x[i+32] sin(p t_i), out[i+32] = x[i+32] cos(p t_i)
+    + x[i] sin(p t_i), t_i = base^(-2i/64), i < 32. x [..., 64], pos broadcast
+    over the leading axes."""
+    x = _f64(x)
+    half = x.shape[-1] // 2
+    theta = base ** (-2.0 * np.arange(half) / x.shape[-1])
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * theta
+    cos, sin = np.cos(ang), np.sin(ang)
+    a, b = x[..., :half], x[..., half:]
+    return np.concatenate([a * cos - b * sin, b * cos + a * sin], axis=-1)
+
+
+def project(x, pos, w_cat, w_uk, H: int, base: float = 10000.0):
+    """The step before the path (R9): x [T, d], pos [T], w_cat [d, 576 + 192 H]
+    = [W_DKV (512) | W_KR (64) | W_Q (head h: 128 no-RoPE + 64 RoPE columns)],
+    w_uk [H, 512, 128]. Returns the cache rows [T, 576] = [c ; RoPE(k^R)] and
+    the absorbed queries [T, H, 576] = [W_UK[h] q^nope_h ; RoPE(q^rope_h)]."""
+    y = _f64(x) @ _f64(w_cat)
+    pos = np.asarray(pos)
+    rows = np.concatenate([y[:, :D_C], rope_rotate(y[:, D_C:D_ROW], pos, base)], axis=-1)
+    q = y[:, D_ROW:].reshape(len(y), H, 192)
+    q_rope = rope_rotate(q[..., 128:], pos[:, None], base)
+    return rows, np.stack([absorb_query(q[t, :, :128], q_rope[t], w_uk) for t in range(len(y))])

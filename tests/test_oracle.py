@@ -585,3 +585,59 @@ def test_gqa_condense_uses_each_groups_own_heads_and_cache():
             a = np.exp(sc - sc.max()) / np.exp(sc - sc.max()).sum()
             np.testing.assert_allclose(rc[0, k, j], a @ c[0, k, j * g:(j + 1) * g], atol=1e-12)
             assert anc[0, k, j] == j * g + int(np.argmax(sc))
+
+
+def _rope_complex(x, pos, base=10000.0):
+    """RoPE written as a complex rotation (an independent formulation): pair
+    (x_i, x_{i+32}) is the complex number x_i + j x_{i+32}, multiplied by
+    exp(j p theta_i)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))
+    z = torch.complex(t[..., :32], t[..., 32:])
+    theta = base ** (-torch.arange(32, dtype=torch.float64) * 2.0 / 64)
+    ang = torch.from_numpy(np.asarray(pos, dtype=np.float64))[..., None] * theta
+    z = z * torch.polar(torch.ones_like(ang), ang)
+    return torch.cat([z.real, z.imag], dim=-1).numpy()
+
+
+def test_rope_matches_complex_rotation_and_is_relative():
+    r = np.random.default_rng(50)
+    x = r.standard_normal((7, 64))
+    pos = np.array([0, 1, 5, 1000, 65535, 1 << 20, 3])
+    got = O.rope_rotate(x, pos)
+    np.testing.assert_allclose(got, _rope_complex(x, pos), atol=1e-12)
+    np.testing.assert_allclose(O.rope_rotate(x[:1], [0]), x[:1], atol=0)     # position 0: identity
+    np.testing.assert_allclose(np.linalg.norm(got, axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
+    a, b = r.standard_normal(64), r.standard_normal(64)
+    for p1, p2 in ((10, 3), (70000, 69990), (5, 5)):  # <R(p1) a, R(p2) b> depends on p1 - p2 only
+        lhs = O.rope_rotate(a[None], [p1])[0] @ O.rope_rotate(b[None], [p2])[0]
+        rhs = O.rope_rotate(a[None], [p1 - p2])[0] @ b
+        assert abs(lhs - rhs) < 1e-9
+
+
+def test_projected_decode_is_textbook_attention_from_hidden_states():
+    """R9 end to end: project hidden states (cache rows and absorbed queries),
+    decode over the cache rows, up-project through W_UV: equals torch's
+    float64 attention with per-head keys [W_UK[h]^T c ; RoPE(k^R)] and values
+    W_UV[h]^T c built directly from x, with RoPE as a complex rotation."""
+    r = np.random.default_rng(51)
+    d, H, L = 48, 3, 19
+    x = r.standard_normal((L + 1, d))
+    pos = np.arange(L + 1) + 1000
+    w_cat = r.standard_normal((d, 576 + 192 * H)) / math.sqrt(d)
+    w_uk = r.standard_normal((H, 512, 128)) / math.sqrt(512)
+    w_uv = r.standard_normal((H, 512, 128)) / math.sqrt(512)
+    rows, q_abs = O.project(x, pos, w_cat, w_uk, H)
+    # the last token queries the L cached tokens before it
+    o_lat, _ = O.decode(q_abs[L][None], None, None, 0, rows[None, :L, :512], rows[None, :L, 512:], 0, L, 0.7)
+    got = O.up_proj(o_lat, w_uv)[0]
+    y = x @ w_cat
+    c = y[:L, :512]
+    kr = _rope_complex(y[:L, 512:576], pos[:L])
+    qh = y[L, 576:].reshape(H, 192)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))  # noqa: E731
+    for h in range(H):
+        k = np.concatenate([c @ w_uk[h], kr], axis=1)
+        v = c @ w_uv[h]
+        qv = np.concatenate([qh[h, :128], _rope_complex(qh[h, 128:][None], [pos[L]])[0]])
+        ref = F.scaled_dot_product_attention(t(qv)[None, None], t(k)[None], t(v)[None], scale=0.7)[0, 0]
+        np.testing.assert_allclose(got[h], ref.numpy(), atol=1e-12)
