@@ -273,6 +273,43 @@ int mla_latent_attn_prefill_chunk(const void* q, int32_t q_dtype, int64_t q_tok_
 int mla_up_proj(const void* o_latent, int32_t o_dtype, int64_t T, int32_t H, const void* w_uv,
                 int32_t w_dtype, void* out, int32_t out_dtype, hipStream_t stream);
 
+/* Workspace bytes lca_project needs: the per-head no-RoPE query parts of the
+ * T tokens, bf16 [T, H, 128]. */
+size_t lca_project_workspace_size(int64_t T, int32_t H);
+
+/* The projection step in front of the attention (MLA: "新一代开源大模型架构
+ * 演进与注意力机制深度对比解析" 三.1, a per-token latent down-projection, with
+ * RoPE handled apart; LCT page 研究背景与动机 / 核心矛盾: the position key K^R
+ * beside the latent C^KV). For every token t with hidden state x_t and
+ * position p_t = pos[t]:
+ *   y = W x_t with W = w_proj, bf16 [576 + 192 H, d_model] row-major: row n
+ *   holds the weights of output n. Outputs [0, 512) are c_t (W_DKV), [512,
+ *   576) the RoPE key before rotation (W_KR), then for head h outputs
+ *   576 + 192 h + [0, 128) are q^nope_h and + [128, 192) q^rope_h (W_Q).
+ *   RoPE(v, p) rotates the 64-wide v in pairs (i, i + 32) by the angle
+ *   p * rope_base^(-i / 32): (v_i, v_{i+32}) -> (v_i cos - v_{i+32} sin,
+ *   v_{i+32} cos + v_i sin).
+ * Writes
+ *   the cache row [c_t ; RoPE(k_t, p_t)] (bf16, 576 values) at
+ *     rows + dst_row[t] * row_stride, skipped where dst_row[t] < 0 (the
+ *     append: dst_row is a device int64 [T] array of row indices into the
+ *     caller's cache or page pool);
+ *   the absorbed query of every head h at q + t * q_tok_stride + 576 h
+ *     (dtype q_dtype): [W_UK[h] q^nope_h ; RoPE(q^rope_h, p_t)] with w_uk
+ *     bf16 [H, 512, 128] (W_UK[h][j][k] multiplies q^nope_h[k]).
+ * x is bf16 [T, d_model] with token stride x_tok_stride; pos is a device int32
+ * [T] array. Matrix products run on bf16 operands with fp32 accumulation;
+ * q^nope is rounded to bf16 before the W_UK product. d_model must be a
+ * multiple of 32. The caller guarantees that the dst_row values name rows
+ * inside its buffer and that no two tokens share one (not checked). q and
+ * rows must not overlap any input. workspace >=
+ * lca_project_workspace_size(T, H) bytes, 16-byte aligned; overwritten.
+ * T == 0 is a no-op. */
+int lca_project(const void* x, int64_t x_tok_stride, int64_t T, int32_t d_model, const int32_t* pos,
+                double rope_base, const void* w_proj, const void* w_uk, int32_t H, void* rows,
+                int64_t row_stride, const int64_t* dst_row, void* q, int32_t q_dtype, int64_t q_tok_stride,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

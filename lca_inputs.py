@@ -21,6 +21,10 @@ Recipe (one generator per tensor, numpy PCG64 seeded with 1000*cfg + id):
         vector rotated to the token's position, and a query's RoPE part is
         it rotated to the query's position (so the RoPE logit depends on the
         distance only).
+  id 8  hidden states x             N(0, 1)             [T, d_model]
+  id 9  projection weights          N(0, 1/d_model)     [576 + 192 H, d_model]
+        (one row per output: c, the RoPE key, then per head 128 no-RoPE
+        and 64 RoPE query outputs), so every projected value is ~N(0, 1)
 Values are drawn in float32 and, for bf16 runs, rounded once on the host, so
 the oracle and the GPU read identical numbers.
 """
@@ -33,7 +37,7 @@ D_R = 64    # decoupled RoPE key width
 D_ROW = D_C + D_R
 D_V = 128   # per-head value width after the up-projection
 
-ID_C, ID_K, ID_Q, ID_WUV, ID_WUK, ID_NEEDLE, ID_POS = 1, 2, 3, 4, 5, 6, 7
+ID_C, ID_K, ID_Q, ID_WUV, ID_WUK, ID_NEEDLE, ID_POS, ID_X, ID_WPROJ = 1, 2, 3, 4, 5, 6, 7, 8, 9
 
 
 def rng(cfg: int, tensor_id: int) -> np.random.Generator:
@@ -144,6 +148,17 @@ def w_uk(cfg: int, H: int, bf16: bool = True) -> np.ndarray:
     return bf16_round(w) if bf16 else w
 
 
+def hidden_states(cfg: int, T: int, d_model: int, bf16: bool = True) -> np.ndarray:
+    x = rng(cfg, ID_X).standard_normal((T, d_model), dtype=np.float32)
+    return bf16_round(x) if bf16 else x
+
+
+def w_proj(cfg: int, H: int, d_model: int, bf16: bool = True) -> np.ndarray:
+    w = (rng(cfg, ID_WPROJ).standard_normal((D_ROW + 192 * H, d_model), dtype=np.float32)
+         * np.float32(1.0 / np.sqrt(d_model)))
+    return bf16_round(w) if bf16 else w
+
+
 # ------------------------------------------------------------------------
 # Device-side generation for the benchmark's large workloads (same recipe,
 # torch's Philox generator instead of PCG64, so values differ from the numpy
@@ -188,3 +203,18 @@ def w_uv_torch(seed: int, H: int, device="cuda", dtype=None):
     g.manual_seed(seed)
     return (torch.randn((H, D_C, D_V), generator=g, device=device, dtype=torch.float32)
             * (1.0 / np.sqrt(D_C))).to(dtype)
+
+
+def projection_torch(seed: int, T: int, d_model: int, H: int, device="cuda", dtype=None):
+    """Hidden states x [T, d] ~ N(0, 1), projection weights [576 + 192 H, d]
+    ~ N(0, 1/d) and W_UK [H, 512, 128] ~ N(0, 1/512)."""
+    import torch
+    dtype = dtype or torch.bfloat16
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn((T, d_model), generator=g, device=device, dtype=torch.float32).to(dtype)
+    w = (torch.randn((D_ROW + 192 * H, d_model), generator=g, device=device, dtype=torch.float32)
+         * (1.0 / np.sqrt(d_model))).to(dtype)
+    wuk = (torch.randn((H, D_C, D_V), generator=g, device=device, dtype=torch.float32)
+           * (1.0 / np.sqrt(D_C))).to(dtype)
+    return x, w, wuk

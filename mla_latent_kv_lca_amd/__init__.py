@@ -31,7 +31,8 @@ D_C, D_R, D_ROW, D_V = 512, 64, 576, 128
 EXPORTS = ("lca_version", "lca_last_error", "lca_plan", "lca_condense_workspace_size",
            "lca_condense", "lca_condense_mode", "lca_condense_paged", "mla_latent_attn_decode_workspace_size",
            "mla_latent_attn_decode", "mla_latent_attn_decode_paged",
-           "mla_latent_attn_decode_up", "mla_latent_attn_prefill_chunk", "mla_up_proj")
+           "mla_latent_attn_decode_up", "mla_latent_attn_prefill_chunk", "mla_up_proj",
+           "lca_project_workspace_size", "lca_project")
 
 
 class LcaError(RuntimeError):
@@ -114,6 +115,12 @@ def load() -> ctypes.CDLL:
     lib.mla_up_proj.restype = c_int32
     lib.mla_up_proj.argtypes = [c_void_p, c_int32, c_int64, c_int32, c_void_p, c_int32, c_void_p,
                                 c_int32, c_void_p]
+    lib.lca_project_workspace_size.restype = ctypes.c_size_t
+    lib.lca_project_workspace_size.argtypes = [c_int64, c_int32]
+    lib.lca_project.restype = c_int32
+    lib.lca_project.argtypes = [c_void_p, c_int64, c_int64, c_int32, c_void_p, ctypes.c_double, c_void_p,
+                                c_void_p, c_int32, c_void_p, c_int64, c_void_p, c_void_p, c_int32, c_int64,
+                                c_void_p, ctypes.c_size_t, c_void_p]
     _lib = lib
     return lib
 
@@ -362,3 +369,35 @@ def mla_up_proj(o_latent: torch.Tensor, w_uv: torch.Tensor, out: torch.Tensor, s
         raise ValueError("shapes must be o_latent [T,H,512], w_uv [H,512,128], out [T,H,128]")
     _check(load().mla_up_proj(o_latent.data_ptr(), dtype_code(o_latent), T, H, w_uv.data_ptr(),
                               dtype_code(w_uv), out.data_ptr(), dtype_code(out), _stream(stream)))
+
+
+def lca_project_workspace_size(T: int, H: int) -> int:
+    return load().lca_project_workspace_size(T, H)
+
+
+def lca_project(x: torch.Tensor, pos: torch.Tensor, w_proj: torch.Tensor, w_uk: torch.Tensor,
+                rows: torch.Tensor, dst_row: torch.Tensor, q: torch.Tensor, rope_base: float = 10000.0,
+                workspace=None, stream=None) -> None:
+    """Hidden states x [T, d] (bf16, rows contiguous) at positions pos (int32
+    [T]) -> cache rows written at rows.view(-1, row_stride)[dst_row[t]] (bf16,
+    last dim contiguous) and absorbed queries q [T, H, 576] (bf16 or f32,
+    token stride q.stride(0)). w_proj bf16 [576 + 192 H, d], w_uk bf16
+    [H, 512, 128], dst_row int64 [T]."""
+    T, d = x.shape
+    H = w_uk.shape[0]
+    if x.stride(1) != 1 or not w_proj.is_contiguous() or not w_uk.is_contiguous():
+        raise ValueError("x rows, w_proj and w_uk must be contiguous")
+    if tuple(w_proj.shape) != (D_ROW + 192 * H, d) or tuple(w_uk.shape[1:]) != (D_C, D_V):
+        raise ValueError("w_proj must be [576 + 192 H, d] and w_uk [H, 512, 128]")
+    if q.dim() != 3 or tuple(q.shape[1:]) != (H, D_ROW) or q.stride(2) != 1 or q.stride(1) != D_ROW:
+        raise ValueError("q must be [T, H, 576] with contiguous heads")
+    if pos.dtype != torch.int32 or dst_row.dtype != torch.int64:
+        raise ValueError("pos must be int32 and dst_row int64")
+    if rows.stride(-1) != 1:
+        raise ValueError("rows must have a contiguous last dim")
+    row_stride = rows.stride(-2) if rows.dim() >= 2 else D_ROW
+    ws = _workspace(lca_project_workspace_size(T, H), x, workspace)
+    _check(load().lca_project(x.data_ptr(), x.stride(0), T, d, pos.data_ptr(), rope_base, w_proj.data_ptr(),
+                              w_uk.data_ptr(), H, rows.data_ptr(), row_stride, dst_row.data_ptr(),
+                              q.data_ptr(), dtype_code(q), q.stride(0), ws.data_ptr(),
+                              ws.numel() * ws.element_size(), _stream(stream)))

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblca.so")
-SOURCES = ["lca_api.cpp", "lca_condense.hip", "lca_decode.hip", "lca_prefill.hip", "lca_upproj.hip"]
+SOURCES = ["lca_api.cpp", "lca_condense.hip", "lca_decode.hip", "lca_prefill.hip", "lca_upproj.hip", "lca_project.hip"]
 ARCH = "gfx950"
 
 

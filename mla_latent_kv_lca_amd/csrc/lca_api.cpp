@@ -340,4 +340,39 @@ int mla_up_proj(const void* o_latent, int32_t o_dtype, int64_t T, int32_t H, con
                     "mla_up_proj launch");
 }
 
+size_t lca_project_workspace_size(int64_t T, int32_t H) {
+  if (T < 0 || H < 1) return 0;
+  return (size_t)T * (size_t)H * LCA_D_V * 2;  // q^nope of every token and head, bf16
+}
+
+int lca_project(const void* x, int64_t x_tok_stride, int64_t T, int32_t d_model, const int32_t* pos,
+                double rope_base, const void* w_proj, const void* w_uk, int32_t H, void* rows,
+                int64_t row_stride, const int64_t* dst_row, void* q, int32_t q_dtype, int64_t q_tok_stride,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (T < 0) return fail(LCA_ERR_INVALID_ARG, "T must be >= 0");
+  if (H < 1 || H > 1024) return fail(LCA_ERR_UNSUPPORTED, "H = %d: supported head counts are 1..1024", H);
+  if (d_model < 32 || d_model % 32 != 0)
+    return fail(LCA_ERR_UNSUPPORTED, "d_model = %d: must be a positive multiple of 32", d_model);
+  if (!(std::isfinite(rope_base) && rope_base > 1.0)) return fail(LCA_ERR_INVALID_ARG, "rope_base must be finite and > 1");
+  if (!valid_dtype(q_dtype)) return fail(LCA_ERR_INVALID_ARG, "q_dtype %d is not LCA_BF16/LCA_F32", q_dtype);
+  if (T == 0) return ok();
+  if (x == nullptr || !aligned16(x) || w_proj == nullptr || !aligned16(w_proj) || w_uk == nullptr ||
+      !aligned16(w_uk))
+    return fail(LCA_ERR_INVALID_ARG, "x, w_proj and w_uk must be non-null 16-byte aligned pointers");
+  if (x_tok_stride < d_model || !mult8(x_tok_stride))
+    return fail(LCA_ERR_INVALID_ARG, "x_tok_stride must be >= d_model and a multiple of 8");
+  if (pos == nullptr || dst_row == nullptr) return fail(LCA_ERR_INVALID_ARG, "pos and dst_row must be non-null device arrays");
+  if (rows == nullptr || !aligned16(rows) || row_stride < LCA_D_ROW || !mult8(row_stride))
+    return fail(LCA_ERR_INVALID_ARG, "rows must be non-null and aligned, row_stride >= 576 and a multiple of 8");
+  if (q == nullptr || !aligned16(q) || q_tok_stride < (int64_t)H * LCA_D_ROW || !mult8(q_tok_stride))
+    return fail(LCA_ERR_INVALID_ARG, "q must be non-null and aligned, q_tok_stride >= 576 H and a multiple of 8");
+  const size_t need = lca_project_workspace_size(T, H);
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need)
+    return fail(LCA_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
+  if ((T + 127) / 128 > 0x7fffffff) return fail(LCA_ERR_UNSUPPORTED, "T too large");
+  return hip_status(lca::launch_project(x, x_tok_stride, T, d_model, pos, rope_base, w_proj, w_uk, H, rows,
+                                        row_stride, dst_row, q, q_dtype, q_tok_stride, workspace, stream),
+                    "lca_project launch");
+}
+
 }  // extern "C"

@@ -71,4 +71,10 @@ constexpr int UP_SMALL_T = 64;  // token counts up to this use the small-T kerne
 hipError_t launch_up_proj(const void* o_latent, int o_dtype, int64_t T, int H, const void* w_uv,
                           int w_dtype, void* out, int out_dtype, hipStream_t stream);
 
+// ---- projection step (hidden states -> cache rows and absorbed queries)
+hipError_t launch_project(const void* x, int64_t x_stride, int64_t T, int d, const int32_t* pos,
+                          double rope_base, const void* w_proj, const void* w_uk, int H, void* rows,
+                          int64_t row_stride, const int64_t* dst_row, void* q, int q_dtype,
+                          int64_t q_stride, void* qn, hipStream_t stream);
+
 }  // namespace lca

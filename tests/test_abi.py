@@ -218,3 +218,33 @@ def test_prefill_and_up_proj_argument_errors():
     assert up(64, 0, -1, 16, 64, 0, 64, 0, None) == lca.LCA_ERR_INVALID_ARG
     assert up(None, 0, 4, 16, 64, 0, 64, 0, None) == lca.LCA_ERR_INVALID_ARG
     assert up(64, 3, 4, 16, 64, 0, 64, 0, None) == lca.LCA_ERR_INVALID_ARG
+
+
+def _project(lib, **kw):
+    a = dict(x=64, xs=2048, T=4, d=2048, pos=64, base=10000.0, w=64, wuk=64, H=16, rows=64, rs=576,
+             dst=64, q=64, qdt=0, qs=16 * 576, ws=64, wsb=4 * 16 * 128 * 2)
+    a.update(kw)
+    return lib.lca_project(a["x"], a["xs"], a["T"], a["d"], a["pos"], a["base"], a["w"], a["wuk"], a["H"],
+                           a["rows"], a["rs"], a["dst"], a["q"], a["qdt"], a["qs"], a["ws"], a["wsb"], None)
+
+
+def test_project_argument_errors():
+    lib = lca.load()
+    assert lca.lca_project_workspace_size(4, 16) == 4 * 16 * 128 * 2
+    assert lca.lca_project_workspace_size(-1, 16) == 0
+    assert _project(lib, T=0) == lca.LCA_OK
+    assert _project(lib, T=-1) == lca.LCA_ERR_INVALID_ARG
+    assert _project(lib, d=100) == lca.LCA_ERR_UNSUPPORTED
+    assert _project(lib, H=0) == lca.LCA_ERR_UNSUPPORTED
+    assert _project(lib, base=1.0) == lca.LCA_ERR_INVALID_ARG
+    assert _project(lib, base=float("nan")) == lca.LCA_ERR_INVALID_ARG
+    assert _project(lib, qdt=5) == lca.LCA_ERR_INVALID_ARG
+    assert _project(lib, x=None) == lca.LCA_ERR_INVALID_ARG
+    assert _project(lib, w=72) == lca.LCA_ERR_INVALID_ARG      # misaligned
+    assert _project(lib, xs=1000) == lca.LCA_ERR_INVALID_ARG   # shorter than d_model
+    assert _project(lib, pos=None) == lca.LCA_ERR_INVALID_ARG
+    assert _project(lib, dst=None) == lca.LCA_ERR_INVALID_ARG
+    assert _project(lib, rs=500) == lca.LCA_ERR_INVALID_ARG
+    assert _project(lib, qs=576) == lca.LCA_ERR_INVALID_ARG    # heads overlap
+    assert _project(lib, wsb=16) == lca.LCA_ERR_WORKSPACE
+    assert _project(lib, ws=None) == lca.LCA_ERR_WORKSPACE

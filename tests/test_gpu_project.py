@@ -1,0 +1,145 @@
+"""GPU parity of the projection step in front of the attention: hidden
+states -> cache rows [c ; RoPE(k_R)] appended at caller-chosen rows, and
+absorbed queries [W_UK q_nope ; RoPE(q_rope)], against the fp64 oracle; then
+a decode loop driven by it (project, append, condense each completed group,
+attend), against the oracle's incremental decode on the same rows."""
+import numpy as np
+import pytest
+import torch
+
+import lca_inputs as li
+import mla_latent_kv_lca_amd as lca
+from oracle import lca_oracle as O
+from tests.gpu_util import assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 7.0
+
+
+def _within(got, ref, rel, floor, what):
+    """|got - ref| <= rel |ref| + floor * rms(ref), element by element. For
+    outputs stored in bf16 (values of a few units, whose half-ulp alone is
+    above 1e-2) rel = 2^-8 covers the storage rounding (2^-9 relative) with
+    room for the fp32 accumulation; the floor covers values near zero."""
+    err = np.abs(got - ref)
+    bound = rel * np.abs(ref) + floor * float(np.sqrt(np.mean(ref ** 2)))
+    bad = np.flatnonzero(err > bound)
+    assert bad.size == 0, f"{what}: {bad.size} of {err.size} elements out of bound, worst {err.max():.3e}"
+
+
+def _project_gpu(x, pos, w, wuk, dst, n_rows, q_dtype):
+    T = x.shape[0]
+    H = wuk.shape[0]
+    rows = torch.full((n_rows, 576), SENTINEL, dtype=torch.bfloat16, device="cuda")
+    q = torch.full((T, H, 576), float("nan"), dtype=q_dtype, device="cuda")
+    lca.lca_project(dev(x), dev(pos, torch.int32), dev(w), dev(wuk), rows, dev(dst, torch.int64), q)
+    torch.cuda.synchronize()
+    return host(rows), host(q)
+
+
+@pytest.mark.parametrize("T,d,H,q_dtype", [(300, 256, 16, torch.bfloat16),   # 3 token tiles, ragged tail
+                                           (37, 2048, 16, torch.float32),    # a decode batch
+                                           (129, 96, 3, torch.float32),      # odd H: half-used rotary block
+                                           (1, 32, 1, torch.bfloat16)])      # one token, one k slice
+def test_project_matches_oracle(T, d, H, q_dtype):
+    seed = 60 + H
+    x = li.hidden_states(seed, T, d)
+    w = li.w_proj(seed, H, d)
+    wuk = li.w_uk(seed, H)
+    r = np.random.default_rng(seed)
+    pos = r.integers(0, 1 << 20, T).astype(np.int32)
+    pos[0] = 0
+    if T > 2:
+        pos[1], pos[2] = 131071, -5
+    n_rows = T + 9
+    dst = r.permutation(n_rows)[:T].astype(np.int64)
+    if T > 4:
+        dst[3] = -1  # this token's row is not written
+    rows, q = _project_gpu(x, pos, w, wuk, dst, n_rows, q_dtype)
+    ref_rows, ref_q = O.project(x, pos, w.T, wuk, H)
+
+    written = dst >= 0
+    got_rows = rows[dst[written]]
+    _within(got_rows, ref_rows[written], 2.0 ** -8, 1e-3, "cache rows")
+    untouched = np.setdiff1d(np.arange(n_rows), dst[written])
+    assert np.all(rows[untouched] == SENTINEL), "rows outside dst_row were written"
+    _within(q[..., 512:], ref_q[..., 512:], 2.0 ** -8, 1e-3, "rotated query part")
+    # the absorbed part also carries the bf16 rounding of q_nope before the
+    # W_UK product: about 2^-9 of the part's rms, hence the larger floor
+    _within(q[..., :512], ref_q[..., :512], 2.0 ** -8, 1e-2, "absorbed query part")
+    if q_dtype == torch.float32:
+        assert_close(q, ref_q, what="absorbed queries")
+
+
+def test_project_rotary_part_is_relative():
+    """Same hidden state at positions p and p + D: the query's rotary part
+    dotted with the key's rotary part depends on the distance only."""
+    d, H = 64, 1
+    x1 = li.hidden_states(70, 1, d)
+    x = np.repeat(x1, 4, axis=0)
+    pos = np.array([10, 10 + 300, 5000, 5000 + 300], dtype=np.int32)
+    w = li.w_proj(70, H, d)
+    wuk = li.w_uk(70, H)
+    rows, q = _project_gpu(x, pos, w, wuk, np.arange(4, dtype=np.int64), 4, torch.float32)
+    # query of token 1 (p + 300) against key of token 0 (p), at two offsets p
+    a = q[1, 0, 512:] @ rows[0, 512:]
+    b = q[3, 0, 512:] @ rows[2, 512:]
+    assert abs(a - b) <= 2e-2 * max(1.0, abs(a)), (a, b)
+
+
+def test_projected_incremental_decode_loop():
+    """The decode loop from hidden states: a prompt of L0 tokens is projected
+    into the cache in one call; every step projects one token (its row is
+    appended after the step's attention, its query joins the history), every
+    completed group beyond the window is condensed with the last g queries."""
+    L0, S, w_, g, d, H = 1300, 40, 1024, 16, 256, 16
+    sm = 0.35
+    x = li.hidden_states(71, L0 + S, d)
+    wp = li.w_proj(71, H, d)
+    wuk = li.w_uk(71, H)
+    pos = np.arange(L0 + S, dtype=np.int32)
+    x_t, wp_t, wuk_t = dev(x), dev(wp), dev(wuk)
+    pos_t = dev(pos, torch.int32)
+    cache = torch.zeros((1, L0 + S, 576), dtype=torch.bfloat16, device="cuda")
+    q_prompt = torch.empty((L0, H, 576), dtype=torch.bfloat16, device="cuda")
+    qall = torch.empty((1, g + S, H, 576), dtype=torch.bfloat16, device="cuda")
+    lca.lca_project(x_t[:L0], pos_t[:L0], wp_t, wuk_t, cache[0],
+                    torch.arange(L0, dtype=torch.int64, device="cuda"), q_prompt)
+    qall[0, :g] = q_prompt[L0 - g:]
+    m_cap = O.plan(L0 + S, w_, g)["m"]
+    reps = torch.empty((1, m_cap, 576), dtype=torch.bfloat16, device="cuda")
+    anchor = torch.empty((1, m_cap), dtype=torch.int32, device="cuda")
+    L = L0
+    m = O.plan(L, w_, g)["m"]
+    lca.lca_condense(lca.packed_latent(cache), 1, g, 0, m, qall, 0, 0, sm, lca.packed_latent(reps), anchor)
+    o = torch.empty((1, H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((1, H), dtype=torch.float32, device="cuda")
+    ws = lca.decode_workspace(1, H, L0 + S)
+    outs = []
+    for st in range(S):
+        t = L0 + st
+        lca.lca_project(x_t[t:t + 1], pos_t[t:t + 1], wp_t, wuk_t, cache[0],
+                        torch.full((1,), t, dtype=torch.int64, device="cuda"), qall[0, g + st:g + st + 1])
+        lca.mla_latent_attn_decode(qall[:, g + st], lca.packed_latent(reps) if m else None, m,
+                                   lca.packed_latent(cache), m * g, L, sm, o, lse, ws)
+        outs.append(o.clone())
+        L += 1
+        if L - w_ >= (m + 1) * g:
+            lca.lca_condense(lca.packed_latent(cache), 1, g, m, 1, qall, st + 1, 0, sm,
+                             lca.packed_latent(reps), anchor)
+            m += 1
+    torch.cuda.synchronize()
+
+    # the projection itself, for every token
+    ref_rows, ref_q = O.project(x, pos, wp.T, wuk, H)
+    rows = host(cache)[0]
+    _within(rows, ref_rows, 2.0 ** -8, 1e-3, "projected cache rows")
+    qh = host(qall)[0]
+    _within(qh[g:, :, 512:], ref_q[L0:, :, 512:], 2.0 ** -8, 1e-3, "projected step queries, rotary part")
+    _within(qh[g:, :, :512], ref_q[L0:, :, :512], 2.0 ** -8, 1e-2, "projected step queries, absorbed part")
+    # the loop, on the rows and queries the GPU produced
+    ro, _, _, _, m_ref = O.decode_loop(rows[:L0, :512], rows[:L0, 512:], qh[:g], qh[g:],
+                                       rows[L0:, :512], rows[L0:, 512:], w_, g, sm)
+    assert m == m_ref
+    assert_close(np.stack([host(v)[0] for v in outs]), ro, what="projected decode loop o_latent")
