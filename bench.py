@@ -42,6 +42,7 @@ def parse():
     ap.add_argument("--roofline-reps", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-paged", action="store_true")
+    ap.add_argument("--no-project", action="store_true")
     ap.add_argument("--prefill-len", type=int, default=131072)
     ap.add_argument("--no-graph", action="store_true",
                     help="launch every kernel from Python instead of replaying a captured HIP graph")
@@ -308,6 +309,10 @@ def main():
     if not args.no_paged:
         paged = paged_leg()
 
+    project = None
+    if not args.no_project:
+        project = project_leg()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cache0, qhist[0], qsteps0, args.cpu_seconds)
@@ -340,6 +345,7 @@ def main():
         "decode_context_tokens_per_s": B * L / t_dec,
         "prefill": prefill,
         "paged": paged,
+        "project": project,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec))
@@ -493,6 +499,55 @@ def paged_leg(B=32, page_rows=64, reps_=20):
             "decode_us": t_dec * 1e6, "decode_gbs": dec_bytes / t_dec / 1e9,
             "decode_context_tokens_per_s": sum(Ls) / t_dec,
             "condense_us": t_con * 1e6, "condense_gbs": con_bytes / t_con / 1e9}
+
+
+D_MODEL = 2048  # hidden width of the projection leg: H heads x 128
+
+
+def project_leg(reps_=20):
+    """The projection step before the attention (lca_project: hidden states
+    -> appended cache rows + absorbed queries) for a decode batch of B tokens
+    and for one prefill chunk of PF_C tokens, d_model = 2048. Calls are
+    captured in a graph and timed with HIP events on the launch stream."""
+    import torch
+
+    import lca_inputs as li
+    import mla_latent_kv_lca_amd as lca
+    stream = torch.cuda.current_stream()
+    res = {"d_model": D_MODEL, "H": H}
+    n_out = 576 + 192 * H
+    for name, T in (("decode", B), ("prefill_chunk", PF_C)):
+        x, w, wuk = li.projection_torch(600 + T, T, D_MODEL, H)
+        pos = torch.arange(L, L + T, dtype=torch.int32, device="cuda")
+        rows = torch.empty((T, 576), dtype=torch.bfloat16, device="cuda")
+        dst = torch.arange(T, dtype=torch.int64, device="cuda")
+        q = torch.empty((T, H, 576), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(lca.lca_project_workspace_size(T, H), dtype=torch.uint8, device="cuda")
+
+        def fn():
+            lca.lca_project(x, pos, w, wuk, rows, dst, q, workspace=ws)
+
+        fn()
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for _ in range(reps_):
+                fn()
+        gr.replay()
+        torch.cuda.synchronize()
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        gr.replay()
+        b_.record(stream)
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b_) / reps_ * 1e-3
+        # weights + hidden states read, cache rows + absorbed queries written
+        byts = (n_out * D_MODEL + H * 512 * 128 + T * D_MODEL) * 2 + T * 576 * 2 + T * H * 576 * 2
+        flop = 2 * T * D_MODEL * n_out + 2 * T * H * 128 * 512
+        res[name] = {"tokens": T, "us": t * 1e6, "gbs": byts / t / 1e9, "hbm_frac": byts / t / 1e9 / HBM_PEAK_GBS,
+                     "tflops": flop / t / 1e12, "mfma_frac": flop / t / 1e12 / MFMA_PEAK_TFLOPS,
+                     "bytes": byts, "flop": flop}
+    return res
 
 
 def cpu_baseline(cache, qhist, qsteps, budget_s):

@@ -258,6 +258,168 @@ __global__ __launch_bounds__(256, 2) void absorb_kernel(const bf16_t* __restrict
     }
 }
 
+// ---- few tokens (decode): the weights stream once, spread over many
+// workgroups. A workgroup computes 16 output columns for up to 32 tokens over
+// the whole model width. The width is cut into 256-wide k chunks dealt to the
+// 8 wavefronts round-robin; per chunk a wave issues all of its loads at once
+// (one memory round trip): the 32 x 256 hidden-state block goes to the wave's
+// own LDS region by direct loads that read whole 512-byte row pieces, and the
+// 16 weight rows go straight into MFMA operand registers. The 8 partial tiles
+// are added in wave order through LDS and the epilogue runs on the sums.
+// Columns are grouped 16 at a time: 32 groups of c, 8 per head of q^nope,
+// then 4 per rotary segment holding the dimension pairs (8 u + i, 32 + 8 u +
+// i), i < 8.
+constexpr int PR_TOK = 32;    // tokens per workgroup
+constexpr int PR_COLS = 16;   // output columns per workgroup
+constexpr int PR_WAVES = 8;   // wavefronts per workgroup
+constexpr int PR_KC = 256;    // k per chunk
+constexpr int PR_MAX_T = 64;  // token counts up to this take this path
+constexpr int PR_XSLOTS = PR_TOK * PR_KC / 8;  // 16-byte slots of one wave's hidden-state block (1024)
+
+__device__ __forceinline__ int64_t rows_wrow(int cg, int j, int H) {
+  if (cg < D_C / PR_COLS) return PR_COLS * cg + j;                        // c
+  cg -= D_C / PR_COLS;
+  if (cg < 8 * H) return D_ROW + 192 * (cg >> 3) + PR_COLS * (cg & 7) + j;  // q^nope
+  cg -= 8 * H;
+  const int s = cg >> 2, u = cg & 3;                                      // rotary segment, quarter
+  const int dd = j < 8 ? 8 * u + j : 32 + 8 * u + (j - 8);
+  return s == 0 ? D_C + dd : D_ROW + 192 * (s - 1) + 128 + dd;
+}
+
+__global__ __launch_bounds__(64 * PR_WAVES) void proj_rows_kernel(ProjArgs pa, int q_f32) {
+  // per wave: token row r of the block holds its 32 chunks with chunk c at
+  // slot 32 r + (c ^ (r & 15)), so the 16 rows of an operand fragment hit 16
+  // different bank groups; after the products the region holds the wave's
+  // partial tile (fp32 [32][17])
+  __shared__ __align__(16) bf16_t xs[PR_WAVES][PR_XSLOTS * 8];
+  __shared__ float fin[PR_TOK][PR_COLS + 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, kg = lane >> 4;
+  const int cg = blockIdx.x;
+  const int64_t tok0 = (int64_t)blockIdx.y * PR_TOK;
+  const int H = pa.H;
+
+  const bf16_t* wr = pa.w + rows_wrow(cg, col, H) * pa.d + 8 * kg;
+  // direct-load sources: instruction i, lane -> row 2 i + lane / 32, chunk (lane % 32) ^ (row & 15)
+  const int xc = lane & 31, xrow0 = lane >> 5;
+  const uint32_t xbase = lds_off(&xs[w][0]);
+  f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  for (int ch = w; ch < pa.d / PR_KC; ch += PR_WAVES) {
+    const int k0 = ch * PR_KC;
+#pragma unroll
+    for (int i = 0; i < PR_XSLOTS / 64; ++i) {
+      const int r = 2 * i + xrow0;
+      const int64_t t = min(tok0 + r, pa.T - 1);  // rows past T load a valid row; never stored
+      dma16(pa.x + t * pa.x_stride + k0 + 8 * (xc ^ (r & 15)), xbase + 1024u * (uint32_t)i);
+    }
+    uint4 b[PR_KC / 32];
+#pragma unroll
+    for (int st = 0; st < PR_KC / 32; ++st) b[st] = load8_bf16(wr + k0 + 32 * st);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int st = 0; st < PR_KC / 32; ++st)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int r = 16 * mt + col;
+        const uint4 a = *reinterpret_cast<const uint4*>(&xs[w][8 * (32 * r + ((4 * st + kg) ^ (r & 15)))]);
+        acc[mt] = mfma16x16x32(a, b[st], acc[mt]);
+      }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the block is consumed before it is reloaded
+  }
+  // acc[mt][r] = partial of out[token 16 mt + 4 kg + r][column col]
+  float* red = reinterpret_cast<float*>(&xs[w][0]);
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[(16 * mt + 4 * kg + r) * (PR_COLS + 1) + col] = acc[mt][r];
+  __syncthreads();
+  {  // thread -> (token, column): the 8 partials in wave order
+    const int tl = tid >> 4, c = tid & 15;
+    float v = 0.f;
+#pragma unroll
+    for (int k = 0; k < PR_WAVES; ++k) v += reinterpret_cast<const float*>(&xs[k][0])[tl * (PR_COLS + 1) + c];
+    fin[tl][c] = v;
+  }
+  __syncthreads();
+  const int tl = tid >> 4, c = tid & 15;
+  const int64_t t = tok0 + tl;
+  if (t >= pa.T) return;
+  int g = cg;
+  if (g < D_C / PR_COLS) {
+    const int64_t dr = pa.dst_row[t];
+    if (dr >= 0) pa.rows[dr * pa.row_stride + PR_COLS * g + c] = (bf16_t)f2bf(fin[tl][c]);
+    return;
+  }
+  g -= D_C / PR_COLS;
+  if (g < 8 * H) {
+    pa.qn[(t * H + (g >> 3)) * D_V + PR_COLS * (g & 7) + c] = (bf16_t)f2bf(fin[tl][c]);
+    return;
+  }
+  g -= 8 * H;
+  if (c >= 8) return;  // one thread per rotary pair
+  const int s = g >> 2, i = 8 * (g & 3) + c;  // pair (i, i + 32)
+  const double theta = exp2(-(double)i * (1.0 / 32.0) * pa.log2_base);
+  float cs, sn;
+  rope_cs(pa.pos[t], theta, cs, sn);
+  const float x1 = fin[tl][c], x2 = fin[tl][c + 8];
+  const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
+  if (s == 0) {
+    const int64_t dr = pa.dst_row[t];
+    if (dr < 0) return;
+    bf16_t* dst = pa.rows + dr * pa.row_stride + D_C;
+    dst[i] = (bf16_t)f2bf(y1);
+    dst[32 + i] = (bf16_t)f2bf(y2);
+  } else if (q_f32) {
+    float* dst = reinterpret_cast<float*>(pa.q) + t * pa.q_stride + (int64_t)(s - 1) * D_ROW + D_C;
+    dst[i] = y1;
+    dst[32 + i] = y2;
+  } else {
+    bf16_t* dst = reinterpret_cast<bf16_t*>(pa.q) + t * pa.q_stride + (int64_t)(s - 1) * D_ROW + D_C;
+    dst[i] = (bf16_t)f2bf(y1);
+    dst[32 + i] = (bf16_t)f2bf(y2);
+  }
+}
+
+// The W_UK product for few tokens: workgroup (head h, 64 outputs), wave ->
+// 16 outputs; each lane loads its 4 W_UK chunks and 8 q^nope chunks at once
+// and the 16x16 tiles are written straight from the accumulators.
+constexpr int AR_J = 64;  // outputs per workgroup
+
+__global__ __launch_bounds__(256) void absorb_rows_kernel(const bf16_t* __restrict__ qn, int64_t T, int H,
+                                                          const bf16_t* __restrict__ wuk, void* q,
+                                                          int64_t q_stride, int q_f32) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 15, kg = lane >> 4;
+  const int h = blockIdx.x / (D_C / AR_J), jb = blockIdx.x % (D_C / AR_J);
+  const int j = AR_J * jb + 16 * w + col;
+  const int64_t tok0 = (int64_t)blockIdx.y * PR_TOK;
+  uint4 b[4], a[2][4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) b[st] = load8_bf16(wuk + ((int64_t)h * D_C + j) * D_V + 32 * st + 8 * kg);
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int64_t t = min(tok0 + 16 * mt + col, T - 1);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) a[mt][st] = load8_bf16(qn + (t * H + h) * D_V + 32 * st + 8 * kg);
+  }
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) acc = mfma16x16x32(a[mt][st], b[st], acc);
+    // acc[r] = q_abs[token 16 mt + 4 kg + r][output j]
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t t = tok0 + 16 * mt + 4 * kg + r;
+      if (t >= T) continue;
+      const int64_t o = t * q_stride + (int64_t)h * D_ROW + j;
+      if (q_f32) reinterpret_cast<float*>(q)[o] = acc[r];
+      else reinterpret_cast<bf16_t*>(q)[o] = (bf16_t)f2bf(acc[r]);
+    }
+  }
+}
+
 hipError_t launch_project(const void* x, int64_t x_stride, int64_t T, int d, const int32_t* pos,
                           double rope_base, const void* w_proj, const void* w_uk, int H, void* rows,
                           int64_t row_stride, const int64_t* dst_row, void* q, int q_dtype,
@@ -267,6 +429,14 @@ hipError_t launch_project(const void* x, int64_t x_stride, int64_t T, int d, con
   const unsigned tiles = (unsigned)((T + PJ_BM - 1) / PJ_BM);
   const dim3 g1(tiles, (unsigned)(4 + H + (H + 2) / 2));
   const dim3 g2(tiles, D_C / PJ_BN, (unsigned)H);
+  if (T <= PR_MAX_T && d % (32 * PR_WAVES) == 0) {
+    const unsigned chunks = (unsigned)((T + PR_TOK - 1) / PR_TOK);
+    hipLaunchKernelGGL(proj_rows_kernel, dim3((unsigned)(D_C / PR_COLS + 12 * H + 4), chunks),
+                       dim3(64 * PR_WAVES), 0, stream, pa, (int)(q_dtype == LCA_F32));
+    hipLaunchKernelGGL(absorb_rows_kernel, dim3((unsigned)(H * (D_C / AR_J)), chunks), dim3(256), 0, stream,
+                       (const bf16_t*)qn, T, H, (const bf16_t*)w_uk, q, q_stride, (int)(q_dtype == LCA_F32));
+    return hipGetLastError();
+  }
   if (q_dtype == LCA_BF16) {
     hipLaunchKernelGGL(proj_kernel<bf16_t>, g1, dim3(256), 0, stream, pa);
     hipLaunchKernelGGL(absorb_kernel<bf16_t>, g2, dim3(256), 0, stream, (const bf16_t*)qn, T, H,

@@ -39,7 +39,9 @@ def _project_gpu(x, pos, w, wuk, dst, n_rows, q_dtype):
 
 
 @pytest.mark.parametrize("T,d,H,q_dtype", [(300, 256, 16, torch.bfloat16),   # 3 token tiles, ragged tail
-                                           (37, 2048, 16, torch.float32),    # a decode batch
+                                           (37, 2048, 16, torch.float32),    # a decode batch (few-token kernel)
+                                           (64, 512, 16, torch.bfloat16),    # few-token kernel, two token chunks
+                                           (5, 256, 3, torch.float32),       # few-token kernel, odd H
                                            (129, 96, 3, torch.float32),      # odd H: half-used rotary block
                                            (1, 32, 1, torch.bfloat16)])      # one token, one k slice
 def test_project_matches_oracle(T, d, H, q_dtype):
