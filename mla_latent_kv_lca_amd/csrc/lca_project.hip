@@ -96,20 +96,23 @@ __device__ __forceinline__ void pj_mainloop(bf16_t* ring, const bf16_t* const (&
     if (s + PJ_NBUF - 1 < nk) issue(s + PJ_NBUF - 1);
     const bf16_t* A = ring + (s % PJ_NBUF) * PJ_SLICE;
     const bf16_t* B = A + PJ_SLOTS * 8;
+    uint4 a[2][2], b[2][2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      uint4 a[2], b[2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
-        a[mt] = *reinterpret_cast<const uint4*>(A + 8 * 4 * (64 * wm + 32 * mt) + fo[kk]);
+        a[kk][mt] = *reinterpret_cast<const uint4*>(A + 8 * 4 * (64 * wm + 32 * mt) + fo[kk]);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
-        b[nt] = *reinterpret_cast<const uint4*>(B + 8 * 4 * (64 * wn + 32 * nt) + fo[kk]);
+        b[kk][nt] = *reinterpret_cast<const uint4*>(B + 8 * 4 * (64 * wn + 32 * nt) + fo[kk]);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // all 8 reads in flight before the first product
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32x32x16(a[mt], b[nt], acc[mt][nt]);
-    }
+        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32x32x16(a[kk][mt], b[kk][nt], acc[mt][nt]);
   }
 }
 
@@ -140,15 +143,19 @@ __device__ __forceinline__ int64_t proj_wrow(int nb, int j, int H) {
   return s == 0 ? D_C + dd : D_ROW + 192 * (s - 1) + 128 + dd;
 }
 
-// cos and sin of p theta_d, theta_d = 2^(-d log2(base) / 32). The angle is
-// formed and reduced to [-pi, pi] in double (positions reach millions of
-// radians), then evaluated in float.
-__device__ __forceinline__ void rope_cs(int32_t p, double theta, float& c, float& s) {
-  const double a = (double)p * theta;
-  const double k = rint(a * 0.15915494309189535);        // 1 / (2 pi)
-  double r = fma(-k, 6.283185307179586, a);              // 2 pi, high part
-  r = fma(-k, 2.4492935982947064e-16, r);                // 2 pi, low part
-  sincosf((float)r, &s, &c);
+// Rotation frequency of pair i in turns per position: base^(-i/32) / (2 pi).
+__device__ __forceinline__ double rope_turns(int i, double log2_base) {
+  return exp2(-(double)i * (1.0 / 32.0) * log2_base) * 0.15915494309189535;
+}
+// cos and sin of the angle p theta_i. The angle in turns, p * turns, is formed
+// and reduced to [-1/2, 1/2] in double (positions reach millions of
+// radians), then the hardware sine and cosine, whose inputs are in turns,
+// evaluate it.
+__device__ __forceinline__ void rope_cs(int32_t p, double turns, float& c, float& s) {
+  const double a = (double)p * turns;
+  const float r = (float)(a - rint(a));
+  s = __builtin_amdgcn_sinf(r);
+  c = __builtin_amdgcn_cosf(r);
 }
 
 template <typename TQ>
@@ -196,7 +203,7 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(ProjArgs pa) {
   }
   const int s = 2 * (nb - 4 - H) + wn;  // this wave's rotary segment: 0 = k^R, 1 + h = q^rope of head h
   if (s > H) return;
-  const double theta = exp2(-(double)r32 * (1.0 / 32.0) * pa.log2_base);
+  const double turns = rope_turns(r32, pa.log2_base);
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -204,7 +211,7 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(ProjArgs pa) {
       const int64_t t = tok0 + 64 * wm + 32 * mt + 8 * (i >> 2) + 4 * hk + (i & 3);
       if (t >= pa.T) continue;
       float cs, sn;
-      rope_cs(pa.pos[t], theta, cs, sn);
+      rope_cs(pa.pos[t], turns, cs, sn);
       const float x1 = acc[mt][0][i], x2 = acc[mt][1][i];
       const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
       if (s == 0) {
@@ -218,6 +225,222 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(ProjArgs pa) {
         dst[r32] = from_f32<TQ>(y1);
         dst[32 + r32] = from_f32<TQ>(y2);
       }
+    }
+}
+
+// ---- many tokens: 256 x 256 output tiles. Eight wavefronts (two per SIMD,
+// so one wave's waits overlap the other's products) of 128 tokens x 64
+// columns: eight 32x32x16 chains each, accumulators in AGPRs. Both operands
+// stream HBM -> LDS by direct loads in 32-deep k slices through a 4-slice
+// ring (128 KB), three slices in flight; per slice a wave issues its 12
+// fragment reads for both k steps before its 16 products. Output columns in
+// 256-wide blocks: 2 of c, one per two heads of q^nope, then the rotary
+// segments four per block, one per wave column (so again both halves of a
+// pair meet in one lane).
+constexpr int PB_BM = 256;                       // tokens per tile
+constexpr int PB_BN = 256;                       // output columns per tile
+constexpr int PB_WAVES = 8;
+constexpr int PB_SLOTS = PB_BM * PJ_BK / 8;      // 16-byte slots per operand slice (1024)
+constexpr int PB_SLICE = 2 * PB_SLOTS * 8;       // bf16 per slice, both operands (32 KB)
+constexpr int PB_DMA = PB_SLOTS / 64 / PB_WAVES; // direct loads per operand, wave and slice (2)
+
+// acc[mt][nt][i] = sum_k A[row 128 wm + 32 mt + 8 (i / 4) + 4 (lane / 32) + i % 4][k]
+//                      * B[row 64 wn + 32 nt + lane % 32][k],   w = 4 wm + wn.
+__device__ __forceinline__ void pb_mainloop(bf16_t* ring, const bf16_t* const (&ap)[PB_DMA],
+                                            const bf16_t* const (&bp)[PB_DMA], int K, int w, int lane,
+                                            f32x16_t (&acc)[4][2]) {
+  const int wm = w >> 2, wn = w & 3;
+  const int nk = K / PJ_BK;
+  const uint32_t ring0 = lds_off(ring);
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.f;
+
+  auto issue = [&](int s) {
+    const uint32_t buf = ring0 + (uint32_t)((s % PJ_NBUF) * PB_SLICE * 2);
+    const int k0 = s * PJ_BK;
+#pragma unroll
+    for (int i = 0; i < PB_DMA; ++i) dma16(ap[i] + k0, buf + 1024u * (uint32_t)(w + PB_WAVES * i));
+#pragma unroll
+    for (int i = 0; i < PB_DMA; ++i)
+      dma16(bp[i] + k0, buf + PB_SLOTS * 16u + 1024u * (uint32_t)(w + PB_WAVES * i));
+  };
+  for (int s = 0; s < PJ_NBUF - 1 && s < nk; ++s) issue(s);
+
+  const int r32 = lane & 31, sw = (lane >> 2) & 3, hk = lane >> 5;
+  int fo[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) fo[kk] = 8 * (4 * r32 + ((2 * kk + hk) ^ sw));
+
+  for (int s = 0; s < nk; ++s) {
+    pj_wait(min(nk - 1 - s, PJ_NBUF - 2));  // 4 direct loads per slice and wave, as in the 128 tiles
+    barrier();  // slice s landed for every wave; slice s - 1 is consumed by every wave
+    if (s + PJ_NBUF - 1 < nk) issue(s + PJ_NBUF - 1);
+    const bf16_t* A = ring + (s % PJ_NBUF) * PB_SLICE + 8 * 4 * 128 * wm;
+    const bf16_t* B = ring + (s % PJ_NBUF) * PB_SLICE + PB_SLOTS * 8 + 8 * 4 * 64 * wn;
+    uint4 a[2][4], b[2][2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) a[kk][mt] = *reinterpret_cast<const uint4*>(A + 8 * 4 * 32 * mt + fo[kk]);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) b[kk][nt] = *reinterpret_cast<const uint4*>(B + 8 * 4 * 32 * nt + fo[kk]);
+    }
+    // all 12 reads in flight before the first product: the compiler would
+    // otherwise interleave them one by one and wait on each
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32x32x16(a[kk][mt], b[kk][nt], acc[mt][nt]);
+  }
+}
+
+// Weight row of local column j (0..255) of a 256-wide column block.
+__device__ __forceinline__ int64_t big_wrow(int nb, int j, int H) {
+  if (nb < 2) return 256 * nb + j;                                  // c
+  const int nh = (H + 1) / 2;
+  if (nb < 2 + nh) {                                                // q^nope of heads 2 (nb - 2) + j / 128
+    const int h = min(2 * (nb - 2) + (j >> 7), H - 1);             // the unused half of an odd H: a valid row
+    return D_ROW + 192 * h + (j & 127);
+  }
+  const int s = min(4 * (nb - 2 - nh) + (j >> 6), H);              // rotary segment
+  const int dd = j & 63;
+  return s == 0 ? D_C + dd : D_ROW + 192 * (s - 1) + 128 + dd;
+}
+
+template <typename TQ>
+__global__ __launch_bounds__(64 * PB_WAVES, 2) void proj_big_kernel(ProjArgs pa) {
+  __shared__ __align__(16) bf16_t ring[PJ_NBUF * PB_SLICE];
+  // the tile's destination rows and positions: loaded before the main loop,
+  // shared through LDS after it (in the epilogue each would otherwise be a
+  // global load ordered after the previous token's stores)
+  __shared__ int64_t tile_dst[PB_BM];
+  __shared__ int32_t tile_pos[PB_BM];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nb = blockIdx.y;
+  const int64_t tok0 = (int64_t)blockIdx.x * PB_BM;
+  const int H = pa.H;
+  int64_t my_dst = 0;
+  int32_t my_pos = 0;
+  if (tid < PB_BM) {
+    const int64_t t = min(tok0 + tid, pa.T - 1);
+    my_dst = pa.dst_row[t];
+    my_pos = pa.pos[t];
+  }
+
+  const bf16_t* ap[PB_DMA];
+  const bf16_t* bp[PB_DMA];
+  const int ch = pj_dma_chunk(lane);
+#pragma unroll
+  for (int i = 0; i < PB_DMA; ++i) {
+    const int r = 16 * (w + PB_WAVES * i) + (lane >> 2);  // slot 64 (w + 8 i) + lane
+    const int64_t t = min(tok0 + r, pa.T - 1);            // rows past T load a valid row; never stored
+    ap[i] = pa.x + t * pa.x_stride + 8 * ch;
+    bp[i] = pa.w + big_wrow(nb, r, H) * pa.d + 8 * ch;
+  }
+  f32x16_t acc[4][2];
+  pb_mainloop(ring, ap, bp, pa.d, w, lane, acc);
+  if (tid < PB_BM) {
+    tile_dst[tid] = my_dst;
+    tile_pos[tid] = my_pos;
+  }
+  __syncthreads();
+
+  const int wm = w >> 2, wn = w & 3, r32 = lane & 31, hk = lane >> 5;
+  const int nh = (H + 1) / 2;
+  if (nb < 2 + nh) {  // c -> cache rows, or q^nope -> workspace (bf16)
+    const int h = 2 * (nb - 2) + (wn >> 1);
+    if (nb >= 2 && h >= H) return;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int tl = 128 * wm + 32 * mt + 8 * (i >> 2) + 4 * hk + (i & 3);
+        const int64_t t = tok0 + tl;
+        if (t >= pa.T) continue;
+        bf16_t* dst;
+        if (nb < 2) {
+          const int64_t dr = tile_dst[tl];
+          if (dr < 0) continue;
+          dst = pa.rows + dr * pa.row_stride + 256 * nb + 64 * wn;
+        } else {
+          dst = pa.qn + (t * H + h) * D_V + 64 * (wn & 1);
+        }
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) dst[32 * nt + r32] = (bf16_t)f2bf(acc[mt][nt][i]);
+      }
+    return;
+  }
+  const int s = 4 * (nb - 2 - nh) + wn;  // this wave's rotary segment: 0 = k^R, 1 + h = q^rope of head h
+  if (s > H) return;
+  const double turns = rope_turns(r32, pa.log2_base);
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int tl = 128 * wm + 32 * mt + 8 * (i >> 2) + 4 * hk + (i & 3);
+      const int64_t t = tok0 + tl;
+      if (t >= pa.T) continue;
+      float cs, sn;
+      rope_cs(tile_pos[tl], turns, cs, sn);
+      const float x1 = acc[mt][0][i], x2 = acc[mt][1][i];
+      const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
+      if (s == 0) {
+        const int64_t dr = tile_dst[tl];
+        if (dr < 0) continue;
+        bf16_t* dst = pa.rows + dr * pa.row_stride + D_C;
+        dst[r32] = (bf16_t)f2bf(y1);
+        dst[32 + r32] = (bf16_t)f2bf(y2);
+      } else {
+        TQ* dst = reinterpret_cast<TQ*>(pa.q) + t * pa.q_stride + (int64_t)(s - 1) * D_ROW + D_C;
+        dst[r32] = from_f32<TQ>(y1);
+        dst[32 + r32] = from_f32<TQ>(y2);
+      }
+    }
+}
+
+// The W_UK product on 256 x 256 tiles (the main loop above with K = 128):
+// q_abs[t, h, 256 jb + j] = sum_k qn[t, h, k] W_UK[h][256 jb + j][k].
+template <typename TQ>
+__global__ __launch_bounds__(64 * PB_WAVES, 2) void absorb_big_kernel(const bf16_t* __restrict__ qn, int64_t T,
+                                                                      int H, const bf16_t* __restrict__ wuk,
+                                                                      void* q, int64_t q_stride) {
+  __shared__ __align__(16) bf16_t ring[PJ_NBUF * PB_SLICE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int jb = blockIdx.y, h = blockIdx.z;
+  const int64_t tok0 = (int64_t)blockIdx.x * PB_BM;
+
+  const bf16_t* ap[PB_DMA];
+  const bf16_t* bp[PB_DMA];
+  const int ch = pj_dma_chunk(lane);
+#pragma unroll
+  for (int i = 0; i < PB_DMA; ++i) {
+    const int r = 16 * (w + PB_WAVES * i) + (lane >> 2);
+    const int64_t t = min(tok0 + r, T - 1);
+    ap[i] = qn + (t * H + h) * D_V + 8 * ch;
+    bp[i] = wuk + ((int64_t)h * D_C + PB_BN * jb + r) * D_V + 8 * ch;
+  }
+  f32x16_t acc[4][2];
+  pb_mainloop(ring, ap, bp, D_V, w, lane, acc);
+
+  const int wm = w >> 2, wn = w & 3, r32 = lane & 31, hk = lane >> 5;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int64_t t = tok0 + 128 * wm + 32 * mt + 8 * (i >> 2) + 4 * hk + (i & 3);
+      if (t >= T) continue;
+      TQ* dst = reinterpret_cast<TQ*>(q) + t * q_stride + (int64_t)h * D_ROW + PB_BN * jb + 64 * wn + r32;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) dst[32 * nt] = from_f32<TQ>(acc[mt][nt][i]);
     }
 }
 
@@ -359,9 +582,9 @@ __global__ __launch_bounds__(64 * PR_WAVES) void proj_rows_kernel(ProjArgs pa, i
   g -= 8 * H;
   if (c >= 8) return;  // one thread per rotary pair
   const int s = g >> 2, i = 8 * (g & 3) + c;  // pair (i, i + 32)
-  const double theta = exp2(-(double)i * (1.0 / 32.0) * pa.log2_base);
+  const double turns = rope_turns(i, pa.log2_base);
   float cs, sn;
-  rope_cs(pa.pos[t], theta, cs, sn);
+  rope_cs(pa.pos[t], turns, cs, sn);
   const float x1 = fin[tl][c], x2 = fin[tl][c + 8];
   const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
   if (s == 0) {
@@ -437,14 +660,31 @@ hipError_t launch_project(const void* x, int64_t x_stride, int64_t T, int d, con
                        (const bf16_t*)qn, T, H, (const bf16_t*)w_uk, q, q_stride, (int)(q_dtype == LCA_F32));
     return hipGetLastError();
   }
+  const dim3 gb((unsigned)((T + PB_BM - 1) / PB_BM), (unsigned)(2 + (H + 1) / 2 + (H + 4) / 4));
+  const dim3 gab((unsigned)((T + PB_BM - 1) / PB_BM), D_C / PB_BN, (unsigned)H);
+  // 256-wide tiles once they fill most of the chip; below that the 128-wide
+  // tiles keep more CUs busy
+  const bool big = (int64_t)gb.x * gb.y >= 224;
   if (q_dtype == LCA_BF16) {
-    hipLaunchKernelGGL(proj_kernel<bf16_t>, g1, dim3(256), 0, stream, pa);
-    hipLaunchKernelGGL(absorb_kernel<bf16_t>, g2, dim3(256), 0, stream, (const bf16_t*)qn, T, H,
-                       (const bf16_t*)w_uk, q, q_stride);
+    if (big) {
+      hipLaunchKernelGGL(proj_big_kernel<bf16_t>, gb, dim3(64 * PB_WAVES), 0, stream, pa);
+      hipLaunchKernelGGL(absorb_big_kernel<bf16_t>, gab, dim3(64 * PB_WAVES), 0, stream, (const bf16_t*)qn, T, H,
+                         (const bf16_t*)w_uk, q, q_stride);
+    } else {
+      hipLaunchKernelGGL(proj_kernel<bf16_t>, g1, dim3(256), 0, stream, pa);
+      hipLaunchKernelGGL(absorb_kernel<bf16_t>, g2, dim3(256), 0, stream, (const bf16_t*)qn, T, H,
+                         (const bf16_t*)w_uk, q, q_stride);
+    }
   } else {
-    hipLaunchKernelGGL(proj_kernel<float>, g1, dim3(256), 0, stream, pa);
-    hipLaunchKernelGGL(absorb_kernel<float>, g2, dim3(256), 0, stream, (const bf16_t*)qn, T, H,
-                       (const bf16_t*)w_uk, q, q_stride);
+    if (big) {
+      hipLaunchKernelGGL(proj_big_kernel<float>, gb, dim3(64 * PB_WAVES), 0, stream, pa);
+      hipLaunchKernelGGL(absorb_big_kernel<float>, gab, dim3(64 * PB_WAVES), 0, stream, (const bf16_t*)qn, T, H,
+                         (const bf16_t*)w_uk, q, q_stride);
+    } else {
+      hipLaunchKernelGGL(proj_kernel<float>, g1, dim3(256), 0, stream, pa);
+      hipLaunchKernelGGL(absorb_kernel<float>, g2, dim3(256), 0, stream, (const bf16_t*)qn, T, H,
+                         (const bf16_t*)w_uk, q, q_stride);
+    }
   }
   return hipGetLastError();
 }
