@@ -123,14 +123,21 @@ __global__ __launch_bounds__(QP_THREADS) void qbar_part_kernel(
     part[((int64_t)b * QBAR_PARTS + p) * D_ROW + c] = s;
   }
 }
-__global__ __launch_bounds__(D_ROW) void qbar_final_kernel(const float* __restrict__ part, int rows,
-                                                           float* __restrict__ qbar) {
-  const int b = blockIdx.x, c = threadIdx.x;
-  const float* pp = part + (int64_t)b * QBAR_PARTS * D_ROW + c;
+// Column c of the summary query from the part sums (pp = part sums of the
+// sequence + c): added in part order, then scaled. The streaming condense
+// kernel forms its summary query with this same function, so both paths
+// hold bitwise equal values.
+__device__ __forceinline__ float qbar_from_parts(const float* pp, int rows) {
   float s = pp[0];
 #pragma unroll
   for (int k = 1; k < QBAR_PARTS; ++k) s += pp[k * D_ROW];
-  qbar[(int64_t)b * D_ROW + c] = s * (1.0f / (float)rows);
+  return s * (1.0f / (float)rows);
+}
+
+__global__ __launch_bounds__(D_ROW) void qbar_final_kernel(const float* __restrict__ part, int rows,
+                                                           float* __restrict__ qbar) {
+  const int b = blockIdx.x, c = threadIdx.x;
+  qbar[(int64_t)b * D_ROW + c] = qbar_from_parts(part + (int64_t)b * QBAR_PARTS * D_ROW + c, rows);
 }
 
 // ---------------------------------------------------------------- K1 -------
@@ -448,8 +455,8 @@ __device__ __forceinline__ void wait_tile(int stores_after, int tiles_after) {
 
 template <int LG, bool ALPHA>
 __global__ __launch_bounds__(256) void condense_ring_kernel(
-    const char* __restrict__ cache, int64_t seq_b, int64_t tok_b, const float* __restrict__ qbar,
-    int64_t group_begin, int64_t n_groups, float sm_scale,
+    const char* __restrict__ cache, int64_t seq_b, int64_t tok_b, const float* __restrict__ qpart,
+    int q_rows, int64_t group_begin, int64_t n_groups, float sm_scale,
     bf16_t* __restrict__ rc, bf16_t* __restrict__ rk, int64_t rc_seq, int64_t rc_tok,
     int64_t rk_seq, int64_t rk_tok, int32_t* __restrict__ anchor, int64_t anchor_seq,
     float* __restrict__ alpha, int64_t alpha_seq) {
@@ -464,10 +471,12 @@ __global__ __launch_bounds__(256) void condense_ring_kernel(
   const int64_t count = wg < n_groups ? (n_groups - 1 - wg) / nw + 1 : 0;
   if (count == 0) return;  // wave-uniform; the kernel has no barriers
 
-  const float* qb = qbar + (int64_t)b * D_ROW;
+  // the summary query straight from the part sums (no separate final pass)
+  const float* qp = qpart + (int64_t)b * QBAR_PARTS * D_ROW;
   float qc[8];
-  load8_f32(qb + 8 * lane, qc);
-  const float qr = qb[D_C + lane];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) qc[i] = qbar_from_parts(qp + 8 * lane + i, q_rows);
+  const float qr = qbar_from_parts(qp + D_C + lane, q_rows);
   // the compiler waits for these loads here, before any tile is in flight
   asm volatile("" ::"v"(qc[0]), "v"(qc[1]), "v"(qc[2]), "v"(qc[3]), "v"(qc[4]), "v"(qc[5]), "v"(qc[6]),
                "v"(qc[7]), "v"(qr));
@@ -590,7 +599,8 @@ static void dispatch_g(int lg, dim3 grid, hipStream_t st, const lca_latent_t& ca
 }
 
 static void launch_qbar_shared(int B, int g, const void* q, int q_dtype, int64_t q_seq_stride,
-                               int64_t q_tok_stride, int H, int64_t q_row0, float* qbar_ws, hipStream_t stream) {
+                               int64_t q_tok_stride, int H, int64_t q_row0, float* qbar_ws, hipStream_t stream,
+                               bool final_pass = true) {
   // workspace: [B][576] summary queries, then [B][QBAR_PARTS][576] part sums
   float* part = qbar_ws + (int64_t)B * D_ROW;
   dim3 gp((unsigned)QBAR_PARTS, (unsigned)B);
@@ -600,7 +610,8 @@ static void launch_qbar_shared(int B, int g, const void* q, int q_dtype, int64_t
   else
     hipLaunchKernelGGL(qbar_part_kernel<float>, gp, dim3(QP_THREADS), 0, stream, (const float*)q,
                        q_seq_stride, q_tok_stride, H, g, q_row0, part);
-  hipLaunchKernelGGL(qbar_final_kernel, dim3((unsigned)B), dim3(D_ROW), 0, stream, part, g * H, qbar_ws);
+  if (final_pass)
+    hipLaunchKernelGGL(qbar_final_kernel, dim3((unsigned)B), dim3(D_ROW), 0, stream, part, g * H, qbar_ws);
 }
 
 hipError_t launch_condense_paged(const lca_paged_t& cache, int B, int g, const int32_t* seq_group_begin,
@@ -647,19 +658,20 @@ hipError_t launch_condense(const lca_latent_t& cache, int B, int g, int64_t grou
     else
       hipLaunchKernelGGL(qbar_kernel<float>, g0, dim3(QBAR_THREADS), 0, stream, (const float*)q,
                          q_seq_stride, q_tok_stride, H, g, q_row0, q_row_step, (int)n_q, qbar_ws);
-  } else {
-    launch_qbar_shared(B, g, q, q_dtype, q_seq_stride, q_tok_stride, H, q_row0, qbar_ws, stream);
   }
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-
   int lg = 0;
   while ((1 << lg) < g) ++lg;
   const bool packed = cache.dtype == LCA_BF16 && reps.dtype == LCA_BF16 &&
                       static_cast<const char*>(cache.kr) == static_cast<const char*>(cache.c) + 2 * D_C &&
                       cache.kr_tok_stride == cache.c_tok_stride && cache.kr_seq_stride == cache.c_seq_stride &&
                       cache.c_tok_stride * 2 * 32 < ((int64_t)1 << 31);
-  if (mode == LCA_MODE_LCA && !per_group_q && packed && (lg == 3 || lg == 4) && n_groups > 0) {
+  const bool ring = mode == LCA_MODE_LCA && !per_group_q && packed && (lg == 3 || lg == 4) && n_groups > 0;
+  if (!per_group_q)  // part sums, then the final pass unless the streaming kernel adds them itself
+    launch_qbar_shared(B, g, q, q_dtype, q_seq_stride, q_tok_stride, H, q_row0, qbar_ws, stream, !ring);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+
+  if (ring) {
     // one resident workgroup per CU; the waves of a sequence share its groups
     const int64_t wpb = B >= 256 ? 1 : (256 + B - 1) / B;  // workgroups per sequence
     const int64_t nblk = std::min(wpb, (n_groups + 3) / 4);
@@ -667,7 +679,7 @@ hipError_t launch_condense(const lca_latent_t& cache, int B, int g, int64_t grou
 #define LCA_RING(LGV, AL)                                                                          \
   hipLaunchKernelGGL((condense_ring_kernel<LGV, AL>), gr, dim3(256), 0, stream,                    \
                      static_cast<const char*>(cache.c), cache.c_seq_stride * 2, cache.c_tok_stride * 2, \
-                     qbar_ws, group_begin, n_groups, sm_scale, (bf16_t*)reps.c,           \
+                     qbar_ws + (int64_t)B * D_ROW, g * H, group_begin, n_groups, sm_scale, (bf16_t*)reps.c, \
                      (bf16_t*)reps.kr, reps.c_seq_stride, reps.c_tok_stride, reps.kr_seq_stride,     \
                      reps.kr_tok_stride, anchor, anchor_seq, alpha, alpha_seq)
     if (lg == 3) { if (alpha) LCA_RING(3, true); else LCA_RING(3, false); }
