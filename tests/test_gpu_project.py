@@ -183,3 +183,26 @@ def test_project_benchmark_sizes_sampled(T):
     _within(rows[sample], ref_rows, 2.0 ** -8, 1e-3, "cache rows")
     _within(q[sample][..., 512:], ref_q[..., 512:], 2.0 ** -8, 1e-3, "rotated query part")
     _absorbed_within(q[sample][..., :512], ref_q[..., :512], x[sample], w, wuk, "absorbed query part")
+
+
+def test_project_strided_inputs_and_outputs():
+    """Hidden states with a token stride wider than d_model, absorbed queries
+    written into every other slot of a history buffer, cache rows into a
+    strided pool: the same values as the dense call."""
+    T, d, H = 300, 128, 16
+    x = li.hidden_states(74, T, d)
+    w = li.w_proj(74, H, d)
+    wuk = li.w_uk(74, H)
+    pos = np.arange(T, dtype=np.int32) * 3
+    xw = torch.zeros((T, d + 40), dtype=torch.bfloat16, device="cuda")
+    xw[:, :d] = dev(x)
+    pool = torch.full((T, 2, 640), SENTINEL, dtype=torch.bfloat16, device="cuda")  # row stride 1,280
+    qbuf = torch.full((T, 2, H, 576), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dst = torch.arange(T, dtype=torch.int64, device="cuda")
+    lca.lca_project(xw[:, :d], dev(pos, torch.int32), dev(w), dev(wuk), pool[:, 0, :576], dst, qbuf[:, 0])
+    rows_d, q_d = _project_gpu(x, pos, w, wuk, np.arange(T, dtype=np.int64), T, torch.bfloat16)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(pool[:, 0, :576]), rows_d)
+    np.testing.assert_array_equal(host(qbuf[:, 0]), q_d)
+    assert np.all(host(pool[:, 0, 576:]) == SENTINEL) and np.all(host(pool[:, 1]) == SENTINEL)
+    assert np.isnan(host(qbuf[:, 1])).all()
