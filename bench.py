@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-paged", action="store_true")
     ap.add_argument("--no-project", action="store_true")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the 128K (LCA vs plain MLA) and million-token decode legs")
     ap.add_argument("--prefill-len", type=int, default=131072)
     ap.add_argument("--no-graph", action="store_true",
                     help="launch every kernel from Python instead of replaying a captured HIP graph")
@@ -313,6 +315,11 @@ def main():
     if not args.no_project:
         project = project_leg()
 
+    long_ctx = million = None
+    if not args.no_long:
+        long_ctx = long_context_leg()
+        million = million_leg()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cache0, qhist[0], qsteps0, args.cpu_seconds)
@@ -343,9 +350,12 @@ def main():
         "condense": {"achieved_gbs": con_gbs, "frac": con_gbs / HBM_PEAK_GBS,
                      "bytes_per_launch": con_bytes, "avg_launch_us": t_con * 1e6},
         "decode_context_tokens_per_s": B * L / t_dec,
+        "generated_tokens_per_s": B * DECODE_STEPS / (ms_per_step / 1e3),
         "prefill": prefill,
         "paged": paged,
         "project": project,
+        "long_context": long_ctx,
+        "million": million,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec))
@@ -499,6 +509,123 @@ def paged_leg(B=32, page_rows=64, reps_=20):
             "decode_us": t_dec * 1e6, "decode_gbs": dec_bytes / t_dec / 1e9,
             "decode_context_tokens_per_s": sum(Ls) / t_dec,
             "condense_us": t_con * 1e6, "condense_gbs": con_bytes / t_con / 1e9}
+
+
+def _graph_time(fn, n):
+    """Mean duration of n calls of fn captured in one graph and replayed
+    between two HIP events on the launch stream (seconds)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    fn(0)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        for k in range(n):
+            fn(k)
+    gr.replay()
+    torch.cuda.synchronize()
+    a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    gr.replay()
+    b_.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b_) / n * 1e-3
+
+
+def long_context_leg(Bl=8, Ll=131072, NLl=4, reps_=16):
+    """B = 8 sequences x 131,072 tokens: one decode step (+W_UV) over the
+    condensed cache (LCA: 8,128 representatives + 1,024 raw rows) and over
+    all 131,072 rows (plain MLA, m = 0), on the same seeded caches, cycling
+    4 layer caches so that LCA's 84 MB per step stream HBM rather than the
+    last-level cache."""
+    import torch
+
+    import lca_inputs as li
+    import mla_latent_kv_lca_amd as lca
+    plan = lca.lca_plan(Ll, W, G)
+    m, rb, n_ent = plan["m"], plan["raw_begin"], plan["n_entries"]
+    caches = [li.latent_cache_torch(700 + i, Bl, Ll) for i in range(NLl)]
+    qh = li.queries_torch(710, (Bl, G, H, 576))
+    qd = li.queries_torch(711, (Bl, H, 576))
+    wuv = li.w_uv_torch(712, H)
+    reps = [torch.empty((Bl, m, 576), dtype=torch.bfloat16, device="cuda") for _ in range(NLl)]
+    anchor = torch.empty((Bl, m), dtype=torch.int32, device="cuda")
+    cws = torch.empty(lca.lca_condense_workspace_size(Bl, m, 0), dtype=torch.uint8, device="cuda")
+    for i in range(NLl):
+        lca.lca_condense(lca.packed_latent(caches[i]), Bl, G, 0, m, qh, 0, 0, 1.0,
+                         lca.packed_latent(reps[i]), anchor, None, cws)
+    o_lat = torch.empty((Bl, H, 512), dtype=torch.float32, device="cuda")
+    out = torch.empty((Bl, H, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((Bl, H), dtype=torch.float32, device="cuda")
+    ws_l = lca.decode_workspace(Bl, H, n_ent)
+    ws_m = lca.decode_workspace(Bl, H, Ll)
+    cl = [lca.packed_latent(c) for c in caches]
+    rl = [lca.packed_latent(r) for r in reps]
+
+    def lca_step(k):
+        lca.mla_latent_attn_decode_up(qd, rl[k % NLl], m, cl[k % NLl], rb, Ll, 1.0, o_lat, wuv, out, lse, ws_l)
+
+    def mla_step(k):
+        lca.mla_latent_attn_decode_up(qd, None, 0, cl[k % NLl], 0, Ll, 1.0, o_lat, wuv, out, lse, ws_m)
+
+    t_l = _graph_time(lca_step, reps_)
+    t_m = _graph_time(mla_step, max(4, reps_ // 4))
+    extra = Bl * H * 576 * 2 + Bl * H * 513 * 4 + H * 512 * 128 * 2 + Bl * H * 128 * 2
+    b_l = Bl * n_ent * ROW_BYTES + extra
+    b_m = Bl * Ll * ROW_BYTES + extra
+    return {"B": Bl, "seq_len": Ll, "entries_lca": n_ent, "entries_mla": Ll,
+            "lca_us": t_l * 1e6, "mla_us": t_m * 1e6, "speedup": t_m / t_l,
+            "lca_step_bytes": b_l, "mla_step_bytes": b_m,
+            "lca_gbs": b_l / t_l / 1e9, "mla_gbs": b_m / t_m / 1e9,
+            "lca_context_tokens_per_s": Bl * Ll / t_l, "mla_context_tokens_per_s": Bl * Ll / t_m}
+
+
+def million_leg(steps=256):
+    """One sequence of 1,048,576 tokens: condense its 65,472 groups, then 256
+    decode steps (+W_UV) that each append a row; every group that leaves the
+    window is condensed with the last 16 decode queries (16 incremental
+    condensations). The whole loop is one graph, timed with HIP events."""
+    import torch
+
+    import lca_inputs as li
+    import mla_latent_kv_lca_amd as lca
+    L0 = 1 << 20
+    cache = li.latent_cache_torch(800, 1, L0 + steps)
+    qall = li.queries_torch(801, (1, G + steps, H, 576))
+    wuv = li.w_uv_torch(802, H)
+    p0, p1 = lca.lca_plan(L0, W, G), lca.lca_plan(L0 + steps, W, G)
+    reps = torch.empty((1, p1["m"], 576), dtype=torch.bfloat16, device="cuda")
+    anchor = torch.empty((1, p1["m"]), dtype=torch.int32, device="cuda")
+    cws = torch.empty(lca.lca_condense_workspace_size(1, p1["m"], 0), dtype=torch.uint8, device="cuda")
+    dws = lca.decode_workspace(1, H, p1["n_entries"])
+    o_lat = torch.empty((1, H, 512), dtype=torch.float32, device="cuda")
+    out = torch.empty((1, H, 128), dtype=torch.bfloat16, device="cuda")
+    cl, rl = lca.packed_latent(cache), lca.packed_latent(reps)
+
+    def initial():
+        lca.lca_condense(cl, 1, G, 0, p0["m"], qall, 0, 0, 1.0, rl, anchor, None, cws)
+
+    n_inc = [0]
+
+    def loop():
+        L, m = L0, p0["m"]
+        n_inc[0] = 0
+        for st in range(steps):
+            lca.mla_latent_attn_decode_up(qall[:, G + st], rl, m, cl, m * G, L, 1.0, o_lat, wuv, out, None, dws)
+            L += 1
+            if L - W >= (m + 1) * G:  # the appended row completed group m
+                lca.lca_condense(cl, 1, G, m, 1, qall, st + 1, 0, 1.0, rl, anchor, None, cws)
+                m += 1
+                n_inc[0] += 1
+
+    t_init = _graph_time(lambda k: initial(), 1)
+    t_loop = _graph_time(lambda k: loop(), 1)
+    ent0 = p0["n_entries"]
+    return {"seq_len": L0, "steps": steps, "entries": ent0, "initial_condense_us": t_init * 1e6,
+            "initial_condense_gbs": p0["m"] * (G * ROW_BYTES + ROW_BYTES + 4) / t_init / 1e9,
+            "incremental_condenses": n_inc[0], "us_per_step": t_loop / steps * 1e6,
+            "decode_gbs": ent0 * ROW_BYTES / (t_loop / steps) / 1e9,
+            "context_tokens_per_s": (L0 + steps / 2) / (t_loop / steps)}
 
 
 D_MODEL = 2048  # hidden width of the projection leg: H heads x 128

@@ -185,3 +185,49 @@ def test_prefill_128k_sampled_rows():
         assert np.all(np.abs(got - ro) <= bound), \
             f"prefill chunk {chunk}: max excess {np.max(np.abs(got - ro) - bound):.3e}"
         assert_close(host(lse[s0 + rows]), rl, what=f"prefill lse chunk {chunk}")
+
+
+@pytest.mark.timeout(400)
+def test_decode_128k_lca_and_plain_mla_sampled():
+    """The 131,072-token shape of the long-context comparison (2 sequences):
+    condense all 8,128 groups, then one decode step over the condensed cache
+    and one over all rows (plain MLA, m = 0), in the benchmark's launch
+    configuration (decode plus W_UV up-projection)."""
+    B, L = 2, 131072
+    c, kr = li.latent_cache(7, B, L)
+    li.plant_needles(7, c, kr, 4, 14.0, 0, L)
+    qh = li.queries(7, B, G, H, rho=0.5)
+    qd = li.queries(7, B, 1, H, rho=0.5, stream=1)[:, 0]
+    wuv = li.w_uv(7, H)
+    p = O.plan(L, W, G)
+    m = p["m"]
+    cache = _packed(c, kr)
+    reps = torch.empty((B, m, 576), dtype=torch.bfloat16, device="cuda")
+    anchor = torch.empty((B, m), dtype=torch.int32, device="cuda")
+    lca.lca_condense(lca.packed_latent(cache), B, G, 0, m, dev(qh), 0, 0, 1.0, lca.packed_latent(reps), anchor)
+    o_l = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
+    o_m = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
+    y_l = torch.empty((B, H, 128), dtype=torch.float32, device="cuda")
+    y_m = torch.empty((B, H, 128), dtype=torch.float32, device="cuda")
+    lse_l = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    lse_m = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    w_t, q_t = dev(wuv), dev(qd)
+    lca.mla_latent_attn_decode_up(q_t, lca.packed_latent(reps), m, lca.packed_latent(cache), p["raw_begin"], L,
+                                  1.0, o_l, w_t, y_l, lse_l)
+    lca.mla_latent_attn_decode_up(q_t, None, 0, lca.packed_latent(cache), 0, L, 1.0, o_m, w_t, y_m, lse_m)
+    torch.cuda.synchronize()
+    r = host(reps)
+    ga = host(anchor).astype(np.int64)
+    for j in np.random.default_rng(8).integers(0, m, 24):
+        rc, _, ra, _, s = O.condense(c, kr, qh, G, int(j), 1, 0, 0, 1.0)
+        for b in range(B):
+            assert_close(r[b, j, :512], rc[b, 0], what=f"rep {b}/{j}")
+        anchors_agree(ga[:, j], ra[:, 0], O.top2_margin(s[:, 0]))
+    ro, rl = O.decode(qd, r[..., :512], r[..., 512:], m, c, kr, p["raw_begin"], L, 1.0)
+    assert_close(host(o_l), ro, what="LCA o_latent")
+    assert_close(host(lse_l), rl, what="LCA lse")
+    assert_close(host(y_l), O.up_proj(ro, wuv), what="LCA up-projected output")
+    mo, ml = O.decode(qd, None, None, 0, c, kr, 0, L, 1.0)
+    assert_close(host(o_m), mo, what="plain MLA o_latent")
+    assert_close(host(lse_m), ml, what="plain MLA lse")
+    assert_close(host(y_m), O.up_proj(mo, wuv), what="plain MLA up-projected output")
