@@ -546,6 +546,12 @@ __global__ __launch_bounds__(256) void merge_small_kernel(const float* __restric
 
 // Many splits (one long sequence): workgroup per (32 columns, head, sequence),
 // 32 split phases x 8 threads of 4 columns; phase partials added in order.
+// Many splits (one long sequence): workgroup (32 latent columns, head,
+// sequence); thread (phase p, 4 columns) takes splits p, p + 32, ...: all of
+// its loads (up to MERGE_UNROLL splits) are issued at once, the max and then
+// the weighted sums are formed from registers in split order, and the 32
+// phase partials are added in phase order.
+constexpr int MERGE_UNROLL = 8;  // splits per thread held in registers (S <= 256)
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml, int S,
                                                     int H, float* __restrict__ o,
@@ -554,26 +560,49 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
   const int HG = H / HB, hg = head / HB, hh = head % HB;
   const int t = threadIdx.x, ph = t >> 3, c4 = t & 7;
   const int64_t slot0 = ((int64_t)b * HG + hg) * S;  // slot(s) = (slot0 + s) * HB + hh
+  const int d = 32 * dchunk + 4 * c4;
   __shared__ float red[2][32];
   __shared__ float4 acc_sh[32][8];
 
+  float2 ml[MERGE_UNROLL];
+  float4 v[MERGE_UNROLL];
+#pragma unroll
+  for (int i = 0; i < MERGE_UNROLL; ++i) {
+    const int s = ph + 32 * i;
+    if (s < S) {
+      const int64_t slot = (slot0 + s) * HB + hh;
+      ml[i] = reinterpret_cast<const float2*>(part_ml)[slot];
+      v[i] = *reinterpret_cast<const float4*>(part_o + slot * D_C + d);
+    } else {
+      ml[i] = make_float2(-INFINITY, 0.f);
+      v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
   float mx = -INFINITY;
-  for (int s = ph; s < S; s += 32) mx = fmaxf(mx, part_ml[((slot0 + s) * HB + hh) * 2]);
+#pragma unroll
+  for (int i = 0; i < MERGE_UNROLL; ++i) mx = fmaxf(mx, ml[i].x);
+  for (int s = ph + 32 * MERGE_UNROLL; s < S; s += 32) mx = fmaxf(mx, part_ml[((slot0 + s) * HB + hh) * 2]);
   if (c4 == 0) red[0][ph] = mx;
   __syncthreads();
   float M = red[0][0];
   for (int p = 1; p < 32; ++p) M = fmaxf(M, red[0][p]);
   float ls = 0.f;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  const int d = 32 * dchunk + 4 * c4;
-  for (int s = ph; s < S; s += 32) {
+#pragma unroll
+  for (int i = 0; i < MERGE_UNROLL; ++i) {
+    const float wgt = ml[i].x == -INFINITY ? 0.f : exp2f(ml[i].x - M);
+    ls = fmaf(wgt, ml[i].y, ls);
+    a.x = fmaf(wgt, v[i].x, a.x); a.y = fmaf(wgt, v[i].y, a.y);
+    a.z = fmaf(wgt, v[i].z, a.z); a.w = fmaf(wgt, v[i].w, a.w);
+  }
+  for (int s = ph + 32 * MERGE_UNROLL; s < S; s += 32) {  // beyond 256 splits (not produced by the planner)
     const int64_t slot = (slot0 + s) * HB + hh;
     const float ms = part_ml[slot * 2];
     const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - M);
     ls = fmaf(wgt, part_ml[slot * 2 + 1], ls);
-    const float4 v = *reinterpret_cast<const float4*>(part_o + slot * D_C + d);
-    a.x = fmaf(wgt, v.x, a.x); a.y = fmaf(wgt, v.y, a.y);
-    a.z = fmaf(wgt, v.z, a.z); a.w = fmaf(wgt, v.w, a.w);
+    const float4 u = *reinterpret_cast<const float4*>(part_o + slot * D_C + d);
+    a.x = fmaf(wgt, u.x, a.x); a.y = fmaf(wgt, u.y, a.y);
+    a.z = fmaf(wgt, u.z, a.z); a.w = fmaf(wgt, u.w, a.w);
   }
   if (c4 == 0) red[1][ph] = ls;
   acc_sh[ph][c4] = a;
@@ -583,8 +612,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
     float4 r = acc_sh[0][c4];
     for (int p = 1; p < 32; ++p) {
       Lt += red[1][p];
-      const float4 v = acc_sh[p][c4];
-      r.x += v.x; r.y += v.y; r.z += v.z; r.w += v.w;
+      const float4 u = acc_sh[p][c4];
+      r.x += u.x; r.y += u.y; r.z += u.z; r.w += u.w;
     }
     const float inv = 1.0f / Lt;
     *reinterpret_cast<float4*>(o + ((int64_t)b * H + head) * D_C + d) =
