@@ -235,7 +235,9 @@ int mla_latent_attn_decode_paged(const void* q, int32_t q_dtype, int64_t q_seq_s
 
 /* mla_latent_attn_decode followed by mla_up_proj of its output (the MLA
  * page's projection back to each head's value space, 三.1), with the split
- * merge and the projection fused into one kernel when B <= 64. Arguments as
+ * merge and the projection fused into one kernel when B <= 64 and the
+ * entries are split 2 to 32 ways (otherwise they run as two kernels, or the
+ * projection alone when there is one split). Arguments as
  * in the two calls: o_latent and lse receive the decode results,
  * out[b, h, :] = o_latent[b, h, :] @ W_UV[h] (w_uv [H, 512, 128] contiguous,
  * out [B, H, 128] contiguous, dtypes w_dtype / out_dtype). The results are
