@@ -64,8 +64,8 @@ def parse():
 TRAFFIC_SOURCES = ("mla_latent_kv_lca_amd/csrc/lca_decode.hip", "mla_latent_kv_lca_amd/csrc/lca_stream.h",
                    "mla_latent_kv_lca_amd/csrc/lca_tile.h", "mla_latent_kv_lca_amd/csrc/lca_device.h",
                    "mla_latent_kv_lca_amd/csrc/lca_up_rows.h")
-TRAFFIC = {"sha256": "720ea616cec084e18277367f479c47d7a4c5ea20480a5372f6e9681f8abda028",
-           "fetch_bytes": 126_791_335, "write_bytes": 9_617_408}
+TRAFFIC = {"sha256": "13d6f3b05ebb01c06ccce460dea1a583ce975430cf2375f6f473a1bf97135bb7",
+           "fetch_bytes": 126_793_315, "write_bytes": 9_617_408}
 
 
 def decode_sources_digest() -> str:
