@@ -14,19 +14,25 @@
 //
 // Two MFMA GEMMs of the same shape class, out[t][n] = sum_k A[t][k] B[n][k]
 // with both operands k-contiguous:
-//   1. x [T, d] against the projection weights [576 + 192 H, d]. Output
-//      columns are taken in 128-wide blocks: 4 blocks of c, H blocks of
-//      per-head q^nope, then the rotary segments (k^R, then q^rope of each
-//      head) two 64-wide segments per block. Since a weight row is the whole
-//      weight vector of one output column, any grouping of columns into
-//      blocks costs nothing, and it puts both halves of a rotary pair in
-//      the same lane of the same wave: the rotation happens in registers.
-//   2. q^nope [T, H, 128] (bf16, from the workspace) against W_UK[h]
+//   1. x [T, d] against the projection weights [576 + 192 H, d], with the
+//      rotation and the scatter of the cache rows in the epilogue. Since a
+//      weight row is the whole weight vector of one output column, any
+//      grouping of output columns into tiles costs nothing: the tiles put
+//      both halves of a rotary pair in the same lane, so the rotation
+//      happens in registers.
+//   2. q^nope [T, H, 128] (bf16, through the workspace) against W_UK[h]
 //      [512, 128], one head per grid z.
-// A workgroup of 4 wavefronts computes a 128 x 128 output tile; each wave a
-// 64 x 64 quarter with four 32x32x16 MFMA chains. Both operands stream
-// HBM -> LDS with direct loads in 32-deep k slices through a 4-slice ring
-// (three slices in flight while one is consumed).
+// Three tile shapes, by token count:
+//   - up to 64 tokens (decode): proj_rows_kernel / absorb_rows_kernel,
+//     16 output columns per workgroup over the whole model width, every
+//     load of a wave in flight at once (HBM-bound on the weights);
+//   - fewer than about 4,096 tokens: proj_kernel / absorb_kernel, 128 x 128
+//     tiles, 4 wavefronts of 64 x 64 (four 32x32x16 chains);
+//   - more: proj_big_kernel / absorb_big_kernel, 256 x 256 tiles, 8
+//     wavefronts of 128 x 64.
+// The two tiled shapes stream both operands HBM -> LDS by direct loads in
+// 32-deep k slices through a 4-slice ring (three slices in flight while one
+// is consumed).
 #include "lca_stream.h"
 #include "lca_internal.h"
 
@@ -230,7 +236,7 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(ProjArgs pa) {
 
 // ---- many tokens: 256 x 256 output tiles. Eight wavefronts (two per SIMD,
 // so one wave's waits overlap the other's products) of 128 tokens x 64
-// columns: eight 32x32x16 chains each, accumulators in AGPRs. Both operands
+// columns: eight 32x32x16 chains each (128 accumulator registers). Both operands
 // stream HBM -> LDS by direct loads in 32-deep k slices through a 4-slice
 // ring (128 KB), three slices in flight; per slice a wave issues its 12
 // fragment reads for both k steps before its 16 products. Output columns in
