@@ -224,6 +224,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(
       if (ks + 5 < 18) kf[ks + 5] = frag(ks + 5);
       sa = mfma32x32x16(kf[ks], qf[ks], sa);
       sb = mfma32x32x16(kf[ks + 1], qf[ks + 1], sb);
+      // keep each k-step's reads ahead of its products (left to itself the
+      // scheduler bunches the reads and waits on them)
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) sx[w][r][lane] = sa[r] + sb[r];
