@@ -201,8 +201,8 @@ def ablation_study(lengths, B=2, steps=4):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
-                                   "(multi-GPU sharding is described in DESIGN.md, not built)"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1 "
+                                   "(the library has no multi-GPU sharding)"}))
         sys.exit(2)
     if args.calib_copy:
         calib_copy()
