@@ -338,6 +338,43 @@ def test_decode_condensed_matches_oracle(dtype, L):
     assert_close(host(lse), rl, what="lse")
 
 
+@pytest.mark.parametrize("q_dtype,c_dtype,layout", [
+    (torch.float32, torch.bfloat16, "packed"),  # direct-load kernel, f32 queries
+    (torch.bfloat16, torch.float32, "packed"),  # register-staged kernel, f32 rows
+    (torch.bfloat16, torch.bfloat16, "split"),  # register-staged kernel, c_KV and k_R apart
+])
+def test_decode_other_dtypes_and_layouts(q_dtype, c_dtype, layout):
+    """Decode kernel instantiations not reached by the tests above, against the
+    oracle: 3 sequences, needles in the window, seeded bf16 representatives
+    given to both sides, several splits; f32 inputs hold bf16-representable values."""
+    B, L, g, w = 3, 2600, 16, 1024
+    c, kr = li.latent_cache(13, B, L)
+    li.plant_needles(13, c, kr, 2, 14.0, L - w, L)
+    qd = li.queries(13, B, 1, H, rho=0.5, stream=1)[:, 0]
+    p = O.plan(L, w, g)
+    m = p["m"]
+    rng = np.random.default_rng(13)
+    rep_c = li.bf16_round((0.3 * rng.standard_normal((B, m, 512))).astype(np.float32))
+    rep_k = li.bf16_round(rng.standard_normal((B, m, 64)).astype(np.float32))
+
+    def describe(xc, xk):
+        if layout == "packed":
+            t = packed(xc, xk, c_dtype)
+            return t, lca.packed_latent(t)
+        tc, tk = dev(xc, c_dtype), dev(xk, c_dtype)
+        return (tc, tk), lca.latent(tc, tk)
+
+    keep_c, cache_l = describe(c, kr)
+    keep_r, reps_l = describe(rep_c, rep_k)
+    o = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    lca.mla_latent_attn_decode(dev(qd, q_dtype), reps_l, m, cache_l, p["raw_begin"], L, 1.0, o, lse)
+    torch.cuda.synchronize()
+    ro, rl = O.decode(qd, rep_c, rep_k, m, c, kr, p["raw_begin"], L, 1.0)
+    assert_close(host(o), ro, what=f"decode o_latent ({layout})")
+    assert_close(host(lse), rl, what=f"decode lse ({layout})")
+
+
 def test_decode_plain_mla_matches_oracle():
     B, L = 2, 2048  # w = L: no groups, exact MLA over every row
     c, kr = li.latent_cache(2, B, L)
@@ -473,6 +510,50 @@ def test_prefill_bf16_output():
     torch.cuda.synchronize()
     ro, _ = O.prefill_chunk(q, 0, np.zeros((0, 512)), np.zeros((0, 64)), 0, c[0], kr[0], 0, 1.0)
     assert_close(host(out), ro, what="prefill bf16 o_latent")
+
+
+@pytest.mark.parametrize("q_dtype,c_dtype,layout", [
+    (torch.float32, torch.bfloat16, "packed"),  # direct-load kernel, f32 queries
+    (torch.bfloat16, torch.float32, "packed"),  # register-staged kernel, f32 rows
+    (torch.bfloat16, torch.bfloat16, "split"),  # register-staged kernel, c_KV and k_R apart
+    (torch.float32, torch.float32, "split"),
+])
+def test_prefill_other_dtypes_and_layouts(q_dtype, c_dtype, layout):
+    """Every prefill kernel instantiation against the oracle: several chunks
+    with representatives (the oracle's, rounded to bf16 and given to both
+    sides), a ragged last chunk; f32 inputs hold bf16-representable values."""
+    L, C, w, g, sm = 230, 72, 64, 16, 1.0
+    c, kr = li.latent_cache(12, 1, L)
+    q = li.queries(12, 1, L, H, rho=0.5)[0]
+    _, _, rep_c, rep_k = O.prefill(q, c[0], kr[0], w, g, C, sm)
+    rep_c, rep_k = li.bf16_round(rep_c), li.bf16_round(rep_k)
+
+    def describe(xc, xk):
+        if layout == "packed":
+            t = packed(xc, xk, c_dtype)
+            return t, lca.packed_latent(t)
+        tc, tk = dev(xc, c_dtype), dev(xk, c_dtype)
+        return (tc, tk), lca.latent(tc, tk)
+
+    keep_c, cache_l = describe(c[0], kr[0])
+    keep_r, reps_l = describe(rep_c, rep_k)
+    q_t = dev(q, q_dtype)
+    out = torch.empty((L, H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((L, H), dtype=torch.float32, device="cuda")
+    for s in range(0, L, C):
+        ms = O.prefill_plan(s, w, g)
+        e = min(L, s + C)
+        lca.mla_latent_attn_prefill_chunk(q_t[s:e], s, reps_l if ms else None, ms, cache_l, ms * g, sm,
+                                          out[s:e], lse[s:e])
+    torch.cuda.synchronize()
+    ro = np.zeros((L, H, 512))
+    rl = np.zeros((L, H))
+    for s in range(0, L, C):
+        ms = O.prefill_plan(s, w, g)
+        e = min(L, s + C)
+        ro[s:e], rl[s:e] = O.prefill_chunk(q[s:e], s, rep_c, rep_k, ms, c[0], kr[0], ms * g, sm)
+    assert_close(host(out), ro, what=f"prefill o_latent ({layout})")
+    assert_close(host(lse), rl, what=f"prefill lse ({layout})")
 
 
 # --------------------------------------------------------------- up-proj ----
