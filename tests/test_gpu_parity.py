@@ -464,6 +464,35 @@ def test_decode_up_equals_decode_then_up_proj(B, L, wdt, odt):
     assert_close(host(y2), O.up_proj(ro, w), what="decode_up out")
 
 
+def test_two_head_blocks_decode_up_and_prefill():
+    """H = 32, two blocks of 16 heads (the grids' head-block axis): the fused
+    decode + up-projection (4 sequences, several splits) and a causal prefill
+    chunk with a ragged last workgroup, against the oracle."""
+    H2, B, L = 32, 4, 3000
+    c, kr = li.latent_cache(14, B, L)
+    li.plant_needles(14, c, kr, 2, 12.0, 0, L)
+    q = li.queries(14, B, 1, H2, rho=0.5)[:, 0]
+    w = li.w_uv(14, H2)
+    cache_t = packed(c, kr)
+    o = torch.empty((B, H2, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H2), dtype=torch.float32, device="cuda")
+    y = torch.empty((B, H2, 128), dtype=torch.float32, device="cuda")
+    lca.mla_latent_attn_decode_up(dev(q), None, 0, lca.packed_latent(cache_t), 0, L, 1.0, o, dev(w), y, lse)
+    Lp = 150
+    qp = li.queries(14, 1, Lp, H2, rho=0.5, stream=2)[0]
+    op = torch.empty((Lp, H2, 512), dtype=torch.float32, device="cuda")
+    lp = torch.empty((Lp, H2), dtype=torch.float32, device="cuda")
+    lca.mla_latent_attn_prefill_chunk(dev(qp), 0, None, 0, lca.packed_latent(cache_t[0]), 0, 1.0, op, lp)
+    torch.cuda.synchronize()
+    ro, rl = O.decode(q, None, None, 0, c, kr, 0, L, 1.0)
+    assert_close(host(o), ro, what="decode o_latent, H = 32")
+    assert_close(host(lse), rl, what="decode lse, H = 32")
+    assert_close(host(y), O.up_proj(ro, w), what="decode_up out, H = 32")
+    rpo, rpl = O.prefill_chunk(qp, 0, np.zeros((0, 512)), np.zeros((0, 64)), 0, c[0], kr[0], 0, 1.0)
+    assert_close(host(op), rpo, what="prefill o_latent, H = 32")
+    assert_close(host(lp), rpl, what="prefill lse, H = 32")
+
+
 @pytest.mark.parametrize("L,C", [(320, 64), (301, 40)])
 def test_prefill_chunks_match_oracle(L, C):
     w, g, sm = 64, 16, 1.0
