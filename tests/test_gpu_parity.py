@@ -146,8 +146,9 @@ def _page_pool(seqs, page_rows, seed):
     return pool, table
 
 
-@pytest.mark.parametrize("page_rows,g", [(64, 16), (16, 8)])
-def test_decode_paged_ragged_matches_oracle(page_rows, g):
+@pytest.mark.parametrize("page_rows,g,q_dtype", [(64, 16, torch.bfloat16), (16, 8, torch.bfloat16),
+                                                 (64, 16, torch.float32)])
+def test_decode_paged_ragged_matches_oracle(page_rows, g, q_dtype):
     """Ragged batch (different lengths, one shorter than the window) over a
     shuffled paged cache against the oracle on each sequence's logical rows.
     With g = 8 the raw ranges start off a 16-row boundary, so tiles straddle
@@ -177,7 +178,7 @@ def test_decode_paged_ragged_matches_oracle(page_rows, g):
     o = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
     max_entries = max(m + L - rb for m, L, rb in zip(ms, Ls, rbs))
-    lca.mla_latent_attn_decode_paged(dev(q), lca.packed_latent(reps_t), i32(ms), lca.paged_latent(pool_t, table_t),
+    lca.mla_latent_attn_decode_paged(dev(q, q_dtype), lca.packed_latent(reps_t), i32(ms), lca.paged_latent(pool_t, table_t),
                                      i32(rbs), i32(Ls), max_entries, 1.0, o, lse)
     torch.cuda.synchronize()
     for b in range(B):
