@@ -64,8 +64,8 @@ def parse():
 TRAFFIC_SOURCES = ("mla_latent_kv_lca_amd/csrc/lca_decode.hip", "mla_latent_kv_lca_amd/csrc/lca_stream.h",
                    "mla_latent_kv_lca_amd/csrc/lca_tile.h", "mla_latent_kv_lca_amd/csrc/lca_device.h",
                    "mla_latent_kv_lca_amd/csrc/lca_up_rows.h")
-TRAFFIC = {"sha256": "13d6f3b05ebb01c06ccce460dea1a583ce975430cf2375f6f473a1bf97135bb7",
-           "fetch_bytes": 126_793_315, "write_bytes": 9_617_408}
+TRAFFIC = {"sha256": "48698c9083081cba23654d9f1f5e9757af22628aec208e5e9f17e0e5087735fb",
+           "fetch_bytes": 126_791_294, "write_bytes": 9_617_408}
 
 
 def decode_sources_digest() -> str:

@@ -179,15 +179,20 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   // the group point at entry rows (l % 16) / 4 of that run, columns
   // 4 ((l % 16) % 4) .. + 3 of the 16-column half: the offsets below are
   // those addresses for ct = 0, kap = 0.
-  // With e = 16 kap + 8 a + tr_row0 (e & 7 = tr_row0) and column chunk
-  // x + 4 ct, the position (x + 4 ct) ^ swz(e) splits into (x ^ (swz & 3)) and
-  // 4 (ct ^ bit 2 of swz): two per-lane bases (even / odd ct) plus constants.
+  // With e = 16 kap + 8 a + tr_row0 (swz(e) = swz(8 a + tr_row0)) and column
+  // chunk x + 4 ct (x & 4 = 0), the position (x + 4 ct) ^ swz(e) splits into
+  // (x ^ (swz & 3)) and 4 (ct ^ bit 2 of swz): per read a, two per-lane bases
+  // (even / odd ct) plus constants.
   const int tr_row0 = 4 * h32 + ((lane & 15) >> 2);
   const int tr_col0 = 256 * kh + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int tr_sw = swz(tr_row0);
-  const int tr_base = 8 * (tr_row0 * (D_ROW / 8) + ((tr_col0 >> 3) ^ (tr_sw & 3))) + (tr_col0 & 7);
-  const int tr_bb = 32 * (tr_sw >> 2);
-  const int tr_off[2] = {tr_base + tr_bb, tr_base - tr_bb};  // + 32 ct + 576 (16 kap + 8 a)
+  int tr_off[2][2];  // [a][ct & 1], + 32 ct + 576 * 16 kap
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int row = 8 * a + tr_row0, sw = swz(row);
+    const int base = 8 * (row * (D_ROW / 8) + ((tr_col0 >> 3) ^ (sw & 3))) + (tr_col0 & 7);
+    tr_off[a][0] = base + 32 * (sw >> 2);
+    tr_off[a][1] = base - 32 * (sw >> 2);
+  }
   // Score-product operand, k-step f (query columns 288 kh + 16 f + 8 h32 ..):
   // chunk c = 36 kh + 2 f + h32 of row r32, at kq[f & 3] + 64 (f >> 2) (swz
   // only flips the low three chunk bits, so four per-lane bases cover all f).
@@ -264,9 +269,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(
                                   pack_bf2(p[8 * kap + 4], p[8 * kap + 5]), pack_bf2(p[8 * kap + 6], p[8 * kap + 7]));
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) {
-        const bf16_t* pa = tile + tr_off[ct & 1] + 32 * ct + D_ROW * 16 * kap;
-        const uint2 lo = lds_read_tr4(pa);
-        const uint2 hi = lds_read_tr4(pa + 8 * D_ROW);
+        const bf16_t* pa = tile + 32 * ct + D_ROW * 16 * kap;
+        const uint2 lo = lds_read_tr4(pa + tr_off[0][ct & 1]);
+        const uint2 hi = lds_read_tr4(pa + tr_off[1][ct & 1]);
         // oacc[ct][r] = O[query row r32][256 kh + 32 ct + 8 (r / 4) + 4 h32 + r % 4]
         oacc[ct] = mfma32x32x16(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, oacc[ct]);
       }

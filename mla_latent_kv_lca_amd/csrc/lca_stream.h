@@ -65,11 +65,19 @@ __device__ __forceinline__ void retire(const uint4& v) {
 }
 
 // Tile rows are dense (576 bf16); the 16-byte chunk c of row r sits at chunk
-// position c ^ swz(r). swz permutes 0..7 over any 8 consecutive rows (so the
-// rows of a K fragment, one chunk each, use 8 different bank groups) and gives
-// the 4 rows of an aligned group distinct values in bits 1-2 (so a transposed
-// read of 4 rows x 2 adjacent chunks touches 8 different bank groups).
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// position c ^ swz(r). LDS has 64 banks of 4 bytes, and a row is 288 bank
+// words, so rows of one parity start on bank 0 and the others on bank 32; a
+// 16-byte read serves 16 lanes per pass and an 8-byte read 32. swz(r) is bits
+// 1..3 of r in reverse order, which makes every access pattern of the kernels
+// use each bank once per pass:
+//  - K fragments (16 consecutive rows, one chunk each): the 8 rows of each
+//    parity get 8 distinct values;
+//  - decode's transposed V reads (8 aligned rows x 2 adjacent chunks): the 4
+//    rows of each parity differ in bits 1-2;
+//  - prefill's transposed V reads (4 aligned rows x 4 adjacent chunks): the 2
+//    rows of each parity differ in bit 2.
+// swz(r) depends on r mod 16 only.
+__device__ __forceinline__ int swz(int r) { return (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1); }
 __device__ __forceinline__ int chunk_pos(int r, int c) { return r * (D_ROW / 8) + (c ^ swz(r)); }
 
 // Packed rows (k_R right after c_KV, one token stride) of the two segments of
