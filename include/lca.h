@@ -49,7 +49,11 @@ extern "C" {
 #define LCA_D_R 64       /* decoupled RoPE key width */
 #define LCA_D_ROW 576    /* one cached row: c_KV ++ k_R */
 #define LCA_D_V 128      /* per-head value width of W_UV */
-#define LCA_MAX_G 32     /* largest supported group size (powers of two) */
+#define LCA_MAX_G 32     /* largest supported group size (powers of two): one
+                          * wavefront holds a whole group in registers, 8
+                          * latent columns of every row per lane; the pages
+                          * use g = 16 throughout (局限与展望 names the fixed
+                          * g as a limitation) */
 
 typedef enum {
   LCA_OK = 0,
@@ -250,7 +254,13 @@ int mla_latent_attn_decode_up(const void* q, int32_t q_dtype, int64_t q_seq_stri
                               int32_t w_dtype, void* out, int32_t out_dtype, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
 
-/* Chunked prefill attention of one sequence over a condensed latent cache.
+/* Chunked prefill attention of one sequence over a condensed latent cache
+ * ("Latent-Condensed Transformer for Efficient Long Context Modeling",
+ * 方法详解 / 整体框架 and its flowchart E -> F: each query attends to the
+ * representatives of the groups older than its local window plus the
+ * uncompressed rows of the window; the pages give no prefill-specific rule,
+ * so the groups are frozen per chunk as described below and the window is
+ * causal, which reduces to exact causal MLA when no group is condensed).
  * Query i of the chunk sits at absolute position t = chunk_start + i (its
  * absorbed query at q + i*q_tok_stride + h*576, H a multiple of 16) and
  * attends to representatives [0, m) (all visible) and raw cache rows

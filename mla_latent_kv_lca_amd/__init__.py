@@ -142,6 +142,16 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _check_lse(lse, rows: int, H: int) -> None:
+    """lse is optional; when given it receives rows * H fp32 values written
+    at lse[row * H + head], so it must be a contiguous fp32 tensor of exactly
+    that many elements (the kernels index it without bounds)."""
+    if lse is None:
+        return
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != rows * H:
+        raise ValueError(f"lse must be a contiguous fp32 tensor of {rows} x {H} elements")
+
+
 def _stream(stream) -> int:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -287,6 +297,7 @@ def mla_latent_attn_decode_paged(q: torch.Tensor, reps: LatentT, seq_m: torch.Te
     for t in (seq_m, seq_raw_begin, seq_raw_end):
         if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() != B:
             raise ValueError("per-sequence arrays must be contiguous int32 [B] tensors")
+    _check_lse(lse, B, H)
     ws = _workspace(mla_latent_attn_decode_workspace_size(B, H, max_entries), q, workspace)
     _check(load().mla_latent_attn_decode_paged(
         q.data_ptr(), dtype_code(q), q.stride(0), B, H, ctypes.byref(reps), seq_m.data_ptr(),
@@ -304,8 +315,7 @@ def mla_latent_attn_decode(q: torch.Tensor, reps: LatentT | None, m: int, raw: L
     B, H = q.shape[0], q.shape[1]
     if o_latent.dtype != torch.float32 or not o_latent.is_contiguous() or o_latent.shape != (B, H, D_C):
         raise ValueError("o_latent must be a contiguous fp32 [B, H, 512] tensor")
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous fp32 [B, H] tensor")
+    _check_lse(lse, B, H)
     n = m + raw_end - raw_begin
     ws = _workspace(mla_latent_attn_decode_workspace_size(B, H, max(n, 1)), q, workspace)
     _check(load().mla_latent_attn_decode(
@@ -327,8 +337,7 @@ def mla_latent_attn_decode_up(q: torch.Tensor, reps: LatentT | None, m: int, raw
     B, H = q.shape[0], q.shape[1]
     if o_latent.dtype != torch.float32 or not o_latent.is_contiguous() or o_latent.shape != (B, H, D_C):
         raise ValueError("o_latent must be a contiguous fp32 [B, H, 512] tensor")
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous fp32 [B, H] tensor")
+    _check_lse(lse, B, H)
     if not w_uv.is_contiguous() or tuple(w_uv.shape) != (H, D_C, D_V):
         raise ValueError("w_uv must be a contiguous [H, 512, 128] tensor")
     if not out.is_contiguous() or tuple(out.shape) != (B, H, D_V):
@@ -353,6 +362,7 @@ def mla_latent_attn_prefill_chunk(q: torch.Tensor, chunk_start: int, reps: Laten
     C, H = q.shape[0], q.shape[1]
     if not o_latent.is_contiguous() or o_latent.shape != (C, H, D_C):
         raise ValueError("o_latent must be a contiguous [C, H, 512] tensor")
+    _check_lse(lse, C, H)
     _check(load().mla_latent_attn_prefill_chunk(
         q.data_ptr(), dtype_code(q), q.stride(0), chunk_start, C, H,
         None if reps is None else ctypes.byref(reps), m, ctypes.byref(raw), raw_begin, sm_scale,

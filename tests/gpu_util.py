@@ -32,11 +32,34 @@ def assert_close(got, ref, tol=TOL, what=""):
     return err, scale
 
 
-def anchors_agree(gpu_anchor, ref_anchor, margin, min_margin=1e-3):
-    """Anchors must match wherever the oracle's top-2 score margin exceeds min_margin."""
+def anchors_agree(gpu_anchor, ref_anchor, margin, min_margin=1e-3, min_sure_frac=0.5):
+    """Anchors must match wherever the oracle's top-2 score margin exceeds
+    min_margin. At least min_sure_frac of the groups must be that clear, so
+    a margin that came out wrong (e.g. always tiny) cannot exempt them all."""
     gpu_anchor = np.asarray(gpu_anchor)
     ref_anchor = np.asarray(ref_anchor)
     sure = np.asarray(margin) > min_margin
+    assert sure.shape == gpu_anchor.shape == ref_anchor.shape, "anchor arrays and margins must align"
     bad = np.flatnonzero((gpu_anchor != ref_anchor) & sure)
     assert bad.size == 0, f"{bad.size} anchors differ at margin > {min_margin}"
-    return int(sure.sum())
+    n_sure = int(sure.sum())
+    assert n_sure >= min_sure_frac * sure.size, \
+        f"only {n_sure} of {sure.size} groups have a top-2 margin > {min_margin}"
+    return n_sure
+
+
+class AnchorTally:
+    """Collects sampled groups one at a time and checks them together with
+    anchors_agree (so the share of clear margins is judged over the sample)."""
+
+    def __init__(self):
+        self.got, self.ref, self.margin = [], [], []
+
+    def add(self, gpu_anchor, ref_anchor, margin):
+        self.got.append(np.ravel(gpu_anchor))
+        self.ref.append(np.ravel(ref_anchor))
+        self.margin.append(np.ravel(margin))
+
+    def check(self, **kw):
+        return anchors_agree(np.concatenate(self.got), np.concatenate(self.ref),
+                             np.concatenate(self.margin), **kw)

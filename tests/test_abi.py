@@ -248,3 +248,31 @@ def test_project_argument_errors():
     assert _project(lib, qs=576) == lca.LCA_ERR_INVALID_ARG    # heads overlap
     assert _project(lib, wsb=16) == lca.LCA_ERR_WORKSPACE
     assert _project(lib, ws=None) == lca.LCA_ERR_WORKSPACE
+
+
+def test_binding_rejects_bad_lse():
+    """The binding checks lse (fp32, contiguous, rows x H elements) before any
+    call reaches the library, since the kernels index it without bounds."""
+    import torch
+    B, H = 2, 16
+    q = torch.zeros((B, H, 576), dtype=torch.bfloat16)
+    o = torch.zeros((B, H, 512), dtype=torch.float32)
+    raw = lca.packed_latent(torch.zeros((B, 8, 576), dtype=torch.bfloat16))
+    for bad in (torch.zeros((B, H), dtype=torch.bfloat16), torch.zeros((B, H - 1)),
+                torch.zeros((H, B)).t()):
+        with pytest.raises(ValueError, match="lse"):
+            lca.mla_latent_attn_decode(q, None, 0, raw, 0, 8, 1.0, o, bad)
+        with pytest.raises(ValueError, match="lse"):
+            lca.mla_latent_attn_decode_up(q, None, 0, raw, 0, 8, 1.0, o, torch.zeros((H, 512, 128)),
+                                          torch.zeros((B, H, 128)), bad)
+    C = 3
+    with pytest.raises(ValueError, match="lse"):
+        lca.mla_latent_attn_prefill_chunk(torch.zeros((C, H, 576), dtype=torch.bfloat16), 0, None, 0, raw, 0, 1.0,
+                                          torch.zeros((C, H, 512)), torch.zeros((C * H + 1,)))
+    pool = torch.zeros((2, 16, 576), dtype=torch.bfloat16)
+    table = torch.zeros((B, 1), dtype=torch.int32)
+    i32 = torch.zeros((B,), dtype=torch.int32)
+    with pytest.raises(ValueError, match="lse"):
+        lca.mla_latent_attn_decode_paged(q, lca.packed_latent(torch.zeros((B, 1, 576), dtype=torch.bfloat16)), i32,
+                                         lca.paged_latent(pool, table), i32, i32, 8, 1.0, o,
+                                         torch.zeros((B, H), dtype=torch.float64))

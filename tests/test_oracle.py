@@ -239,6 +239,31 @@ def test_permutation_moves_anchor_with_its_row():
     np.testing.assert_allclose(a2, a[perm], atol=1e-15)
 
 
+def test_top2_margin_hand_values():
+    """The anchor-parity rule (anchors must agree where the largest score
+    beats the runner-up by more than 1e-3) rests on top2_margin: the gap
+    between the largest and the second-largest score of each group, ties
+    counted twice. Hand values: unsorted rows, ties, all-negative scores,
+    and batched leading axes."""
+    assert O.top2_margin(np.array([3.0, 1.0, 2.0])) == 1.0
+    assert O.top2_margin(np.array([0.1, -2.0, 0.7, 0.4])) == pytest.approx(0.3, abs=1e-15)
+    assert O.top2_margin(np.array([5.0, 1.0, 5.0])) == 0.0          # tie at the top
+    assert O.top2_margin(np.array([-5.0, -1.0, -3.0])) == 2.0       # sign of the values
+    assert O.top2_margin(np.array([2.0, 2.0, 2.0, 2.0])) == 0.0     # all equal
+    assert O.top2_margin(np.array([7.0, 7.0 - 2e-3])) == pytest.approx(2e-3, abs=1e-15)
+    batched = np.array([[[1.0, 4.0, 2.0], [0.0, 0.0, -1.0]],
+                        [[9.0, -9.0, 8.5], [1.0, 3.0, 3.0 - 5e-4]]])
+    np.testing.assert_allclose(O.top2_margin(batched), [[2.0, 0.0], [0.5, 5e-4]], atol=1e-15)
+    # the margin is taken along the last axis only, and is never negative
+    r = np.random.default_rng(21).standard_normal((3, 5, 16))
+    got = O.top2_margin(r)
+    assert got.shape == (3, 5) and np.all(got >= 0)
+    i, j = 2, 4
+    row = r[i, j]
+    top = row.max()
+    assert got[i, j] == top - row[row != top].max()
+
+
 def test_scores_are_mean_textbook_logits():
     """R1-R2: s_i is the mean over g queries and H heads of the textbook MLA
     logit [W_UK^T c_i ; k_i^R] . [q_nope ; q_rope] (keys built explicitly)."""
