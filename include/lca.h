@@ -19,7 +19,9 @@
  *
  * Conventions shared by every call:
  *  - Device buffers are owned by the caller. The library never allocates or
- *    frees device memory; scratch space comes from a caller workspace.
+ *    frees device memory; scratch space comes from a caller workspace (the
+ *    one exception, mla_latent_attn_decode_up_noalloc, uses a fixed device
+ *    array that the library holds per GPU).
  *  - Inputs are never written. Outputs are fully written, except that
  *    lca_condense writes only the representative rows it is asked for.
  *  - Calls are asynchronous on `stream` (a hipStream_t; 0 = the null stream)
@@ -253,6 +255,32 @@ int mla_latent_attn_decode_up(const void* q, int32_t q_dtype, int64_t q_seq_stri
                               float sm_scale, float* o_latent, float* lse, const void* w_uv,
                               int32_t w_dtype, void* out, int32_t out_dtype, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device scratch the library keeps for
+ * mla_latent_attn_decode_up_noalloc on every GPU it runs on (16 MiB; every
+ * split plan of the decode calls fits). */
+#define LCA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* mla_latent_attn_decode_up for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same operation, arguments, layouts, results (bitwise equal
+ * to mla_latent_attn_decode_up on the same inputs) and errors, without the
+ * workspace argument. The split-K partial results live instead in a
+ * file-scope device array of LCA_NOALLOC_SCRATCH_BYTES that the library holds
+ * on each GPU until the process ends; its address is looked up once per
+ * device, on the first call with that device current. The call allocates
+ * nothing and never synchronises. A shape whose partial results would exceed
+ * the array returns LCA_ERR_UNSUPPORTED (none of the decode split plans
+ * does). Every call on one GPU shares that GPU's array and leaves the last
+ * call's partials in it; no value is read there before the same call wrote
+ * it, so nothing needs clearing. Calls that overlap on one GPU (several
+ * streams, or threads without ordering) race on the array and must not be
+ * issued. */
+int mla_latent_attn_decode_up_noalloc(const void* q, int32_t q_dtype, int64_t q_seq_stride, int32_t B,
+                                      int32_t H, const lca_latent_t* reps, int64_t m,
+                                      const lca_latent_t* raw, int64_t raw_begin, int64_t raw_end,
+                                      float sm_scale, float* o_latent, float* lse, const void* w_uv,
+                                      int32_t w_dtype, void* out, int32_t out_dtype, hipStream_t stream);
 
 /* Chunked prefill attention of one sequence over a condensed latent cache
  * ("Latent-Condensed Transformer for Efficient Long Context Modeling",

@@ -262,12 +262,15 @@ int mla_latent_attn_decode_paged(const void* q, int32_t q_dtype, int64_t q_seq_s
                     "mla_latent_attn_decode_paged launch");
 }
 
-int mla_latent_attn_decode_up(const void* q, int32_t q_dtype, int64_t q_seq_stride, int32_t B,
-                              int32_t H, const lca_latent_t* reps, int64_t m,
-                              const lca_latent_t* raw, int64_t raw_begin, int64_t raw_end,
-                              float sm_scale, float* o_latent, float* lse, const void* w_uv,
-                              int32_t w_dtype, void* out, int32_t out_dtype, void* workspace,
-                              size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+// Arguments of mla_latent_attn_decode_up / _noalloc other than the scratch;
+// on success *need receives the bytes of split-K partials the call uses.
+int check_decode_up(const void* q, int32_t q_dtype, int64_t q_seq_stride, int32_t B, int32_t H,
+                    const lca_latent_t* reps, int64_t m, const lca_latent_t* raw, int64_t raw_begin,
+                    int64_t raw_end, float sm_scale, float* o_latent, const void* w_uv, int32_t w_dtype,
+                    void* out, int32_t out_dtype, size_t* need) {
   int rc;
   if (q == nullptr || !aligned16(q)) return fail(LCA_ERR_INVALID_ARG, "q must be a non-null 16-byte aligned pointer");
   if (!valid_dtype(q_dtype)) return fail(LCA_ERR_INVALID_ARG, "q_dtype %d is not LCA_BF16/LCA_F32", q_dtype);
@@ -287,7 +290,23 @@ int mla_latent_attn_decode_up(const void* q, int32_t q_dtype, int64_t q_seq_stri
   if (w_uv == nullptr || !aligned16(w_uv) || out == nullptr || !aligned16(out))
     return fail(LCA_ERR_INVALID_ARG, "w_uv and out must be non-null 16-byte aligned pointers");
   const lca::DecodeSplit sp = lca::decode_split(B, H / 16, n);
-  const size_t need = lca::decode_workspace_bytes(B, H / 16, sp.S);
+  *need = lca::decode_workspace_bytes(B, H / 16, sp.S);
+  return LCA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int mla_latent_attn_decode_up(const void* q, int32_t q_dtype, int64_t q_seq_stride, int32_t B,
+                              int32_t H, const lca_latent_t* reps, int64_t m,
+                              const lca_latent_t* raw, int64_t raw_begin, int64_t raw_end,
+                              float sm_scale, float* o_latent, float* lse, const void* w_uv,
+                              int32_t w_dtype, void* out, int32_t out_dtype, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  size_t need = 0;
+  const int rc = check_decode_up(q, q_dtype, q_seq_stride, B, H, reps, m, raw, raw_begin, raw_end, sm_scale,
+                                 o_latent, w_uv, w_dtype, out, out_dtype, &need);
+  if (rc != LCA_OK) return rc;
   if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need))
     return fail(LCA_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
   const lca_latent_t none = {nullptr, nullptr, 0, 0, 0, 0, m > 0 ? reps->dtype : raw->dtype};
@@ -297,6 +316,32 @@ int mla_latent_attn_decode_up(const void* q, int32_t q_dtype, int64_t q_seq_stri
                                           sm_scale, o_latent, lse, w_uv, w_dtype, out, out_dtype,
                                           workspace, stream),
                     "mla_latent_attn_decode_up launch");
+}
+
+int mla_latent_attn_decode_up_noalloc(const void* q, int32_t q_dtype, int64_t q_seq_stride, int32_t B,
+                                      int32_t H, const lca_latent_t* reps, int64_t m,
+                                      const lca_latent_t* raw, int64_t raw_begin, int64_t raw_end,
+                                      float sm_scale, float* o_latent, float* lse, const void* w_uv,
+                                      int32_t w_dtype, void* out, int32_t out_dtype, hipStream_t stream) {
+  size_t need = 0;
+  const int rc = check_decode_up(q, q_dtype, q_seq_stride, B, H, reps, m, raw, raw_begin, raw_end, sm_scale,
+                                 o_latent, w_uv, w_dtype, out, out_dtype, &need);
+  if (rc != LCA_OK) return rc;
+  if (need > LCA_NOALLOC_SCRATCH_BYTES)
+    return fail(LCA_ERR_UNSUPPORTED, "this call needs %zu bytes of split-K scratch; the library's fixed scratch "
+                "holds %zu", need, (size_t)LCA_NOALLOC_SCRATCH_BYTES);
+  void* scratch = nullptr;
+  if (need > 0) {
+    const int st = hip_status(lca::noalloc_scratch(&scratch), "scratch address lookup");
+    if (st != LCA_OK) return st;
+  }
+  const lca_latent_t none = {nullptr, nullptr, 0, 0, 0, 0, m > 0 ? reps->dtype : raw->dtype};
+  const lca_latent_t& rp = m > 0 ? *reps : none;
+  const lca_latent_t& rw = raw_end > raw_begin ? *raw : none;
+  return hip_status(lca::launch_decode_up(q, q_dtype, q_seq_stride, B, H, rp, m, rw, raw_begin, raw_end,
+                                          sm_scale, o_latent, lse, w_uv, w_dtype, out, out_dtype,
+                                          scratch, stream),
+                    "mla_latent_attn_decode_up_noalloc launch");
 }
 
 int mla_latent_attn_prefill_chunk(const void* q, int32_t q_dtype, int64_t q_tok_stride,

@@ -11,6 +11,8 @@
 //                        direct loads, one workgroup per CU (details below).
 //  decode_kernel_staged  any strides / f32 rows: register-staged 32-entry tiles.
 //  merge_kernel          combines split-K partial results in split order.
+#include <mutex>
+
 #include "lca_stream.h"
 #include "lca_up_rows.h"
 
@@ -757,6 +759,38 @@ hipError_t launch_decode_paged(const void* q, int q_dtype, int64_t q_seq_stride,
   if (err != hipSuccess || sp.S == 1) return err;
   launch_merge(sp, B, H, po, pml, o_latent, lse, stream);
   return hipGetLastError();
+}
+
+// ---- scratch for the entry point that allocates nothing
+// Split-K partial results of mla_latent_attn_decode_up_noalloc live in this
+// file-scope array instead of a caller workspace. Every GPU the library runs
+// on holds its own copy until the process ends. In host code the name is
+// only a stand-in: its device address comes from hipGetSymbolAddress, looked
+// up once per device (with that device current) and kept here.
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** out) {
+  *out = nullptr;
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode_up(const void* q, int q_dtype, int64_t q_seq_stride, int B, int H,

@@ -47,6 +47,12 @@ hipError_t launch_decode(const void* q, int q_dtype, int64_t q_seq_stride, int B
                          int64_t raw_begin, int64_t raw_end, float sm_scale, float* o_latent,
                          float* lse, void* workspace, hipStream_t stream);
 
+// Scratch of the entry point that allocates nothing: a file-scope device
+// array of NOALLOC_SCRATCH_BYTES (every split plan of decode_split fits), its
+// device address for the current device (looked up once per device).
+constexpr size_t NOALLOC_SCRATCH_BYTES = LCA_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch(void** out);
+
 // decode followed by the W_UV up-projection of its output; the split merge
 // and the projection share one kernel when B <= UP_SMALL_T.
 hipError_t launch_decode_paged(const void* q, int q_dtype, int64_t q_seq_stride, int B, int H,

@@ -205,6 +205,28 @@ def test_decode_up_argument_errors():
     assert _decode_up(lib, lat, re=60000) == lca.LCA_ERR_WORKSPACE
 
 
+def test_decode_up_noalloc_argument_errors():
+    """The entry point that allocates nothing rejects bad arguments like
+    mla_latent_attn_decode_up (it has no workspace argument to get wrong)."""
+    lib = lca.load()
+    lat = _lat()
+
+    def call(**kw):
+        a = dict(q=64, qdt=0, qss=16 * 576, B=1, H=16, m=0, rb=0, re=8, sm=1.0, o=64, lse=None,
+                 w=64, wdt=0, out=64, odt=0)
+        a.update(kw)
+        return lib.mla_latent_attn_decode_up_noalloc(a["q"], a["qdt"], a["qss"], a["B"], a["H"], None, a["m"],
+                                                     ctypes.byref(lat), a["rb"], a["re"], a["sm"], a["o"],
+                                                     a["lse"], a["w"], a["wdt"], a["out"], a["odt"], None)
+    assert call(q=None) == lca.LCA_ERR_INVALID_ARG
+    assert call(w=None) == lca.LCA_ERR_INVALID_ARG
+    assert call(out=72) == lca.LCA_ERR_INVALID_ARG
+    assert call(H=8) == lca.LCA_ERR_UNSUPPORTED
+    assert call(rb=9) == lca.LCA_ERR_INVALID_ARG
+    assert call(sm=-1.0) == lca.LCA_ERR_INVALID_ARG
+    assert "sm_scale" in lca.lca_last_error()
+
+
 def test_prefill_and_up_proj_argument_errors():
     lib = lca.load()
     lat = _lat()
