@@ -14,6 +14,8 @@
 // registers), runs the online softmax in registers (four lanes per head) and
 // accumulates O for all 512 latent columns (32 MFMA 16x16x32 per tile).
 // Workgroups are issued heaviest (latest tokens) first.
+#include <type_traits>
+
 #include "lca_stream.h"
 
 namespace lca {
@@ -107,26 +109,37 @@ __global__ __launch_bounds__(NT) void prefill_kernel_staged(
 // prefill_kernel: the fast path for packed bf16 rows. Workgroup = 4
 // wavefronts = 2 pairs; pair p holds 2 query tokens x 16 heads = 32 query
 // rows, so every LDS fragment feeds a 32x32x16 MFMA. Entry tiles of 32 rows
-// stream HBM -> LDS by direct loads into a 3-slot ring (two tiles in flight).
-// Within a pair, wave k
+// stream HBM -> LDS by direct loads into a 4-slot ring (two tiles in
+// flight). Within a pair, wave k
 //   forms the partial S^T = K Q^T over query columns [288 k, 288 k + 288)
-//   (18 MFMA 32x32x16, those query columns in registers), adds its partner's
-//   partial read through LDS in a fixed order (columns 0..287 first), so both
-//   waves hold identical scores and run the same online softmax (two lanes per
-//   query row; the reference max only moves when a row's max grows by more
-//   than 2^8, so the accumulators are rarely rescaled), and
+//   (18 MFMA 32x32x16, those query columns in registers) and adds its
+//   partner's partial read through LDS, so both waves hold identical scores
+//   and run the same online softmax (two lanes per query row; the reference
+//   max only moves when a row's max grows by more than 2^8, so the
+//   accumulators are rarely rescaled), and
 //   accumulates O^T += V^T P^T for latent columns [256 k, 256 k + 256)
 //   (16 MFMA 32x32x16; P comes straight from the score registers, V^T from
-//   row fragments with half-word shuffles).
+//   transposed LDS reads).
+// The tiles run as a software pipeline, so that the matrix cores never wait
+// for the vector work of the same tile: iteration t issues the score
+// products of tile t + 1 with the softmax of tile t spread between them
+// (phase A), then the value products of tile t with the partial-score
+// exchange, sum, mask and row max of tile t + 1 spread between them (phase
+// B). Scheduling fences keep every slot's few vector instructions next to
+// its matrix product. Causal masking is compiled only into the (at most two)
+// tiles that cross the diagonal of the workgroup's rows.
 constexpr int PF2_TOK = 4;  // query tokens per workgroup
-constexpr int PBUF = 3;     // LDS ring depth (tiles)
+constexpr int PBUF = 4;     // LDS ring depth (tiles): 4 x 36 KB + 16 KB exchange = 160 KB
+constexpr int KF_RING = 6;  // score-product fragments in registers (read four products ahead)
+
+template <bool V> using bool_c = std::integral_constant<bool, V>;
 
 template <typename TQ, typename TO>
 __global__ __launch_bounds__(256) void prefill_kernel(
     const TQ* __restrict__ q, int64_t q_tok, int64_t chunk_start, int C, int H, DmaSrc src,
     int64_t m, int64_t raw_begin, float scale_log2, TO* __restrict__ o, float* __restrict__ lse) {
   __shared__ __align__(16) bf16_t ring[PBUF][STILE_ELEMS];
-  __shared__ __align__(16) float sx[4][16][64];  // partial scores [wave][r][lane]
+  __shared__ __align__(16) f32x4_t sx[4][4][64];  // partial scores [wave][r / 4][lane]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -143,6 +156,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   const int64_t vis0 = m + (chunk_start - raw_begin + 1);
   const int64_t n_blk = vis0 + i_last, n_min = vis0 + tok0, n_mine = vis0 + i_ld;
   const int n_tiles = (int)((n_blk + STILE - 1) / STILE);
+  const int n_full = (int)(n_min / STILE);  // tiles every row of the workgroup sees whole
 
   uint32_t off[DMA_PER_WAVE];
 #pragma unroll
@@ -203,99 +217,160 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     const int F = jj + 2 * kh;
     kq[jj] = 8 * (r32 * (D_ROW / 8)) + 256 * kh + 64 * (F >> 2) + 8 * ((2 * (F & 3) + h32) ^ sw32);
   }
+  auto kfrag = [&](const bf16_t* tile, int f) {
+    return *reinterpret_cast<const uint4*>(tile + kq[f & 3] + 64 * (f >> 2));
+  };
+  // value-product operand j = 8 kap + ct of a tile
+  auto vfrag = [&](const bf16_t* tile, int j) {
+    const int kap = j >> 3, ct = j & 7;
+    const bf16_t* pa = tile + 32 * ct + D_ROW * 16 * kap;
+    const uint2 lo = lds_read_tr4(pa + tr_off[0][ct & 1]);
+    const uint2 hi = lds_read_tr4(pa + tr_off[1][ct & 1]);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+  };
 
-  // Scores of tile t: this lane's query row r32 against entries
-  // 8 (r / 4) + 4 h32 + r % 4 (log2 units, causally masked); returns the row
-  // max over the tile (the two lanes of a query row combined).
-  auto scores = [&](int t, float (&z)[16]) -> float {
-    const int64_t e0 = (int64_t)t * STILE;
-    wait_dma_newer(min(n_tiles - 1 - t, PBUF - 2));
-    barrier();  // tile t landed for every wave; tile t-1's slot and sx are free
-    if (t + PBUF - 1 < n_tiles)
-      tile_dma(src, e0 + (int64_t)(PBUF - 1) * STILE, n_blk, ring[(t + PBUF - 1) % PBUF], w, lane, off);
-    const bf16_t* tile = ring[t % PBUF];
-    // partial S^T[entry 8(r/4) + 4 h32 + r%4][query row r32] over this half;
-    // fragments are read four k-steps ahead of their MFMA
-    auto frag = [&](int f) { return *reinterpret_cast<const uint4*>(tile + kq[f & 3] + 64 * (f >> 2)); };
-    f32x16_t sa, sb;
+  float z[16];   // scores of the current tile (log2 units, masked)
+  uint4 pb[2];   // its softmax weights as bf16, entry k-steps 0 and 1
+  f32x16_t S;    // partial scores of the next tile
+  uint4 vf[3];   // value-product operands, read two products ahead
+
+  // Phase A: score products of tile tn (QK) and, spread between them, the
+  // softmax of the current tile z (SM): p = 2^(z - m_run), row sum into
+  // l_run, p packed to bf16 into pb. Also reads the first two value operands
+  // of the current tile tc for phase B (PV).
+  auto phase_a = [&](auto qk, auto sm, auto pv, const bf16_t* tn, const bf16_t* tc) {
+    constexpr bool QK = decltype(qk)::value, SM = decltype(sm)::value, PV = decltype(pv)::value;
+    const float m_ref = m_run;
+    float p[16], ps = 0.f;
+    uint4 kf[KF_RING];
+    if constexpr (QK) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { sa[r] = 0.f; sb[r] = 0.f; }
-    uint4 kf[18];
+      for (int r = 0; r < 16; ++r) S[r] = 0.f;
 #pragma unroll
-    for (int f = 0; f < 4; ++f) kf[f] = frag(f);
+      for (int f = 0; f < 4; ++f) kf[f] = kfrag(tn, f);
+    }
 #pragma unroll
-    for (int ks = 0; ks < 18; ks += 2) {
-      if (ks + 4 < 18) kf[ks + 4] = frag(ks + 4);
-      if (ks + 5 < 18) kf[ks + 5] = frag(ks + 5);
-      sa = mfma32x32x16(kf[ks], qf[ks], sa);
-      sb = mfma32x32x16(kf[ks + 1], qf[ks + 1], sb);
-      // keep each k-step's reads ahead of its products (left to itself the
-      // scheduler bunches the reads and waits on them)
+    for (int ks = 0; ks < 18; ++ks) {
+      if constexpr (QK) {
+        S = mfma32x32x16(kf[ks % KF_RING], qf[ks], S);
+        if (ks + 4 < 18) kf[(ks + 4) % KF_RING] = kfrag(tn, ks + 4);
+      }
+      if constexpr (SM) {
+        if (ks < 16) {
+          p[ks] = __builtin_amdgcn_exp2f(z[ks] - m_ref);
+          ps += p[ks];
+          if (ks & 1) {
+            const int k = ks >> 1;  // packed pair k of 8: entry k-step k / 4, word k % 4
+            const uint32_t wd = pack_bf2(p[ks - 1], p[ks]);
+            if ((k & 3) == 0) pb[k >> 2].x = wd;
+            else if ((k & 3) == 1) pb[k >> 2].y = wd;
+            else if ((k & 3) == 2) pb[k >> 2].z = wd;
+            else pb[k >> 2].w = wd;
+          }
+        } else if (ks == 16) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps), __float_as_uint(ps), false, false);
+          l_run += __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        }
+      }
+      if constexpr (PV) {
+        if (ks == 16) vf[0] = vfrag(tc, 0);
+        if (ks == 17) vf[1] = vfrag(tc, 1);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sx[w][r][lane] = sa[r] + sb[r];
-    barrier();
-#pragma unroll
-    for (int r = 0; r < 16; ++r) z[r] = (sx[2 * pr][r][lane] + sx[2 * pr + 1][r][lane]) * scale_log2;
-    if (e0 + STILE > n_min) {  // causal boundary inside this tile
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (e0 + 8 * (r >> 2) + 4 * h32 + (r & 3) >= n_mine) z[r] = -INFINITY;
-    }
-    float tmax = z[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, z[r]);
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
-    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
   };
-  // P relative to the running max, its row sum, and O^T += V^T P^T for
-  // latent columns [256 kh, 256 kh + 256) (8 column tiles x 2 entry k-steps
-  // of MFMA 32x32x16).
-  auto accumulate = [&](int t, const float (&z)[16]) {
-    const bf16_t* tile = ring[t % PBUF];
-    const float m_ref = m_run == -INFINITY ? 0.f : m_run;
-    float p[16];
+
+  // Phase B: value products of tile tc (PV) and, spread between them, the
+  // exchange of the partial scores S of the next tile (XC): written to LDS,
+  // a barrier, the partner's read back and added (columns 0..287 first, the
+  // same order in both waves), scaled, causally masked (MASKED, entries from
+  // en0), and the row max returned.
+  auto phase_b = [&](auto pv, auto xc, auto masked, const bf16_t* tc, int64_t en0) -> float {
+    constexpr bool PV = decltype(pv)::value, XC = decltype(xc)::value, MASKED = decltype(masked)::value;
+    f32x4_t sp[4];
+    float tmax = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(z[r] - m_ref);
-    float ps = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) ps += p[r];
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps), __float_as_uint(ps), false, false);
-    l_run += __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-#pragma unroll
-    for (int kap = 0; kap < 2; ++kap) {
-      const uint4 pb = make_uint4(pack_bf2(p[8 * kap + 0], p[8 * kap + 1]), pack_bf2(p[8 * kap + 2], p[8 * kap + 3]),
-                                  pack_bf2(p[8 * kap + 4], p[8 * kap + 5]), pack_bf2(p[8 * kap + 6], p[8 * kap + 7]));
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
-        const bf16_t* pa = tile + 32 * ct + D_ROW * 16 * kap;
-        const uint2 lo = lds_read_tr4(pa + tr_off[0][ct & 1]);
-        const uint2 hi = lds_read_tr4(pa + tr_off[1][ct & 1]);
-        // oacc[ct][r] = O[query row r32][256 kh + 32 ct + 8 (r / 4) + 4 h32 + r % 4]
-        oacc[ct] = mfma32x32x16(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, oacc[ct]);
+    for (int j = 0; j < 16; ++j) {
+      if constexpr (PV) {
+        const int kap = j >> 3, ct = j & 7;
+        oacc[ct] = mfma32x32x16(vf[j % 3], pb[kap], oacc[ct]);
+        if (j + 2 < 16) vf[(j + 2) % 3] = vfrag(tc, j + 2);
       }
+      if constexpr (XC) {
+        if (j >= 2 && j < 6) {
+          const int r4 = j - 2;
+          sx[w][r4][lane] = f32x4_t{S[4 * r4], S[4 * r4 + 1], S[4 * r4 + 2], S[4 * r4 + 3]};
+        }
+        if (j == 7) barrier();  // both partials of the pair are in LDS
+        if (j >= 8 && j < 12) sp[j - 8] = sx[w ^ 1][j - 8][lane];
+        if (j >= 12) {
+          const int r4 = j - 12;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * r4 + i;
+            float v = (S[r] + sp[r4][i]) * scale_log2;
+            if constexpr (MASKED) {
+              if (en0 + 8 * (r >> 2) + 4 * h32 + (r & 3) >= n_mine) v = -INFINITY;
+            }
+            z[r] = v;
+            tmax = fmaxf(tmax, v);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (XC) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    return tmax;
+  };
+  // Lazy rescale: the reference max only moves when some row's new max
+  // exceeds it by more than 2^LAZY_LOG2 (always on the first tile).
+  auto rescale = [&](float tmax) {
+    if (__builtin_amdgcn_ballot_w64(tmax > m_run + LAZY_LOG2) != 0) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float corr = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= corr;
+      // one accumulator tile at a time (left to itself the compiler copies
+      // all 128 accumulator registers out at once and spills)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        oacc[c] *= corr;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      m_run = m_new;
     }
   };
-  // Online softmax with a lazy rescale; the accumulators are touched only by
-  // the MFMA inside the inner loop (see the decode kernel).
+  const bool_c<true> Y;
+  const bool_c<false> N;
+
+  // prologue: scores of tile 0
+  wait_dma_newer(min(n_tiles - 1, PBUF - 2));
+  barrier();
+  phase_a(Y, N, N, ring[0], ring[0]);
+  rescale(n_full > 0 ? phase_b(N, Y, N, ring[0], 0) : phase_b(N, Y, Y, ring[0], 0));
+  // iteration t: scores of tile t + 1, weights and values of tile t
+  auto iteration = [&](int t, auto masked) {
+    // tile t + 1 landed for every wave; tile t - 1's slot is free
+    wait_dma_newer(min(n_tiles - 2 - t, PBUF - 3));
+    barrier();
+    if (t + PBUF - 1 < n_tiles)
+      tile_dma(src, (int64_t)(t + PBUF - 1) * STILE, n_blk, ring[(t + PBUF - 1) % PBUF], w, lane, off);
+    const bf16_t* tc = ring[t % PBUF];
+    const bf16_t* tn = ring[(t + 1) % PBUF];
+    phase_a(Y, Y, Y, tn, tc);
+    rescale(phase_b(Y, Y, masked, tc, (int64_t)(t + 1) * STILE));
+  };
+  // two loops, so that the masked body does not share registers with the
+  // main one: tiles below n_full are whole for every row
   int t = 0;
-  while (t < n_tiles) {
-    float z[16], tmax = 0.f;
-    for (; t < n_tiles; ++t) {
-      tmax = scores(t, z);
-      if (__builtin_amdgcn_ballot_w64(tmax > m_run + LAZY_LOG2) != 0) break;
-      accumulate(t, z);
-    }
-    if (t >= n_tiles) break;
-    const float m_new = fmaxf(m_run, tmax);
-    const float corr = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-    l_run *= corr;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) oacc[c] *= corr;
-    m_run = m_new;
-    accumulate(t, z);
-    ++t;
+  for (; t + 1 < n_tiles && t + 1 < n_full; ++t) iteration(t, N);
+  for (; t + 1 < n_tiles; ++t) iteration(t, Y);
+  {
+    const bf16_t* tc = ring[(n_tiles - 1) % PBUF];
+    phase_a(N, Y, Y, tc, tc);
+    phase_b(Y, N, N, tc, 0);
   }
 
   if (!active) return;
