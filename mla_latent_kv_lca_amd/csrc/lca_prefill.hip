@@ -14,6 +14,7 @@
 // registers), runs the online softmax in registers (four lanes per head) and
 // accumulates O for all 512 latent columns (32 MFMA 16x16x32 per tile).
 // Workgroups are issued heaviest (latest tokens) first.
+#include <cfloat>
 #include <type_traits>
 
 #include "lca_stream.h"
@@ -131,6 +132,8 @@ __global__ __launch_bounds__(NT) void prefill_kernel_staged(
 constexpr int PF2_TOK = 4;  // query tokens per workgroup
 constexpr int PBUF = 4;     // LDS ring depth (tiles): 4 x 36 KB + 16 KB exchange = 160 KB
 constexpr int KF_RING = 6;  // score-product fragments in registers (read four products ahead)
+constexpr int VF_AHEAD = 4; // value-product operands read this many products ahead
+constexpr int VF_RING = VF_AHEAD + 1;
 
 template <bool V> using bool_c = std::integral_constant<bool, V>;
 
@@ -229,15 +232,16 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     return make_uint4(lo.x, lo.y, hi.x, hi.y);
   };
 
-  float z[16];   // scores of the current tile (log2 units, masked)
+  float z[16];   // scores of the current tile, unscaled (-inf where masked)
   uint4 pb[2];   // its softmax weights as bf16, entry k-steps 0 and 1
-  f32x16_t S;    // partial scores of the next tile
-  uint4 vf[3];   // value-product operands, read two products ahead
+  f32x16_t S, S2;  // partial scores of the next tile, two product chains (even / odd k-steps)
+  uint4 vf[VF_RING];  // value-product operands, read VF_AHEAD products ahead
 
-  // Phase A: score products of tile tn (QK) and, spread between them, the
-  // softmax of the current tile z (SM): p = 2^(z - m_run), row sum into
-  // l_run, p packed to bf16 into pb. Also reads the first two value operands
-  // of the current tile tc for phase B (PV).
+  // Phase A: score products of tile tn (QK, two independent accumulator
+  // chains, so that no product waits for the previous one) and, spread
+  // between them, the softmax of the current tile z (SM): p = 2^(scale z -
+  // m_run), row sum into l_run, p packed to bf16 into pb. Also reads the
+  // first VF_AHEAD value operands of the current tile tc for phase B (PV).
   auto phase_a = [&](auto qk, auto sm, auto pv, const bf16_t* tn, const bf16_t* tc) {
     constexpr bool QK = decltype(qk)::value, SM = decltype(sm)::value, PV = decltype(pv)::value;
     const float m_ref = m_run;
@@ -245,19 +249,20 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     uint4 kf[KF_RING];
     if constexpr (QK) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) S[r] = 0.f;
+      for (int r = 0; r < 16; ++r) { S[r] = 0.f; S2[r] = 0.f; }
 #pragma unroll
       for (int f = 0; f < 4; ++f) kf[f] = kfrag(tn, f);
     }
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
       if constexpr (QK) {
-        S = mfma32x32x16(kf[ks % KF_RING], qf[ks], S);
+        if (ks & 1) S2 = mfma32x32x16(kf[ks % KF_RING], qf[ks], S2);
+        else S = mfma32x32x16(kf[ks % KF_RING], qf[ks], S);
         if (ks + 4 < 18) kf[(ks + 4) % KF_RING] = kfrag(tn, ks + 4);
       }
       if constexpr (SM) {
         if (ks < 16) {
-          p[ks] = __builtin_amdgcn_exp2f(z[ks] - m_ref);
+          p[ks] = __builtin_amdgcn_exp2f(fmaf(z[ks], scale_log2, -m_ref));
           ps += p[ks];
           if (ks & 1) {
             const int k = ks >> 1;  // packed pair k of 8: entry k-step k / 4, word k % 4
@@ -272,19 +277,19 @@ __global__ __launch_bounds__(256) void prefill_kernel(
           l_run += __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         }
       }
-      if constexpr (PV) {
-        if (ks == 16) vf[0] = vfrag(tc, 0);
-        if (ks == 17) vf[1] = vfrag(tc, 1);
+      if constexpr (PV) {  // the score fragments are all read by slot 13
+        if (ks >= 18 - VF_AHEAD) vf[ks - (18 - VF_AHEAD)] = vfrag(tc, ks - (18 - VF_AHEAD));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   // Phase B: value products of tile tc (PV) and, spread between them, the
-  // exchange of the partial scores S of the next tile (XC): written to LDS,
-  // a barrier, the partner's read back and added (columns 0..287 first, the
-  // same order in both waves), scaled, causally masked (MASKED, entries from
-  // en0), and the row max returned.
+  // exchange of the partial scores of the next tile (XC): this wave's
+  // partial written to LDS, a barrier, the partner's read back and added
+  // (fp32 addition commutes, so both waves of the pair hold the same sums),
+  // causally masked (MASKED, entries from en0), and the row max returned in
+  // log2 units.
   auto phase_b = [&](auto pv, auto xc, auto masked, const bf16_t* tc, int64_t en0) -> float {
     constexpr bool PV = decltype(pv)::value, XC = decltype(xc)::value, MASKED = decltype(masked)::value;
     f32x4_t sp[4];
@@ -293,13 +298,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     for (int j = 0; j < 16; ++j) {
       if constexpr (PV) {
         const int kap = j >> 3, ct = j & 7;
-        oacc[ct] = mfma32x32x16(vf[j % 3], pb[kap], oacc[ct]);
-        if (j + 2 < 16) vf[(j + 2) % 3] = vfrag(tc, j + 2);
+        oacc[ct] = mfma32x32x16(vf[j % VF_RING], pb[kap], oacc[ct]);
+        if (j + VF_AHEAD < 16) vf[(j + VF_AHEAD) % VF_RING] = vfrag(tc, j + VF_AHEAD);
       }
       if constexpr (XC) {
-        if (j >= 2 && j < 6) {
+        if (j >= 2 && j < 6) {  // this wave's partial: the two chains added
           const int r4 = j - 2;
-          sx[w][r4][lane] = f32x4_t{S[4 * r4], S[4 * r4 + 1], S[4 * r4 + 2], S[4 * r4 + 3]};
+          sx[w][r4][lane] = f32x4_t{S[4 * r4] + S2[4 * r4], S[4 * r4 + 1] + S2[4 * r4 + 1],
+                                    S[4 * r4 + 2] + S2[4 * r4 + 2], S[4 * r4 + 3] + S2[4 * r4 + 3]};
         }
         if (j == 7) barrier();  // both partials of the pair are in LDS
         if (j >= 8 && j < 12) sp[j - 8] = sx[w ^ 1][j - 8][lane];
@@ -308,7 +314,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 4 * r4 + i;
-            float v = (S[r] + sp[r4][i]) * scale_log2;
+            float v = (S[r] + S2[r]) + sp[r4][i];
             if constexpr (MASKED) {
               if (en0 + 8 * (r >> 2) + 4 * h32 + (r & 3) >= n_mine) v = -INFINITY;
             }
@@ -323,7 +329,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
       tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
-    return tmax;
+    return tmax * scale_log2;  // scale > 0, so the max commutes with it
   };
   // Lazy rescale: the reference max only moves when some row's new max
   // exceeds it by more than 2^LAZY_LOG2 (always on the first tile).
@@ -431,14 +437,20 @@ hipError_t launch_prefill(const void* q, int q_dtype, int64_t q_tok_stride, int6
   const bool fast = packed_rows_pf(raw) && (m == 0 || (packed_rows_pf(reps) && reps.c_tok_stride == raw.c_tok_stride)) &&
                     raw.c_tok_stride * 2 * STILE < ((int64_t)1 << 31);
   if (fast) {
+    // The fast kernel scales unscaled scores inside one fma before exp2, and
+    // masks with -inf; a scale of exactly 0 would turn -inf * 0 into NaN.
+    // The smallest normal float scale gives the same weights (every finite
+    // logit times it rounds to an exponent of 0, i.e. the uniform softmax
+    // that sm_scale = 0 means) and keeps -inf masked.
+    const float sl2_fast = sl2 > 0.f ? sl2 : FLT_MIN;
     DmaSrc src;
     src.rep = m > 0 ? static_cast<const char*>(reps.c) : nullptr;
     src.raw = static_cast<const char*>(raw.c) + raw_begin * raw.c_tok_stride * 2;
     src.tok = raw.c_tok_stride * 2;
     src.m = m;
     dim3 grid((unsigned)((C + PF2_TOK - 1) / PF2_TOK), (unsigned)(H / HB));
-    if (q_dtype == LCA_BF16) launch_pf2<bf16_t>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, src, m, raw_begin, sl2, o_latent, lse);
-    else launch_pf2<float>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, src, m, raw_begin, sl2, o_latent, lse);
+    if (q_dtype == LCA_BF16) launch_pf2<bf16_t>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, src, m, raw_begin, sl2_fast, o_latent, lse);
+    else launch_pf2<float>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, src, m, raw_begin, sl2_fast, o_latent, lse);
     return hipGetLastError();
   }
   const Seg rs = to_seg(reps), ws = to_seg(raw);

@@ -113,6 +113,7 @@ __device__ __forceinline__ void tile_dma(const DmaSrc& src, int64_t e0, int64_t 
     for (int i = 0; i < DMA_PER_WAVE; ++i) dma16(b0 + off[i], base + 1024u * (w + SNW * i));
   } else {
     const int valid = (int)min((int64_t)STILE, e_end - e0);
+#pragma unroll 1  // rare boundary tiles: keep the per-lane row arithmetic small
     for (int i = 0; i < DMA_PER_WAVE; ++i) {
       int row, col;
       slot_rowcol(w, i, lane, row, col);
