@@ -60,7 +60,7 @@ extern "C" {
 typedef enum {
   LCA_OK = 0,
   LCA_ERR_INVALID_ARG = -1, /* null pointer, bad size, misalignment, out-of-range rows */
-  LCA_ERR_UNSUPPORTED = -2, /* a size the kernels are not built for (e.g. H % 16 != 0) */
+  LCA_ERR_UNSUPPORTED = -2, /* a size the kernels are not built for (e.g. H = 24) */
   LCA_ERR_WORKSPACE = -3,   /* workspace pointer null or smaller than required */
   LCA_ERR_HIP = -4          /* the HIP runtime refused a launch */
 } lca_status_t;
@@ -195,7 +195,10 @@ size_t mla_latent_attn_decode_workspace_size(int32_t B, int32_t H, int64_t max_e
  * then standard attention).
  *
  *  q        absorbed queries [B, H, 576] (head h of sequence b at
- *           q + b*q_seq_stride + h*576), H a multiple of 16.
+ *           q + b*q_seq_stride + h*576). H is a multiple of 16, or 1, 2,
+ *           4 or 8 (one head group of grouped-query attention: one latent
+ *           cache per key-value head, attended by its Hg query heads, run
+ *           as B * n_kv sequences of Hg heads each).
  *  reps     entries [0, m) of each sequence are representative rows 0..m-1.
  *  raw      entries [m, m + raw_end - raw_begin) are cache rows
  *           [raw_begin, raw_end). reps->dtype must equal raw->dtype.
@@ -290,7 +293,8 @@ int mla_latent_attn_decode_up_noalloc(const void* q, int32_t q_dtype, int64_t q_
  * so the groups are frozen per chunk as described below and the window is
  * causal, which reduces to exact causal MLA when no group is condensed).
  * Query i of the chunk sits at absolute position t = chunk_start + i (its
- * absorbed query at q + i*q_tok_stride + h*576, H a multiple of 16) and
+ * absorbed query at q + i*q_tok_stride + h*576; H a multiple of 16, or 1,
+ * 2, 4 or 8 as in mla_latent_attn_decode) and
  * attends to representatives [0, m) (all visible) and raw cache rows
  * [raw_begin, t] (causal, inclusive). Requires raw_begin <= chunk_start.
  * The groups a chunk sees are frozen before its window: with window w and

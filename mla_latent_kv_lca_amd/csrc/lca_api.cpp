@@ -184,9 +184,9 @@ int lca_condense_paged(const lca_paged_t* cache, int32_t B, int32_t g, const int
 }
 
 size_t mla_latent_attn_decode_workspace_size(int32_t B, int32_t H, int64_t max_entries) {
-  if (B < 1 || H < 16 || H % 16 != 0 || max_entries < 1) return 0;
-  const lca::DecodeSplit sp = lca::decode_split(B, H / 16, max_entries);
-  return lca::decode_workspace_bytes(B, H / 16, sp.S);
+  if (B < 1 || !lca::heads_supported(H) || max_entries < 1) return 0;
+  const lca::DecodeSplit sp = lca::decode_split(B, lca::head_blocks(H), max_entries);
+  return lca::decode_workspace_bytes(B, lca::head_blocks(H), sp.S);
 }
 
 int mla_latent_attn_decode(const void* q, int32_t q_dtype, int64_t q_seq_stride, int32_t B,
@@ -199,7 +199,8 @@ int mla_latent_attn_decode(const void* q, int32_t q_dtype, int64_t q_seq_stride,
   if (!valid_dtype(q_dtype)) return fail(LCA_ERR_INVALID_ARG, "q_dtype %d is not LCA_BF16/LCA_F32", q_dtype);
   if (!mult8(q_seq_stride) || q_seq_stride < 0) return fail(LCA_ERR_INVALID_ARG, "q_seq_stride must be a non-negative multiple of 8");
   if (B < 1 || B > 65535) return fail(LCA_ERR_INVALID_ARG, "B must be in [1, 65535]");
-  if (H < 16 || H % 16 != 0 || H / 16 > 65535) return fail(LCA_ERR_UNSUPPORTED, "H = %d: the head count must be a positive multiple of 16", H);
+  if (!lca::heads_supported(H) || lca::head_blocks(H) > 65535)
+    return fail(LCA_ERR_UNSUPPORTED, "H = %d: the head count must be a multiple of 16 or divide 16", H);
   if (m < 0 || raw_begin < 0 || raw_end < raw_begin) return fail(LCA_ERR_INVALID_ARG, "need m >= 0 and 0 <= raw_begin <= raw_end");
   const int64_t n = m + (raw_end - raw_begin);
   if (n < 1) return fail(LCA_ERR_INVALID_ARG, "nothing to attend: m + raw_end - raw_begin must be >= 1");
@@ -209,8 +210,8 @@ int mla_latent_attn_decode(const void* q, int32_t q_dtype, int64_t q_seq_stride,
     return fail(LCA_ERR_UNSUPPORTED, "reps and raw must share one dtype");
   if ((rc = check_scale(sm_scale)) != LCA_OK) return rc;
   if (o_latent == nullptr || !aligned16(o_latent)) return fail(LCA_ERR_INVALID_ARG, "o_latent must be a non-null 16-byte aligned pointer");
-  const lca::DecodeSplit sp = lca::decode_split(B, H / 16, n);
-  const size_t need = lca::decode_workspace_bytes(B, H / 16, sp.S);
+  const lca::DecodeSplit sp = lca::decode_split(B, lca::head_blocks(H), n);
+  const size_t need = lca::decode_workspace_bytes(B, lca::head_blocks(H), sp.S);
   if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need))
     return fail(LCA_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
   const lca_latent_t none = {nullptr, nullptr, 0, 0, 0, 0, m > 0 ? reps->dtype : raw->dtype};
@@ -232,7 +233,8 @@ int mla_latent_attn_decode_paged(const void* q, int32_t q_dtype, int64_t q_seq_s
   if (!valid_dtype(q_dtype)) return fail(LCA_ERR_INVALID_ARG, "q_dtype %d is not LCA_BF16/LCA_F32", q_dtype);
   if (!mult8(q_seq_stride) || q_seq_stride < 0) return fail(LCA_ERR_INVALID_ARG, "q_seq_stride must be a non-negative multiple of 8");
   if (B < 1 || B > 65535) return fail(LCA_ERR_INVALID_ARG, "B must be in [1, 65535]");
-  if (H < 16 || H % 16 != 0 || H / 16 > 65535) return fail(LCA_ERR_UNSUPPORTED, "H = %d: the head count must be a positive multiple of 16", H);
+  if (!lca::heads_supported(H) || lca::head_blocks(H) > 65535)
+    return fail(LCA_ERR_UNSUPPORTED, "H = %d: the head count must be a multiple of 16 or divide 16", H);
   if (cache == nullptr || cache->pages == nullptr || !aligned16(cache->pages))
     return fail(LCA_ERR_INVALID_ARG, "cache pages must be a non-null 16-byte aligned pointer");
   if (cache->row_stride < LCA_D_ROW || !mult8(cache->row_stride))
@@ -253,8 +255,8 @@ int mla_latent_attn_decode_paged(const void* q, int32_t q_dtype, int64_t q_seq_s
   if (cache->row_stride * 2 * 16 >= ((int64_t)1 << 31)) return fail(LCA_ERR_UNSUPPORTED, "row stride too large");
   if ((rc = check_scale(sm_scale)) != LCA_OK) return rc;
   if (o_latent == nullptr || !aligned16(o_latent)) return fail(LCA_ERR_INVALID_ARG, "o_latent must be a non-null 16-byte aligned pointer");
-  const lca::DecodeSplit sp = lca::decode_split(B, H / 16, max_entries);
-  const size_t need = lca::decode_workspace_bytes(B, H / 16, sp.S);
+  const lca::DecodeSplit sp = lca::decode_split(B, lca::head_blocks(H), max_entries);
+  const size_t need = lca::decode_workspace_bytes(B, lca::head_blocks(H), sp.S);
   if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need))
     return fail(LCA_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
   return hip_status(lca::launch_decode_paged(q, q_dtype, q_seq_stride, B, H, *reps, seq_m, *cache, seq_raw_begin,
@@ -276,7 +278,8 @@ int check_decode_up(const void* q, int32_t q_dtype, int64_t q_seq_stride, int32_
   if (!valid_dtype(q_dtype)) return fail(LCA_ERR_INVALID_ARG, "q_dtype %d is not LCA_BF16/LCA_F32", q_dtype);
   if (!mult8(q_seq_stride) || q_seq_stride < 0) return fail(LCA_ERR_INVALID_ARG, "q_seq_stride must be a non-negative multiple of 8");
   if (B < 1 || B > 65535) return fail(LCA_ERR_INVALID_ARG, "B must be in [1, 65535]");
-  if (H < 16 || H % 16 != 0 || H / 16 > 65535) return fail(LCA_ERR_UNSUPPORTED, "H = %d: the head count must be a positive multiple of 16", H);
+  if (!lca::heads_supported(H) || lca::head_blocks(H) > 65535)
+    return fail(LCA_ERR_UNSUPPORTED, "H = %d: the head count must be a multiple of 16 or divide 16", H);
   if (m < 0 || raw_begin < 0 || raw_end < raw_begin) return fail(LCA_ERR_INVALID_ARG, "need m >= 0 and 0 <= raw_begin <= raw_end");
   const int64_t n = m + (raw_end - raw_begin);
   if (n < 1) return fail(LCA_ERR_INVALID_ARG, "nothing to attend: m + raw_end - raw_begin must be >= 1");
@@ -289,8 +292,8 @@ int check_decode_up(const void* q, int32_t q_dtype, int64_t q_seq_stride, int32_
   if (!valid_dtype(w_dtype) || !valid_dtype(out_dtype)) return fail(LCA_ERR_INVALID_ARG, "w_dtype and out_dtype must be LCA_BF16 or LCA_F32");
   if (w_uv == nullptr || !aligned16(w_uv) || out == nullptr || !aligned16(out))
     return fail(LCA_ERR_INVALID_ARG, "w_uv and out must be non-null 16-byte aligned pointers");
-  const lca::DecodeSplit sp = lca::decode_split(B, H / 16, n);
-  *need = lca::decode_workspace_bytes(B, H / 16, sp.S);
+  const lca::DecodeSplit sp = lca::decode_split(B, lca::head_blocks(H), n);
+  *need = lca::decode_workspace_bytes(B, lca::head_blocks(H), sp.S);
   return LCA_OK;
 }
 }  // namespace
@@ -355,7 +358,8 @@ int mla_latent_attn_prefill_chunk(const void* q, int32_t q_dtype, int64_t q_tok_
   if (!valid_dtype(q_dtype)) return fail(LCA_ERR_INVALID_ARG, "q_dtype %d is not LCA_BF16/LCA_F32", q_dtype);
   if (!mult8(q_tok_stride) || q_tok_stride < 0) return fail(LCA_ERR_INVALID_ARG, "q_tok_stride must be a non-negative multiple of 8");
   if (C < 1) return fail(LCA_ERR_INVALID_ARG, "C must be >= 1");
-  if (H < 16 || H % 16 != 0 || H / 16 > 65535) return fail(LCA_ERR_UNSUPPORTED, "H = %d: the head count must be a positive multiple of 16", H);
+  if (!lca::heads_supported(H) || lca::head_blocks(H) > 65535)
+    return fail(LCA_ERR_UNSUPPORTED, "H = %d: the head count must be a multiple of 16 or divide 16", H);
   if (m < 0 || raw_begin < 0 || chunk_start < raw_begin)
     return fail(LCA_ERR_INVALID_ARG, "need m >= 0 and 0 <= raw_begin <= chunk_start");
   if (m > 0 && (rc = check_latent(reps, "reps", true, true)) != LCA_OK) return rc;

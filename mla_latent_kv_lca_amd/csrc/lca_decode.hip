@@ -206,13 +206,14 @@ __device__ __forceinline__ void decode_body(bf16_t (&ring)[DNW][WSLOT][WT_ELEMS]
   // flight (requested behind the tiles, they would only arrive with them).
   uint4 qa[18];
   const TQ* qh = q + (int64_t)b * q_seq + (int64_t)(hg * HB) * D_ROW;
+  const int last_row = min(HB, H - hg * HB) - 1;  // rows past it repeat it (never stored)
   if constexpr (sizeof(TQ) == 2) {
     if (n_mine > 0) issue(0);
     const uint32_t qbase = lds_off(&ring[w][1][0]);
 #pragma unroll
     for (int i = 0; i < WT_DMA; ++i) {
       const int P = 64 * i + lane, row = P / (D_ROW / 8);
-      dma16(qh + row * D_ROW + 8 * ((P - row * (D_ROW / 8)) ^ swz(row)), qbase + 1024u * i);
+      dma16(qh + min(row, last_row) * D_ROW + 8 * ((P - row * (D_ROW / 8)) ^ swz(row)), qbase + 1024u * i);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     const bf16_t* qt = &ring[w][1][0];
@@ -222,7 +223,7 @@ __device__ __forceinline__ void decode_body(bf16_t (&ring)[DNW][WSLOT][WT_ELEMS]
     if (n_mine > 1) issue(1);
   } else {
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) qa[ks] = load8_bf16(qh + col * D_ROW + 32 * ks + 8 * kg);
+    for (int ks = 0; ks < 18; ++ks) qa[ks] = load8_bf16(qh + min(col, last_row) * D_ROW + 32 * ks + 8 * kg);
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) retire(qa[ks]);
 #pragma unroll
@@ -355,6 +356,7 @@ __device__ __forceinline__ void decode_body(bf16_t (&ring)[DNW][WSLOT][WT_ELEMS]
   }
   const int head = hg * HB + col;
   if (S == 1) {
+    if (head >= H) return;
     const float inv = 1.0f / Lsum;
     float* dst = o_final + ((int64_t)b * H + head) * D_C + d0;
 #pragma unroll
@@ -437,8 +439,9 @@ __global__ __launch_bounds__(NT) void decode_kernel_staged(
   const int64_t e_end = min(n_entries, e_begin + (int64_t)per_tiles * TILE);
   const int n_tiles = e_end > e_begin ? (int)((e_end - e_begin + TILE - 1) / TILE) : 0;
 
-  // this wave's query fragments: head col of the block, its k columns
-  const TQ* qh = q + (int64_t)b * q_seq + (int64_t)(hg * HB + col) * D_ROW;
+  // this wave's query fragments: head col of the block (rows past the last
+  // head repeat it and are never stored), its k columns
+  const TQ* qh = q + (int64_t)b * q_seq + (int64_t)(hg * HB + min(col, H - 1 - hg * HB)) * D_ROW;
   uint4 qa[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) qa[ks] = load8_bf16(qh + 128 * w + 32 * ks + 8 * kg);
@@ -499,6 +502,7 @@ __global__ __launch_bounds__(NT) void decode_kernel_staged(
   const int head = hg * HB + col;
   const int dbase = 128 * w + 32 * kg;
   if (S == 1) {
+    if (head >= H) return;
     const float inv = 1.0f / l_run;
     float* dst = o_final + ((int64_t)b * H + head) * D_C + dbase;
 #pragma unroll
@@ -539,7 +543,7 @@ __global__ __launch_bounds__(256) void merge_small_kernel(const float* __restric
   const int c4 = (int)(gid % (D_C / 4));
   const int64_t bh = gid / (D_C / 4);
   const int head = (int)(bh % H), b = (int)(bh / H);
-  const int HG = H / HB, hg = head / HB, hh = head % HB;
+  const int HG = head_blocks(H), hg = head / HB, hh = head % HB;
   float M, L;
   const float4 v = merge_cols4(part_o, part_ml, S, ((int64_t)b * HG + hg) * S, hh, c4, M, L);
   reinterpret_cast<float4*>(o + ((int64_t)b * H + head) * D_C)[c4] = v;
@@ -559,7 +563,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
                                                     int H, float* __restrict__ o,
                                                     float* __restrict__ lse) {
   const int dchunk = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
-  const int HG = H / HB, hg = head / HB, hh = head % HB;
+  const int HG = head_blocks(H), hg = head / HB, hh = head % HB;
   const int t = threadIdx.x, ph = t >> 3, c4 = t & 7;
   const int64_t slot0 = ((int64_t)b * HG + hg) * S;  // slot(s) = (slot0 + s) * HB + hh
   const int d = 32 * dchunk + 4 * c4;
@@ -658,7 +662,7 @@ static hipError_t decode_attention(const void* q, int q_dtype, int64_t q_seq_str
                                    int64_t raw_begin, int64_t raw_end, float sm_scale,
                                    float* o_latent, float* lse, const DecodeSplit& sp, float* po,
                                    float* pml, hipStream_t stream) {
-  const int HG = H / HB;
+  const int HG = head_blocks(H);
   const int64_t n = m + (raw_end - raw_begin);
   const float sl2 = sm_scale * 1.44269504088896340736f;
   dim3 grid((unsigned)sp.S, (unsigned)B, (unsigned)HG);
@@ -723,9 +727,9 @@ hipError_t launch_decode(const void* q, int q_dtype, int64_t q_seq_stride, int B
                          const lca_latent_t& reps, int64_t m, const lca_latent_t& raw,
                          int64_t raw_begin, int64_t raw_end, float sm_scale, float* o_latent,
                          float* lse, void* workspace, hipStream_t stream) {
-  const DecodeSplit sp = decode_split(B, H / HB, m + (raw_end - raw_begin));
+  const DecodeSplit sp = decode_split(B, head_blocks(H), m + (raw_end - raw_begin));
   float *po, *pml;
-  split_buffers(workspace, B, H / HB, sp, po, pml);
+  split_buffers(workspace, B, head_blocks(H), sp, po, pml);
   hipError_t err = decode_attention(q, q_dtype, q_seq_stride, B, H, reps, m, raw, raw_begin, raw_end,
                                     sm_scale, o_latent, lse, sp, po, pml, stream);
   if (err != hipSuccess || sp.S == 1) return err;
@@ -738,7 +742,7 @@ hipError_t launch_decode_paged(const void* q, int q_dtype, int64_t q_seq_stride,
                                const int32_t* seq_raw_begin, const int32_t* seq_raw_end,
                                int64_t max_entries, float sm_scale, float* o_latent, float* lse,
                                void* workspace, hipStream_t stream) {
-  const int HG = H / HB;
+  const int HG = head_blocks(H);
   const DecodeSplit sp = decode_split(B, HG, max_entries);
   float *po, *pml;
   split_buffers(workspace, B, HG, sp, po, pml);
@@ -798,9 +802,9 @@ hipError_t launch_decode_up(const void* q, int q_dtype, int64_t q_seq_stride, in
                             int64_t raw_begin, int64_t raw_end, float sm_scale, float* o_latent,
                             float* lse, const void* w_uv, int w_dtype, void* out, int out_dtype,
                             void* workspace, hipStream_t stream) {
-  const DecodeSplit sp = decode_split(B, H / HB, m + (raw_end - raw_begin));
+  const DecodeSplit sp = decode_split(B, head_blocks(H), m + (raw_end - raw_begin));
   float *po, *pml;
-  split_buffers(workspace, B, H / HB, sp, po, pml);
+  split_buffers(workspace, B, head_blocks(H), sp, po, pml);
   hipError_t err = decode_attention(q, q_dtype, q_seq_stride, B, H, reps, m, raw, raw_begin, raw_end,
                                     sm_scale, o_latent, lse, sp, po, pml, stream);
   if (err != hipSuccess) return err;

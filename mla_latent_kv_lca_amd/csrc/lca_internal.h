@@ -8,6 +8,14 @@
 
 namespace lca {
 
+// Head counts: the attention kernels work on blocks of 16 heads (one side of
+// a 16-row matrix tile). H may be a multiple of 16, or a divisor of 16 (a
+// grouped-query attention group of 1, 2, 4 or 8 heads, held in one block
+// whose rows past H repeat a valid query and are never stored).
+constexpr int HEAD_BLOCK = 16;
+__host__ __device__ inline bool heads_supported(int H) { return H >= 1 && (H % HEAD_BLOCK == 0 || HEAD_BLOCK % H == 0); }
+__host__ __device__ inline int head_blocks(int H) { return (H + HEAD_BLOCK - 1) / HEAD_BLOCK; }
+
 struct Seg {  // one latent tensor segment, strides in elements
   const void* c;
   const void* kr;

@@ -21,12 +21,11 @@
 
 namespace lca {
 
-constexpr int PF_TOK = 4;  // query tokens per workgroup (one per wave)
 
 // Register-staged variant for strided or f32 rows, one token (16 rows) per wave.
 template <typename TQ, typename TC, typename TO>
 __global__ __launch_bounds__(NT) void prefill_kernel_staged(
-    const TQ* __restrict__ q, int64_t q_tok, int64_t chunk_start, int C, int H, Seg reps,
+    const TQ* __restrict__ q, int64_t q_tok, int64_t chunk_start, int C, int H, int lhb, Seg reps,
     int64_t m, Seg raw, int64_t raw_begin, float scale_log2, TO* __restrict__ o,
     float* __restrict__ lse) {
   __shared__ __align__(16) bf16_t tile[TILE * LDS_ROW];
@@ -36,9 +35,12 @@ __global__ __launch_bounds__(NT) void prefill_kernel_staged(
   const int nblk = gridDim.x;
   const int blk = nblk - 1 - (int)blockIdx.x;  // heavy blocks first
   const int hg = blockIdx.y;
-  const int i_tok = blk * PF_TOK + w;            // chunk row of this wave
+  // query row R = 16 w + col is (token R >> lhb, head R % Hb), Hb = 2^lhb =
+  // min(H, 16) heads per block: 64 / Hb tokens per workgroup
+  const int n_tok = 64 >> lhb, hmask = (1 << lhb) - 1;
+  const int i_tok = blk * n_tok + ((16 * w + col) >> lhb);  // chunk row of this lane's query row
   const bool active = i_tok < C;
-  const int i_last = min(blk * PF_TOK + PF_TOK, C) - 1;
+  const int i_last = min(blk * n_tok + n_tok, C) - 1;
 
   EntrySrc<TC> src;
   src.init(reps, raw, 0, m, raw_begin);
@@ -47,7 +49,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel_staged(
   const int64_t n_blk = m + (chunk_start + i_last - raw_begin + 1);
   const int n_tiles = (int)((n_blk + TILE - 1) / TILE);
 
-  const TQ* qh = q + (int64_t)(active ? i_tok : i_last) * q_tok + (int64_t)(hg * HB + col) * D_ROW;
+  const TQ* qh = q + (int64_t)(active ? i_tok : i_last) * q_tok + (int64_t)(hg * HB + (col & hmask)) * D_ROW;
   uint4 qa[18];
 #pragma unroll
   for (int ks = 0; ks < 18; ++ks) qa[ks] = load8_bf16(qh + 32 * ks + 8 * kg);
@@ -89,8 +91,8 @@ __global__ __launch_bounds__(NT) void prefill_kernel_staged(
   }
 
   if (!active) return;
-  // oacc[8 slab + c][r] = O[head col][128 slab + 32 kg + 8 r + c]
-  const int head = hg * HB + col;
+  // oacc[8 slab + c][r] = O[query row col][128 slab + 32 kg + 8 r + c]
+  const int head = hg * HB + (col & hmask);
   const float inv = 1.0f / l_run;
   TO* dst = o + ((int64_t)i_tok * H + head) * D_C + 32 * kg;
 #pragma unroll
@@ -108,8 +110,9 @@ __global__ __launch_bounds__(NT) void prefill_kernel_staged(
 }
 
 // prefill_kernel: the fast path for packed bf16 rows. Workgroup = 4
-// wavefronts = 2 pairs; pair p holds 2 query tokens x 16 heads = 32 query
-// rows, so every LDS fragment feeds a 32x32x16 MFMA. Entry tiles of 32 rows
+// wavefronts = 2 pairs; pair p holds 32 query rows (2 query tokens x 16
+// heads; with Hb < 16 heads, as in grouped-query attention, 32 / Hb tokens x
+// Hb heads), so every LDS fragment feeds a 32x32x16 MFMA. Entry tiles of 32 rows
 // stream HBM -> LDS by direct loads into a 4-slot ring (two tiles in
 // flight). Within a pair, wave k
 //   forms the partial S^T = K Q^T over query columns [288 k, 288 k + 288)
@@ -129,7 +132,6 @@ __global__ __launch_bounds__(NT) void prefill_kernel_staged(
 // B). Scheduling fences keep every slot's few vector instructions next to
 // its matrix product. Causal masking is compiled only into the (at most two)
 // tiles that cross the diagonal of the workgroup's rows.
-constexpr int PF2_TOK = 4;  // query tokens per workgroup
 constexpr int PBUF = 4;     // LDS ring depth (tiles): 4 x 36 KB + 16 KB exchange = 160 KB
 constexpr int KF_RING = 6;  // score-product fragments in registers (read four products ahead)
 constexpr int VF_AHEAD = 4; // value-product operands read this many products ahead
@@ -139,7 +141,7 @@ template <bool V> using bool_c = std::integral_constant<bool, V>;
 
 template <typename TQ, typename TO>
 __global__ __launch_bounds__(256) void prefill_kernel(
-    const TQ* __restrict__ q, int64_t q_tok, int64_t chunk_start, int C, int H, DmaSrc src,
+    const TQ* __restrict__ q, int64_t q_tok, int64_t chunk_start, int C, int H, int lhb, DmaSrc src,
     int64_t m, int64_t raw_begin, float scale_log2, TO* __restrict__ o, float* __restrict__ lse) {
   __shared__ __align__(16) bf16_t ring[PBUF][STILE_ELEMS];
   __shared__ __align__(16) f32x4_t sx[4][4][64];  // partial scores [wave][r / 4][lane]
@@ -150,11 +152,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   const int h32 = lane >> 5, r32 = lane & 31;
   const int blk = (int)gridDim.x - 1 - (int)blockIdx.x;  // heavy workgroups first
   const int hg = blockIdx.y;
-  const int tok0 = blk * PF2_TOK;
-  const int i_tok = tok0 + 2 * pr + (r32 >> 4);  // chunk row of this lane's query row
+  // query row R = 32 pr + r32 of the workgroup is (token R >> lhb, head
+  // R % Hb) with Hb = 2^lhb = min(H, 16) heads per block: 64 / Hb tokens
+  const int n_tok = 64 >> lhb, hmask = (1 << lhb) - 1;
+  const int tok0 = blk * n_tok;
+  const int i_tok = tok0 + ((32 * pr + r32) >> lhb);  // chunk row of this lane's query row
   const bool active = i_tok < C;
   const int i_ld = active ? i_tok : C - 1;
-  const int i_last = min(tok0 + PF2_TOK, C) - 1;
+  const int i_last = min(tok0 + n_tok, C) - 1;
   // entries visible to chunk row i: m + (chunk_start + i - raw_begin + 1)
   const int64_t vis0 = m + (chunk_start - raw_begin + 1);
   const int64_t n_blk = vis0 + i_last, n_min = vis0 + tok0, n_mine = vis0 + i_ld;
@@ -172,8 +177,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   for (int t = 0; t < PBUF - 1; ++t)
     if (t < n_tiles) tile_dma(src, (int64_t)t * STILE, n_blk, ring[t], w, lane, off);
 
-  // Q^T operand: query row (token i_ld, head hg*16 + r32%16), k = 288 kh + 16 ks + 8 h32 ..
-  const TQ* qh = q + (int64_t)i_ld * q_tok + (int64_t)(hg * HB + (r32 & 15)) * D_ROW + 288 * kh + 8 * h32;
+  // Q^T operand: query row (token i_ld, head hg*16 + r32 % Hb), k = 288 kh + 16 ks + 8 h32 ..
+  const TQ* qh = q + (int64_t)i_ld * q_tok + (int64_t)(hg * HB + (r32 & hmask)) * D_ROW + 288 * kh + 8 * h32;
   uint4 qf[18];
 #pragma unroll
   for (int ks = 0; ks < 18; ++ks) qf[ks] = load8_bf16(qh + 16 * ks);
@@ -381,7 +386,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 
   if (!active) return;
   // oacc[ct][r] = O[query row r32][256 kh + 32 ct + 8 (r / 4) + 4 h32 + r % 4]
-  const int head = hg * HB + (r32 & 15);
+  const int head = hg * HB + (r32 & hmask);
   const float inv = 1.0f / l_run;
   TO* dst = o + ((int64_t)i_tok * H + head) * D_C + 256 * kh + 4 * h32;
 #pragma unroll
@@ -399,18 +404,18 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 
 template <typename TQ, typename TC, typename TO>
 static void launch_pf_t(dim3 grid, hipStream_t st, const void* q, int64_t q_tok, int64_t cs,
-                        int C, int H, Seg reps, int64_t m, Seg raw, int64_t rb, float sl2, void* o,
+                        int C, int H, int lhb, Seg reps, int64_t m, Seg raw, int64_t rb, float sl2, void* o,
                         float* lse) {
   hipLaunchKernelGGL((prefill_kernel_staged<TQ, TC, TO>), grid, dim3(NT), 0, st, (const TQ*)q, q_tok, cs,
-                     C, H, reps, m, raw, rb, sl2, (TO*)o, lse);
+                     C, H, lhb, reps, m, raw, rb, sl2, (TO*)o, lse);
 }
 
 template <typename TQ, typename TC>
 static void launch_pf_o(int o_dtype, dim3 grid, hipStream_t st, const void* q, int64_t q_tok,
-                        int64_t cs, int C, int H, Seg reps, int64_t m, Seg raw, int64_t rb,
+                        int64_t cs, int C, int H, int lhb, Seg reps, int64_t m, Seg raw, int64_t rb,
                         float sl2, void* o, float* lse) {
-  if (o_dtype == LCA_BF16) launch_pf_t<TQ, TC, bf16_t>(grid, st, q, q_tok, cs, C, H, reps, m, raw, rb, sl2, o, lse);
-  else launch_pf_t<TQ, TC, float>(grid, st, q, q_tok, cs, C, H, reps, m, raw, rb, sl2, o, lse);
+  if (o_dtype == LCA_BF16) launch_pf_t<TQ, TC, bf16_t>(grid, st, q, q_tok, cs, C, H, lhb, reps, m, raw, rb, sl2, o, lse);
+  else launch_pf_t<TQ, TC, float>(grid, st, q, q_tok, cs, C, H, lhb, reps, m, raw, rb, sl2, o, lse);
 }
 
 static bool packed_rows_pf(const lca_latent_t& t) {
@@ -421,12 +426,12 @@ static bool packed_rows_pf(const lca_latent_t& t) {
 
 template <typename TQ>
 static void launch_pf2(int o_dtype, dim3 grid, hipStream_t st, const void* q, int64_t q_tok,
-                       int64_t cs, int C, int H, const DmaSrc& src, int64_t m, int64_t rb, float sl2,
+                       int64_t cs, int C, int H, int lhb, const DmaSrc& src, int64_t m, int64_t rb, float sl2,
                        void* o, float* lse) {
   if (o_dtype == LCA_BF16)
-    hipLaunchKernelGGL((prefill_kernel<TQ, bf16_t>), grid, dim3(256), 0, st, (const TQ*)q, q_tok, cs, C, H, src, m, rb, sl2, (bf16_t*)o, lse);
+    hipLaunchKernelGGL((prefill_kernel<TQ, bf16_t>), grid, dim3(256), 0, st, (const TQ*)q, q_tok, cs, C, H, lhb, src, m, rb, sl2, (bf16_t*)o, lse);
   else
-    hipLaunchKernelGGL((prefill_kernel<TQ, float>), grid, dim3(256), 0, st, (const TQ*)q, q_tok, cs, C, H, src, m, rb, sl2, (float*)o, lse);
+    hipLaunchKernelGGL((prefill_kernel<TQ, float>), grid, dim3(256), 0, st, (const TQ*)q, q_tok, cs, C, H, lhb, src, m, rb, sl2, (float*)o, lse);
 }
 
 hipError_t launch_prefill(const void* q, int q_dtype, int64_t q_tok_stride, int64_t chunk_start,
@@ -434,6 +439,11 @@ hipError_t launch_prefill(const void* q, int q_dtype, int64_t q_tok_stride, int6
                           const lca_latent_t& raw, int64_t raw_begin, float sm_scale,
                           void* o_latent, int o_dtype, float* lse, hipStream_t stream) {
   const float sl2 = sm_scale * 1.44269504088896340736f;
+  // heads per 16-row block and query tokens per workgroup (64 query rows)
+  const int hb = H < HB ? H : HB;
+  int lhb = 0;
+  while ((1 << lhb) < hb) ++lhb;
+  const int n_tok = 64 >> lhb;
   const bool fast = packed_rows_pf(raw) && (m == 0 || (packed_rows_pf(reps) && reps.c_tok_stride == raw.c_tok_stride)) &&
                     raw.c_tok_stride * 2 * STILE < ((int64_t)1 << 31);
   if (fast) {
@@ -448,20 +458,20 @@ hipError_t launch_prefill(const void* q, int q_dtype, int64_t q_tok_stride, int6
     src.raw = static_cast<const char*>(raw.c) + raw_begin * raw.c_tok_stride * 2;
     src.tok = raw.c_tok_stride * 2;
     src.m = m;
-    dim3 grid((unsigned)((C + PF2_TOK - 1) / PF2_TOK), (unsigned)(H / HB));
-    if (q_dtype == LCA_BF16) launch_pf2<bf16_t>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, src, m, raw_begin, sl2_fast, o_latent, lse);
-    else launch_pf2<float>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, src, m, raw_begin, sl2_fast, o_latent, lse);
+    dim3 grid((unsigned)((C + n_tok - 1) / n_tok), (unsigned)head_blocks(H));
+    if (q_dtype == LCA_BF16) launch_pf2<bf16_t>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, lhb, src, m, raw_begin, sl2_fast, o_latent, lse);
+    else launch_pf2<float>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, lhb, src, m, raw_begin, sl2_fast, o_latent, lse);
     return hipGetLastError();
   }
   const Seg rs = to_seg(reps), ws = to_seg(raw);
   const int cdt = raw.dtype;
-  dim3 grid((unsigned)((C + PF_TOK - 1) / PF_TOK), (unsigned)(H / HB));
+  dim3 grid((unsigned)((C + n_tok - 1) / n_tok), (unsigned)head_blocks(H));
   if (q_dtype == LCA_BF16) {
-    if (cdt == LCA_BF16) launch_pf_o<bf16_t, bf16_t>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, rs, m, ws, raw_begin, sl2, o_latent, lse);
-    else launch_pf_o<bf16_t, float>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, rs, m, ws, raw_begin, sl2, o_latent, lse);
+    if (cdt == LCA_BF16) launch_pf_o<bf16_t, bf16_t>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, lhb, rs, m, ws, raw_begin, sl2, o_latent, lse);
+    else launch_pf_o<bf16_t, float>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, lhb, rs, m, ws, raw_begin, sl2, o_latent, lse);
   } else {
-    if (cdt == LCA_BF16) launch_pf_o<float, bf16_t>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, rs, m, ws, raw_begin, sl2, o_latent, lse);
-    else launch_pf_o<float, float>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, rs, m, ws, raw_begin, sl2, o_latent, lse);
+    if (cdt == LCA_BF16) launch_pf_o<float, bf16_t>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, lhb, rs, m, ws, raw_begin, sl2, o_latent, lse);
+    else launch_pf_o<float, float>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, lhb, rs, m, ws, raw_begin, sl2, o_latent, lse);
   }
   return hipGetLastError();
 }

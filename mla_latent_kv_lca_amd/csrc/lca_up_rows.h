@@ -18,6 +18,7 @@
 #pragma once
 #include "lca.h"
 #include "lca_device.h"
+#include "lca_internal.h"
 
 namespace lca {
 
@@ -99,7 +100,7 @@ struct RowsFromSplits {  // decode partials; writes o_latent and lse as it merge
   float* o;
   float* lse;
   __device__ __forceinline__ float4 get(int64_t b, int h, int H, int c4) const {
-    const int HG = H / HB, hg = h / HB, hh = h % HB;
+    const int HG = head_blocks(H), hg = h / HB, hh = h % HB;
     float M, L;
     const float4 v = merge_cols4(part_o, part_ml, S, (b * HG + hg) * S, hh, c4, M, L);
     reinterpret_cast<float4*>(o + (b * H + h) * D_C)[c4] = v;

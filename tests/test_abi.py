@@ -201,8 +201,20 @@ def test_decode_up_argument_errors():
     assert _decode_up(lib, lat, out=None) == lca.LCA_ERR_INVALID_ARG
     assert _decode_up(lib, lat, w=72) == lca.LCA_ERR_INVALID_ARG   # misaligned
     assert _decode_up(lib, lat, odt=7) == lca.LCA_ERR_INVALID_ARG
-    assert _decode_up(lib, lat, H=8) == lca.LCA_ERR_UNSUPPORTED
+    assert _decode_up(lib, lat, H=24) == lca.LCA_ERR_UNSUPPORTED
     assert _decode_up(lib, lat, re=60000) == lca.LCA_ERR_WORKSPACE
+
+
+def test_head_group_sizes():
+    """Head counts that divide 16 (grouped-query attention groups) use one
+    16-row head block, so they need the workspace of 16 heads; other counts
+    below 16, or not a multiple of 16, are not supported."""
+    for h in (1, 2, 4, 8):
+        assert lca.mla_latent_attn_decode_workspace_size(3, h, 66496) == \
+            lca.mla_latent_attn_decode_workspace_size(3, 16, 66496) > 0
+    for h in (3, 12, 24, 40):
+        assert lca.mla_latent_attn_decode_workspace_size(3, h, 66496) == 0
+    assert lca.mla_latent_attn_decode_workspace_size(3, 48, 66496) > 0
 
 
 def test_decode_up_noalloc_argument_errors():
@@ -221,7 +233,7 @@ def test_decode_up_noalloc_argument_errors():
     assert call(q=None) == lca.LCA_ERR_INVALID_ARG
     assert call(w=None) == lca.LCA_ERR_INVALID_ARG
     assert call(out=72) == lca.LCA_ERR_INVALID_ARG
-    assert call(H=8) == lca.LCA_ERR_UNSUPPORTED
+    assert call(H=24) == lca.LCA_ERR_UNSUPPORTED
     assert call(rb=9) == lca.LCA_ERR_INVALID_ARG
     assert call(sm=-1.0) == lca.LCA_ERR_INVALID_ARG
     assert "sm_scale" in lca.lca_last_error()
@@ -233,7 +245,7 @@ def test_prefill_and_up_proj_argument_errors():
     pf = lib.mla_latent_attn_prefill_chunk
     assert pf(64, 0, 9216, 10, 4, 16, None, 0, ctypes.byref(lat), 11, 1.0, 64, 0, None, None) == lca.LCA_ERR_INVALID_ARG
     assert pf(64, 0, 9216, 10, 0, 16, None, 0, ctypes.byref(lat), 0, 1.0, 64, 0, None, None) == lca.LCA_ERR_INVALID_ARG
-    assert pf(64, 0, 9216, 10, 4, 8, None, 0, ctypes.byref(lat), 0, 1.0, 64, 0, None, None) == lca.LCA_ERR_UNSUPPORTED
+    assert pf(64, 0, 9216, 10, 4, 24, None, 0, ctypes.byref(lat), 0, 1.0, 64, 0, None, None) == lca.LCA_ERR_UNSUPPORTED
     assert pf(64, 0, 9216, 10, 4, 16, None, 0, ctypes.byref(lat), 0, 1.0, 64, 5, None, None) == lca.LCA_ERR_INVALID_ARG
     up = lib.mla_up_proj
     assert up(64, 0, 0, 16, 64, 0, 64, 0, None) == lca.LCA_OK  # T == 0
