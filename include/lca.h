@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define LCA_VERSION 1000 /* major*1000 + minor */
+#define LCA_VERSION 1001 /* major*1000 + minor */
 #define LCA_D_C 512      /* latent c_KV width */
 #define LCA_D_R 64       /* decoupled RoPE key width */
 #define LCA_D_ROW 576    /* one cached row: c_KV ++ k_R */
@@ -167,22 +167,27 @@ typedef struct {
 } lca_paged_t;
 
 /* lca_condense over a ragged batch with a paged cache (lca_paged_t
- * above): for every sequence b, groups j in [seq_group_begin[b],
- * seq_group_begin[b] + seq_n_groups[b]) (tokens [j g, (j+1) g) read through
- * the block table) are condensed as in lca_condense with one summary query
- * per sequence, the mean over query rows [q_row0, q_row0 + g) and the H
- * heads of that sequence. Representative j is written to row j of reps
+ * above): for every sequence b, groups j = seq_group_begin[b] + n, n in
+ * [0, seq_n_groups[b]) (tokens [j g, (j+1) g) read through the block table)
+ * are condensed as in lca_condense, group j with the summary query of query
+ * rows [q_row0 + n q_row_step, + g) of sequence b (the mean over those g
+ * tokens and the H heads). q_row_step = 0 gives every group of a sequence
+ * the same summary query (decode: the most recent g queries); q_row_step = g
+ * with q_row0 = (seq_group_begin + 1) g gives each group the g queries that
+ * follow it (chunked prefill, 整体框架 as for mla_latent_attn_prefill_chunk).
+ * The rows must lie in [0, T) for every n < max_groups. Representative j is written to row j of reps
  * (packed bf16, dense, row b at reps->c + b * reps->c_seq_stride); anchors
  * are absolute token indices; alpha optional as in lca_condense.
  * seq_group_begin and seq_n_groups are device int32 [B] arrays read only by
  * the kernel; the caller guarantees 0 <= seq_n_groups[b] <= max_groups, that
  * the representative rows exist and that the block table maps every token
  * of the groups. page_rows must be a multiple of g (a group never straddles
- * pages). workspace >= lca_condense_workspace_size(B, max_groups, 0). */
+ * pages). workspace >= lca_condense_workspace_size(B, max_groups,
+ * q_row_step). */
 int lca_condense_paged(const lca_paged_t* cache, int32_t B, int32_t g, const int32_t* seq_group_begin,
                        const int32_t* seq_n_groups, int64_t max_groups, const void* q, int32_t q_dtype,
                        int64_t q_seq_stride, int64_t q_tok_stride, int64_t T, int32_t H, int64_t q_row0,
-                       float sm_scale, const lca_latent_t* reps, int32_t* anchor_idx,
+                       int64_t q_row_step, float sm_scale, const lca_latent_t* reps, int32_t* anchor_idx,
                        int64_t anchor_seq_stride, float* alpha, int64_t alpha_seq_stride,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
@@ -241,6 +246,21 @@ int mla_latent_attn_decode_paged(const void* q, int32_t q_dtype, int64_t q_seq_s
                                  const int32_t* seq_raw_end, int64_t max_entries, float sm_scale,
                                  float* o_latent, float* lse, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream);
+
+/* mla_latent_attn_decode_paged followed by mla_up_proj of its output (a
+ * serving layout; the MLA page's projection back to each head's value space,
+ * 三.1), with the split merge and the projection fused as in
+ * mla_latent_attn_decode_up. Arguments as in mla_latent_attn_decode_paged
+ * plus w_uv [H, 512, 128] contiguous (w_dtype) and out [B, H, 128]
+ * contiguous (out_dtype). The results are bitwise equal to the two calls in
+ * sequence; workspace as for mla_latent_attn_decode_paged. */
+int mla_latent_attn_decode_paged_up(const void* q, int32_t q_dtype, int64_t q_seq_stride, int32_t B,
+                                    int32_t H, const lca_latent_t* reps, const int32_t* seq_m,
+                                    const lca_paged_t* cache, const int32_t* seq_raw_begin,
+                                    const int32_t* seq_raw_end, int64_t max_entries, float sm_scale,
+                                    float* o_latent, float* lse, const void* w_uv, int32_t w_dtype, void* out,
+                                    int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
 
 /* mla_latent_attn_decode followed by mla_up_proj of its output (the MLA
  * page's projection back to each head's value space, 三.1), with the split
@@ -308,6 +328,24 @@ int mla_latent_attn_prefill_chunk(const void* q, int32_t q_dtype, int64_t q_tok_
                                   const lca_latent_t* raw, int64_t raw_begin, float sm_scale,
                                   void* o_latent, int32_t o_dtype, float* lse,
                                   hipStream_t stream);
+
+/* mla_latent_attn_prefill_chunk for sequence `seq` of a paged cache (a
+ * serving layout; the attention is that of mla_latent_attn_prefill_chunk,
+ * 整体框架): query i of the chunk at position t = chunk_start + i attends
+ * representatives [0, m) (dense packed bf16 rows, reps->c_tok_stride equal
+ * to cache->row_stride; reps may be null when m = 0) and the cache tokens
+ * [raw_begin, t] of sequence seq, token u at row u % page_rows of page
+ * block_table[seq * table_stride + u / page_rows]. page_rows is a multiple
+ * of 16. The caller guarantees that the block table maps every token in
+ * [raw_begin, chunk_start + C) to a page of the pool (not checked). q,
+ * o_latent, lse, dtypes and errors as in mla_latent_attn_prefill_chunk.
+ * Tiles are formed as in the dense call, so on the same rows and
+ * representatives the results are bitwise equal to it. */
+int mla_latent_attn_prefill_chunk_paged(const void* q, int32_t q_dtype, int64_t q_tok_stride,
+                                        int64_t chunk_start, int32_t C, int32_t H,
+                                        const lca_latent_t* reps, int64_t m, const lca_paged_t* cache,
+                                        int32_t seq, int64_t raw_begin, float sm_scale, void* o_latent,
+                                        int32_t o_dtype, float* lse, hipStream_t stream);
 
 /* Per-head value up-projection (the MLA page's projection back to the head
  * space, 三.1): out[t, h, :] = o_latent[t, h, :] @ W_UV[h].

@@ -30,8 +30,9 @@ D_C, D_R, D_ROW, D_V = 512, 64, 576, 128
 # every symbol include/lca.h declares
 EXPORTS = ("lca_version", "lca_last_error", "lca_plan", "lca_condense_workspace_size",
            "lca_condense", "lca_condense_mode", "lca_condense_paged", "mla_latent_attn_decode_workspace_size",
-           "mla_latent_attn_decode", "mla_latent_attn_decode_paged",
+           "mla_latent_attn_decode", "mla_latent_attn_decode_paged", "mla_latent_attn_decode_paged_up",
            "mla_latent_attn_decode_up", "mla_latent_attn_decode_up_noalloc", "mla_latent_attn_prefill_chunk",
+           "mla_latent_attn_prefill_chunk_paged",
            "mla_up_proj",
            "lca_project_workspace_size", "lca_project")
 
@@ -97,12 +98,21 @@ def load() -> ctypes.CDLL:
                                            c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.lca_condense_paged.restype = c_int32
     lib.lca_condense_paged.argtypes = [P(PagedT), c_int32, c_int32, c_void_p, c_void_p, c_int64, c_void_p, c_int32,
-                                       c_int64, c_int64, c_int64, c_int32, c_int64, c_float, P(LatentT), c_void_p,
-                                       c_int64, c_void_p, c_int64, c_void_p, c_size_t, c_void_p]
+                                       c_int64, c_int64, c_int64, c_int32, c_int64, c_int64, c_float, P(LatentT),
+                                       c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_size_t, c_void_p]
     lib.mla_latent_attn_decode_paged.restype = c_int32
     lib.mla_latent_attn_decode_paged.argtypes = [c_void_p, c_int32, c_int64, c_int32, c_int32, P(LatentT),
                                                  c_void_p, P(PagedT), c_void_p, c_void_p, c_int64, c_float,
                                                  c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.mla_latent_attn_decode_paged_up.restype = c_int32
+    lib.mla_latent_attn_decode_paged_up.argtypes = [c_void_p, c_int32, c_int64, c_int32, c_int32, P(LatentT),
+                                                    c_void_p, P(PagedT), c_void_p, c_void_p, c_int64, c_float,
+                                                    c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_int32,
+                                                    c_void_p, c_size_t, c_void_p]
+    lib.mla_latent_attn_prefill_chunk_paged.restype = c_int32
+    lib.mla_latent_attn_prefill_chunk_paged.argtypes = [c_void_p, c_int32, c_int64, c_int64, c_int32, c_int32,
+                                                        P(LatentT), c_int64, P(PagedT), c_int32, c_int64, c_float,
+                                                        c_void_p, c_int32, c_void_p, c_void_p]
     lib.mla_latent_attn_decode_up.restype = c_int32
     lib.mla_latent_attn_decode_up.argtypes = [c_void_p, c_int32, c_int64, c_int32, c_int32, P(LatentT),
                                               c_int64, P(LatentT), c_int64, c_int64, c_float,
@@ -271,9 +281,11 @@ def lca_condense(cache: LatentT, B: int, g: int, group_begin: int, n_groups: int
 def lca_condense_paged(cache: PagedT, B: int, g: int, seq_group_begin: torch.Tensor, seq_n_groups: torch.Tensor,
                        max_groups: int, q: torch.Tensor, q_row0: int, sm_scale: float, reps: LatentT,
                        anchor: torch.Tensor, alpha: torch.Tensor | None = None,
-                       workspace: torch.Tensor | None = None, stream=None) -> None:
+                       workspace: torch.Tensor | None = None, stream=None, q_row_step: int = 0) -> None:
     """Ragged condensation over a paged cache; q [B, T, H, 576]; per-sequence
-    int32 [B] device arrays; one summary query per sequence (rows [q_row0, + g))."""
+    int32 [B] device arrays; group seq_group_begin[b] + n of sequence b uses
+    query rows [q_row0 + n * q_row_step, + g) (q_row_step = 0: one summary
+    query per sequence)."""
     if q.dim() != 4 or q.shape[-1] != D_ROW or q.stride(-1) != 1 or q.stride(-2) != D_ROW:
         raise ValueError("q must be [B, T, H, 576] with contiguous heads")
     if anchor.dtype != torch.int32:
@@ -281,10 +293,11 @@ def lca_condense_paged(cache: PagedT, B: int, g: int, seq_group_begin: torch.Ten
     for t in (seq_group_begin, seq_n_groups):
         if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() != B:
             raise ValueError("per-sequence arrays must be contiguous int32 [B] tensors")
-    ws = _workspace(lca_condense_workspace_size(B, max_groups, 0), q, workspace)
+    ws = _workspace(lca_condense_workspace_size(B, max_groups, q_row_step), q, workspace)
     _check(load().lca_condense_paged(
         ctypes.byref(cache), B, g, seq_group_begin.data_ptr(), seq_n_groups.data_ptr(), max_groups, q.data_ptr(),
-        dtype_code(q), q.stride(0), q.stride(1), q.shape[1], q.shape[2], q_row0, sm_scale, ctypes.byref(reps),
+        dtype_code(q), q.stride(0), q.stride(1), q.shape[1], q.shape[2], q_row0, q_row_step, sm_scale,
+        ctypes.byref(reps),
         anchor.data_ptr(), anchor.stride(0), _ptr(alpha), 0 if alpha is None else alpha.stride(0),
         ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
 
@@ -309,6 +322,34 @@ def mla_latent_attn_decode_paged(q: torch.Tensor, reps: LatentT, seq_m: torch.Te
         q.data_ptr(), dtype_code(q), q.stride(0), B, H, ctypes.byref(reps), seq_m.data_ptr(),
         ctypes.byref(cache), seq_raw_begin.data_ptr(), seq_raw_end.data_ptr(), max_entries, sm_scale,
         o_latent.data_ptr(), _ptr(lse), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def mla_latent_attn_decode_paged_up(q: torch.Tensor, reps: LatentT, seq_m: torch.Tensor, cache: PagedT,
+                                    seq_raw_begin: torch.Tensor, seq_raw_end: torch.Tensor, max_entries: int,
+                                    sm_scale: float, o_latent: torch.Tensor, w_uv: torch.Tensor, out: torch.Tensor,
+                                    lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                                    stream=None) -> None:
+    """Paged decode plus W_UV up-projection: arguments of
+    mla_latent_attn_decode_paged, w_uv [H, 512, 128], out [B, H, 128]."""
+    if q.dim() != 3 or q.shape[-1] != D_ROW or q.stride(-1) != 1 or q.stride(-2) != D_ROW:
+        raise ValueError("q must be [B, H, 576] with contiguous heads")
+    B, H = q.shape[0], q.shape[1]
+    if o_latent.dtype != torch.float32 or not o_latent.is_contiguous() or o_latent.shape != (B, H, D_C):
+        raise ValueError("o_latent must be a contiguous fp32 [B, H, 512] tensor")
+    for t in (seq_m, seq_raw_begin, seq_raw_end):
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() != B:
+            raise ValueError("per-sequence arrays must be contiguous int32 [B] tensors")
+    _check_lse(lse, B, H)
+    if not w_uv.is_contiguous() or tuple(w_uv.shape) != (H, D_C, D_V):
+        raise ValueError("w_uv must be a contiguous [H, 512, 128] tensor")
+    if not out.is_contiguous() or tuple(out.shape) != (B, H, D_V):
+        raise ValueError("out must be a contiguous [B, H, 128] tensor")
+    ws = _workspace(mla_latent_attn_decode_workspace_size(B, H, max_entries), q, workspace)
+    _check(load().mla_latent_attn_decode_paged_up(
+        q.data_ptr(), dtype_code(q), q.stride(0), B, H, ctypes.byref(reps), seq_m.data_ptr(),
+        ctypes.byref(cache), seq_raw_begin.data_ptr(), seq_raw_end.data_ptr(), max_entries, sm_scale,
+        o_latent.data_ptr(), _ptr(lse), w_uv.data_ptr(), dtype_code(w_uv), out.data_ptr(), dtype_code(out),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def mla_latent_attn_decode(q: torch.Tensor, reps: LatentT | None, m: int, raw: LatentT | None,
@@ -397,6 +438,24 @@ def mla_latent_attn_prefill_chunk(q: torch.Tensor, chunk_start: int, reps: Laten
     _check(load().mla_latent_attn_prefill_chunk(
         q.data_ptr(), dtype_code(q), q.stride(0), chunk_start, C, H,
         None if reps is None else ctypes.byref(reps), m, ctypes.byref(raw), raw_begin, sm_scale,
+        o_latent.data_ptr(), dtype_code(o_latent), _ptr(lse), _stream(stream)))
+
+
+def mla_latent_attn_prefill_chunk_paged(q: torch.Tensor, chunk_start: int, reps: LatentT | None, m: int,
+                                        cache: PagedT, seq: int, raw_begin: int, sm_scale: float,
+                                        o_latent: torch.Tensor, lse: torch.Tensor | None = None,
+                                        stream=None) -> None:
+    """Chunked prefill of sequence `seq` of a paged cache: q [C, H, 576]
+    (queries at positions chunk_start ..), o_latent [C, H, 512]."""
+    if q.dim() != 3 or q.shape[-1] != D_ROW or q.stride(-1) != 1 or q.stride(-2) != D_ROW:
+        raise ValueError("q must be [C, H, 576] with contiguous heads")
+    C, H = q.shape[0], q.shape[1]
+    if not o_latent.is_contiguous() or o_latent.shape != (C, H, D_C):
+        raise ValueError("o_latent must be a contiguous [C, H, 512] tensor")
+    _check_lse(lse, C, H)
+    _check(load().mla_latent_attn_prefill_chunk_paged(
+        q.data_ptr(), dtype_code(q), q.stride(0), chunk_start, C, H,
+        None if reps is None else ctypes.byref(reps), m, ctypes.byref(cache), seq, raw_begin, sm_scale,
         o_latent.data_ptr(), dtype_code(o_latent), _ptr(lse), _stream(stream)))
 
 

@@ -141,7 +141,7 @@ int lca_condense_mode(const lca_latent_t* cache, int32_t B, int32_t g, int64_t g
 int lca_condense_paged(const lca_paged_t* cache, int32_t B, int32_t g, const int32_t* seq_group_begin,
                        const int32_t* seq_n_groups, int64_t max_groups, const void* q, int32_t q_dtype,
                        int64_t q_seq_stride, int64_t q_tok_stride, int64_t T, int32_t H, int64_t q_row0,
-                       float sm_scale, const lca_latent_t* reps, int32_t* anchor_idx,
+                       int64_t q_row_step, float sm_scale, const lca_latent_t* reps, int32_t* anchor_idx,
                        int64_t anchor_seq_stride, float* alpha, int64_t alpha_seq_stride,
                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int rc;
@@ -164,7 +164,13 @@ int lca_condense_paged(const lca_paged_t* cache, int32_t B, int32_t g, const int
   if (!valid_dtype(q_dtype)) return fail(LCA_ERR_INVALID_ARG, "q_dtype %d is not LCA_BF16/LCA_F32", q_dtype);
   if (!mult8(q_seq_stride) || !mult8(q_tok_stride) || q_seq_stride < 0 || q_tok_stride < 0)
     return fail(LCA_ERR_INVALID_ARG, "q strides must be non-negative multiples of 8 elements");
-  if (q_row0 < 0 || q_row0 + g > T) return fail(LCA_ERR_INVALID_ARG, "summary-query rows [q_row0, q_row0 + g) must lie in [0, T)");
+  if (q_row0 < 0 || q_row_step < 0) return fail(LCA_ERR_INVALID_ARG, "q_row0 and q_row_step must be >= 0");
+  if (q_row_step != 0 && max_groups > 0x7fffffff) return fail(LCA_ERR_UNSUPPORTED, "too many summary queries");
+  {
+    const int64_t last_row = q_row0 + (max_groups > 0 ? max_groups - 1 : 0) * q_row_step + g - 1;
+    if (last_row >= T)
+      return fail(LCA_ERR_INVALID_ARG, "summary-query rows reach row %lld but T = %lld", (long long)last_row, (long long)T);
+  }
   if ((rc = check_latent(reps, "reps", true, true)) != LCA_OK) return rc;
   if (reps->dtype != LCA_BF16 || static_cast<const char*>(reps->kr) != static_cast<const char*>(reps->c) + 2 * LCA_D_C ||
       reps->kr_tok_stride != reps->c_tok_stride || reps->kr_seq_stride != reps->c_seq_stride)
@@ -173,11 +179,11 @@ int lca_condense_paged(const lca_paged_t* cache, int32_t B, int32_t g, const int
   if (anchor_seq_stride < 0 || alpha_seq_stride < 0) return fail(LCA_ERR_INVALID_ARG, "negative output stride");
   if ((rc = check_scale(sm_scale)) != LCA_OK) return rc;
   if (max_groups == 0) return ok();
-  const size_t need = lca_condense_workspace_size(B, max_groups, 0);
+  const size_t need = lca_condense_workspace_size(B, max_groups, q_row_step);
   if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need)
     return fail(LCA_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
   return hip_status(lca::launch_condense_paged(*cache, B, g, seq_group_begin, seq_n_groups, max_groups, q, q_dtype,
-                                               q_seq_stride, q_tok_stride, H, q_row0, sm_scale, *reps, anchor_idx,
+                                               q_seq_stride, q_tok_stride, H, q_row0, q_row_step, sm_scale, *reps, anchor_idx,
                                                anchor_seq_stride, alpha, alpha_seq_stride,
                                                static_cast<float*>(workspace), stream),
                     "lca_condense_paged launch");
@@ -222,12 +228,15 @@ int mla_latent_attn_decode(const void* q, int32_t q_dtype, int64_t q_seq_stride,
                     "mla_latent_attn_decode launch");
 }
 
-int mla_latent_attn_decode_paged(const void* q, int32_t q_dtype, int64_t q_seq_stride, int32_t B,
-                                 int32_t H, const lca_latent_t* reps, const int32_t* seq_m,
-                                 const lca_paged_t* cache, const int32_t* seq_raw_begin,
-                                 const int32_t* seq_raw_end, int64_t max_entries, float sm_scale,
-                                 float* o_latent, float* lse, void* workspace,
-                                 size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+// Arguments of mla_latent_attn_decode_paged / _paged_up shared by both;
+// on success *need receives the bytes of split-K partials.
+int check_decode_paged(const void* q, int32_t q_dtype, int64_t q_seq_stride, int32_t B, int32_t H,
+                       const lca_latent_t* reps, const int32_t* seq_m, const lca_paged_t* cache,
+                       const int32_t* seq_raw_begin, const int32_t* seq_raw_end, int64_t max_entries,
+                       float sm_scale, float* o_latent, size_t* need) {
   int rc;
   if (q == nullptr || !aligned16(q)) return fail(LCA_ERR_INVALID_ARG, "q must be a non-null 16-byte aligned pointer");
   if (!valid_dtype(q_dtype)) return fail(LCA_ERR_INVALID_ARG, "q_dtype %d is not LCA_BF16/LCA_F32", q_dtype);
@@ -256,12 +265,50 @@ int mla_latent_attn_decode_paged(const void* q, int32_t q_dtype, int64_t q_seq_s
   if ((rc = check_scale(sm_scale)) != LCA_OK) return rc;
   if (o_latent == nullptr || !aligned16(o_latent)) return fail(LCA_ERR_INVALID_ARG, "o_latent must be a non-null 16-byte aligned pointer");
   const lca::DecodeSplit sp = lca::decode_split(B, lca::head_blocks(H), max_entries);
-  const size_t need = lca::decode_workspace_bytes(B, lca::head_blocks(H), sp.S);
+  *need = lca::decode_workspace_bytes(B, lca::head_blocks(H), sp.S);
+  return LCA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int mla_latent_attn_decode_paged(const void* q, int32_t q_dtype, int64_t q_seq_stride, int32_t B,
+                                 int32_t H, const lca_latent_t* reps, const int32_t* seq_m,
+                                 const lca_paged_t* cache, const int32_t* seq_raw_begin,
+                                 const int32_t* seq_raw_end, int64_t max_entries, float sm_scale,
+                                 float* o_latent, float* lse, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  size_t need = 0;
+  const int rc = check_decode_paged(q, q_dtype, q_seq_stride, B, H, reps, seq_m, cache, seq_raw_begin, seq_raw_end,
+                                    max_entries, sm_scale, o_latent, &need);
+  if (rc != LCA_OK) return rc;
   if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need))
     return fail(LCA_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
   return hip_status(lca::launch_decode_paged(q, q_dtype, q_seq_stride, B, H, *reps, seq_m, *cache, seq_raw_begin,
                                              seq_raw_end, max_entries, sm_scale, o_latent, lse, workspace, stream),
                     "mla_latent_attn_decode_paged launch");
+}
+
+int mla_latent_attn_decode_paged_up(const void* q, int32_t q_dtype, int64_t q_seq_stride, int32_t B,
+                                    int32_t H, const lca_latent_t* reps, const int32_t* seq_m,
+                                    const lca_paged_t* cache, const int32_t* seq_raw_begin,
+                                    const int32_t* seq_raw_end, int64_t max_entries, float sm_scale,
+                                    float* o_latent, float* lse, const void* w_uv, int32_t w_dtype, void* out,
+                                    int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  size_t need = 0;
+  const int rc = check_decode_paged(q, q_dtype, q_seq_stride, B, H, reps, seq_m, cache, seq_raw_begin, seq_raw_end,
+                                    max_entries, sm_scale, o_latent, &need);
+  if (rc != LCA_OK) return rc;
+  if (!valid_dtype(w_dtype) || !valid_dtype(out_dtype)) return fail(LCA_ERR_INVALID_ARG, "w_dtype and out_dtype must be LCA_BF16 or LCA_F32");
+  if (w_uv == nullptr || !aligned16(w_uv) || out == nullptr || !aligned16(out))
+    return fail(LCA_ERR_INVALID_ARG, "w_uv and out must be non-null 16-byte aligned pointers");
+  if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need))
+    return fail(LCA_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
+  return hip_status(lca::launch_decode_paged_up(q, q_dtype, q_seq_stride, B, H, *reps, seq_m, *cache, seq_raw_begin,
+                                                seq_raw_end, max_entries, sm_scale, o_latent, lse, w_uv, w_dtype,
+                                                out, out_dtype, workspace, stream),
+                    "mla_latent_attn_decode_paged_up launch");
 }
 
 }  // extern "C"
@@ -372,6 +419,47 @@ int mla_latent_attn_prefill_chunk(const void* q, int32_t q_dtype, int64_t q_tok_
   return hip_status(lca::launch_prefill(q, q_dtype, q_tok_stride, chunk_start, C, H, m > 0 ? *reps : none,
                                         m, *raw, raw_begin, sm_scale, o_latent, o_dtype, lse, stream),
                     "mla_latent_attn_prefill_chunk launch");
+}
+
+int mla_latent_attn_prefill_chunk_paged(const void* q, int32_t q_dtype, int64_t q_tok_stride,
+                                        int64_t chunk_start, int32_t C, int32_t H,
+                                        const lca_latent_t* reps, int64_t m, const lca_paged_t* cache,
+                                        int32_t seq, int64_t raw_begin, float sm_scale, void* o_latent,
+                                        int32_t o_dtype, float* lse, hipStream_t stream) {
+  int rc;
+  if (q == nullptr || !aligned16(q)) return fail(LCA_ERR_INVALID_ARG, "q must be a non-null 16-byte aligned pointer");
+  if (!valid_dtype(q_dtype)) return fail(LCA_ERR_INVALID_ARG, "q_dtype %d is not LCA_BF16/LCA_F32", q_dtype);
+  if (!mult8(q_tok_stride) || q_tok_stride < 0) return fail(LCA_ERR_INVALID_ARG, "q_tok_stride must be a non-negative multiple of 8");
+  if (C < 1) return fail(LCA_ERR_INVALID_ARG, "C must be >= 1");
+  if (!lca::heads_supported(H) || lca::head_blocks(H) > 65535)
+    return fail(LCA_ERR_UNSUPPORTED, "H = %d: the head count must be a multiple of 16 or divide 16", H);
+  if (m < 0 || raw_begin < 0 || chunk_start < raw_begin)
+    return fail(LCA_ERR_INVALID_ARG, "need m >= 0 and 0 <= raw_begin <= chunk_start");
+  if (cache == nullptr || cache->pages == nullptr || !aligned16(cache->pages))
+    return fail(LCA_ERR_INVALID_ARG, "cache pages must be a non-null 16-byte aligned pointer");
+  if (cache->row_stride < LCA_D_ROW || !mult8(cache->row_stride))
+    return fail(LCA_ERR_INVALID_ARG, "cache row_stride must be >= 576 and a multiple of 8");
+  if (cache->page_rows < 16 || cache->page_rows % 16 != 0)
+    return fail(LCA_ERR_UNSUPPORTED, "page_rows = %d: must be a positive multiple of 16", cache->page_rows);
+  if (cache->block_table == nullptr || cache->table_stride < 1)
+    return fail(LCA_ERR_INVALID_ARG, "block_table must be non-null with table_stride >= 1");
+  if (seq < 0) return fail(LCA_ERR_INVALID_ARG, "seq must be >= 0");
+  if (cache->row_stride * 2 * 32 >= ((int64_t)1 << 31)) return fail(LCA_ERR_UNSUPPORTED, "row stride too large");
+  if (m > 0) {
+    if ((rc = check_latent(reps, "reps", true, true)) != LCA_OK) return rc;
+    if (reps->dtype != LCA_BF16 || static_cast<const char*>(reps->kr) != static_cast<const char*>(reps->c) + 2 * LCA_D_C ||
+        reps->kr_tok_stride != reps->c_tok_stride)
+      return fail(LCA_ERR_UNSUPPORTED, "paged prefill needs packed bf16 representatives (k_R right after c_KV)");
+    if (reps->c_tok_stride != cache->row_stride)
+      return fail(LCA_ERR_UNSUPPORTED, "representatives and cache pages must share one row stride");
+  }
+  if ((rc = check_scale(sm_scale)) != LCA_OK) return rc;
+  if (!valid_dtype(o_dtype)) return fail(LCA_ERR_INVALID_ARG, "o_dtype %d is not LCA_BF16/LCA_F32", o_dtype);
+  if (o_latent == nullptr || !aligned16(o_latent)) return fail(LCA_ERR_INVALID_ARG, "o_latent must be a non-null 16-byte aligned pointer");
+  const lca_latent_t none = {nullptr, nullptr, 0, 0, 0, 0, LCA_BF16};
+  return hip_status(lca::launch_prefill_paged(q, q_dtype, q_tok_stride, chunk_start, C, H, m > 0 ? *reps : none, m,
+                                              *cache, seq, raw_begin, sm_scale, o_latent, o_dtype, lse, stream),
+                    "mla_latent_attn_prefill_chunk_paged launch");
 }
 
 int mla_up_proj(const void* o_latent, int32_t o_dtype, int64_t T, int32_t H, const void* w_uv,

@@ -539,7 +539,8 @@ template <int LG>
 __global__ __launch_bounds__(256) void condense_paged_kernel(
     const bf16_t* __restrict__ pages, int64_t row_stride, int page_rows, const int32_t* __restrict__ table,
     int64_t table_stride, const int32_t* __restrict__ seq_group_begin, const int32_t* __restrict__ seq_n_groups,
-    const float* __restrict__ qbar, float sm_scale, bf16_t* __restrict__ rc, int64_t rc_seq, int64_t rc_tok,
+    const float* __restrict__ qbar, int per_group_q, int64_t n_q, float sm_scale, bf16_t* __restrict__ rc,
+    int64_t rc_seq, int64_t rc_tok,
     int32_t* __restrict__ anchor, int64_t anchor_seq, float* __restrict__ alpha, int64_t alpha_seq) {
   constexpr int G = 1 << LG;
   const int lane = threadIdx.x & 63;
@@ -550,7 +551,7 @@ __global__ __launch_bounds__(256) void condense_paged_kernel(
   const int64_t page = table[(int64_t)b * table_stride + t0 / page_rows];
   const bf16_t* rows0 = pages + (page * page_rows + t0 % page_rows) * row_stride;
 
-  const float* qb = qbar + (int64_t)b * D_ROW;
+  const float* qb = qbar + ((int64_t)b * n_q + (per_group_q ? n : 0)) * D_ROW;
   float qc[8];
   load8_f32(qb + 8 * lane, qc);
   const float qr = qb[D_C + lane];
@@ -617,9 +618,25 @@ static void launch_qbar_shared(int B, int g, const void* q, int q_dtype, int64_t
 hipError_t launch_condense_paged(const lca_paged_t& cache, int B, int g, const int32_t* seq_group_begin,
                                  const int32_t* seq_n_groups, int64_t max_groups, const void* q, int q_dtype,
                                  int64_t q_seq_stride, int64_t q_tok_stride, int H, int64_t q_row0,
-                                 float sm_scale, const lca_latent_t& reps, int32_t* anchor, int64_t anchor_seq,
-                                 float* alpha, int64_t alpha_seq, float* qbar_ws, hipStream_t stream) {
-  launch_qbar_shared(B, g, q, q_dtype, q_seq_stride, q_tok_stride, H, q_row0, qbar_ws, stream);
+                                 int64_t q_row_step, float sm_scale, const lca_latent_t& reps, int32_t* anchor,
+                                 int64_t anchor_seq, float* alpha, int64_t alpha_seq, float* qbar_ws,
+                                 hipStream_t stream) {
+  // summary queries: one per sequence (decode), or one per group slot n <
+  // max_groups (rows q_row0 + n q_row_step, the queries after each group in
+  // chunked prefill); slots past a sequence's group count are not used
+  const int per_group_q = q_row_step != 0;
+  const int64_t n_q = per_group_q ? max_groups : 1;
+  if (per_group_q) {
+    dim3 g0((unsigned)n_q, (unsigned)B);
+    if (q_dtype == LCA_BF16)
+      hipLaunchKernelGGL(qbar_kernel<bf16_t>, g0, dim3(QBAR_THREADS), 0, stream, (const bf16_t*)q,
+                         q_seq_stride, q_tok_stride, H, g, q_row0, q_row_step, (int)n_q, qbar_ws);
+    else
+      hipLaunchKernelGGL(qbar_kernel<float>, g0, dim3(QBAR_THREADS), 0, stream, (const float*)q,
+                         q_seq_stride, q_tok_stride, H, g, q_row0, q_row_step, (int)n_q, qbar_ws);
+  } else {
+    launch_qbar_shared(B, g, q, q_dtype, q_seq_stride, q_tok_stride, H, q_row0, qbar_ws, stream);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   int lg = 0;
@@ -628,7 +645,8 @@ hipError_t launch_condense_paged(const lca_paged_t& cache, int B, int g, const i
 #define LCA_PAGED(LGV)                                                                                     \
   hipLaunchKernelGGL((condense_paged_kernel<LGV>), grid, dim3(256), 0, stream, (const bf16_t*)cache.pages,   \
                      cache.row_stride, cache.page_rows, cache.block_table, cache.table_stride, seq_group_begin, \
-                     seq_n_groups, qbar_ws, sm_scale, (bf16_t*)reps.c, reps.c_seq_stride, reps.c_tok_stride,  \
+                     seq_n_groups, qbar_ws, per_group_q, n_q, sm_scale, (bf16_t*)reps.c, reps.c_seq_stride,     \
+                     reps.c_tok_stride,                                                                      \
                      anchor, anchor_seq, alpha, alpha_seq)
   switch (lg) {
     case 0: LCA_PAGED(0); break;

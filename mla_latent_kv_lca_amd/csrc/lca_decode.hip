@@ -737,15 +737,14 @@ hipError_t launch_decode(const void* q, int q_dtype, int64_t q_seq_stride, int B
   return hipGetLastError();
 }
 
-hipError_t launch_decode_paged(const void* q, int q_dtype, int64_t q_seq_stride, int B, int H,
-                               const lca_latent_t& reps, const int32_t* seq_m, const lca_paged_t& cache,
-                               const int32_t* seq_raw_begin, const int32_t* seq_raw_end,
-                               int64_t max_entries, float sm_scale, float* o_latent, float* lse,
-                               void* workspace, hipStream_t stream) {
+// The attention kernel of one paged decode call; with sp.S > 1 it leaves
+// split partials in the workspace.
+static hipError_t decode_paged_attention(const void* q, int q_dtype, int64_t q_seq_stride, int B, int H,
+                                         const lca_latent_t& reps, const int32_t* seq_m, const lca_paged_t& cache,
+                                         const int32_t* seq_raw_begin, const int32_t* seq_raw_end,
+                                         float sm_scale, float* o_latent, float* lse, const DecodeSplit& sp,
+                                         float* po, float* pml, hipStream_t stream) {
   const int HG = head_blocks(H);
-  const DecodeSplit sp = decode_split(B, HG, max_entries);
-  float *po, *pml;
-  split_buffers(workspace, B, HG, sp, po, pml);
   const float sl2 = sm_scale * 1.44269504088896340736f;
   dim3 grid((unsigned)sp.S, (unsigned)B, (unsigned)HG);
   const char* rep = static_cast<const char*>(reps.c);
@@ -759,10 +758,53 @@ hipError_t launch_decode_paged(const void* q, int q_dtype, int64_t q_seq_stride,
     hipLaunchKernelGGL(decode_paged_kernel<float>, grid, dim3(DNT), 0, stream, (const float*)q, q_seq_stride,
                        rep, rep_seq_b, seq_m, pages, cache.block_table, cache.table_stride, cache.page_rows,
                        seq_raw_begin, seq_raw_end, tok_b, sp.S, sl2, H, po, pml, o_latent, lse);
-  hipError_t err = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_paged(const void* q, int q_dtype, int64_t q_seq_stride, int B, int H,
+                               const lca_latent_t& reps, const int32_t* seq_m, const lca_paged_t& cache,
+                               const int32_t* seq_raw_begin, const int32_t* seq_raw_end,
+                               int64_t max_entries, float sm_scale, float* o_latent, float* lse,
+                               void* workspace, hipStream_t stream) {
+  const DecodeSplit sp = decode_split(B, head_blocks(H), max_entries);
+  float *po, *pml;
+  split_buffers(workspace, B, head_blocks(H), sp, po, pml);
+  hipError_t err = decode_paged_attention(q, q_dtype, q_seq_stride, B, H, reps, seq_m, cache, seq_raw_begin,
+                                          seq_raw_end, sm_scale, o_latent, lse, sp, po, pml, stream);
   if (err != hipSuccess || sp.S == 1) return err;
   launch_merge(sp, B, H, po, pml, o_latent, lse, stream);
   return hipGetLastError();
+}
+
+// The split merge (or the W_UV projection of the merged rows) after a
+// decode attention kernel that left its partials in po / pml.
+static hipError_t merge_and_up(const DecodeSplit& sp, int B, int H, float* po, float* pml, float* o_latent,
+                               float* lse, const void* w_uv, int w_dtype, void* out, int out_dtype,
+                               hipStream_t stream) {
+  hipError_t err;
+  if (sp.S == 1 || sp.S > MERGE_SMALL_S || B > UP_SMALL_T) {
+    if (sp.S > 1) launch_merge(sp, B, H, po, pml, o_latent, lse, stream);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    return launch_up_proj(o_latent, LCA_F32, B, H, w_uv, w_dtype, out, out_dtype, stream);
+  }
+  const RowsFromSplits rows{po, pml, sp.S, o_latent, lse};
+  if (w_dtype == LCA_BF16) launch_up_rows<RowsFromSplits, bf16_t>(rows, B, H, w_uv, out, out_dtype, stream);
+  else launch_up_rows<RowsFromSplits, float>(rows, B, H, w_uv, out, out_dtype, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_paged_up(const void* q, int q_dtype, int64_t q_seq_stride, int B, int H,
+                                  const lca_latent_t& reps, const int32_t* seq_m, const lca_paged_t& cache,
+                                  const int32_t* seq_raw_begin, const int32_t* seq_raw_end, int64_t max_entries,
+                                  float sm_scale, float* o_latent, float* lse, const void* w_uv, int w_dtype,
+                                  void* out, int out_dtype, void* workspace, hipStream_t stream) {
+  const DecodeSplit sp = decode_split(B, head_blocks(H), max_entries);
+  float *po, *pml;
+  split_buffers(workspace, B, head_blocks(H), sp, po, pml);
+  const hipError_t err = decode_paged_attention(q, q_dtype, q_seq_stride, B, H, reps, seq_m, cache, seq_raw_begin,
+                                                seq_raw_end, sm_scale, o_latent, lse, sp, po, pml, stream);
+  if (err != hipSuccess) return err;
+  return merge_and_up(sp, B, H, po, pml, o_latent, lse, w_uv, w_dtype, out, out_dtype, stream);
 }
 
 // ---- scratch for the entry point that allocates nothing
@@ -805,18 +847,10 @@ hipError_t launch_decode_up(const void* q, int q_dtype, int64_t q_seq_stride, in
   const DecodeSplit sp = decode_split(B, head_blocks(H), m + (raw_end - raw_begin));
   float *po, *pml;
   split_buffers(workspace, B, head_blocks(H), sp, po, pml);
-  hipError_t err = decode_attention(q, q_dtype, q_seq_stride, B, H, reps, m, raw, raw_begin, raw_end,
-                                    sm_scale, o_latent, lse, sp, po, pml, stream);
+  const hipError_t err = decode_attention(q, q_dtype, q_seq_stride, B, H, reps, m, raw, raw_begin, raw_end,
+                                          sm_scale, o_latent, lse, sp, po, pml, stream);
   if (err != hipSuccess) return err;
-  if (sp.S == 1 || sp.S > MERGE_SMALL_S || B > UP_SMALL_T) {
-    if (sp.S > 1) launch_merge(sp, B, H, po, pml, o_latent, lse, stream);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    return launch_up_proj(o_latent, LCA_F32, B, H, w_uv, w_dtype, out, out_dtype, stream);
-  }
-  const RowsFromSplits rows{po, pml, sp.S, o_latent, lse};
-  if (w_dtype == LCA_BF16) launch_up_rows<RowsFromSplits, bf16_t>(rows, B, H, w_uv, out, out_dtype, stream);
-  else launch_up_rows<RowsFromSplits, float>(rows, B, H, w_uv, out, out_dtype, stream);
-  return hipGetLastError();
+  return merge_and_up(sp, B, H, po, pml, o_latent, lse, w_uv, w_dtype, out, out_dtype, stream);
 }
 
 }  // namespace lca

@@ -30,8 +30,9 @@ inline Seg to_seg(const lca_latent_t& t) {
 hipError_t launch_condense_paged(const lca_paged_t& cache, int B, int g, const int32_t* seq_group_begin,
                                  const int32_t* seq_n_groups, int64_t max_groups, const void* q, int q_dtype,
                                  int64_t q_seq_stride, int64_t q_tok_stride, int H, int64_t q_row0,
-                                 float sm_scale, const lca_latent_t& reps, int32_t* anchor, int64_t anchor_seq,
-                                 float* alpha, int64_t alpha_seq, float* qbar_ws, hipStream_t stream);
+                                 int64_t q_row_step, float sm_scale, const lca_latent_t& reps, int32_t* anchor,
+                                 int64_t anchor_seq, float* alpha, int64_t alpha_seq, float* qbar_ws,
+                                 hipStream_t stream);
 hipError_t launch_condense(const lca_latent_t& cache, int B, int g, int64_t group_begin,
                            int64_t n_groups, const void* q, int q_dtype, int64_t q_seq_stride,
                            int64_t q_tok_stride, int H, int64_t q_row0, int64_t q_row_step,
@@ -68,6 +69,11 @@ hipError_t launch_decode_paged(const void* q, int q_dtype, int64_t q_seq_stride,
                                const int32_t* seq_raw_begin, const int32_t* seq_raw_end,
                                int64_t max_entries, float sm_scale, float* o_latent, float* lse,
                                void* workspace, hipStream_t stream);
+hipError_t launch_decode_paged_up(const void* q, int q_dtype, int64_t q_seq_stride, int B, int H,
+                                  const lca_latent_t& reps, const int32_t* seq_m, const lca_paged_t& cache,
+                                  const int32_t* seq_raw_begin, const int32_t* seq_raw_end, int64_t max_entries,
+                                  float sm_scale, float* o_latent, float* lse, const void* w_uv, int w_dtype,
+                                  void* out, int out_dtype, void* workspace, hipStream_t stream);
 hipError_t launch_decode_up(const void* q, int q_dtype, int64_t q_seq_stride, int B, int H,
                             const lca_latent_t& reps, int64_t m, const lca_latent_t& raw,
                             int64_t raw_begin, int64_t raw_end, float sm_scale, float* o_latent,
@@ -79,6 +85,13 @@ hipError_t launch_prefill(const void* q, int q_dtype, int64_t q_tok_stride, int6
                           int C, int H, const lca_latent_t& reps, int64_t m,
                           const lca_latent_t& raw, int64_t raw_begin, float sm_scale,
                           void* o_latent, int o_dtype, float* lse, hipStream_t stream);
+
+// chunked prefill of sequence `seq` of a paged cache (raw rows through its
+// block table; representatives dense, same row stride as the pages)
+hipError_t launch_prefill_paged(const void* q, int q_dtype, int64_t q_tok_stride, int64_t chunk_start,
+                                int C, int H, const lca_latent_t& reps, int64_t m, const lca_paged_t& cache,
+                                int seq, int64_t raw_begin, float sm_scale, void* o_latent, int o_dtype,
+                                float* lse, hipStream_t stream);
 
 // ---- up-projection
 constexpr int UP_SMALL_T = 64;  // token counts up to this use the small-T kernel

@@ -139,9 +139,9 @@ constexpr int VF_RING = VF_AHEAD + 1;
 
 template <bool V> using bool_c = std::integral_constant<bool, V>;
 
-template <typename TQ, typename TO>
+template <typename TQ, typename TO, class Src>
 __global__ __launch_bounds__(256) void prefill_kernel(
-    const TQ* __restrict__ q, int64_t q_tok, int64_t chunk_start, int C, int H, int lhb, DmaSrc src,
+    const TQ* __restrict__ q, int64_t q_tok, int64_t chunk_start, int C, int H, int lhb, Src src,
     int64_t m, int64_t raw_begin, float scale_log2, TO* __restrict__ o, float* __restrict__ lse) {
   __shared__ __align__(16) bf16_t ring[PBUF][STILE_ELEMS];
   __shared__ __align__(16) f32x4_t sx[4][4][64];  // partial scores [wave][r / 4][lane]
@@ -424,14 +424,52 @@ static bool packed_rows_pf(const lca_latent_t& t) {
          t.kr_tok_stride == t.c_tok_stride;
 }
 
-template <typename TQ>
+template <typename TQ, class Src>
 static void launch_pf2(int o_dtype, dim3 grid, hipStream_t st, const void* q, int64_t q_tok,
-                       int64_t cs, int C, int H, int lhb, const DmaSrc& src, int64_t m, int64_t rb, float sl2,
+                       int64_t cs, int C, int H, int lhb, const Src& src, int64_t m, int64_t rb, float sl2,
                        void* o, float* lse) {
   if (o_dtype == LCA_BF16)
-    hipLaunchKernelGGL((prefill_kernel<TQ, bf16_t>), grid, dim3(256), 0, st, (const TQ*)q, q_tok, cs, C, H, lhb, src, m, rb, sl2, (bf16_t*)o, lse);
+    hipLaunchKernelGGL((prefill_kernel<TQ, bf16_t, Src>), grid, dim3(256), 0, st, (const TQ*)q, q_tok, cs, C, H, lhb, src, m, rb, sl2, (bf16_t*)o, lse);
   else
-    hipLaunchKernelGGL((prefill_kernel<TQ, float>), grid, dim3(256), 0, st, (const TQ*)q, q_tok, cs, C, H, lhb, src, m, rb, sl2, (float*)o, lse);
+    hipLaunchKernelGGL((prefill_kernel<TQ, float, Src>), grid, dim3(256), 0, st, (const TQ*)q, q_tok, cs, C, H, lhb, src, m, rb, sl2, (float*)o, lse);
+}
+
+// query tokens per workgroup and their log2 heads-per-block (64 query rows)
+static void pf_rows(int H, int& lhb, int& n_tok) {
+  const int hb = H < HB ? H : HB;
+  lhb = 0;
+  while ((1 << lhb) < hb) ++lhb;
+  n_tok = 64 >> lhb;
+}
+// The fast kernel scales unscaled scores inside one fma before exp2, and
+// masks with -inf; a scale of exactly 0 would turn -inf * 0 into NaN. The
+// smallest normal float scale gives the same weights (every finite logit
+// times it rounds to an exponent of 0, i.e. the uniform softmax that
+// sm_scale = 0 means) and keeps -inf masked.
+static float fast_scale(float sm_scale) {
+  const float sl2 = sm_scale * 1.44269504088896340736f;
+  return sl2 > 0.f ? sl2 : FLT_MIN;
+}
+
+hipError_t launch_prefill_paged(const void* q, int q_dtype, int64_t q_tok_stride, int64_t chunk_start,
+                                int C, int H, const lca_latent_t& reps, int64_t m, const lca_paged_t& cache,
+                                int seq, int64_t raw_begin, float sm_scale, void* o_latent, int o_dtype,
+                                float* lse, hipStream_t stream) {
+  int lhb, n_tok;
+  pf_rows(H, lhb, n_tok);
+  PagedDmaSrc src;
+  src.rep = m > 0 ? static_cast<const char*>(reps.c) : nullptr;
+  src.pages = static_cast<const char*>(cache.pages);
+  src.table = cache.block_table + (int64_t)seq * cache.table_stride;
+  src.tok = cache.row_stride * 2;
+  src.m = m;
+  src.raw_begin = raw_begin;
+  src.P = cache.page_rows;
+  const float sl2 = fast_scale(sm_scale);
+  dim3 grid((unsigned)((C + n_tok - 1) / n_tok), (unsigned)head_blocks(H));
+  if (q_dtype == LCA_BF16) launch_pf2<bf16_t>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, lhb, src, m, raw_begin, sl2, o_latent, lse);
+  else launch_pf2<float>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, lhb, src, m, raw_begin, sl2, o_latent, lse);
+  return hipGetLastError();
 }
 
 hipError_t launch_prefill(const void* q, int q_dtype, int64_t q_tok_stride, int64_t chunk_start,
@@ -439,20 +477,12 @@ hipError_t launch_prefill(const void* q, int q_dtype, int64_t q_tok_stride, int6
                           const lca_latent_t& raw, int64_t raw_begin, float sm_scale,
                           void* o_latent, int o_dtype, float* lse, hipStream_t stream) {
   const float sl2 = sm_scale * 1.44269504088896340736f;
-  // heads per 16-row block and query tokens per workgroup (64 query rows)
-  const int hb = H < HB ? H : HB;
-  int lhb = 0;
-  while ((1 << lhb) < hb) ++lhb;
-  const int n_tok = 64 >> lhb;
+  int lhb, n_tok;
+  pf_rows(H, lhb, n_tok);
   const bool fast = packed_rows_pf(raw) && (m == 0 || (packed_rows_pf(reps) && reps.c_tok_stride == raw.c_tok_stride)) &&
                     raw.c_tok_stride * 2 * STILE < ((int64_t)1 << 31);
   if (fast) {
-    // The fast kernel scales unscaled scores inside one fma before exp2, and
-    // masks with -inf; a scale of exactly 0 would turn -inf * 0 into NaN.
-    // The smallest normal float scale gives the same weights (every finite
-    // logit times it rounds to an exponent of 0, i.e. the uniform softmax
-    // that sm_scale = 0 means) and keeps -inf masked.
-    const float sl2_fast = sl2 > 0.f ? sl2 : FLT_MIN;
+    const float sl2_fast = fast_scale(sm_scale);
     DmaSrc src;
     src.rep = m > 0 ? static_cast<const char*>(reps.c) : nullptr;
     src.raw = static_cast<const char*>(raw.c) + raw_begin * raw.c_tok_stride * 2;

@@ -124,4 +124,60 @@ __device__ __forceinline__ void tile_dma(const DmaSrc& src, int64_t e0, int64_t 
   }
 }
 
+// The same tiles over a paged cache (one sequence): entries [0, m) are
+// dense representative rows, entry e >= m is raw token t = raw_begin + e - m,
+// row t % P of page table[t / P] of the pool (P rows per page, a multiple of
+// 16, so a 32-entry tile touches at most three pages). Representatives and
+// pages share one row stride.
+struct PagedDmaSrc {
+  const char* rep;      // representative rows
+  const char* pages;    // page pool
+  const int32_t* table; // this sequence's block table
+  int64_t tok;          // row stride in bytes
+  int64_t m, raw_begin;
+  int P;                // rows per page
+};
+
+__device__ __forceinline__ void tile_dma(const PagedDmaSrc& src, int64_t e0, int64_t e_end,
+                                         const bf16_t* buf, int w, int lane,
+                                         const uint32_t (&off)[DMA_PER_WAVE]) {
+  const uint32_t base = lds_off(buf);
+  const int valid = (int)min((int64_t)STILE, e_end - e0);
+  if (e0 + STILE <= src.m && valid == STILE) {  // whole tile of representatives
+    const char* b0 = src.rep + e0 * src.tok;
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i) dma16(b0 + off[i], base + 1024u * (w + SNW * i));
+    return;
+  }
+  // raw tokens of the tile's raw entries and their pages (page indices are
+  // wave-uniform scalar loads)
+  const int64_t r_first = max(e0, src.m), r_last = e0 + valid - 1;
+  const int64_t t_first = src.raw_begin + (r_first - src.m), t_last = src.raw_begin + (r_last - src.m);
+  const int64_t pg0 = t_first / src.P, pg_last = r_last >= src.m ? t_last / src.P : pg0;
+  const int64_t pa = src.table[__builtin_amdgcn_readfirstlane((int)pg0)];
+  const int64_t pb = src.table[__builtin_amdgcn_readfirstlane((int)min(pg0 + 1, pg_last))];
+  const int64_t pc = src.table[__builtin_amdgcn_readfirstlane((int)min(pg0 + 2, pg_last))];
+  if (e0 >= src.m && valid == STILE && pg0 == pg_last) {  // whole tile of raw rows in one page
+    const char* b0 = src.pages + (pa * src.P + (t_first - pg0 * src.P)) * src.tok;
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i) dma16(b0 + off[i], base + 1024u * (w + SNW * i));
+    return;
+  }
+#pragma unroll 1  // rare boundary tiles: keep the per-lane row arithmetic small
+  for (int i = 0; i < DMA_PER_WAVE; ++i) {
+    int row, col;
+    slot_rowcol(w, i, lane, row, col);
+    const int64_t e = e0 + min(row, valid - 1);
+    const char* p;
+    if (e < src.m) {
+      p = src.rep + e * src.tok;
+    } else {
+      const int64_t t = src.raw_begin + (e - src.m), pg = t / src.P;
+      const int64_t page = pg == pg0 ? pa : (pg == pg0 + 1 ? pb : pc);
+      p = src.pages + (page * src.P + (t - pg * src.P)) * src.tok;
+    }
+    dma16(p + 16 * col, base + 1024u * (w + SNW * i));
+  }
+}
+
 }  // namespace lca

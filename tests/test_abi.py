@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert lca.lca_version() == 1000
+    assert lca.lca_version() == 1001
 
 
 def test_plan_matches_golden():
@@ -144,10 +144,10 @@ def test_condense_paged_argument_errors():
     lib = lca.load()
     reps = lca.LatentT(64, 64 + 1024, 0, 576, 0, 576, 0)
 
-    def call(page_rows=64, g=16, table=128, seq=256, max_groups=4, T=16, reps_=reps):
+    def call(page_rows=64, g=16, table=128, seq=256, max_groups=4, T=16, reps_=reps, step=0):
         cache = lca.PagedT(64, 576, page_rows, table, 4)
         return lib.lca_condense_paged(ctypes.byref(cache), 1, g, seq, seq, max_groups, 64, 0, 0, 16 * 576, T, 16,
-                                      0, 1.0, ctypes.byref(reps_), 64, 0, None, 0, 64, 1 << 20, None)
+                                      0, step, 1.0, ctypes.byref(reps_), 64, 0, None, 0, 64, 1 << 20, None)
     assert call(page_rows=40) == lca.LCA_ERR_UNSUPPORTED  # not a multiple of g
     assert call(g=12) == lca.LCA_ERR_UNSUPPORTED
     assert call(table=None) == lca.LCA_ERR_INVALID_ARG
@@ -156,6 +156,37 @@ def test_condense_paged_argument_errors():
     assert call(max_groups=-1) == lca.LCA_ERR_INVALID_ARG
     assert call(reps_=lca.LatentT(64, 64 + 1024, 0, 576, 0, 576, 1)) == lca.LCA_ERR_UNSUPPORTED
     assert call(max_groups=0) == lca.LCA_OK  # nothing to condense: no launch
+    # per-group summary queries: rows q_row0 + n * step .. + g must exist for n < max_groups
+    assert call(step=16, T=63) == lca.LCA_ERR_INVALID_ARG
+    assert "T = 63" in lca.lca_last_error()
+    assert call(step=-16, T=64) == lca.LCA_ERR_INVALID_ARG
+
+
+def test_paged_prefill_and_paged_decode_up_argument_errors():
+    lib = lca.load()
+    reps = lca.LatentT(64, 64 + 1024, 0, 576, 0, 576, 0)
+
+    def prefill(page_rows=64, table=128, seq=0, H=16, rb=0, cs=10, m=0, reps_=reps, row_stride=576):
+        cache = lca.PagedT(64, row_stride, page_rows, table, 4)
+        return lib.mla_latent_attn_prefill_chunk_paged(64, 0, 16 * 576, cs, 4, H, ctypes.byref(reps_), m,
+                                                       ctypes.byref(cache), seq, rb, 1.0, 64, 0, None, None)
+    assert prefill(page_rows=40) == lca.LCA_ERR_UNSUPPORTED
+    assert prefill(table=None) == lca.LCA_ERR_INVALID_ARG
+    assert prefill(seq=-1) == lca.LCA_ERR_INVALID_ARG
+    assert prefill(H=24) == lca.LCA_ERR_UNSUPPORTED
+    assert prefill(rb=11) == lca.LCA_ERR_INVALID_ARG               # raw rows must start at or before the chunk
+    assert prefill(m=2, reps_=lca.LatentT(64, 64 + 1024, 0, 576, 0, 576, 1)) == lca.LCA_ERR_UNSUPPORTED
+    assert prefill(m=2, row_stride=640) == lca.LCA_ERR_UNSUPPORTED  # reps and pages share one row stride
+
+    def dec(w=64, out=64, H=16, ws=None, wsb=0, max_entries=8):
+        cache = lca.PagedT(64, 576, 64, 128, 4)
+        return lib.mla_latent_attn_decode_paged_up(64, 0, 16 * 576, 1, H, ctypes.byref(reps), 256,
+                                                   ctypes.byref(cache), 256, 256, max_entries, 1.0, 64, None,
+                                                   w, 0, out, 0, ws, wsb, None)
+    assert dec(w=None) == lca.LCA_ERR_INVALID_ARG
+    assert dec(out=72) == lca.LCA_ERR_INVALID_ARG
+    assert dec(H=24) == lca.LCA_ERR_UNSUPPORTED
+    assert dec(max_entries=60000) == lca.LCA_ERR_WORKSPACE
 
 
 def _decode(lib, reps, raw, **kw):

@@ -291,6 +291,115 @@ def test_condense_and_decode_paged_ragged_end_to_end():
     tally.check()
 
 
+@pytest.mark.parametrize("page_rows", [16, 64])
+def test_prefill_paged_ragged_end_to_end(page_rows):
+    """Chunked prefill of three sequences of different lengths over shuffled
+    pages: before each chunk (ragged chunk starts) the groups that left the
+    window are condensed through lca_condense_paged with the g queries that
+    follow each group, then mla_latent_attn_prefill_chunk_paged attends the
+    chunk. Representatives against the oracle's condensation; attention
+    against the oracle on the GPU's representatives, and bitwise against the
+    dense prefill call on the same rows."""
+    Ls, w, g, sm = [1500, 2300, 900], 256, 16, 1.0
+    bounds = {0: [0, 300, 700, 1100, 1500], 1: [0, 500, 650, 1400, 2300], 2: [0, 257, 900]}
+    B, H = len(Ls), 16
+    cs, ks, qs = [], [], []
+    for b, L in enumerate(Ls):
+        c, kr = li.latent_cache(30 + b, 1, L)
+        li.plant_needles(30 + b, c, kr, 3, 14.0, 0, L)
+        cs.append(c[0]); ks.append(kr[0])
+        qs.append(li.queries(30 + b, 1, L, H, rho=0.5)[0])
+    pool, table = _page_pool([np.concatenate([c, k], -1) for c, k in zip(cs, ks)], page_rows, 17)
+    pool_t, table_t = dev(pool), torch.from_numpy(table).cuda()
+    cache_all = lca.paged_latent(pool_t, table_t)
+    i32 = lambda x: torch.tensor(x, dtype=torch.int32, device="cuda")  # noqa: E731
+    tally = AnchorTally()
+    for b, L in enumerate(Ls):
+        q_t = dev(qs[b])
+        m_cap = max(O.prefill_plan(bounds[b][-2], w, g), 1)
+        reps = torch.zeros((1, m_cap, 576), dtype=torch.bfloat16, device="cuda")
+        anchor = torch.full((1, m_cap), -1, dtype=torch.int32, device="cuda")
+        out = torch.empty((L, H, 512), dtype=torch.float32, device="cuda")
+        lse = torch.empty((L, H), dtype=torch.float32, device="cuda")
+        cache_b = lca.paged_latent(pool_t, table_t[b:b + 1])   # this sequence's block-table row
+        m = 0
+        for s0, e in zip(bounds[b][:-1], bounds[b][1:]):
+            ms = O.prefill_plan(s0, w, g)
+            if ms > m:
+                lca.lca_condense_paged(cache_b, 1, g, i32([m]), i32([ms - m]), ms - m, q_t[None], (m + 1) * g, sm,
+                                       lca.packed_latent(reps), anchor, q_row_step=g)
+                m = ms
+            lca.mla_latent_attn_prefill_chunk_paged(q_t[s0:e], s0, lca.packed_latent(reps[0]) if m else None, m,
+                                                    cache_all, b, m * g, sm, out[s0:e], lse[s0:e])
+        # the dense call on the same rows and representatives
+        dense = packed(cs[b], ks[b])
+        out_d = torch.empty_like(out)
+        lse_d = torch.empty_like(lse)
+        for s0, e in zip(bounds[b][:-1], bounds[b][1:]):
+            ms = O.prefill_plan(s0, w, g)
+            lca.mla_latent_attn_prefill_chunk(q_t[s0:e], s0, lca.packed_latent(reps[0]) if ms else None, ms,
+                                              lca.packed_latent(dense), ms * g, sm, out_d[s0:e], lse_d[s0:e])
+        torch.cuda.synchronize()
+        assert torch.equal(out, out_d) and torch.equal(lse, lse_d), f"paged and dense prefill differ (seq {b})"
+        r = host(reps)[0]
+        ga = host(anchor)[0].astype(np.int64)
+        m_final = O.prefill_plan(bounds[b][-2], w, g)
+        if m_final:
+            rc, rk, ra, ralpha, sc = O.condense(cs[b][None], ks[b][None], qs[b][None], g, 0, m_final, g, g, sm)
+            assert_close(r[:m_final, :512], rc[0], what=f"paged prefill reps seq {b}")
+            tally.add(ga[:m_final], ra[0], O.top2_margin(sc[0]))
+            np.testing.assert_array_equal(r[:m_final, 512:], ks[b][ga[:m_final]].astype(np.float64))
+        for s0, e in zip(bounds[b][:-1], bounds[b][1:]):
+            ms = O.prefill_plan(s0, w, g)
+            ro, rl = O.prefill_chunk(qs[b][s0:e], s0, r[:, :512], r[:, 512:], ms, cs[b], ks[b], ms * g, sm)
+            assert_close(host(out[s0:e]), ro, what=f"paged prefill o_latent seq {b} chunk {s0}")
+            assert_close(host(lse[s0:e]), rl, what=f"paged prefill lse seq {b} chunk {s0}")
+    tally.check()
+
+
+def test_decode_paged_up_equals_paged_decode_then_up_proj():
+    """Paged decode fused with W_UV: bitwise the paged decode followed by
+    mla_up_proj, and the up-projected output against the oracle."""
+    Ls, w, g, P = [1500, 2077, 3000, 1040, 777], 1024, 16, 64
+    B = len(Ls)
+    seqs, ms, rbs, reps = [], [], [], []
+    for b, L in enumerate(Ls):
+        c, kr = li.latent_cache(50 + b, 1, L)
+        li.plant_needles(50 + b, c, kr, 2, 14.0, 0, L)
+        seqs.append(np.concatenate([c[0], kr[0]], -1))
+        p = O.plan(L, w, g)
+        ms.append(p["m"]); rbs.append(p["raw_begin"])
+        rc, rk = li.latent_cache(70 + b, 1, max(p["m"], 1))
+        reps.append(np.concatenate([rc[0], rk[0]], -1)[:p["m"]])
+    pool, table = _page_pool(seqs, P, 9)
+    reps_t = torch.zeros((B, max(ms), 576), dtype=torch.bfloat16, device="cuda")
+    for b in range(B):
+        if ms[b]:
+            reps_t[b, :ms[b]] = dev(reps[b])
+    q = li.queries(51, B, 1, H, rho=0.5)[:, 0]
+    wuv = li.w_uv(51, H)
+    pool_t, table_t = dev(pool), torch.from_numpy(table).cuda()
+    i32 = lambda x: torch.tensor(x, dtype=torch.int32, device="cuda")  # noqa: E731
+    max_entries = max(m + L - rb for m, L, rb in zip(ms, Ls, rbs))
+    args = (dev(q), lca.packed_latent(reps_t), i32(ms), lca.paged_latent(pool_t, table_t), i32(rbs), i32(Ls),
+            max_entries, 1.0)
+    o1 = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
+    l1 = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    lca.mla_latent_attn_decode_paged(*args, o1, l1)
+    y1 = torch.empty((B, H, 128), dtype=torch.float32, device="cuda")
+    lca.mla_up_proj(o1, dev(wuv), y1)
+    o2, l2, y2 = torch.empty_like(o1), torch.empty_like(l1), torch.empty_like(y1)
+    lca.mla_latent_attn_decode_paged_up(*args, o2, dev(wuv), y2, l2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(y1, y2)
+    for b in range(B):
+        x = seqs[b][None]
+        rep = reps[b][None] if ms[b] else None
+        ro, _ = O.decode(q[b:b + 1], None if rep is None else rep[..., :512], None if rep is None else rep[..., 512:],
+                         ms[b], x[..., :512], x[..., 512:], rbs[b], Ls[b], 1.0)
+        assert_close(host(y2[b:b + 1]), O.up_proj(ro, wuv), what=f"paged decode_up out seq {b}")
+
+
 @pytest.mark.parametrize("B,L,g,with_alpha", [(3, 5000, 16, True), (2, 4100, 8, False), (1, 70000, 16, False)])
 def test_condense_streaming_kernel_equals_general_kernel(B, L, g, with_alpha):
     """Packed bf16 rows with one summary query per sequence take the streaming
