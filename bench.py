@@ -416,13 +416,18 @@ def prefill_leg(Lp):
                                               o_lat[s:e])
             if ev is not None:
                 ev[s // PF_C][1].record()
+        if ev is not None:
+            ev_up[0].record()
         lca.mla_up_proj(o_lat, wuv, out)
+        if ev is not None:
+            ev_up[1].record()
 
     run()
     torch.cuda.synchronize()
     n_chunks = (Lp + PF_C - 1) // PF_C
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(n_chunks)]
+    ev_up = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
@@ -431,6 +436,7 @@ def prefill_leg(Lp):
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
     attn_ms = sum(a.elapsed_time(b) for a, b in ev)
+    up_ms = ev_up[0].elapsed_time(ev_up[1])
     # algorithmic flops: every visible (query, entry) pair, 16 heads, QK 576 + PV 512
     pairs = 0
     for s in range(0, Lp, PF_C):
@@ -445,6 +451,9 @@ def prefill_leg(Lp):
             "attention_tflops": attn_flop / (attn_ms * 1e-3) / 1e12,
             "mfma_frac": attn_flop / (attn_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS,
             "up_proj_tflop": up_flop / 1e12,
+            "up_proj_ms": up_ms,
+            # latent read + output written + W_UV, bf16
+            "up_proj_hbm_frac": Lp * H * (512 + 128) * 2 / (up_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "context": "pages: 128K prefill 10.78 s MLA vs 4.40 s LCA, whole model on 8xH200"}
 
 

@@ -193,7 +193,8 @@ def test_prefill_128k_sampled_rows():
     that outputs stay unit-scale: per chunk the newly eligible groups are
     condensed with the 16 queries that follow each group; 256 sampled query
     rows of chunks 0, 1, 15 and 31 (each chunk's first and last row among
-    them) and 256 sampled representatives against the oracle."""
+    them) and 256 sampled representatives against the oracle; the W_UV
+    up-projection of all 131,072 x 16 outputs in one call, on the same rows."""
     L, C = 131072, 4096
     c, kr = li.latent_cache(7, 1, L)
     li.plant_needles(7, c, kr, 2, 14.0, 0, 64)       # visible to (almost) every row of chunk 0
@@ -217,6 +218,9 @@ def test_prefill_128k_sampled_rows():
             m = ms
         lca.mla_latent_attn_prefill_chunk(q_t[s0:s0 + C], s0, lca.packed_latent(reps) if m else None, m,
                                           lca.packed_latent(cache), m * G, 1.0, out[s0:s0 + C], lse[s0:s0 + C])
+    wuv = li.w_uv(7, H)
+    y = torch.empty((L, H, 128), dtype=torch.bfloat16, device="cuda")
+    lca.mla_up_proj(out, dev(wuv), y)  # the whole prefill's up-projection in one call
     torch.cuda.synchronize()
     r = host(reps)
     ga = host(anchor).astype(np.int64)
@@ -239,6 +243,7 @@ def test_prefill_128k_sampled_rows():
             assert np.abs(ro).max(axis=(1, 2)).min() > 0.5, "needles should keep every sampled row unit-scale"
         _assert_close_bf16_out(host(out[s0 + rows]), ro, what=f"prefill o_latent chunk {chunk}")
         assert_close(host(lse[s0 + rows]), rl, what=f"prefill lse chunk {chunk}")
+        assert_close(host(y[s0 + rows]), O.up_proj(host(out[s0 + rows]), wuv), what=f"up-projected chunk {chunk}")
 
 
 @pytest.mark.timeout(400)

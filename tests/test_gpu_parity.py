@@ -805,6 +805,24 @@ def test_up_proj_matches_oracle(xdt, ydt, T):
     assert_close(host(out), O.up_proj(x, w), tol=TOL, what="up_proj")
 
 
+@pytest.mark.parametrize("T,Hh,wdt,ydt", [(65, 16, torch.bfloat16, torch.bfloat16),
+                                          (1000, 16, torch.float32, torch.float32),
+                                          (4097, 1, torch.bfloat16, torch.bfloat16),
+                                          (777, 8, torch.float32, torch.bfloat16),
+                                          (600, 128, torch.bfloat16, torch.float32)])
+def test_up_proj_bf16_latent_shapes(T, Hh, wdt, ydt):
+    """bf16 latent above 64 tokens (the persistent streaming kernel): ragged
+    ends of the 32-token tiles, 1 to 128 heads, W_UV and output in either
+    precision."""
+    rng = np.random.default_rng(13 + T)
+    x = li.bf16_round((0.25 * rng.standard_normal((T, Hh, 512))).astype(np.float32))
+    w = li.w_uv(13, Hh)
+    out = torch.empty((T, Hh, 128), dtype=ydt, device="cuda")
+    lca.mla_up_proj(dev(x, torch.bfloat16), dev(w, wdt), out)
+    torch.cuda.synchronize()
+    assert_close(host(out), O.up_proj(x, w), tol=TOL, what=f"up_proj T={T} H={Hh}")
+
+
 # ------------------------------------------------------------- HIP graphs --
 def test_graph_replay_matches_eager():
     """Condense + fused decode captured in a HIP graph: every replay, with
