@@ -320,6 +320,28 @@ __device__ __forceinline__ int64_t big_wrow(int nb, int j, int H) {
   return s == 0 ? D_C + dd : D_ROW + 192 * (s - 1) + 128 + dd;
 }
 
+// Tile order of proj_big_kernel. Workgroups are dealt to the 8 XCDs round
+// robin (workgroup b runs on XCD b % 8), so XCD k takes the contiguous run
+// [k c, k c + c) of a tile order that walks groups of PB_GX token tiles
+// column block by column block: each XCD's L2 then serves about PB_GX token
+// tiles and a share of the weight columns, instead of two token tiles and
+// every weight column (x fastest). Measured at 4,096 tokens, d = 2,048,
+// H = 16: L2 misses drop from 134 to 96 MB per call while the call time stays
+// the same (the loop is bound by its own instruction stream, not by these
+// re-reads).
+constexpr int PB_GX = 4;
+__host__ __device__ inline int pb_columns(int H) { return 2 + (H + 1) / 2 + (H + 4) / 4; }
+__device__ __forceinline__ bool pb_tile_of(int b, int nx, int ny, int& x, int& y) {
+  const int n = nx * ny, c = (n + 7) / 8;
+  const int L = (b & 7) * c + (b >> 3);
+  if (L >= n) return false;
+  const int gsize = PB_GX * ny, g = L / gsize, r = L - g * gsize;
+  const int x0 = g * PB_GX, gw = min(PB_GX, nx - x0);
+  y = r / gw;
+  x = x0 + r - y * gw;
+  return true;
+}
+
 template <typename TQ>
 __global__ __launch_bounds__(64 * PB_WAVES, 2) void proj_big_kernel(ProjArgs pa) {
   __shared__ __align__(16) bf16_t ring[PJ_NBUF * PB_SLICE];
@@ -330,9 +352,10 @@ __global__ __launch_bounds__(64 * PB_WAVES, 2) void proj_big_kernel(ProjArgs pa)
   __shared__ int32_t tile_pos[PB_BM];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nb = blockIdx.y;
-  const int64_t tok0 = (int64_t)blockIdx.x * PB_BM;
   const int H = pa.H;
+  int bx, nb;
+  if (!pb_tile_of((int)blockIdx.x, (int)((pa.T + PB_BM - 1) / PB_BM), pb_columns(H), bx, nb)) return;
+  const int64_t tok0 = (int64_t)bx * PB_BM;
   int64_t my_dst = 0;
   int32_t my_pos = 0;
   if (tid < PB_BM) {
@@ -666,11 +689,12 @@ hipError_t launch_project(const void* x, int64_t x_stride, int64_t T, int d, con
                        (const bf16_t*)qn, T, H, (const bf16_t*)w_uk, q, q_stride, (int)(q_dtype == LCA_F32));
     return hipGetLastError();
   }
-  const dim3 gb((unsigned)((T + PB_BM - 1) / PB_BM), (unsigned)(2 + (H + 1) / 2 + (H + 4) / 4));
+  const int64_t pb_n = (T + PB_BM - 1) / PB_BM * pb_columns(H);
+  const dim3 gb((unsigned)(8 * ((pb_n + 7) / 8)));
   const dim3 gab((unsigned)((T + PB_BM - 1) / PB_BM), D_C / PB_BN, (unsigned)H);
   // 256-wide tiles once they fill most of the chip; below that the 128-wide
   // tiles keep more CUs busy
-  const bool big = (int64_t)gb.x * gb.y >= 224;
+  const bool big = pb_n >= 224;
   if (q_dtype == LCA_BF16) {
     if (big) {
       hipLaunchKernelGGL(proj_big_kernel<bf16_t>, gb, dim3(64 * PB_WAVES), 0, stream, pa);
