@@ -492,9 +492,7 @@ __global__ __launch_bounds__(256) void condense_ring_kernel(
   const char* seq = cache + (int64_t)b * seq_b;
   auto issue = [&](int64_t k) {
     const char* g0 = seq + (group_begin + wg + k * nw) * G * tok_b;
-    const uint32_t base = lds_off(&ring[w][k % NS][0]);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) dma16_nt(g0 + off[i], base + 1024u * i);
+    dma16_rows<1024u, true>(g0, off, lds_off(&ring[w][k % NS][0]));
   };
 #pragma unroll
   for (int k = 0; k < NS; ++k)

@@ -84,8 +84,7 @@ __device__ __forceinline__ void wave_tile_dma(const DmaSrc& src, int64_t e0, int
   const uint32_t base = lds_off(slot);
   if (e0 + WT <= e_end && (e0 + WT <= src.m || e0 >= src.m)) {
     const char* b0 = e0 < src.m ? src.rep + e0 * src.tok : src.raw + (e0 - src.m) * src.tok;
-#pragma unroll
-    for (int i = 0; i < WT_DMA; ++i) dma16_nt(b0 + off[i], base + 1024u * i);
+    dma16_rows<1024u, true>(b0, off, base);
   } else {
     const int valid = (int)min((int64_t)WT, e_end - e0);
     for (int i = 0; i < WT_DMA; ++i) {
@@ -139,8 +138,7 @@ struct PagedTiles {
     if (u < R) {
       const char* b0 = rep + u * WT * tok;
       if (v == WT) {
-#pragma unroll
-        for (int i = 0; i < WT_DMA; ++i) dma16_nt(b0 + off[i], base + 1024u * i);
+        dma16_rows<1024u, true>(b0, off, base);
       } else {
         for (int i = 0; i < WT_DMA; ++i) {
           const int Q = 64 * i + lane, row = Q / (D_ROW / 8), c = (Q - row * (D_ROW / 8)) ^ swz(row);
@@ -153,9 +151,7 @@ struct PagedTiles {
     const int64_t p0 = table[__builtin_amdgcn_readfirstlane((int)pg0)];
     const int64_t p1 = table[__builtin_amdgcn_readfirstlane((int)pg1)];
     if (v == WT && pg0 == pg1) {
-      const char* b0 = pages + (p0 * P + (t0 - pg0 * P)) * tok;
-#pragma unroll
-      for (int i = 0; i < WT_DMA; ++i) dma16_nt(b0 + off[i], base + 1024u * i);
+      dma16_rows<1024u, true>(pages + (p0 * P + (t0 - pg0 * P)) * tok, off, base);
     } else {
       for (int i = 0; i < WT_DMA; ++i) {
         const int Q = 64 * i + lane, row = Q / (D_ROW / 8), c = (Q - row * (D_ROW / 8)) ^ swz(row);

@@ -326,7 +326,7 @@ __device__ __forceinline__ int64_t big_wrow(int nb, int j, int H) {
 // column block by column block: each XCD's L2 then serves about PB_GX token
 // tiles and a share of the weight columns, instead of two token tiles and
 // every weight column (x fastest). Measured at 4,096 tokens, d = 2,048,
-// H = 16: L2 misses drop from 134 to 96 MB per call while the call time stays
+// H = 16: L2 misses drop from 137 to 98 MB per call while the call time stays
 // the same (the loop is bound by its own instruction stream, not by these
 // re-reads).
 constexpr int PB_GX = 4;

@@ -49,6 +49,47 @@ __device__ __forceinline__ void dma16_nt(const void* g, uint32_t lds_block) {
       : "v"(g), "s"(lds_block)
       : "memory");
 }
+// N direct loads of 16 bytes per lane: load i reads base + off[i] (base
+// wave-uniform, off[i] a per-lane byte offset below 4 GiB that the load adds
+// itself, so there is no 64-bit address arithmetic per load) into the LDS
+// block lds0 + STEP i. Three loads per asm block with m0 saved once; the
+// blocks step m0 with s_add_u32, which writes SCC (declared clobbered).
+// readfirstlane returns int, so the uniform values pass through uint32_t and
+// nothing is sign-extended into the 64-bit base.
+#define LCA_DMA3(MOD)                                  \
+  "s_mov_b32 %0, m0\n\t"                               \
+  "s_mov_b32 m0, %4\n\t"                               \
+  "global_load_lds_dwordx4 %1, %5" MOD "\n\t"          \
+  "s_add_u32 m0, m0, %6\n\t"                           \
+  "global_load_lds_dwordx4 %2, %5" MOD "\n\t"          \
+  "s_add_u32 m0, m0, %6\n\t"                           \
+  "global_load_lds_dwordx4 %3, %5" MOD "\n\t"          \
+  "s_mov_b32 m0, %0"
+template <uint32_t STEP, bool NT, int N>
+__device__ __forceinline__ void dma16_rows(const void* base, const uint32_t (&off)[N], uint32_t lds0) {
+  static_assert(N % 3 == 0, "three loads per asm block");
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint32_t b_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t b_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  const uint64_t bu = ((uint64_t)b_hi << 32) | (uint64_t)b_lo;
+  const uint32_t l0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds0);
+#pragma unroll
+  for (int j = 0; j < N; j += 3) {
+    uint32_t saved;
+    if constexpr (NT)
+      asm volatile(LCA_DMA3(" nt")
+                   : "=&s"(saved)
+                   : "v"(off[j]), "v"(off[j + 1]), "v"(off[j + 2]), "s"(l0 + STEP * (uint32_t)j), "s"(bu), "i"(STEP)
+                   : "memory", "scc");
+    else
+      asm volatile(LCA_DMA3("")
+                   : "=&s"(saved)
+                   : "v"(off[j]), "v"(off[j + 1]), "v"(off[j + 2]), "s"(l0 + STEP * (uint32_t)j), "s"(bu), "i"(STEP)
+                   : "memory", "scc");
+  }
+}
+#undef LCA_DMA3
+
 // wait until at most `newer` tiles issued after the one wanted are in flight
 __device__ __forceinline__ void wait_dma_newer(int newer) {
   static_assert(DMA_PER_WAVE == 9, "vmcnt immediates assume 9 loads per tile per wave");
@@ -109,8 +150,7 @@ __device__ __forceinline__ void tile_dma(const DmaSrc& src, int64_t e0, int64_t 
   const uint32_t base = lds_off(buf);
   if (e0 + STILE <= e_end && (e0 + STILE <= src.m || e0 >= src.m)) {
     const char* b0 = e0 < src.m ? src.rep + e0 * src.tok : src.raw + (e0 - src.m) * src.tok;
-#pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i) dma16(b0 + off[i], base + 1024u * (w + SNW * i));
+    dma16_rows<1024u * SNW, false>(b0, off, base + 1024u * w);
   } else {
     const int valid = (int)min((int64_t)STILE, e_end - e0);
 #pragma unroll 1  // rare boundary tiles: keep the per-lane row arithmetic small
@@ -144,9 +184,7 @@ __device__ __forceinline__ void tile_dma(const PagedDmaSrc& src, int64_t e0, int
   const uint32_t base = lds_off(buf);
   const int valid = (int)min((int64_t)STILE, e_end - e0);
   if (e0 + STILE <= src.m && valid == STILE) {  // whole tile of representatives
-    const char* b0 = src.rep + e0 * src.tok;
-#pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i) dma16(b0 + off[i], base + 1024u * (w + SNW * i));
+    dma16_rows<1024u * SNW, false>(src.rep + e0 * src.tok, off, base + 1024u * w);
     return;
   }
   // raw tokens of the tile's raw entries and their pages (page indices are
@@ -158,9 +196,8 @@ __device__ __forceinline__ void tile_dma(const PagedDmaSrc& src, int64_t e0, int
   const int64_t pb = src.table[__builtin_amdgcn_readfirstlane((int)min(pg0 + 1, pg_last))];
   const int64_t pc = src.table[__builtin_amdgcn_readfirstlane((int)min(pg0 + 2, pg_last))];
   if (e0 >= src.m && valid == STILE && pg0 == pg_last) {  // whole tile of raw rows in one page
-    const char* b0 = src.pages + (pa * src.P + (t_first - pg0 * src.P)) * src.tok;
-#pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i) dma16(b0 + off[i], base + 1024u * (w + SNW * i));
+    dma16_rows<1024u * SNW, false>(src.pages + (pa * src.P + (t_first - pg0 * src.P)) * src.tok, off,
+                                   base + 1024u * w);
     return;
   }
 #pragma unroll 1  // rare boundary tiles: keep the per-lane row arithmetic small
