@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define LCA_VERSION 1001 /* major*1000 + minor */
+#define LCA_VERSION 1002 /* major*1000 + minor */
 #define LCA_D_C 512      /* latent c_KV width */
 #define LCA_D_R 64       /* decoupled RoPE key width */
 #define LCA_D_ROW 576    /* one cached row: c_KV ++ k_R */
@@ -190,6 +190,48 @@ int lca_condense_paged(const lca_paged_t* cache, int32_t B, int32_t g, const int
                        int64_t q_row_step, float sm_scale, const lca_latent_t* reps, int32_t* anchor_idx,
                        int64_t anchor_seq_stride, float* alpha, int64_t alpha_seq_stride,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* One decode step's incremental condensation over a ragged batch on a
+ * paged cache, with the per-sequence state kept on the device, so that a
+ * decode step (lca_project, mla_latent_attn_decode_paged[_up], then this
+ * call) is the same launch sequence every step and a graph of one step can
+ * be replayed. 关键设计 1: a group is condensed with the mean of the most
+ * recent g queries once it leaves the window (reading R7: representatives
+ * are frozen afterwards).
+ *
+ * State of sequence b, device int32 [B] arrays (read and rewritten):
+ *   seq_raw_end[b]   L: cache tokens before this step's row. The step's row
+ *                    (token L) has been written to the cache by the caller,
+ *                    after the step's attention read [seq_raw_begin, L).
+ *   seq_m[b]         m: representatives so far; seq_raw_begin[b] = m g.
+ * For every b this call (one launch):
+ *   1. writes this step's query q[b] ([H, 576], q + b*q_seq_stride) to row
+ *      L mod g of the sequence's query ring (q_ring + b*q_ring_seq_stride,
+ *      g rows of [H, 576], contiguous, same dtype as q). Ring row j holds
+ *      the query of the latest token t = j (mod g); the caller fills it for
+ *      the g tokens before the first step;
+ *   2. if L + 1 - w >= (m + 1) g, condenses group m (tokens [m g, (m+1) g),
+ *      through the block table) with the mean over the g ring rows and the
+ *      H heads as its summary query, exactly as lca_condense_paged: the
+ *      representative goes to row m of reps (packed bf16 rows, sequence b
+ *      at reps->c + b * reps->c_seq_stride), the anchor (absolute token
+ *      index) to anchor_idx[b * anchor_seq_stride + m]; then m = m + 1;
+ *   3. writes the next step's state: seq_m = m, seq_raw_begin = m g,
+ *      seq_raw_end = L + 1, and, when non-null, pos[b] = L + 1 (int32) and
+ *      dst_row[b] (int64) = the pool row of token L + 1 through the block
+ *      table (-1 when token L + 1 lies past table_stride pages), which is
+ *      what lca_project needs for the next token.
+ * The caller guarantees that the block table maps every token read, that
+ * reps and anchor_idx have a row for every group condensed, and that the
+ * state is consistent (seq_raw_begin = seq_m g); out-of-range state is not
+ * detected. page_rows must be a multiple of g. Errors as for the other
+ * calls; nothing is allocated. */
+int lca_condense_step(const lca_paged_t* cache, int32_t B, int64_t w, int32_t g, const void* q,
+                      int32_t q_dtype, int64_t q_seq_stride, int32_t H, void* q_ring,
+                      int64_t q_ring_seq_stride, float sm_scale, const lca_latent_t* reps,
+                      int32_t* anchor_idx, int64_t anchor_seq_stride, int32_t* seq_m,
+                      int32_t* seq_raw_begin, int32_t* seq_raw_end, int32_t* pos, int64_t* dst_row,
+                      hipStream_t stream);
 
 /* Workspace bytes mla_latent_attn_decode needs for up to max_entries
  * attended rows per sequence (split-K partial results). */

@@ -29,7 +29,8 @@ D_C, D_R, D_ROW, D_V = 512, 64, 576, 128
 
 # every symbol include/lca.h declares
 EXPORTS = ("lca_version", "lca_last_error", "lca_plan", "lca_condense_workspace_size",
-           "lca_condense", "lca_condense_mode", "lca_condense_paged", "mla_latent_attn_decode_workspace_size",
+           "lca_condense", "lca_condense_mode", "lca_condense_paged", "lca_condense_step",
+           "mla_latent_attn_decode_workspace_size",
            "mla_latent_attn_decode", "mla_latent_attn_decode_paged", "mla_latent_attn_decode_paged_up",
            "mla_latent_attn_decode_up", "mla_latent_attn_decode_up_noalloc", "mla_latent_attn_prefill_chunk",
            "mla_latent_attn_prefill_chunk_paged",
@@ -100,6 +101,10 @@ def load() -> ctypes.CDLL:
     lib.lca_condense_paged.argtypes = [P(PagedT), c_int32, c_int32, c_void_p, c_void_p, c_int64, c_void_p, c_int32,
                                        c_int64, c_int64, c_int64, c_int32, c_int64, c_int64, c_float, P(LatentT),
                                        c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_size_t, c_void_p]
+    lib.lca_condense_step.restype = c_int32
+    lib.lca_condense_step.argtypes = [P(PagedT), c_int32, c_int64, c_int32, c_void_p, c_int32, c_int64, c_int32,
+                                      c_void_p, c_int64, c_float, P(LatentT), c_void_p, c_int64, c_void_p,
+                                      c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
     lib.mla_latent_attn_decode_paged.restype = c_int32
     lib.mla_latent_attn_decode_paged.argtypes = [c_void_p, c_int32, c_int64, c_int32, c_int32, P(LatentT),
                                                  c_void_p, P(PagedT), c_void_p, c_void_p, c_int64, c_float,
@@ -300,6 +305,33 @@ def lca_condense_paged(cache: PagedT, B: int, g: int, seq_group_begin: torch.Ten
         ctypes.byref(reps),
         anchor.data_ptr(), anchor.stride(0), _ptr(alpha), 0 if alpha is None else alpha.stride(0),
         ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def lca_condense_step(cache: PagedT, w: int, g: int, q: torch.Tensor, q_ring: torch.Tensor, sm_scale: float,
+                      reps: LatentT, anchor: torch.Tensor, seq_m: torch.Tensor, seq_raw_begin: torch.Tensor,
+                      seq_raw_end: torch.Tensor, pos: torch.Tensor | None = None,
+                      dst_row: torch.Tensor | None = None, stream=None) -> None:
+    """One decode step's incremental condensation with device-side state:
+    q [B, H, 576] (this step's queries), q_ring [B, g, H, 576] (same dtype);
+    seq_m, seq_raw_begin, seq_raw_end int32 [B] (rewritten); pos int32 [B] and
+    dst_row int64 [B] (optional) receive the next token's position and pool row."""
+    if q.dim() != 3 or q.shape[-1] != D_ROW or q.stride(-1) != 1 or q.stride(-2) != D_ROW:
+        raise ValueError("q must be [B, H, 576] with contiguous heads")
+    B, H = q.shape[0], q.shape[1]
+    if q_ring.dtype != q.dtype or q_ring.dim() != 4 or q_ring.shape[1:] != (g, H, D_ROW) or q_ring.shape[0] != B \
+            or q_ring.stride(1) != H * D_ROW or q_ring.stride(2) != D_ROW or q_ring.stride(3) != 1:
+        raise ValueError("q_ring must be [B, g, H, 576] of q's dtype with contiguous rows")
+    if anchor.dtype != torch.int32:
+        raise TypeError("anchor must be int32")
+    for t in (seq_m, seq_raw_begin, seq_raw_end) + ((pos,) if pos is not None else ()):
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() != B:
+            raise ValueError("per-sequence arrays must be contiguous int32 [B] tensors")
+    if dst_row is not None and (dst_row.dtype != torch.int64 or not dst_row.is_contiguous() or dst_row.numel() != B):
+        raise ValueError("dst_row must be a contiguous int64 [B] tensor")
+    _check(load().lca_condense_step(
+        ctypes.byref(cache), B, w, g, q.data_ptr(), dtype_code(q), q.stride(0), H, q_ring.data_ptr(),
+        q_ring.stride(0), sm_scale, ctypes.byref(reps), anchor.data_ptr(), anchor.stride(0), seq_m.data_ptr(),
+        seq_raw_begin.data_ptr(), seq_raw_end.data_ptr(), _ptr(pos), _ptr(dst_row), _stream(stream)))
 
 
 def mla_latent_attn_decode_paged(q: torch.Tensor, reps: LatentT, seq_m: torch.Tensor, cache: PagedT,

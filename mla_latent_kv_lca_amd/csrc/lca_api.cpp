@@ -189,6 +189,49 @@ int lca_condense_paged(const lca_paged_t* cache, int32_t B, int32_t g, const int
                     "lca_condense_paged launch");
 }
 
+int lca_condense_step(const lca_paged_t* cache, int32_t B, int64_t w, int32_t g, const void* q, int32_t q_dtype,
+                      int64_t q_seq_stride, int32_t H, void* q_ring, int64_t q_ring_seq_stride, float sm_scale,
+                      const lca_latent_t* reps, int32_t* anchor_idx, int64_t anchor_seq_stride, int32_t* seq_m,
+                      int32_t* seq_raw_begin, int32_t* seq_raw_end, int32_t* pos, int64_t* dst_row,
+                      hipStream_t stream) {
+  int rc;
+  if (cache == nullptr || cache->pages == nullptr || !aligned16(cache->pages))
+    return fail(LCA_ERR_INVALID_ARG, "cache pages must be a non-null 16-byte aligned pointer");
+  if (cache->row_stride < LCA_D_ROW || !mult8(cache->row_stride))
+    return fail(LCA_ERR_INVALID_ARG, "cache row_stride must be >= 576 and a multiple of 8");
+  if (cache->block_table == nullptr || cache->table_stride < 1)
+    return fail(LCA_ERR_INVALID_ARG, "block_table must be non-null with table_stride >= 1");
+  if (B < 1 || B > 65535) return fail(LCA_ERR_INVALID_ARG, "B must be in [1, 65535]");
+  if (w < 0) return fail(LCA_ERR_INVALID_ARG, "w must be >= 0");
+  if (g < 1 || g > LCA_MAX_G || (g & (g - 1)) != 0)
+    return fail(LCA_ERR_UNSUPPORTED, "g = %d: supported group sizes are powers of two up to %d", g, LCA_MAX_G);
+  if (cache->page_rows < 1 || cache->page_rows % g != 0)
+    return fail(LCA_ERR_UNSUPPORTED, "page_rows = %d must be a positive multiple of g = %d", cache->page_rows, g);
+  if (H < 1 || H > 1024) return fail(LCA_ERR_INVALID_ARG, "H must be in [1, 1024]");
+  if (q == nullptr || !aligned16(q)) return fail(LCA_ERR_INVALID_ARG, "q must be a non-null 16-byte aligned pointer");
+  if (!valid_dtype(q_dtype)) return fail(LCA_ERR_INVALID_ARG, "q_dtype %d is not LCA_BF16/LCA_F32", q_dtype);
+  if (!mult8(q_seq_stride) || q_seq_stride < 0)
+    return fail(LCA_ERR_INVALID_ARG, "q_seq_stride must be a non-negative multiple of 8 elements");
+  if (q_ring == nullptr || !aligned16(q_ring))
+    return fail(LCA_ERR_INVALID_ARG, "q_ring must be a non-null 16-byte aligned pointer");
+  if (!mult8(q_ring_seq_stride) || q_ring_seq_stride < (int64_t)g * H * LCA_D_ROW)
+    return fail(LCA_ERR_INVALID_ARG, "q_ring_seq_stride must be a multiple of 8 and >= g * H * 576 = %lld",
+                (long long)g * H * LCA_D_ROW);
+  if ((rc = check_latent(reps, "reps", true, true)) != LCA_OK) return rc;
+  if (reps->dtype != LCA_BF16 || static_cast<const char*>(reps->kr) != static_cast<const char*>(reps->c) + 2 * LCA_D_C ||
+      reps->kr_tok_stride != reps->c_tok_stride || reps->kr_seq_stride != reps->c_seq_stride)
+    return fail(LCA_ERR_UNSUPPORTED, "the step condensation writes packed bf16 representatives (k_R right after c_KV)");
+  if (anchor_idx == nullptr) return fail(LCA_ERR_INVALID_ARG, "anchor_idx is null");
+  if (anchor_seq_stride < 0) return fail(LCA_ERR_INVALID_ARG, "negative anchor_seq_stride");
+  if (seq_m == nullptr || seq_raw_begin == nullptr || seq_raw_end == nullptr)
+    return fail(LCA_ERR_INVALID_ARG, "seq_m, seq_raw_begin and seq_raw_end must be non-null device arrays");
+  if ((rc = check_scale(sm_scale)) != LCA_OK) return rc;
+  return hip_status(lca::launch_condense_step(*cache, B, w, g, q, q_dtype, q_seq_stride, H, q_ring, q_ring_seq_stride,
+                                              sm_scale, *reps, anchor_idx, anchor_seq_stride, seq_m, seq_raw_begin,
+                                              seq_raw_end, pos, dst_row, stream),
+                    "lca_condense_step launch");
+}
+
 size_t mla_latent_attn_decode_workspace_size(int32_t B, int32_t H, int64_t max_entries) {
   if (B < 1 || !lca::heads_supported(H) || max_entries < 1) return 0;
   const lca::DecodeSplit sp = lca::decode_split(B, lca::head_blocks(H), max_entries);

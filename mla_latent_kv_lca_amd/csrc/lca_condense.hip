@@ -569,6 +569,155 @@ __global__ __launch_bounds__(256) void condense_paged_kernel(
     alpha[(int64_t)b * alpha_seq + j * G + gr.my_row] = gr.a_mine;
 }
 
+// ---------------------------------------------------------------- step ----
+// One decode step's incremental condensation and bookkeeping over a ragged
+// batch on a paged cache, as one launch (so a decode step is a fixed
+// sequence of launches). Workgroup b = sequence b, QS_THREADS threads:
+//  - this step's query (token L = seq_raw_end[b]) goes to ring row L mod g;
+//  - after the step's row is appended the cache holds L + 1 tokens; when
+//    L + 1 - w >= (m + 1) g, group m is complete and is condensed (整体框架;
+//    关键设计 1: the mean of the most recent g queries, i.e. of the g ring
+//    rows, this step's query included, over all H heads) with the same group
+//    function as the other condense kernels, by wave 0;
+//  - the state for the next step is written: m, the raw range [m g, L + 1),
+//    and the position and physical cache row of token L + 1.
+// Every thread reads the state before the barrier that precedes its update.
+// The summary query reads this step's query from q, never from the ring row
+// the same workgroup writes.
+constexpr int QS_PH = 4;
+constexpr int QS_THREADS = 72 * QS_PH;
+template <typename TQ, int LG>
+__global__ __launch_bounds__(QS_THREADS) void condense_step_kernel(
+    const bf16_t* __restrict__ pages, int64_t row_stride, int page_rows, const int32_t* __restrict__ table,
+    int64_t table_stride, int64_t w, const TQ* __restrict__ q, int64_t q_seq, int H, TQ* __restrict__ ring,
+    int64_t ring_seq, float sm_scale, bf16_t* __restrict__ rc, int64_t rc_seq, int64_t rc_tok,
+    int32_t* __restrict__ anchor, int64_t anchor_seq, int32_t* __restrict__ seq_m,
+    int32_t* __restrict__ seq_raw_begin, int32_t* __restrict__ seq_raw_end, int32_t* __restrict__ pos,
+    int64_t* __restrict__ dst_row) {
+  constexpr int G = 1 << LG;
+  const int b = blockIdx.x, t = threadIdx.x, ch = t % 72, ph = t / 72;
+  const int64_t L = seq_raw_end[b];
+  const int64_t m = seq_m[b];
+  const int cur = (int)(L & (G - 1));
+  const bool cond = L + 1 - w >= (m + 1) * G;
+  const int64_t row_elems = (int64_t)H * D_ROW;
+  const TQ* qb = q + (int64_t)b * q_seq;
+  TQ* rb = ring + (int64_t)b * ring_seq;
+
+  // this step's query into its ring row (8 elements per store)
+  for (int64_t i = t; i < row_elems / 8; i += QS_THREADS) {
+    if constexpr (sizeof(TQ) == 2) {
+      *reinterpret_cast<uint4*>(rb + cur * row_elems + 8 * i) = *reinterpret_cast<const uint4*>(qb + 8 * i);
+    } else {
+      reinterpret_cast<float4*>(rb + cur * row_elems + 8 * i)[0] = reinterpret_cast<const float4*>(qb + 8 * i)[0];
+      reinterpret_cast<float4*>(rb + cur * row_elems + 8 * i)[1] = reinterpret_cast<const float4*>(qb + 8 * i)[1];
+    }
+  }
+  __shared__ float sh[QS_PH][D_ROW];
+  if (cond) {  // workgroup-uniform
+    // summary query: thread (chunk ch, phase ph) sums rows ph, ph + QS_PH, ...
+    // of the g*H rows (row r = ring row r / H, head r % H); the phases are
+    // added in phase order
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const int rows = G * H;
+    for (int r0 = ph; r0 < rows; r0 += 8 * QS_PH) {
+      float v[8][8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int r = r0 + u * QS_PH;
+        if (r < rows) {
+          const int slot = r / H, h = r - slot * H;
+          const TQ* src = slot == cur ? qb + h * D_ROW : rb + slot * row_elems + h * D_ROW;
+          load8_f32(src + ch * 8, v[u]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[u][i] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += v[u][i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sh[ph][ch * 8 + i] = acc[i];
+    __syncthreads();
+    if (t < 64) {  // wave 0 condenses group m
+      const int lane = t;
+      const float inv = 1.0f / (float)rows;
+      float qc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float sum = sh[0][8 * lane + i];
+        for (int k = 1; k < QS_PH; ++k) sum += sh[k][8 * lane + i];
+        qc[i] = sum * inv;
+      }
+      float qr = sh[0][D_C + lane];
+      for (int k = 1; k < QS_PH; ++k) qr += sh[k][D_C + lane];
+      qr *= inv;
+      const int64_t t0 = m * G;
+      const int64_t page = table[(int64_t)b * table_stride + t0 / page_rows];
+      const bf16_t* rows0 = pages + (page * page_rows + t0 % page_rows) * row_stride;
+      RowChunk<bf16_t> rowsv[G];
+      bf16_t krv[G];
+#pragma unroll
+      for (int r = 0; r < G; ++r) {
+        rowsv[r].load(rows0 + r * row_stride + 8 * lane);
+        krv[r] = __builtin_nontemporal_load(rows0 + r * row_stride + D_C + lane);
+      }
+      const GroupResult<bf16_t, LG> gr = condense_group<bf16_t, LG>(rowsv, krv, qc, qr, sm_scale, lane, LCA_MODE_LCA);
+      bf16_t* dst = rc + (int64_t)b * rc_seq + m * rc_tok;
+      store8(dst + 8 * lane, gr.acc);
+      dst[D_C + lane] = (bf16_t)f2bf(gr.kval);
+      if (lane == 0) anchor[(int64_t)b * anchor_seq + m] = (int32_t)(t0 + gr.arg);
+    }
+  }
+  __syncthreads();  // every thread has read the state it is about to be replaced
+  if (t == 0) {
+    const int64_t mn = m + (cond ? 1 : 0), Ln = L + 1;
+    seq_m[b] = (int32_t)mn;
+    seq_raw_begin[b] = (int32_t)(mn * G);
+    seq_raw_end[b] = (int32_t)Ln;
+    if (pos != nullptr) pos[b] = (int32_t)Ln;
+    if (dst_row != nullptr)
+      dst_row[b] = Ln / page_rows < table_stride
+                       ? (int64_t)table[(int64_t)b * table_stride + Ln / page_rows] * page_rows + Ln % page_rows
+                       : -1;
+  }
+}
+
+hipError_t launch_condense_step(const lca_paged_t& cache, int B, int64_t w, int g, const void* q, int q_dtype,
+                                int64_t q_seq_stride, int H, void* q_ring, int64_t q_ring_seq_stride,
+                                float sm_scale, const lca_latent_t& reps, int32_t* anchor, int64_t anchor_seq,
+                                int32_t* seq_m, int32_t* seq_raw_begin, int32_t* seq_raw_end, int32_t* pos,
+                                int64_t* dst_row, hipStream_t stream) {
+  int lg = 0;
+  while ((1 << lg) < g) ++lg;
+#define LCA_STEP(TQV, LGV)                                                                                    \
+  hipLaunchKernelGGL((condense_step_kernel<TQV, LGV>), dim3((unsigned)B), dim3(QS_THREADS), 0, stream,      \
+                     (const bf16_t*)cache.pages, cache.row_stride, cache.page_rows, cache.block_table,        \
+                     cache.table_stride, w, (const TQV*)q, q_seq_stride, H, (TQV*)q_ring, q_ring_seq_stride, \
+                     sm_scale, (bf16_t*)reps.c, reps.c_seq_stride, reps.c_tok_stride, anchor, anchor_seq,    \
+                     seq_m, seq_raw_begin, seq_raw_end, pos, dst_row)
+#define LCA_STEP_G(TQV)            \
+  switch (lg) {                    \
+    case 0: LCA_STEP(TQV, 0); break; \
+    case 1: LCA_STEP(TQV, 1); break; \
+    case 2: LCA_STEP(TQV, 2); break; \
+    case 3: LCA_STEP(TQV, 3); break; \
+    case 4: LCA_STEP(TQV, 4); break; \
+    default: LCA_STEP(TQV, 5); break; \
+  }
+  if (q_dtype == LCA_BF16) {
+    LCA_STEP_G(bf16_t)
+  } else {
+    LCA_STEP_G(float)
+  }
+#undef LCA_STEP_G
+#undef LCA_STEP
+  return hipGetLastError();
+}
+
 template <typename TC, typename TR, int LG>
 static void launch_k1(dim3 grid, hipStream_t st, const lca_latent_t& cache, const float* qbar,
                       int per_group_q, int64_t n_q, int64_t gb, int64_t ng, float sm,

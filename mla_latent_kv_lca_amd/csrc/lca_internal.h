@@ -33,6 +33,12 @@ hipError_t launch_condense_paged(const lca_paged_t& cache, int B, int g, const i
                                  int64_t q_row_step, float sm_scale, const lca_latent_t& reps, int32_t* anchor,
                                  int64_t anchor_seq, float* alpha, int64_t alpha_seq, float* qbar_ws,
                                  hipStream_t stream);
+// one decode step's incremental condensation and state update (paged cache)
+hipError_t launch_condense_step(const lca_paged_t& cache, int B, int64_t w, int g, const void* q, int q_dtype,
+                                int64_t q_seq_stride, int H, void* q_ring, int64_t q_ring_seq_stride,
+                                float sm_scale, const lca_latent_t& reps, int32_t* anchor, int64_t anchor_seq,
+                                int32_t* seq_m, int32_t* seq_raw_begin, int32_t* seq_raw_end, int32_t* pos,
+                                int64_t* dst_row, hipStream_t stream);
 hipError_t launch_condense(const lca_latent_t& cache, int B, int g, int64_t group_begin,
                            int64_t n_groups, const void* q, int q_dtype, int64_t q_seq_stride,
                            int64_t q_tok_stride, int H, int64_t q_row0, int64_t q_row_step,

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert lca.lca_version() == 1001
+    assert lca.lca_version() == 1002
 
 
 def test_plan_matches_golden():
@@ -187,6 +187,33 @@ def test_paged_prefill_and_paged_decode_up_argument_errors():
     assert dec(out=72) == lca.LCA_ERR_INVALID_ARG
     assert dec(H=24) == lca.LCA_ERR_UNSUPPORTED
     assert dec(max_entries=60000) == lca.LCA_ERR_WORKSPACE
+
+
+def test_condense_step_argument_errors():
+    lib = lca.load()
+    reps = lca.LatentT(64, 64 + 1024, 0, 576, 0, 576, 0)
+
+    def step(page_rows=64, table=128, B=2, w=1024, g=16, q=64, qdt=0, H=16, ring=64, ring_seq=16 * 16 * 576,
+             reps_=reps, anchor=64, sm=1.0, sm_arr=64, rb_arr=64, re_arr=64):
+        cache = lca.PagedT(64, 576, page_rows, table, 4)
+        return lib.lca_condense_step(ctypes.byref(cache), B, w, g, q, qdt, 16 * 576, H, ring, ring_seq, sm,
+                                     ctypes.byref(reps_), anchor, 0, sm_arr, rb_arr, re_arr, None, None, None)
+    assert step(page_rows=40) == lca.LCA_ERR_UNSUPPORTED          # not a multiple of g
+    assert step(g=12) == lca.LCA_ERR_UNSUPPORTED
+    assert step(g=64) == lca.LCA_ERR_UNSUPPORTED
+    assert step(table=None) == lca.LCA_ERR_INVALID_ARG
+    assert step(B=0) == lca.LCA_ERR_INVALID_ARG
+    assert step(w=-1) == lca.LCA_ERR_INVALID_ARG
+    assert step(q=None) == lca.LCA_ERR_INVALID_ARG
+    assert step(qdt=7) == lca.LCA_ERR_INVALID_ARG
+    assert step(ring=None) == lca.LCA_ERR_INVALID_ARG
+    assert step(ring_seq=16 * 16 * 576 - 8) == lca.LCA_ERR_INVALID_ARG  # ring shorter than g rows of H heads
+    assert step(reps_=lca.LatentT(64, 64 + 1024, 0, 576, 0, 576, 1)) == lca.LCA_ERR_UNSUPPORTED
+    assert step(anchor=None) == lca.LCA_ERR_INVALID_ARG
+    assert step(sm_arr=None) == lca.LCA_ERR_INVALID_ARG
+    assert step(re_arr=None) == lca.LCA_ERR_INVALID_ARG
+    assert step(sm=float("nan")) == lca.LCA_ERR_INVALID_ARG
+    assert "g = 12" in (step(g=12), lca.lca_last_error())[1]
 
 
 def _decode(lib, reps, raw, **kw):

@@ -10,7 +10,7 @@ import torch
 import lca_inputs as li
 import mla_latent_kv_lca_amd as lca
 from oracle import lca_oracle as O
-from tests.gpu_util import assert_close, dev, host
+from tests.gpu_util import AnchorTally, assert_close, dev, host
 
 pytestmark = pytest.mark.gpu
 
@@ -164,6 +164,106 @@ def test_projected_incremental_decode_loop():
                                        rows[L0:, :512], rows[L0:, 512:], w_, g, sm)
     assert m == m_ref
     assert_close(np.stack([host(v)[0] for v in outs]), ro, what="projected decode loop o_latent")
+
+
+def test_projected_decode_step_graph_ragged_paged():
+    """One projected decode step as a fixed launch sequence with its state on
+    the device (lca_project -> mla_latent_attn_decode_paged ->
+    lca_condense_step), captured once as a HIP graph and replayed for every
+    step of a ragged batch on shuffled 64-row pages, so that the sequences
+    complete groups at different steps. Per sequence: the step outputs
+    against the oracle's incremental loop on the rows and queries the GPU
+    produced; the final state, and the representatives and anchors
+    condensed during the loop."""
+    L0s, S, w_, g, d, H, P = [1300, 1111, 1057], 40, 1024, 16, 256, 16, 64
+    sm = 0.35
+    B = len(L0s)
+    cap = max(L0s) + S + 1                       # tokens mapped per sequence (the state looks one token ahead)
+    n_pg = -(-cap // P)
+    perm = np.random.default_rng(81).permutation(B * n_pg).astype(np.int32)
+    table = torch.from_numpy(perm.reshape(B, n_pg)).cuda()
+    pool = torch.zeros((B * n_pg, P, 576), dtype=torch.bfloat16, device="cuda")
+    rows_flat = pool.view(-1, 576)
+    cache = lca.paged_latent(pool, table)
+
+    def phys(b, t):
+        return int(perm[b * n_pg + t // P]) * P + t % P
+
+    wp, wuk = li.w_proj(81, H, d), li.w_uk(81, H)
+    wp_t, wuk_t = dev(wp), dev(wuk)
+    xs = [li.hidden_states(82 + b, L0s[b] + S, d) for b in range(B)]
+    ring = torch.empty((B, g, H, 576), dtype=torch.bfloat16, device="cuda")
+    q_hist = []
+    for b in range(B):                           # prompts into their pages; their last g queries fill the ring
+        L0 = L0s[b]
+        qp = torch.empty((L0, H, 576), dtype=torch.bfloat16, device="cuda")
+        dst = torch.tensor([phys(b, t) for t in range(L0)], dtype=torch.int64, device="cuda")
+        lca.lca_project(dev(xs[b][:L0]), torch.arange(L0, dtype=torch.int32, device="cuda"), wp_t, wuk_t,
+                        rows_flat, dst, qp)
+        for t in range(L0 - g, L0):
+            ring[b, t % g] = qp[t]
+        q_hist.append(qp[L0 - g:].clone())
+    m0 = [O.plan(L, w_, g)["m"] for L in L0s]
+    m_cap = O.plan(max(L0s) + S, w_, g)["m"] + 1
+    reps = torch.zeros((B, m_cap, 576), dtype=torch.bfloat16, device="cuda")
+    anchor = torch.full((B, m_cap), -1, dtype=torch.int32, device="cuda")
+    i32 = lambda v: torch.tensor(v, dtype=torch.int32, device="cuda")  # noqa: E731
+    lca.lca_condense_paged(cache, B, g, i32([0] * B), i32(m0), max(m0), ring, 0, sm, lca.packed_latent(reps),
+                           anchor)
+    seq_m, seq_rb, seq_re = i32(m0), i32([m * g for m in m0]), i32(L0s)
+    pos = i32(L0s)
+    dst_row = torch.tensor([phys(b, L0s[b]) for b in range(B)], dtype=torch.int64, device="cuda")
+    x_step = torch.empty((B, d), dtype=torch.bfloat16, device="cuda")
+    q_step = torch.empty((B, H, 576), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
+    max_entries = max(m0) + cap
+    ws_dec = lca.decode_workspace(B, H, max_entries)
+    ws_proj = torch.empty(lca.lca_project_workspace_size(B, H), dtype=torch.uint8, device="cuda")
+    reps_l = lca.packed_latent(reps)
+
+    def step():
+        lca.lca_project(x_step, pos, wp_t, wuk_t, rows_flat, dst_row, q_step, workspace=ws_proj)
+        lca.mla_latent_attn_decode_paged(q_step, reps_l, seq_m, cache, seq_rb, seq_re, max_entries, sm, o,
+                                         workspace=ws_dec)
+        lca.lca_condense_step(cache, w_, g, q_step, ring, sm, reps_l, anchor, seq_m, seq_rb, seq_re, pos, dst_row)
+
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    x_all = [dev(xs[b]) for b in range(B)]
+    outs, qs = [], []
+    for st in range(S):
+        for b in range(B):
+            x_step[b].copy_(x_all[b][L0s[b] + st])
+        graph.replay()
+        outs.append(o.clone())
+        qs.append(q_step.clone())
+    torch.cuda.synchronize()
+
+    pool_h = host(pool).reshape(-1, 576)
+    reps_h, anchor_h = host(reps), host(anchor).astype(np.int64)
+    tally = AnchorTally()
+    for b in range(B):
+        L0 = L0s[b]
+        rows = pool_h[[phys(b, t) for t in range(L0 + S)]]
+        steps_q = np.stack([host(v[b]) for v in qs])
+        ro, _, rc_ref, rk_ref, m_ref = O.decode_loop(rows[:L0, :512], rows[:L0, 512:], host(q_hist[b]), steps_q,
+                                                     rows[L0:, :512], rows[L0:, 512:], w_, g, sm)
+        assert_close(np.stack([host(v[b]) for v in outs]), ro, what=f"step outputs, sequence {b}")
+        assert host(seq_m)[b] == m_ref and host(seq_rb)[b] == m_ref * g and host(seq_re)[b] == L0 + S
+        assert host(pos)[b] == L0 + S and host(dst_row)[b] == phys(b, L0 + S)
+        new = slice(m0[b], m_ref)               # the groups the loop condensed
+        assert m_ref > m0[b]
+        assert_close(reps_h[b, new, :512], rc_ref[new], what=f"loop representatives, sequence {b}")
+        np.testing.assert_array_equal(reps_h[b, new, 512:], rows[anchor_h[b, new], 512:])
+        allq = np.concatenate([host(q_hist[b]), steps_q])   # history, then one query per step
+        for j in range(m0[b], m_ref):           # anchors: the oracle's argmax wherever it is clear
+            st = (j + 1) * g + w_ - L0 - 1     # the step after which group j completes
+            _, _, _, a_ref, sc = O.condense_group(rows[j * g:(j + 1) * g, :512], rows[j * g:(j + 1) * g, 512:],
+                                                  O.summary_query(allq[st + 1:st + 1 + g]), sm)
+            tally.add(anchor_h[b, j:j + 1] - j * g, np.array([a_ref]), O.top2_margin(sc)[None])
+    tally.check()
 
 
 @pytest.mark.parametrize("T", [32, 4096])
