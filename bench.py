@@ -692,11 +692,57 @@ def million_leg(steps=256):
     t_init = _graph_time(lambda k: initial(), 1)
     t_loop = _graph_time(lambda k: loop(), 1)
     ent0 = p0["n_entries"]
+
+    # The same loop with its state on the device: every step is the same two
+    # launches sequences (mla_latent_attn_decode_paged_up over the cache seen
+    # as one page, then lca_condense_step), no host decision inside the graph.
+    pool = cache.view(1, L0 + steps, 576)
+    table = torch.zeros((1, 1), dtype=torch.int32, device="cuda")
+    pc = lca.paged_latent(pool, table)
+    ring = torch.empty((1, G, H, 576), dtype=torch.bfloat16, device="cuda")
+    i32 = lambda v: torch.tensor([v], dtype=torch.int32, device="cuda")  # noqa: E731
+    st0 = [i32(p0["m"]), i32(p0["m"] * G), i32(L0)]
+    state = [torch.empty_like(t) for t in st0]
+    o_d = torch.empty_like(o_lat)
+    out_d = torch.empty_like(out)
+
+    def reset():
+        for a_, b_ in zip(state, st0):
+            a_.copy_(b_)
+        for t in range(L0 - G, L0):  # ring row t mod g: the history's query of token t
+            ring[0, t % G] = qall[0, t - (L0 - G)]
+
+    def dev_loop():
+        for st in range(steps):
+            lca.mla_latent_attn_decode_paged_up(qall[:, G + st], rl, state[0], pc, state[1], state[2],
+                                                p1["n_entries"], 1.0, o_d, wuv, out_d, None, dws)
+            lca.lca_condense_step(pc, W, G, qall[:, G + st], ring, 1.0, rl, anchor, state[0], state[1], state[2])
+
+    stream = torch.cuda.current_stream()
+    reset()
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        dev_loop()
+    reset()
+    gr.replay()
+    reset()
+    torch.cuda.synchronize()
+    a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    gr.replay()
+    b_.record(stream)
+    torch.cuda.synchronize()
+    t_dev = a.elapsed_time(b_) * 1e-3
+    m_end = int(state[0].item())
     return {"seq_len": L0, "steps": steps, "entries": ent0, "initial_condense_us": t_init * 1e6,
             "initial_condense_gbs": p0["m"] * (G * ROW_BYTES + ROW_BYTES + 4) / t_init / 1e9,
             "incremental_condenses": n_inc[0], "us_per_step": t_loop / steps * 1e6,
             "decode_gbs": ent0 * ROW_BYTES / (t_loop / steps) / 1e9,
-            "context_tokens_per_s": (L0 + steps / 2) / (t_loop / steps)}
+            "context_tokens_per_s": (L0 + steps / 2) / (t_loop / steps),
+            "device_state_loop": {"us_per_step": t_dev / steps * 1e6,
+                                  "launches_per_step": "mla_latent_attn_decode_paged_up + lca_condense_step",
+                                  "incremental_condenses": m_end - p0["m"]}}
 
 
 D_MODEL = 2048  # hidden width of the projection leg: H heads x 128
