@@ -693,9 +693,10 @@ def million_leg(steps=256):
     t_loop = _graph_time(lambda k: loop(), 1)
     ent0 = p0["n_entries"]
 
-    # The same loop with its state on the device: every step is the same two
-    # launches sequences (mla_latent_attn_decode_paged_up over the cache seen
-    # as one page, then lca_condense_step), no host decision inside the graph.
+    # The same loop with its state on the device: every step is the same call,
+    # mla_latent_attn_decode_paged_up_step over the cache seen as one page (the
+    # step condensation inside its up-projection launch), no host decision
+    # inside the graph.
     pool = cache.view(1, L0 + steps, 576)
     table = torch.zeros((1, 1), dtype=torch.int32, device="cuda")
     pc = lca.paged_latent(pool, table)
@@ -714,9 +715,9 @@ def million_leg(steps=256):
 
     def dev_loop():
         for st in range(steps):
-            lca.mla_latent_attn_decode_paged_up(qall[:, G + st], rl, state[0], pc, state[1], state[2],
-                                                p1["n_entries"], 1.0, o_d, wuv, out_d, None, dws)
-            lca.lca_condense_step(pc, W, G, qall[:, G + st], ring, 1.0, rl, anchor, state[0], state[1], state[2])
+            lca.mla_latent_attn_decode_paged_up_step(qall[:, G + st], rl, state[0], pc, state[1], state[2],
+                                                     p1["n_entries"], 1.0, o_d, wuv, out_d, W, G, ring, anchor,
+                                                     workspace=dws)
 
     stream = torch.cuda.current_stream()
     reset()
@@ -741,7 +742,7 @@ def million_leg(steps=256):
             "decode_gbs": ent0 * ROW_BYTES / (t_loop / steps) / 1e9,
             "context_tokens_per_s": (L0 + steps / 2) / (t_loop / steps),
             "device_state_loop": {"us_per_step": t_dev / steps * 1e6,
-                                  "launches_per_step": "mla_latent_attn_decode_paged_up + lca_condense_step",
+                                  "call_per_step": "mla_latent_attn_decode_paged_up_step",
                                   "incremental_condenses": m_end - p0["m"]}}
 
 

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define LCA_VERSION 1002 /* major*1000 + minor */
+#define LCA_VERSION 1003 /* major*1000 + minor */
 #define LCA_D_C 512      /* latent c_KV width */
 #define LCA_D_R 64       /* decoupled RoPE key width */
 #define LCA_D_ROW 576    /* one cached row: c_KV ++ k_R */
@@ -303,6 +303,38 @@ int mla_latent_attn_decode_paged_up(const void* q, int32_t q_dtype, int64_t q_se
                                     float* o_latent, float* lse, const void* w_uv, int32_t w_dtype, void* out,
                                     int32_t out_dtype, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
+
+/* The step condensation of lca_condense_step as the tail of a paged decode
+ * with W_UV (a serving layout: one decode step is then two calls,
+ * lca_project and this one, the same every step). Fields as the arguments
+ * of lca_condense_step of the same names; pos and dst_row may be null. */
+typedef struct {
+  int64_t w;                  /* window */
+  int32_t g;                  /* group size */
+  void* q_ring;               /* [B, g, H, 576] query ring, q's dtype */
+  int64_t q_ring_seq_stride;  /* elements between sequences of the ring */
+  int32_t* anchor_idx;
+  int64_t anchor_seq_stride;
+  int32_t* pos;               /* out: next token's position, int32 [B] */
+  int64_t* dst_row;           /* out: next token's pool row, int64 [B] */
+} lca_step_t;
+
+/* mla_latent_attn_decode_paged_up, then lca_condense_step with this step's
+ * queries q and the same reps, cache, seq_m, seq_raw_begin, seq_raw_end and
+ * sm_scale (整体框架 for the attention, 关键设计 1 for the condensation).
+ * The per-sequence arrays are read by the attention and then rewritten for
+ * the next step, so they are not const here. For B <= 64 the condensation
+ * runs as extra workgroups of the W_UV up-projection kernel, which follows
+ * the attention kernel, so the step costs no launch of its own; for larger
+ * batches it is launched after the projection. Results are bitwise those of
+ * the two calls in sequence. Workspace as for mla_latent_attn_decode_paged. */
+int mla_latent_attn_decode_paged_up_step(const void* q, int32_t q_dtype, int64_t q_seq_stride, int32_t B,
+                                         int32_t H, const lca_latent_t* reps, int32_t* seq_m,
+                                         const lca_paged_t* cache, int32_t* seq_raw_begin,
+                                         int32_t* seq_raw_end, int64_t max_entries, float sm_scale,
+                                         float* o_latent, float* lse, const void* w_uv, int32_t w_dtype,
+                                         void* out, int32_t out_dtype, const lca_step_t* step,
+                                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* mla_latent_attn_decode followed by mla_up_proj of its output (the MLA
  * page's projection back to each head's value space, 三.1), with the split

@@ -32,6 +32,7 @@ EXPORTS = ("lca_version", "lca_last_error", "lca_plan", "lca_condense_workspace_
            "lca_condense", "lca_condense_mode", "lca_condense_paged", "lca_condense_step",
            "mla_latent_attn_decode_workspace_size",
            "mla_latent_attn_decode", "mla_latent_attn_decode_paged", "mla_latent_attn_decode_paged_up",
+           "mla_latent_attn_decode_paged_up_step",
            "mla_latent_attn_decode_up", "mla_latent_attn_decode_up_noalloc", "mla_latent_attn_prefill_chunk",
            "mla_latent_attn_prefill_chunk_paged",
            "mla_up_proj",
@@ -53,6 +54,11 @@ class LatentT(ctypes.Structure):
 class PagedT(ctypes.Structure):
     _fields_ = [("pages", c_void_p), ("row_stride", c_int64), ("page_rows", c_int32),
                 ("block_table", c_void_p), ("table_stride", c_int64)]
+
+
+class StepT(ctypes.Structure):
+    _fields_ = [("w", c_int64), ("g", c_int32), ("q_ring", c_void_p), ("q_ring_seq_stride", c_int64),
+                ("anchor_idx", c_void_p), ("anchor_seq_stride", c_int64), ("pos", c_void_p), ("dst_row", c_void_p)]
 
 
 class PlanT(ctypes.Structure):
@@ -114,6 +120,11 @@ def load() -> ctypes.CDLL:
                                                     c_void_p, P(PagedT), c_void_p, c_void_p, c_int64, c_float,
                                                     c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_int32,
                                                     c_void_p, c_size_t, c_void_p]
+    lib.mla_latent_attn_decode_paged_up_step.restype = c_int32
+    lib.mla_latent_attn_decode_paged_up_step.argtypes = [c_void_p, c_int32, c_int64, c_int32, c_int32, P(LatentT),
+                                                         c_void_p, P(PagedT), c_void_p, c_void_p, c_int64, c_float,
+                                                         c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_int32,
+                                                         P(StepT), c_void_p, c_size_t, c_void_p]
     lib.mla_latent_attn_prefill_chunk_paged.restype = c_int32
     lib.mla_latent_attn_prefill_chunk_paged.argtypes = [c_void_p, c_int32, c_int64, c_int64, c_int32, c_int32,
                                                         P(LatentT), c_int64, P(PagedT), c_int32, c_int64, c_float,
@@ -382,6 +393,45 @@ def mla_latent_attn_decode_paged_up(q: torch.Tensor, reps: LatentT, seq_m: torch
         ctypes.byref(cache), seq_raw_begin.data_ptr(), seq_raw_end.data_ptr(), max_entries, sm_scale,
         o_latent.data_ptr(), _ptr(lse), w_uv.data_ptr(), dtype_code(w_uv), out.data_ptr(), dtype_code(out),
         ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def mla_latent_attn_decode_paged_up_step(q: torch.Tensor, reps: LatentT, seq_m: torch.Tensor, cache: PagedT,
+                                         seq_raw_begin: torch.Tensor, seq_raw_end: torch.Tensor, max_entries: int,
+                                         sm_scale: float, o_latent: torch.Tensor, w_uv: torch.Tensor,
+                                         out: torch.Tensor, w: int, g: int, q_ring: torch.Tensor,
+                                         anchor: torch.Tensor, pos: torch.Tensor | None = None,
+                                         dst_row: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                                         workspace: torch.Tensor | None = None, stream=None) -> None:
+    """mla_latent_attn_decode_paged_up followed by lca_condense_step (the step
+    condensation inside the merge / W_UV launch): arguments of the two."""
+    if q.dim() != 3 or q.shape[-1] != D_ROW or q.stride(-1) != 1 or q.stride(-2) != D_ROW:
+        raise ValueError("q must be [B, H, 576] with contiguous heads")
+    B, H = q.shape[0], q.shape[1]
+    if o_latent.dtype != torch.float32 or not o_latent.is_contiguous() or o_latent.shape != (B, H, D_C):
+        raise ValueError("o_latent must be a contiguous fp32 [B, H, 512] tensor")
+    for t in (seq_m, seq_raw_begin, seq_raw_end) + ((pos,) if pos is not None else ()):
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() != B:
+            raise ValueError("per-sequence arrays must be contiguous int32 [B] tensors")
+    if dst_row is not None and (dst_row.dtype != torch.int64 or not dst_row.is_contiguous() or dst_row.numel() != B):
+        raise ValueError("dst_row must be a contiguous int64 [B] tensor")
+    if q_ring.dtype != q.dtype or q_ring.dim() != 4 or q_ring.shape[1:] != (g, H, D_ROW) or q_ring.shape[0] != B \
+            or q_ring.stride(1) != H * D_ROW or q_ring.stride(2) != D_ROW or q_ring.stride(3) != 1:
+        raise ValueError("q_ring must be [B, g, H, 576] of q's dtype with contiguous rows")
+    if anchor.dtype != torch.int32:
+        raise TypeError("anchor must be int32")
+    _check_lse(lse, B, H)
+    if not w_uv.is_contiguous() or tuple(w_uv.shape) != (H, D_C, D_V):
+        raise ValueError("w_uv must be a contiguous [H, 512, 128] tensor")
+    if not out.is_contiguous() or tuple(out.shape) != (B, H, D_V):
+        raise ValueError("out must be a contiguous [B, H, 128] tensor")
+    step = StepT(w, g, q_ring.data_ptr(), q_ring.stride(0), anchor.data_ptr(), anchor.stride(0), _ptr(pos),
+                 _ptr(dst_row))
+    ws = _workspace(mla_latent_attn_decode_workspace_size(B, H, max_entries), q, workspace)
+    _check(load().mla_latent_attn_decode_paged_up_step(
+        q.data_ptr(), dtype_code(q), q.stride(0), B, H, ctypes.byref(reps), seq_m.data_ptr(),
+        ctypes.byref(cache), seq_raw_begin.data_ptr(), seq_raw_end.data_ptr(), max_entries, sm_scale,
+        o_latent.data_ptr(), _ptr(lse), w_uv.data_ptr(), dtype_code(w_uv), out.data_ptr(), dtype_code(out),
+        ctypes.byref(step), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def mla_latent_attn_decode(q: torch.Tensor, reps: LatentT | None, m: int, raw: LatentT | None,

@@ -189,11 +189,15 @@ int lca_condense_paged(const lca_paged_t* cache, int32_t B, int32_t g, const int
                     "lca_condense_paged launch");
 }
 
-int lca_condense_step(const lca_paged_t* cache, int32_t B, int64_t w, int32_t g, const void* q, int32_t q_dtype,
-                      int64_t q_seq_stride, int32_t H, void* q_ring, int64_t q_ring_seq_stride, float sm_scale,
-                      const lca_latent_t* reps, int32_t* anchor_idx, int64_t anchor_seq_stride, int32_t* seq_m,
-                      int32_t* seq_raw_begin, int32_t* seq_raw_end, int32_t* pos, int64_t* dst_row,
-                      hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+// Arguments of the step condensation (lca_condense_step, and the step part of
+// mla_latent_attn_decode_paged_up_step) other than the query buffer.
+int check_step(const lca_paged_t* cache, int32_t B, int64_t w, int32_t g, int32_t H, const void* q_ring,
+               int64_t q_ring_seq_stride, const lca_latent_t* reps, const int32_t* anchor_idx,
+               int64_t anchor_seq_stride, const int32_t* seq_m, const int32_t* seq_raw_begin,
+               const int32_t* seq_raw_end) {
   int rc;
   if (cache == nullptr || cache->pages == nullptr || !aligned16(cache->pages))
     return fail(LCA_ERR_INVALID_ARG, "cache pages must be a non-null 16-byte aligned pointer");
@@ -208,10 +212,6 @@ int lca_condense_step(const lca_paged_t* cache, int32_t B, int64_t w, int32_t g,
   if (cache->page_rows < 1 || cache->page_rows % g != 0)
     return fail(LCA_ERR_UNSUPPORTED, "page_rows = %d must be a positive multiple of g = %d", cache->page_rows, g);
   if (H < 1 || H > 1024) return fail(LCA_ERR_INVALID_ARG, "H must be in [1, 1024]");
-  if (q == nullptr || !aligned16(q)) return fail(LCA_ERR_INVALID_ARG, "q must be a non-null 16-byte aligned pointer");
-  if (!valid_dtype(q_dtype)) return fail(LCA_ERR_INVALID_ARG, "q_dtype %d is not LCA_BF16/LCA_F32", q_dtype);
-  if (!mult8(q_seq_stride) || q_seq_stride < 0)
-    return fail(LCA_ERR_INVALID_ARG, "q_seq_stride must be a non-negative multiple of 8 elements");
   if (q_ring == nullptr || !aligned16(q_ring))
     return fail(LCA_ERR_INVALID_ARG, "q_ring must be a non-null 16-byte aligned pointer");
   if (!mult8(q_ring_seq_stride) || q_ring_seq_stride < (int64_t)g * H * LCA_D_ROW)
@@ -225,6 +225,25 @@ int lca_condense_step(const lca_paged_t* cache, int32_t B, int64_t w, int32_t g,
   if (anchor_seq_stride < 0) return fail(LCA_ERR_INVALID_ARG, "negative anchor_seq_stride");
   if (seq_m == nullptr || seq_raw_begin == nullptr || seq_raw_end == nullptr)
     return fail(LCA_ERR_INVALID_ARG, "seq_m, seq_raw_begin and seq_raw_end must be non-null device arrays");
+  return LCA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int lca_condense_step(const lca_paged_t* cache, int32_t B, int64_t w, int32_t g, const void* q, int32_t q_dtype,
+                      int64_t q_seq_stride, int32_t H, void* q_ring, int64_t q_ring_seq_stride, float sm_scale,
+                      const lca_latent_t* reps, int32_t* anchor_idx, int64_t anchor_seq_stride, int32_t* seq_m,
+                      int32_t* seq_raw_begin, int32_t* seq_raw_end, int32_t* pos, int64_t* dst_row,
+                      hipStream_t stream) {
+  int rc;
+  if ((rc = check_step(cache, B, w, g, H, q_ring, q_ring_seq_stride, reps, anchor_idx, anchor_seq_stride, seq_m,
+                       seq_raw_begin, seq_raw_end)) != LCA_OK)
+    return rc;
+  if (q == nullptr || !aligned16(q)) return fail(LCA_ERR_INVALID_ARG, "q must be a non-null 16-byte aligned pointer");
+  if (!valid_dtype(q_dtype)) return fail(LCA_ERR_INVALID_ARG, "q_dtype %d is not LCA_BF16/LCA_F32", q_dtype);
+  if (!mult8(q_seq_stride) || q_seq_stride < 0)
+    return fail(LCA_ERR_INVALID_ARG, "q_seq_stride must be a non-negative multiple of 8 elements");
   if ((rc = check_scale(sm_scale)) != LCA_OK) return rc;
   return hip_status(lca::launch_condense_step(*cache, B, w, g, q, q_dtype, q_seq_stride, H, q_ring, q_ring_seq_stride,
                                               sm_scale, *reps, anchor_idx, anchor_seq_stride, seq_m, seq_raw_begin,
@@ -352,6 +371,34 @@ int mla_latent_attn_decode_paged_up(const void* q, int32_t q_dtype, int64_t q_se
                                                 seq_raw_end, max_entries, sm_scale, o_latent, lse, w_uv, w_dtype,
                                                 out, out_dtype, workspace, stream),
                     "mla_latent_attn_decode_paged_up launch");
+}
+
+int mla_latent_attn_decode_paged_up_step(const void* q, int32_t q_dtype, int64_t q_seq_stride, int32_t B,
+                                         int32_t H, const lca_latent_t* reps, int32_t* seq_m,
+                                         const lca_paged_t* cache, int32_t* seq_raw_begin, int32_t* seq_raw_end,
+                                         int64_t max_entries, float sm_scale, float* o_latent, float* lse,
+                                         const void* w_uv, int32_t w_dtype, void* out, int32_t out_dtype,
+                                         const lca_step_t* step, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
+  size_t need = 0;
+  int rc = check_decode_paged(q, q_dtype, q_seq_stride, B, H, reps, seq_m, cache, seq_raw_begin, seq_raw_end,
+                              max_entries, sm_scale, o_latent, &need);
+  if (rc != LCA_OK) return rc;
+  if (!valid_dtype(w_dtype) || !valid_dtype(out_dtype)) return fail(LCA_ERR_INVALID_ARG, "w_dtype and out_dtype must be LCA_BF16 or LCA_F32");
+  if (w_uv == nullptr || !aligned16(w_uv) || out == nullptr || !aligned16(out))
+    return fail(LCA_ERR_INVALID_ARG, "w_uv and out must be non-null 16-byte aligned pointers");
+  if (step == nullptr) return fail(LCA_ERR_INVALID_ARG, "step is null");
+  if ((rc = check_step(cache, B, step->w, step->g, H, step->q_ring, step->q_ring_seq_stride, reps, step->anchor_idx,
+                       step->anchor_seq_stride, seq_m, seq_raw_begin, seq_raw_end)) != LCA_OK)
+    return rc;
+  if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need))
+    return fail(LCA_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
+  return hip_status(lca::launch_decode_paged_up_step(q, q_dtype, q_seq_stride, B, H, *reps, seq_m, *cache,
+                                                     seq_raw_begin, seq_raw_end, max_entries, sm_scale, o_latent, lse,
+                                                     w_uv, w_dtype, out, out_dtype, workspace, step->w, step->g,
+                                                     step->q_ring, step->q_ring_seq_stride, step->anchor_idx,
+                                                     step->anchor_seq_stride, step->pos, step->dst_row, stream),
+                    "mla_latent_attn_decode_paged_up_step launch");
 }
 
 }  // extern "C"

@@ -28,6 +28,7 @@
 #include "lca_device.h"
 #include "lca_internal.h"
 #include "lca_stream.h"
+#include "lca_up_rows.h"
 
 namespace lca {
 
@@ -584,123 +585,163 @@ __global__ __launch_bounds__(256) void condense_paged_kernel(
 // Every thread reads the state before the barrier that precedes its update.
 // The summary query reads this step's query from q, never from the ring row
 // the same workgroup writes.
-constexpr int QS_PH = 4;
-constexpr int QS_THREADS = 72 * QS_PH;
-template <typename TQ, int LG>
-__global__ __launch_bounds__(QS_THREADS) void condense_step_kernel(
-    const bf16_t* __restrict__ pages, int64_t row_stride, int page_rows, const int32_t* __restrict__ table,
-    int64_t table_stride, int64_t w, const TQ* __restrict__ q, int64_t q_seq, int H, TQ* __restrict__ ring,
-    int64_t ring_seq, float sm_scale, bf16_t* __restrict__ rc, int64_t rc_seq, int64_t rc_tok,
-    int32_t* __restrict__ anchor, int64_t anchor_seq, int32_t* __restrict__ seq_m,
-    int32_t* __restrict__ seq_raw_begin, int32_t* __restrict__ seq_raw_end, int32_t* __restrict__ pos,
-    int64_t* __restrict__ dst_row) {
-  constexpr int G = 1 << LG;
-  const int b = blockIdx.x, t = threadIdx.x, ch = t % 72, ph = t / 72;
-  const int64_t L = seq_raw_end[b];
-  const int64_t m = seq_m[b];
-  const int cur = (int)(L & (G - 1));
-  const bool cond = L + 1 - w >= (m + 1) * G;
-  const int64_t row_elems = (int64_t)H * D_ROW;
-  const TQ* qb = q + (int64_t)b * q_seq;
-  TQ* rb = ring + (int64_t)b * ring_seq;
+constexpr int QS_THREADS = 256;            // threads of a step workgroup
+constexpr int QS_PH = QS_THREADS / 72;      // row phases of the summary-query sum (3)
+static_assert(QS_THREADS == 64 * UPR_WAVES, "step workgroups also run inside up_rows_kernel");
 
-  // this step's query into its ring row (8 elements per store)
-  for (int64_t i = t; i < row_elems / 8; i += QS_THREADS) {
-    if constexpr (sizeof(TQ) == 2) {
-      *reinterpret_cast<uint4*>(rb + cur * row_elems + 8 * i) = *reinterpret_cast<const uint4*>(qb + 8 * i);
-    } else {
-      reinterpret_cast<float4*>(rb + cur * row_elems + 8 * i)[0] = reinterpret_cast<const float4*>(qb + 8 * i)[0];
-      reinterpret_cast<float4*>(rb + cur * row_elems + 8 * i)[1] = reinterpret_cast<const float4*>(qb + 8 * i)[1];
+template <typename TQ, int LG>
+struct CondenseStep {
+  int B;  // sequences (step workgroups)
+  const bf16_t* pages;
+  int64_t row_stride;
+  int page_rows;
+  const int32_t* table;
+  int64_t table_stride;
+  int64_t w;
+  const TQ* q;
+  int64_t q_seq;
+  int H;
+  TQ* ring;
+  int64_t ring_seq;
+  float sm_scale;
+  bf16_t* rc;
+  int64_t rc_seq, rc_tok;
+  int32_t* anchor;
+  int64_t anchor_seq;
+  int32_t* seq_m;
+  int32_t* seq_raw_begin;
+  int32_t* seq_raw_end;
+  int32_t* pos;
+  int64_t* dst_row;
+
+  __device__ void run(int b) const {
+    constexpr int G = 1 << LG;
+    const int t = threadIdx.x, ch = t % 72, ph = t / 72;
+    const int64_t L = seq_raw_end[b];
+    const int64_t m = seq_m[b];
+    const int cur = (int)(L & (G - 1));
+    const bool cond = L + 1 - w >= (m + 1) * G;
+    const int64_t row_elems = (int64_t)H * D_ROW;
+    const TQ* qb = q + (int64_t)b * q_seq;
+    TQ* rb = ring + (int64_t)b * ring_seq;
+
+    // this step's query into its ring row (8 elements per store)
+    for (int64_t i = t; i < row_elems / 8; i += QS_THREADS) {
+      if constexpr (sizeof(TQ) == 2) {
+        *reinterpret_cast<uint4*>(rb + cur * row_elems + 8 * i) = *reinterpret_cast<const uint4*>(qb + 8 * i);
+      } else {
+        reinterpret_cast<float4*>(rb + cur * row_elems + 8 * i)[0] = reinterpret_cast<const float4*>(qb + 8 * i)[0];
+        reinterpret_cast<float4*>(rb + cur * row_elems + 8 * i)[1] = reinterpret_cast<const float4*>(qb + 8 * i)[1];
+      }
     }
-  }
-  __shared__ float sh[QS_PH][D_ROW];
-  if (cond) {  // workgroup-uniform
-    // summary query: thread (chunk ch, phase ph) sums rows ph, ph + QS_PH, ...
-    // of the g*H rows (row r = ring row r / H, head r % H); the phases are
-    // added in phase order
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    const int rows = G * H;
-    for (int r0 = ph; r0 < rows; r0 += 8 * QS_PH) {
-      float v[8][8];
+    __shared__ float sh[QS_PH][D_ROW];
+    if (cond) {  // workgroup-uniform
+      // summary query: thread (chunk ch, phase ph < QS_PH) sums rows ph,
+      // ph + QS_PH, ... of the g*H rows (row r = ring row r / H, head r % H);
+      // the phases are added in phase order
+      if (ph < QS_PH) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        const int rows = G * H;
+        for (int r0 = ph; r0 < rows; r0 += 8 * QS_PH) {
+          float v[8][8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int r = r0 + u * QS_PH;
-        if (r < rows) {
-          const int slot = r / H, h = r - slot * H;
-          const TQ* src = slot == cur ? qb + h * D_ROW : rb + slot * row_elems + h * D_ROW;
-          load8_f32(src + ch * 8, v[u]);
-        } else {
+          for (int u = 0; u < 8; ++u) {
+            const int r = r0 + u * QS_PH;
+            if (r < rows) {
+              const int slot = r / H, h = r - slot * H;
+              const TQ* src = slot == cur ? qb + h * D_ROW : rb + slot * row_elems + h * D_ROW;
+              load8_f32(src + ch * 8, v[u]);
+            } else {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) v[u][i] = 0.f;
+              for (int k = 0; k < 8; ++k) v[u][k] = 0.f;
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[k] += v[u][k];
         }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sh[ph][ch * 8 + k] = acc[k];
       }
+      __syncthreads();
+      if (t < 64) {  // wave 0 condenses group m
+        const int lane = t;
+        const float inv = 1.0f / (float)(G * H);
+        float qc[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+        for (int k = 0; k < 8; ++k) {
+          float sum = sh[0][8 * lane + k];
+          for (int p = 1; p < QS_PH; ++p) sum += sh[p][8 * lane + k];
+          qc[k] = sum * inv;
+        }
+        float qr = sh[0][D_C + lane];
+        for (int p = 1; p < QS_PH; ++p) qr += sh[p][D_C + lane];
+        qr *= inv;
+        const int64_t t0 = m * G;
+        const int64_t page = table[(int64_t)b * table_stride + t0 / page_rows];
+        const bf16_t* rows0 = pages + (page * page_rows + t0 % page_rows) * row_stride;
+        RowChunk<bf16_t> rowsv[G];
+        bf16_t krv[G];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += v[u][i];
+        for (int r = 0; r < G; ++r) {
+          rowsv[r].load(rows0 + r * row_stride + 8 * lane);
+          krv[r] = __builtin_nontemporal_load(rows0 + r * row_stride + D_C + lane);
+        }
+        const GroupResult<bf16_t, LG> gr =
+            condense_group<bf16_t, LG>(rowsv, krv, qc, qr, sm_scale, lane, LCA_MODE_LCA);
+        bf16_t* dst = rc + (int64_t)b * rc_seq + m * rc_tok;
+        store8(dst + 8 * lane, gr.acc);
+        dst[D_C + lane] = (bf16_t)f2bf(gr.kval);
+        if (lane == 0) anchor[(int64_t)b * anchor_seq + m] = (int32_t)(t0 + gr.arg);
+      }
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) sh[ph][ch * 8 + i] = acc[i];
-    __syncthreads();
-    if (t < 64) {  // wave 0 condenses group m
-      const int lane = t;
-      const float inv = 1.0f / (float)rows;
-      float qc[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float sum = sh[0][8 * lane + i];
-        for (int k = 1; k < QS_PH; ++k) sum += sh[k][8 * lane + i];
-        qc[i] = sum * inv;
-      }
-      float qr = sh[0][D_C + lane];
-      for (int k = 1; k < QS_PH; ++k) qr += sh[k][D_C + lane];
-      qr *= inv;
-      const int64_t t0 = m * G;
-      const int64_t page = table[(int64_t)b * table_stride + t0 / page_rows];
-      const bf16_t* rows0 = pages + (page * page_rows + t0 % page_rows) * row_stride;
-      RowChunk<bf16_t> rowsv[G];
-      bf16_t krv[G];
-#pragma unroll
-      for (int r = 0; r < G; ++r) {
-        rowsv[r].load(rows0 + r * row_stride + 8 * lane);
-        krv[r] = __builtin_nontemporal_load(rows0 + r * row_stride + D_C + lane);
-      }
-      const GroupResult<bf16_t, LG> gr = condense_group<bf16_t, LG>(rowsv, krv, qc, qr, sm_scale, lane, LCA_MODE_LCA);
-      bf16_t* dst = rc + (int64_t)b * rc_seq + m * rc_tok;
-      store8(dst + 8 * lane, gr.acc);
-      dst[D_C + lane] = (bf16_t)f2bf(gr.kval);
-      if (lane == 0) anchor[(int64_t)b * anchor_seq + m] = (int32_t)(t0 + gr.arg);
+    __syncthreads();  // every thread has read the state it is about to be replaced
+    if (t == 0) {
+      const int64_t mn = m + (cond ? 1 : 0), Ln = L + 1;
+      seq_m[b] = (int32_t)mn;
+      seq_raw_begin[b] = (int32_t)(mn * G);
+      seq_raw_end[b] = (int32_t)Ln;
+      if (pos != nullptr) pos[b] = (int32_t)Ln;
+      if (dst_row != nullptr)
+        dst_row[b] = Ln / page_rows < table_stride
+                         ? (int64_t)table[(int64_t)b * table_stride + Ln / page_rows] * page_rows + Ln % page_rows
+                         : -1;
     }
   }
-  __syncthreads();  // every thread has read the state it is about to be replaced
-  if (t == 0) {
-    const int64_t mn = m + (cond ? 1 : 0), Ln = L + 1;
-    seq_m[b] = (int32_t)mn;
-    seq_raw_begin[b] = (int32_t)(mn * G);
-    seq_raw_end[b] = (int32_t)Ln;
-    if (pos != nullptr) pos[b] = (int32_t)Ln;
-    if (dst_row != nullptr)
-      dst_row[b] = Ln / page_rows < table_stride
-                       ? (int64_t)table[(int64_t)b * table_stride + Ln / page_rows] * page_rows + Ln % page_rows
-                       : -1;
-  }
+};
+
+template <class StepT>
+__global__ __launch_bounds__(QS_THREADS) void condense_step_kernel(StepT st) {
+  st.run((int)blockIdx.x);
 }
 
-hipError_t launch_condense_step(const lca_paged_t& cache, int B, int64_t w, int g, const void* q, int q_dtype,
-                                int64_t q_seq_stride, int H, void* q_ring, int64_t q_ring_seq_stride,
-                                float sm_scale, const lca_latent_t& reps, int32_t* anchor, int64_t anchor_seq,
-                                int32_t* seq_m, int32_t* seq_raw_begin, int32_t* seq_raw_end, int32_t* pos,
-                                int64_t* dst_row, hipStream_t stream) {
+// The step's arguments as the kernels take them.
+template <typename TQ, int LG>
+static CondenseStep<TQ, LG> make_step(const lca_paged_t& cache, int B, int64_t w, const void* q, int64_t q_seq_stride,
+                                      int H, void* q_ring, int64_t q_ring_seq_stride, float sm_scale,
+                                      const lca_latent_t& reps, int32_t* anchor, int64_t anchor_seq, int32_t* seq_m,
+                                      int32_t* seq_raw_begin, int32_t* seq_raw_end, int32_t* pos, int64_t* dst_row) {
+  return CondenseStep<TQ, LG>{B, (const bf16_t*)cache.pages, cache.row_stride, cache.page_rows, cache.block_table,
+                              cache.table_stride, w, (const TQ*)q, q_seq_stride, H, (TQ*)q_ring, q_ring_seq_stride,
+                              sm_scale, (bf16_t*)reps.c, reps.c_seq_stride, reps.c_tok_stride, anchor, anchor_seq,
+                              seq_m, seq_raw_begin, seq_raw_end, pos, dst_row};
+}
+
+// Dispatch on the query dtype and log2(g): F(step) is called with the
+// step arguments of the matching instantiation.
+template <class F>
+static void with_step(int q_dtype, int g, const lca_paged_t& cache, int B, int64_t w, const void* q,
+                      int64_t q_seq_stride, int H, void* q_ring, int64_t q_ring_seq_stride, float sm_scale,
+                      const lca_latent_t& reps, int32_t* anchor, int64_t anchor_seq, int32_t* seq_m,
+                      int32_t* seq_raw_begin, int32_t* seq_raw_end, int32_t* pos, int64_t* dst_row, F&& f) {
   int lg = 0;
   while ((1 << lg) < g) ++lg;
-#define LCA_STEP(TQV, LGV)                                                                                    \
-  hipLaunchKernelGGL((condense_step_kernel<TQV, LGV>), dim3((unsigned)B), dim3(QS_THREADS), 0, stream,      \
-                     (const bf16_t*)cache.pages, cache.row_stride, cache.page_rows, cache.block_table,        \
-                     cache.table_stride, w, (const TQV*)q, q_seq_stride, H, (TQV*)q_ring, q_ring_seq_stride, \
-                     sm_scale, (bf16_t*)reps.c, reps.c_seq_stride, reps.c_tok_stride, anchor, anchor_seq,    \
-                     seq_m, seq_raw_begin, seq_raw_end, pos, dst_row)
-#define LCA_STEP_G(TQV)            \
-  switch (lg) {                    \
+#define LCA_STEP(TQV, LGV)                                                                                       \
+  f(make_step<TQV, LGV>(cache, B, w, q, q_seq_stride, H, q_ring, q_ring_seq_stride, sm_scale, reps, anchor,      \
+                        anchor_seq, seq_m, seq_raw_begin, seq_raw_end, pos, dst_row))
+#define LCA_STEP_G(TQV)              \
+  switch (lg) {                      \
     case 0: LCA_STEP(TQV, 0); break; \
     case 1: LCA_STEP(TQV, 1); break; \
     case 2: LCA_STEP(TQV, 2); break; \
@@ -715,7 +756,71 @@ hipError_t launch_condense_step(const lca_paged_t& cache, int B, int64_t w, int 
   }
 #undef LCA_STEP_G
 #undef LCA_STEP
+}
+
+hipError_t launch_condense_step(const lca_paged_t& cache, int B, int64_t w, int g, const void* q, int q_dtype,
+                                int64_t q_seq_stride, int H, void* q_ring, int64_t q_ring_seq_stride,
+                                float sm_scale, const lca_latent_t& reps, int32_t* anchor, int64_t anchor_seq,
+                                int32_t* seq_m, int32_t* seq_raw_begin, int32_t* seq_raw_end, int32_t* pos,
+                                int64_t* dst_row, hipStream_t stream) {
+  with_step(q_dtype, g, cache, B, w, q, q_seq_stride, H, q_ring, q_ring_seq_stride, sm_scale, reps, anchor,
+            anchor_seq, seq_m, seq_raw_begin, seq_raw_end, pos, dst_row, [&](auto st) {
+              hipLaunchKernelGGL((condense_step_kernel<decltype(st)>), dim3((unsigned)B), dim3(QS_THREADS), 0,
+                                 stream, st);
+            });
   return hipGetLastError();
+}
+
+// The W_UV up-projection of a decode's rows (up_rows_kernel over the split
+// partials, which it merges, or over the merged fp32 rows) with the step
+// condensation appended as B more workgroups of the same launch: they run
+// after the decode attention kernel, the last reader of the state they
+// rewrite.
+template <class Src>
+static hipError_t up_rows_step(const Src& rows, int B, int H, const void* w_uv, int w_dtype, void* out,
+                               int out_dtype, const lca_paged_t& cache, int64_t w, int g, const void* q,
+                               int q_dtype, int64_t q_seq_stride, void* q_ring, int64_t q_ring_seq_stride,
+                               float sm_scale, const lca_latent_t& reps, int32_t* anchor, int64_t anchor_seq,
+                               int32_t* seq_m, int32_t* seq_raw_begin, int32_t* seq_raw_end, int32_t* pos,
+                               int64_t* dst_row, hipStream_t stream) {
+  const unsigned n_up = (unsigned)(((B + UPR_TOK - 1) / UPR_TOK) * H);
+  const dim3 grid(n_up + (unsigned)B);
+  with_step(q_dtype, g, cache, B, w, q, q_seq_stride, H, q_ring, q_ring_seq_stride, sm_scale, reps, anchor,
+            anchor_seq, seq_m, seq_raw_begin, seq_raw_end, pos, dst_row, [&](auto st) {
+              using ST = decltype(st);
+              if (w_dtype == LCA_BF16) {
+                if (out_dtype == LCA_BF16)
+                  hipLaunchKernelGGL((up_rows_kernel<Src, bf16_t, bf16_t, ST>), grid, dim3(64 * UPR_WAVES), 0,
+                                     stream, rows, (int64_t)B, H, (const bf16_t*)w_uv, (bf16_t*)out, st);
+                else
+                  hipLaunchKernelGGL((up_rows_kernel<Src, bf16_t, float, ST>), grid, dim3(64 * UPR_WAVES), 0,
+                                     stream, rows, (int64_t)B, H, (const bf16_t*)w_uv, (float*)out, st);
+              } else {
+                if (out_dtype == LCA_BF16)
+                  hipLaunchKernelGGL((up_rows_kernel<Src, float, bf16_t, ST>), grid, dim3(64 * UPR_WAVES), 0,
+                                     stream, rows, (int64_t)B, H, (const float*)w_uv, (bf16_t*)out, st);
+                else
+                  hipLaunchKernelGGL((up_rows_kernel<Src, float, float, ST>), grid, dim3(64 * UPR_WAVES), 0,
+                                     stream, rows, (int64_t)B, H, (const float*)w_uv, (float*)out, st);
+              }
+            });
+  return hipGetLastError();
+}
+
+hipError_t launch_up_rows_step(const float* part_o, const float* part_ml, int S, float* o_latent, float* lse,
+                               int B, int H, const void* w_uv, int w_dtype, void* out, int out_dtype,
+                               const lca_paged_t& cache, int64_t w, int g, const void* q, int q_dtype,
+                               int64_t q_seq_stride, void* q_ring, int64_t q_ring_seq_stride, float sm_scale,
+                               const lca_latent_t& reps, int32_t* anchor, int64_t anchor_seq, int32_t* seq_m,
+                               int32_t* seq_raw_begin, int32_t* seq_raw_end, int32_t* pos, int64_t* dst_row,
+                               hipStream_t stream) {
+  if (S > 1)
+    return up_rows_step(RowsFromSplits{part_o, part_ml, S, o_latent, lse}, B, H, w_uv, w_dtype, out, out_dtype,
+                        cache, w, g, q, q_dtype, q_seq_stride, q_ring, q_ring_seq_stride, sm_scale, reps, anchor,
+                        anchor_seq, seq_m, seq_raw_begin, seq_raw_end, pos, dst_row, stream);
+  return up_rows_step(RowsFromLatent<float>{o_latent}, B, H, w_uv, w_dtype, out, out_dtype, cache, w, g, q, q_dtype,
+                      q_seq_stride, q_ring, q_ring_seq_stride, sm_scale, reps, anchor, anchor_seq, seq_m,
+                      seq_raw_begin, seq_raw_end, pos, dst_row, stream);
 }
 
 template <typename TC, typename TR, int LG>

@@ -803,6 +803,36 @@ hipError_t launch_decode_paged_up(const void* q, int q_dtype, int64_t q_seq_stri
   return merge_and_up(sp, B, H, po, pml, o_latent, lse, w_uv, w_dtype, out, out_dtype, stream);
 }
 
+hipError_t launch_decode_paged_up_step(const void* q, int q_dtype, int64_t q_seq_stride, int B, int H,
+                                       const lca_latent_t& reps, int32_t* seq_m, const lca_paged_t& cache,
+                                       int32_t* seq_raw_begin, int32_t* seq_raw_end, int64_t max_entries,
+                                       float sm_scale, float* o_latent, float* lse, const void* w_uv, int w_dtype,
+                                       void* out, int out_dtype, void* workspace, int64_t w, int g, void* q_ring,
+                                       int64_t q_ring_seq_stride, int32_t* anchor, int64_t anchor_seq, int32_t* pos,
+                                       int64_t* dst_row, hipStream_t stream) {
+  const DecodeSplit sp = decode_split(B, head_blocks(H), max_entries);
+  float *po, *pml;
+  split_buffers(workspace, B, head_blocks(H), sp, po, pml);
+  hipError_t err = decode_paged_attention(q, q_dtype, q_seq_stride, B, H, reps, seq_m, cache, seq_raw_begin,
+                                          seq_raw_end, sm_scale, o_latent, lse, sp, po, pml, stream);
+  if (err != hipSuccess) return err;
+  if (B > UP_SMALL_T) {  // the projection takes the large-T kernel: the step is its own launch
+    if ((err = merge_and_up(sp, B, H, po, pml, o_latent, lse, w_uv, w_dtype, out, out_dtype, stream)) != hipSuccess)
+      return err;
+    return launch_condense_step(cache, B, w, g, q, q_dtype, q_seq_stride, H, q_ring, q_ring_seq_stride, sm_scale,
+                                reps, anchor, anchor_seq, seq_m, seq_raw_begin, seq_raw_end, pos, dst_row, stream);
+  }
+  int s_rows = sp.S;  // the rows the projection kernel reads: split partials (merged there) or merged rows
+  if (sp.S > MERGE_SMALL_S) {
+    launch_merge(sp, B, H, po, pml, o_latent, lse, stream);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    s_rows = 1;
+  }
+  return launch_up_rows_step(po, pml, s_rows, o_latent, lse, B, H, w_uv, w_dtype, out, out_dtype, cache, w, g, q,
+                             q_dtype, q_seq_stride, q_ring, q_ring_seq_stride, sm_scale, reps, anchor, anchor_seq,
+                             seq_m, seq_raw_begin, seq_raw_end, pos, dst_row, stream);
+}
+
 // ---- scratch for the entry point that allocates nothing
 // Split-K partial results of mla_latent_attn_decode_up_noalloc live in this
 // file-scope array instead of a caller workspace. Every GPU the library runs

@@ -39,6 +39,16 @@ hipError_t launch_condense_step(const lca_paged_t& cache, int B, int64_t w, int 
                                 float sm_scale, const lca_latent_t& reps, int32_t* anchor, int64_t anchor_seq,
                                 int32_t* seq_m, int32_t* seq_raw_begin, int32_t* seq_raw_end, int32_t* pos,
                                 int64_t* dst_row, hipStream_t stream);
+// the W_UV up-projection of a decode's rows (up_rows_kernel: merging the S > 1
+// split partials, or over the merged fp32 o_latent when S = 1) with the step
+// condensation appended as B workgroups of the same launch (B <= UP_SMALL_T)
+hipError_t launch_up_rows_step(const float* part_o, const float* part_ml, int S, float* o_latent, float* lse,
+                               int B, int H, const void* w_uv, int w_dtype, void* out, int out_dtype,
+                               const lca_paged_t& cache, int64_t w, int g, const void* q, int q_dtype,
+                               int64_t q_seq_stride, void* q_ring, int64_t q_ring_seq_stride, float sm_scale,
+                               const lca_latent_t& reps, int32_t* anchor, int64_t anchor_seq, int32_t* seq_m,
+                               int32_t* seq_raw_begin, int32_t* seq_raw_end, int32_t* pos, int64_t* dst_row,
+                               hipStream_t stream);
 hipError_t launch_condense(const lca_latent_t& cache, int B, int g, int64_t group_begin,
                            int64_t n_groups, const void* q, int q_dtype, int64_t q_seq_stride,
                            int64_t q_tok_stride, int H, int64_t q_row0, int64_t q_row_step,
@@ -80,6 +90,15 @@ hipError_t launch_decode_paged_up(const void* q, int q_dtype, int64_t q_seq_stri
                                   const int32_t* seq_raw_begin, const int32_t* seq_raw_end, int64_t max_entries,
                                   float sm_scale, float* o_latent, float* lse, const void* w_uv, int w_dtype,
                                   void* out, int out_dtype, void* workspace, hipStream_t stream);
+// launch_decode_paged_up followed by the step condensation (lca_condense_step),
+// the latter inside the merge/up-projection launch when that kernel runs
+hipError_t launch_decode_paged_up_step(const void* q, int q_dtype, int64_t q_seq_stride, int B, int H,
+                                       const lca_latent_t& reps, int32_t* seq_m, const lca_paged_t& cache,
+                                       int32_t* seq_raw_begin, int32_t* seq_raw_end, int64_t max_entries,
+                                       float sm_scale, float* o_latent, float* lse, const void* w_uv, int w_dtype,
+                                       void* out, int out_dtype, void* workspace, int64_t w, int g, void* q_ring,
+                                       int64_t q_ring_seq_stride, int32_t* anchor, int64_t anchor_seq, int32_t* pos,
+                                       int64_t* dst_row, hipStream_t stream);
 hipError_t launch_decode_up(const void* q, int q_dtype, int64_t q_seq_stride, int B, int H,
                             const lca_latent_t& reps, int64_t m, const lca_latent_t& raw,
                             int64_t raw_begin, int64_t raw_end, float sm_scale, float* o_latent,

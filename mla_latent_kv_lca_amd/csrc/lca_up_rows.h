@@ -20,6 +20,8 @@
 #include "lca_device.h"
 #include "lca_internal.h"
 
+#include <type_traits>
+
 namespace lca {
 
 constexpr int UPR_TOK = 2;     // rows per workgroup
@@ -109,10 +111,26 @@ struct RowsFromSplits {  // decode partials; writes o_latent and lse as it merge
   }
 };
 
-template <class Src, typename TW, typename TY>
+// No extra work after the up-projection blocks.
+struct NoStep {
+  int B = 0;
+  __device__ void run(int) const {}
+};
+
+// Grid: ceil(T / UPR_TOK) * H up-projection workgroups, then step.B
+// workgroups that run step.run(b) for b < step.B (work that must follow the
+// previous kernel, appended here instead of launched on its own).
+template <class Src, typename TW, typename TY, class Step = NoStep>
 __global__ __launch_bounds__(64 * UPR_WAVES) void up_rows_kernel(Src src, int64_t T, int H,
                                                                  const TW* __restrict__ wuv,
-                                                                 TY* __restrict__ y) {
+                                                                 TY* __restrict__ y, Step step = Step{}) {
+  if constexpr (!std::is_same<Step, NoStep>::value) {
+    const int64_t n_up = ((T + UPR_TOK - 1) / UPR_TOK) * H;
+    if ((int64_t)blockIdx.x >= n_up) {  // workgroup-uniform
+      step.run((int)((int64_t)blockIdx.x - n_up));
+      return;
+    }
+  }
   __shared__ __align__(16) bf16_t rows[UPR_TOK][D_C + 8];
   __shared__ __align__(16) float red[UPR_SLICES][UPR_TOK][D_V + 4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;

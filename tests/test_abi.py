@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert lca.lca_version() == 1002
+    assert lca.lca_version() == 1003
 
 
 def test_plan_matches_golden():
@@ -214,6 +214,26 @@ def test_condense_step_argument_errors():
     assert step(re_arr=None) == lca.LCA_ERR_INVALID_ARG
     assert step(sm=float("nan")) == lca.LCA_ERR_INVALID_ARG
     assert "g = 12" in (step(g=12), lca.lca_last_error())[1]
+
+
+def test_decode_paged_up_step_argument_errors():
+    lib = lca.load()
+    reps = lca.LatentT(64, 64 + 1024, 0, 576, 0, 576, 0)
+
+    def call(step=True, g=16, ring=64, ring_seq=16 * 16 * 576, anchor=64, w=1024, H=16, wuv=64):
+        cache = lca.PagedT(64, 576, 64, 128, 4)
+        st = lca.StepT(w, g, ring, ring_seq, anchor, 0, None, None)
+        return lib.mla_latent_attn_decode_paged_up_step(
+            64, 0, 16 * 576, 1, H, ctypes.byref(reps), 256, ctypes.byref(cache), 256, 256, 8, 1.0, 64, None,
+            wuv, 0, 64, 0, ctypes.byref(st) if step else None, None, 0, None)
+    assert call(step=False) == lca.LCA_ERR_INVALID_ARG
+    assert call(g=12) == lca.LCA_ERR_UNSUPPORTED
+    assert call(ring=None) == lca.LCA_ERR_INVALID_ARG
+    assert call(ring_seq=100) == lca.LCA_ERR_INVALID_ARG
+    assert call(anchor=None) == lca.LCA_ERR_INVALID_ARG
+    assert call(w=-1) == lca.LCA_ERR_INVALID_ARG
+    assert call(H=24) == lca.LCA_ERR_UNSUPPORTED
+    assert call(wuv=None) == lca.LCA_ERR_INVALID_ARG
 
 
 def _decode(lib, reps, raw, **kw):

@@ -166,7 +166,10 @@ def test_projected_incremental_decode_loop():
     assert_close(np.stack([host(v)[0] for v in outs]), ro, what="projected decode loop o_latent")
 
 
-def test_projected_decode_step_graph_ragged_paged():
+# 3 sequences: 43 splits, so the step runs as its own launch after the merge;
+# 8 sequences: 22 splits, so it runs inside the merge / W_UV launch
+@pytest.mark.parametrize("L0s", [[1300, 1111, 1057], [1300, 1111, 1057, 1024, 1200, 1033, 1150, 1090]])
+def test_projected_decode_step_graph_ragged_paged(L0s):
     """One projected decode step as a fixed launch sequence with its state on
     the device (lca_project -> mla_latent_attn_decode_paged ->
     lca_condense_step), captured once as a HIP graph and replayed for every
@@ -174,8 +177,10 @@ def test_projected_decode_step_graph_ragged_paged():
     complete groups at different steps. Per sequence: the step outputs
     against the oracle's incremental loop on the rows and queries the GPU
     produced; the final state, and the representatives and anchors
-    condensed during the loop."""
-    L0s, S, w_, g, d, H, P = [1300, 1111, 1057], 40, 1024, 16, 256, 16, 64
+    condensed during the loop. The same loop with the fused step call
+    (mla_latent_attn_decode_paged_up_step) is bitwise equal, and its W_UV
+    outputs match the oracle's up-projection."""
+    S, w_, g, d, H, P = 40, 1024, 16, 256, 16, 64
     sm = 0.35
     B = len(L0s)
     cap = max(L0s) + S + 1                       # tokens mapped per sequence (the state looks one token ahead)
@@ -210,36 +215,62 @@ def test_projected_decode_step_graph_ragged_paged():
     i32 = lambda v: torch.tensor(v, dtype=torch.int32, device="cuda")  # noqa: E731
     lca.lca_condense_paged(cache, B, g, i32([0] * B), i32(m0), max(m0), ring, 0, sm, lca.packed_latent(reps),
                            anchor)
-    seq_m, seq_rb, seq_re = i32(m0), i32([m * g for m in m0]), i32(L0s)
-    pos = i32(L0s)
-    dst_row = torch.tensor([phys(b, L0s[b]) for b in range(B)], dtype=torch.int64, device="cuda")
+    state0 = (i32(m0), i32([m * g for m in m0]), i32(L0s), i32(L0s),
+              torch.tensor([phys(b, L0s[b]) for b in range(B)], dtype=torch.int64, device="cuda"))
+    ring0, reps0, anchor0 = ring.clone(), reps.clone(), anchor.clone()
     x_step = torch.empty((B, d), dtype=torch.bfloat16, device="cuda")
     q_step = torch.empty((B, H, 576), dtype=torch.bfloat16, device="cuda")
     o = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
+    y = torch.empty((B, H, 128), dtype=torch.float32, device="cuda")
+    wuv = li.w_uv(81, H)
+    wuv_t = dev(wuv)
     max_entries = max(m0) + cap
     ws_dec = lca.decode_workspace(B, H, max_entries)
     ws_proj = torch.empty(lca.lca_project_workspace_size(B, H), dtype=torch.uint8, device="cuda")
-    reps_l = lca.packed_latent(reps)
-
-    def step():
-        lca.lca_project(x_step, pos, wp_t, wuk_t, rows_flat, dst_row, q_step, workspace=ws_proj)
-        lca.mla_latent_attn_decode_paged(q_step, reps_l, seq_m, cache, seq_rb, seq_re, max_entries, sm, o,
-                                         workspace=ws_dec)
-        lca.lca_condense_step(cache, w_, g, q_step, ring, sm, reps_l, anchor, seq_m, seq_rb, seq_re, pos, dst_row)
-
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step()
     x_all = [dev(xs[b]) for b in range(B)]
-    outs, qs = [], []
-    for st in range(S):
-        for b in range(B):
-            x_step[b].copy_(x_all[b][L0s[b] + st])
-        graph.replay()
-        outs.append(o.clone())
-        qs.append(q_step.clone())
-    torch.cuda.synchronize()
+
+    def run(fused):
+        """The loop from the same initial state: unfused = decode_paged then
+        lca_condense_step; fused = mla_latent_attn_decode_paged_up_step."""
+        seq_m, seq_rb, seq_re, pos, dst_row = (t.clone() for t in state0)
+        ring.copy_(ring0)
+        reps.copy_(reps0)
+        anchor.copy_(anchor0)
+        reps_l = lca.packed_latent(reps)
+
+        def step():
+            lca.lca_project(x_step, pos, wp_t, wuk_t, rows_flat, dst_row, q_step, workspace=ws_proj)
+            if fused:
+                lca.mla_latent_attn_decode_paged_up_step(q_step, reps_l, seq_m, cache, seq_rb, seq_re, max_entries,
+                                                         sm, o, wuv_t, y, w_, g, ring, anchor, pos, dst_row,
+                                                         workspace=ws_dec)
+            else:
+                lca.mla_latent_attn_decode_paged(q_step, reps_l, seq_m, cache, seq_rb, seq_re, max_entries, sm, o,
+                                                 workspace=ws_dec)
+                lca.lca_condense_step(cache, w_, g, q_step, ring, sm, reps_l, anchor, seq_m, seq_rb, seq_re, pos,
+                                      dst_row)
+
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        outs, qs, ys = [], [], []
+        for st in range(S):
+            for b in range(B):
+                x_step[b].copy_(x_all[b][L0s[b] + st])
+            graph.replay()
+            outs.append(o.clone())
+            qs.append(q_step.clone())
+            ys.append(y.clone())
+        torch.cuda.synchronize()
+        return outs, qs, ys, (seq_m, seq_rb, seq_re, pos, dst_row), reps.clone(), anchor.clone()
+
+    outs_f, _, ys_f, state_f, reps_f, anchor_f = run(True)
+    outs, qs, _, (seq_m, seq_rb, seq_re, pos, dst_row), reps, anchor = run(False)
+    # the fused call is bitwise the two calls in sequence
+    assert all(torch.equal(a, b) for a, b in zip(outs_f, outs))
+    assert all(torch.equal(a, b) for a, b in zip(state_f, (seq_m, seq_rb, seq_re, pos, dst_row)))
+    assert torch.equal(reps_f, reps) and torch.equal(anchor_f, anchor)
 
     pool_h = host(pool).reshape(-1, 576)
     reps_h, anchor_h = host(reps), host(anchor).astype(np.int64)
@@ -251,6 +282,8 @@ def test_projected_decode_step_graph_ragged_paged():
         ro, _, rc_ref, rk_ref, m_ref = O.decode_loop(rows[:L0, :512], rows[:L0, 512:], host(q_hist[b]), steps_q,
                                                      rows[L0:, :512], rows[L0:, 512:], w_, g, sm)
         assert_close(np.stack([host(v[b]) for v in outs]), ro, what=f"step outputs, sequence {b}")
+        assert_close(np.stack([host(v[b]) for v in ys_f]), O.up_proj(ro, wuv),
+                     what=f"fused step W_UV outputs, sequence {b}")
         assert host(seq_m)[b] == m_ref and host(seq_rb)[b] == m_ref * g and host(seq_re)[b] == L0 + S
         assert host(pos)[b] == L0 + S and host(dst_row)[b] == phys(b, L0 + S)
         new = slice(m0[b], m_ref)               # the groups the loop condensed
