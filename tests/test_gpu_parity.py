@@ -198,13 +198,16 @@ def _page_pool(seqs, page_rows, seed):
     return pool, table
 
 
-@pytest.mark.parametrize("page_rows,g,q_dtype", [(64, 16, torch.bfloat16), (16, 8, torch.bfloat16),
-                                                 (64, 16, torch.float32)])
-def test_decode_paged_ragged_matches_oracle(page_rows, g, q_dtype):
+@pytest.mark.parametrize("page_rows,g,q_dtype,Hh", [(64, 16, torch.bfloat16, 16), (16, 8, torch.bfloat16, 16),
+                                                    (64, 16, torch.float32, 16), (64, 16, torch.bfloat16, 4),
+                                                    (16, 16, torch.bfloat16, 1)])
+def test_decode_paged_ragged_matches_oracle(page_rows, g, q_dtype, Hh):
     """Ragged batch (different lengths, one shorter than the window) over a
     shuffled paged cache against the oracle on each sequence's logical rows.
     With g = 8 the raw ranges start off a 16-row boundary, so tiles straddle
-    pages."""
+    pages. Hh = 4 and 1: one key-value group of grouped-query attention per
+    sequence (reading R8)."""
+    H = Hh
     Ls, w = [1500, 2077, 3000, 1040, 777], 1024
     B = len(Ls)
     seqs, reps, ms, rbs = [], [], [], []
@@ -291,18 +294,19 @@ def test_condense_and_decode_paged_ragged_end_to_end():
     tally.check()
 
 
-@pytest.mark.parametrize("page_rows", [16, 64])
-def test_prefill_paged_ragged_end_to_end(page_rows):
+@pytest.mark.parametrize("page_rows,Hh", [(16, 16), (64, 16), (64, 4)])
+def test_prefill_paged_ragged_end_to_end(page_rows, Hh):
     """Chunked prefill of three sequences of different lengths over shuffled
     pages: before each chunk (ragged chunk starts) the groups that left the
     window are condensed through lca_condense_paged with the g queries that
     follow each group, then mla_latent_attn_prefill_chunk_paged attends the
     chunk. Representatives against the oracle's condensation; attention
     against the oracle on the GPU's representatives, and bitwise against the
-    dense prefill call on the same rows."""
+    dense prefill call on the same rows. Hh = 4: one key-value group of
+    grouped-query attention (8 tokens x 4 heads per 32-row block)."""
     Ls, w, g, sm = [1500, 2300, 900], 256, 16, 1.0
     bounds = {0: [0, 300, 700, 1100, 1500], 1: [0, 500, 650, 1400, 2300], 2: [0, 257, 900]}
-    B, H = len(Ls), 16
+    B, H = len(Ls), Hh
     cs, ks, qs = [], [], []
     for b, L in enumerate(Ls):
         c, kr = li.latent_cache(30 + b, 1, L)
