@@ -106,19 +106,19 @@ __device__ __forceinline__ void retire(const uint4& v) {
 }
 
 // Tile rows are dense (576 bf16); the 16-byte chunk c of row r sits at chunk
-// position c ^ swz(r). LDS has 64 banks of 4 bytes, and a row is 288 bank
-// words, so rows of one parity start on bank 0 and the others on bank 32; a
-// 16-byte read serves 16 lanes per pass and an 8-byte read 32. swz(r) is bits
-// 1..3 of r in reverse order, which makes every access pattern of the kernels
-// use each bank once per pass:
-//  - K fragments (16 consecutive rows, one chunk each): the 8 rows of each
-//    parity get 8 distinct values;
-//  - decode's transposed V reads (8 aligned rows x 2 adjacent chunks): the 4
-//    rows of each parity differ in bits 1-2;
-//  - prefill's transposed V reads (4 aligned rows x 4 adjacent chunks): the 2
-//    rows of each parity differ in bit 2.
-// swz(r) depends on r mod 16 only.
-__device__ __forceinline__ int swz(int r) { return (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1); }
+// position c ^ swz(r), swz(r) = r mod 8. The kernels read a tile in two
+// patterns, both the operands of 16x16 MFMA tiles:
+//  - K fragments: lane (g, i) of the four 16-lane groups reads chunk 4 s + g
+//    of row i (16 rows, four adjacent chunks per row);
+//  - transposed V reads (ds_read_b64_tr_b16): lane (g, i) points at row
+//    4 g + i / 4, 8 bytes of two adjacent chunks (8 rows x 2 chunks per 32
+//    lanes).
+// With this swizzle both run without LDS bank conflicts (SQ_LDS_BANK_CONFLICT
+// = 0 in a probe that reads a tile in each pattern). A swizzle built from
+// bits 1..3 of r in reverse order, which suits 32x32 fragments, gives the
+// K fragments two-way conflicts on gfx950 (about half of the LDS cycles).
+// swz(r) depends on r mod 8, so rows r and r + 16 share it.
+__device__ __forceinline__ int swz(int r) { return r & 7; }
 __device__ __forceinline__ int chunk_pos(int r, int c) { return r * (D_ROW / 8) + (c ^ swz(r)); }
 
 // Packed rows (k_R right after c_KV, one token stride) of the two segments of
