@@ -195,9 +195,27 @@ __device__ __forceinline__ void tile_dma(const PagedDmaSrc& src, int64_t e0, int
   const int64_t pa = src.table[__builtin_amdgcn_readfirstlane((int)pg0)];
   const int64_t pb = src.table[__builtin_amdgcn_readfirstlane((int)min(pg0 + 1, pg_last))];
   const int64_t pc = src.table[__builtin_amdgcn_readfirstlane((int)min(pg0 + 2, pg_last))];
-  if (e0 >= src.m && valid == STILE && pg0 == pg_last) {  // whole tile of raw rows in one page
-    dma16_rows<1024u * SNW, false>(src.pages + (pa * src.P + (t_first - pg0 * src.P)) * src.tok, off,
-                                   base + 1024u * w);
+  if (e0 >= src.m && valid == STILE) {  // whole tile of raw rows
+    const uint64_t b0 = (uint64_t)(uintptr_t)(src.pages + (pa * src.P + (t_first - pg0 * src.P)) * src.tok);
+    if (pg0 == pg_last) {  // in one page
+      dma16_rows<1024u * SNW, false>((const void*)(uintptr_t)b0, off, base + 1024u * w);
+      return;
+    }
+    // across two or three pages: rows [0, k1) continue page pa, rows [k1,
+    // k1 + P) are page pb, the rest page pc; each segment's base is shifted
+    // back by its first row, so that base + row x stride addresses the row
+    // inside its page (a rolled loop: the kernel's registers are spoken for)
+    const int k1 = (int)(src.P - (t_first - pg0 * src.P));
+    const uint64_t tok = (uint64_t)src.tok, p0 = (uint64_t)(uintptr_t)src.pages;
+    const uint64_t b1 = p0 + (uint64_t)pb * src.P * tok - (uint64_t)k1 * tok;
+    const uint64_t b2 = p0 + (uint64_t)pc * src.P * tok - (uint64_t)(k1 + src.P) * tok;
+#pragma unroll 1
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+      int row, col;
+      slot_rowcol(w, i, lane, row, col);
+      const uint64_t b = row < k1 ? b0 : (row < k1 + src.P ? b1 : b2);
+      dma16((const void*)(uintptr_t)(b + (uint64_t)row * tok + 16u * col), base + 1024u * (w + SNW * i));
+    }
     return;
   }
 #pragma unroll 1  // rare boundary tiles: keep the per-lane row arithmetic small
