@@ -68,7 +68,7 @@ def parse():
 TRAFFIC_SOURCES = ("mla_latent_kv_lca_amd/csrc/lca_decode.hip", "mla_latent_kv_lca_amd/csrc/lca_stream.h",
                    "mla_latent_kv_lca_amd/csrc/lca_tile.h", "mla_latent_kv_lca_amd/csrc/lca_device.h",
                    "mla_latent_kv_lca_amd/csrc/lca_up_rows.h")
-TRAFFIC = {"sha256": "ea11a2c784c357ccc7740420489c6a966631e091eb7952cede866c49c0532303",
+TRAFFIC = {"sha256": "9f83361c279152c9b1ef00bba133022d0015124743ab156045423fc76e112887",
            "fetch_bytes": 126_777_948, "write_bytes": 9_617_408}
 
 

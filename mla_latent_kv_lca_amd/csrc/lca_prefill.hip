@@ -120,9 +120,9 @@ __global__ __launch_bounds__(NT) void prefill_kernel_staged(
 // MFMA, its queries in registers), runs the online softmax in registers (four
 // lanes per query row) and accumulates O^T += V^T P^T over all 512 latent
 // columns (32 MFMA; P straight from the score registers, V^T from transposed
-// LDS reads). Its 16 + 128 + ~50 registers leave room for a second wave on
-// every SIMD, which is what keeps the matrix cores fed while the other wave
-// runs its softmax. Tiles stream HBM -> LDS by direct loads into a 4-slot
+// LDS reads). Its 72 (queries) + 128 (accumulators) + ~56 registers stay
+// within the 256 that a second wave on every SIMD allows, and that second
+// wave is what keeps the matrix cores fed while the other runs its softmax. Tiles stream HBM -> LDS by direct loads into a 4-slot
 // ring (waves 0-3 issue them); one barrier per tile. Waves 0-3 run each tile
 // as scores, softmax, values; waves 4-7 run the values of the previous tile
 // first, so the two waves of a SIMD reach their softmax at different times.

@@ -4,9 +4,10 @@
 // A tile is 32 consecutive attended entries (representative rows first, then
 // raw cache rows), stored densely in LDS (576 bf16 per row) with the 16-byte
 // chunk c of row r at chunk position c ^ swz(r) (swz below): the rows read by
-// one MFMA fragment then fall on distinct LDS banks. A workgroup of 4
-// wavefronts fills a tile with 36 global_load_lds_dwordx4 wave instructions
-// (16 bytes per lane straight into LDS, no register staging), 9 per wave.
+// one MFMA fragment then fall on distinct LDS banks. Four wavefronts of the
+// prefill workgroup fill a tile with 36 global_load_lds_dwordx4 wave
+// instructions (16 bytes per lane straight into LDS, no register staging), 9
+// per wave; the decode kernel's waves each load their own 16-row tiles.
 #pragma once
 #include "lca_tile.h"
 
