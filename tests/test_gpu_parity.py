@@ -133,7 +133,7 @@ def test_gqa_condense_and_decode_match_oracle(n_kv, Hq):
     assert_close(host(y), O.up_proj(ro, wuv), what="GQA up-projected output")
 
 
-@pytest.mark.parametrize("n_kv,Hq,L,C", [(4, 16, 700, 256), (8, 8, 300, 128)])  # Hg = 4, 1
+@pytest.mark.parametrize("n_kv,Hq,L,C", [(4, 16, 700, 256), (8, 8, 300, 128), (8, 16, 400, 200), (2, 16, 500, 160)])  # Hg = 4, 1, 2, 8
 def test_gqa_prefill_matches_oracle(n_kv, Hq, L, C):
     """GQA chunked prefill: per key-value head k, its cache condensed with its
     own Hg query heads (the g queries after each group) and its Hg heads'
@@ -703,7 +703,9 @@ def test_two_head_blocks_decode_up_and_prefill():
     assert_close(host(lp), rpl, what="prefill lse, H = 32")
 
 
-@pytest.mark.parametrize("L,C", [(320, 64), (301, 40)])
+# chunks of 64 and 40 rows, of 129 rows (a second workgroup of 128 query rows
+# holding one token), and of one token
+@pytest.mark.parametrize("L,C", [(320, 64), (301, 40), (300, 129), (70, 1)])
 def test_prefill_chunks_match_oracle(L, C):
     w, g, sm = 64, 16, 1.0
     c, kr = li.latent_cache(10, 1, L)
