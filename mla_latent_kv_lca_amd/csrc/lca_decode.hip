@@ -195,23 +195,29 @@ __device__ __forceinline__ void decode_body(bf16_t (&ring)[DNW][WSLOT][WT_ELEMS]
   const int kb[2] = {8 * (col * (D_ROW / 8) + (kg ^ swc)), 8 * (col * (D_ROW / 8) + ((4 + kg) ^ swc))};
 
   // The queries (B operand of head col, 18 k-steps of 32 columns). bf16: the
-  // 16 query rows travel like a tile, by direct loads into slot 1 right
-  // behind tile 0, so both are in flight together; one wait covers them, the
-  // wave copies the queries into registers, and slot 1 then takes tile 1.
+  // 16 query rows travel like a tile, by direct loads into slot 1, with tile
+  // 0 right behind them; the wave waits for the queries only (the splits of
+  // a sequence share them, so they usually come from L2 before tile 0),
+  // copies them into registers, and slot 1 then takes tile 1 while tile 0 may
+  // still be in flight.
   // f32: register loads (rounded to bf16), waited for before any tile is in
   // flight (requested behind the tiles, they would only arrive with them).
   uint4 qa[18];
   const TQ* qh = q + (int64_t)b * q_seq + (int64_t)(hg * HB) * D_ROW;
   const int last_row = min(HB, H - hg * HB) - 1;  // rows past it repeat it (never stored)
   if constexpr (sizeof(TQ) == 2) {
-    if (n_mine > 0) issue(0);
     const uint32_t qbase = lds_off(&ring[w][1][0]);
 #pragma unroll
     for (int i = 0; i < WT_DMA; ++i) {
       const int P = 64 * i + lane, row = P / (D_ROW / 8);
       dma16(qh + min(row, last_row) * D_ROW + 8 * ((P - row * (D_ROW / 8)) ^ swz(row)), qbase + 1024u * i);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (n_mine > 0) {
+      issue(0);
+      asm volatile("s_waitcnt vmcnt(18)" ::: "memory");  // the queries (tile 0 may still be in flight)
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     const bf16_t* qt = &ring[w][1][0];
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) qa[ks] = *reinterpret_cast<const uint4*>(qt + kb[ks & 1] + 64 * (ks >> 1));
