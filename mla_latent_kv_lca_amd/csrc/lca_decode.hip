@@ -282,14 +282,20 @@ __device__ __forceinline__ void decode_body(bf16_t (&ring)[DNW][WSLOT][WT_ELEMS]
     for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(z[r] - m_ref);
     l_run += xor32_sum(xor16_sum((p[0] + p[1]) + (p[2] + p[3])));
     const uint2 pb = make_uint2(pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3]));
+    // every V^T operand read first, so that the slot takes tile k + WSLOT
+    // before the value products run rather than after them
+    uint2 vf[32];
 #pragma unroll
-    for (int ct = 0; ct < 32; ++ct) {
-      // o[ct][r] = O[head col][16 ct + 4 kg + r]
-      o[ct] = mfma16x16x16(lds_read_tr4(tile + vb[ct & 3] + 64 * (ct >> 2)), pb, o[ct]);
-    }
+    for (int ct = 0; ct < 32; ++ct) vf[ct] = lds_read_tr4(tile + vb[ct & 3] + 64 * (ct >> 2));
     if (k + WSLOT < n_mine) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       issue(k + WSLOT);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ct = 0; ct < 32; ++ct) {
+      // o[ct][r] = O[head col][16 ct + 4 kg + r]
+      o[ct] = mfma16x16x16(vf[ct], pb, o[ct]);
     }
   };
   // Online softmax with a lazy rescale: the inner loop runs while the running
