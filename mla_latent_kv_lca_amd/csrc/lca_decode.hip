@@ -249,6 +249,10 @@ __device__ __forceinline__ void decode_body(bf16_t (&ring)[DNW][WSLOT][WT_ELEMS]
 
   // Scores of wave tile k (log2 units, rows past the tile's valid ones masked); returns their
   // per-head maximum.
+  // The tile's V^T operands (all 32 transposed reads), read right after the
+  // score products so that their latency hides under the softmax and the
+  // slot can take its next tile before the value products.
+  uint2 vf[32];
   auto scores = [&](int k, float (&z)[4]) -> float {
     const int valid = tiles.valid(u0 + ustep * k);
     wait_wave_tile(min(n_mine - 1 - k, WSLOT - 1));
@@ -259,6 +263,10 @@ __device__ __forceinline__ void decode_body(bf16_t (&ring)[DNW][WSLOT][WT_ELEMS]
       sa = mfma16x16x32(*reinterpret_cast<const uint4*>(tile + kb[0] + 64 * (ks >> 1)), qa[ks], sa);
       sb = mfma16x16x32(*reinterpret_cast<const uint4*>(tile + kb[1] + 64 * (ks >> 1)), qa[ks + 1], sb);
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ct = 0; ct < 32; ++ct) vf[ct] = lds_read_tr4(tile + vb[ct & 3] + 64 * (ct >> 2));
+    __builtin_amdgcn_sched_barrier(0);
     const f32x4_t sc = sa + sb;  // S[entry 4 kg + r][head col]
 #pragma unroll
     for (int r = 0; r < 4; ++r) z[r] = sc[r] * scale_log2;
@@ -270,11 +278,10 @@ __device__ __forceinline__ void decode_body(bf16_t (&ring)[DNW][WSLOT][WT_ELEMS]
     // per head: lanes col, col + 16, col + 32, col + 48
     return xor32_max(xor16_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]))));
   };
-  // Probabilities relative to the running max, their sum, and the value
-  // product O^T += V^T P^T (32 column tiles); then the slot takes wave tile
-  // k + WSLOT.
+  // Probabilities relative to the running max, their sum, the slot's next
+  // tile (wave tile k + WSLOT, once the V^T reads are done), and the value
+  // product O^T += V^T P^T (32 column tiles).
   auto accumulate = [&](int k, const float (&z)[4]) {
-    const bf16_t* tile = &ring[w][k % WSLOT][0];
     // a wave with no visible entry yet keeps m_run = -inf: its p must be 0
     const float m_ref = m_run == -INFINITY ? 0.f : m_run;
     float p[4];
@@ -282,11 +289,6 @@ __device__ __forceinline__ void decode_body(bf16_t (&ring)[DNW][WSLOT][WT_ELEMS]
     for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(z[r] - m_ref);
     l_run += xor32_sum(xor16_sum((p[0] + p[1]) + (p[2] + p[3])));
     const uint2 pb = make_uint2(pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3]));
-    // every V^T operand read first, so that the slot takes tile k + WSLOT
-    // before the value products run rather than after them
-    uint2 vf[32];
-#pragma unroll
-    for (int ct = 0; ct < 32; ++ct) vf[ct] = lds_read_tr4(tile + vb[ct & 3] + 64 * (ct >> 2));
     if (k + WSLOT < n_mine) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       issue(k + WSLOT);
