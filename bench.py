@@ -68,8 +68,8 @@ def parse():
 TRAFFIC_SOURCES = ("mla_latent_kv_lca_amd/csrc/lca_decode.hip", "mla_latent_kv_lca_amd/csrc/lca_stream.h",
                    "mla_latent_kv_lca_amd/csrc/lca_tile.h", "mla_latent_kv_lca_amd/csrc/lca_device.h",
                    "mla_latent_kv_lca_amd/csrc/lca_up_rows.h")
-TRAFFIC = {"sha256": "ad611aa25f9739939e89247f74e00fc9c51c9588037dac81a2b543ca8279e40f",
-           "fetch_bytes": 126_781_988, "write_bytes": 9_617_408}
+TRAFFIC = {"sha256": "73e79272da4cae5c0873ddbd23b167fd4b5b1351c0bec4da377afe28b0a7fa39",
+           "fetch_bytes": 126_788_152, "write_bytes": 9_617_408}
 
 
 def decode_sources_digest() -> str:
