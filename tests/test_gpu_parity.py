@@ -508,6 +508,40 @@ def test_decode_condensed_matches_oracle(dtype, L):
     assert_close(host(lse), rl, what="lse")
 
 
+# (seed, heads, representatives m, raw_begin, chunk_start, chunk rows C, bf16 output):
+# single-token and odd chunks, two head blocks with C > 128, grouped heads
+# (16 / Hg tokens per wave), a window that starts at the chunk, m not a
+# multiple of the 32-entry tile
+PREFILL_SHAPES = [
+    (1, 16, 0, 0, 0, 1, False), (2, 16, 37, 40, 95, 33, True), (3, 32, 5, 0, 7, 130, False),
+    (4, 4, 64, 128, 300, 77, False), (5, 1, 10, 20, 60, 200, True), (6, 2, 100, 16, 16, 129, False),
+    (7, 8, 0, 0, 250, 251, False), (8, 16, 31, 33, 33, 64, True),
+]
+
+
+@pytest.mark.parametrize("seed,Hq,m,raw_begin,s0,C,bf16_out", PREFILL_SHAPES)
+def test_prefill_kernel_shapes(seed, Hq, m, raw_begin, s0, C, bf16_out):
+    """The packed-row prefill kernel called directly at assorted (m,
+    raw_begin, chunk_start, C, H) against the oracle's chunk attention:
+    representatives are arbitrary bf16 rows, raw rows [raw_begin, s0 + i]
+    are visible to chunk row i."""
+    L, sm = s0 + C, 1.0
+    c, kr = li.latent_cache(200 + seed, 1, L)
+    li.plant_needles(200 + seed, c, kr, min(2, L - raw_begin), 14.0, raw_begin, L)
+    rc, rk = li.latent_cache(300 + seed, 1, max(m, 1))
+    q = li.queries(200 + seed, 1, C, Hq, rho=0.5)[0]
+    cache_t = packed(c, kr)[0]
+    reps_t = packed(rc[:, :m], rk[:, :m])[0] if m else None
+    out = torch.empty((C, Hq, 512), dtype=torch.bfloat16 if bf16_out else torch.float32, device="cuda")
+    lse = torch.empty((C, Hq), dtype=torch.float32, device="cuda")
+    lca.mla_latent_attn_prefill_chunk(dev(q), s0, lca.packed_latent(reps_t) if m else None, m,
+                                      lca.packed_latent(cache_t), raw_begin, sm, out, lse)
+    torch.cuda.synchronize()
+    ro, rl = O.prefill_chunk(q, s0, rc[0, :m], rk[0, :m], m, c[0], kr[0], raw_begin, sm)
+    assert_close(host(out), ro, what=f"prefill o_latent, shape {seed}")
+    assert_close(host(lse), rl, what=f"prefill lse, shape {seed}")
+
+
 @pytest.mark.parametrize("q_dtype,c_dtype,layout", [
     (torch.float32, torch.bfloat16, "packed"),  # direct-load kernel, f32 queries
     (torch.bfloat16, torch.float32, "packed"),  # register-staged kernel, f32 rows
