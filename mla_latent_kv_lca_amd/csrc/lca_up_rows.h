@@ -78,21 +78,72 @@ __device__ __forceinline__ float4 merge_cols4(const float* __restrict__ part_o,
   return make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
 }
 
+// The same merge in two steps for S <= MERGE_BATCH: every load first
+// (merge_load), the arithmetic later (merge_math), so that a kernel can put
+// other loads in flight between them. The loads take no branch (a branch per
+// load made the compiler wait for each one); merge_math masks the splits past
+// S. The arithmetic is merge_cols4's, in the same order, so the two give
+// bitwise equal results.
+struct MergeLoads {
+  float2 ml[MERGE_BATCH];
+  float4 o[MERGE_BATCH];
+};
+__device__ __forceinline__ void merge_load(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+                                           int S, int64_t slot0, int hh, int c4, MergeLoads& ld) {
+  const float2* ml = reinterpret_cast<const float2*>(part_ml);
+  const float4* po = reinterpret_cast<const float4*>(part_o);
+#pragma unroll
+  for (int s = 0; s < MERGE_BATCH; ++s) {  // splits past S reload split S - 1 (no branch per load)
+    const int64_t sl = slot0 + (s < S ? s : S - 1);
+    ld.ml[s] = ml[sl * HB + hh];
+    ld.o[s] = po[(sl * HB + hh) * (D_C / 4) + c4];
+  }
+}
+__device__ __forceinline__ float4 merge_math(const MergeLoads& ld, int S, float& M, float& L) {
+  float2 v_ml[MERGE_BATCH];
+  float4 v_o[MERGE_BATCH];
+#pragma unroll
+  for (int s = 0; s < MERGE_BATCH; ++s) {
+    v_ml[s] = s < S ? ld.ml[s] : make_float2(-INFINITY, 0.f);
+    v_o[s] = s < S ? ld.o[s] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < MERGE_BATCH; ++s) M = fmaxf(M, v_ml[s].x);
+  L = 0.f;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int s = 0; s < MERGE_BATCH; ++s) {
+    const float ms = v_ml[s].x;
+    const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - M);
+    L = fmaf(wgt, v_ml[s].y, L);
+    a.x = fmaf(wgt, v_o[s].x, a.x); a.y = fmaf(wgt, v_o[s].y, a.y);
+    a.z = fmaf(wgt, v_o[s].z, a.z); a.w = fmaf(wgt, v_o[s].w, a.w);
+  }
+  const float inv = 1.0f / L;
+  return make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
+}
+
 // ---- row sources
+// A source's loads can be issued (prefetch) before its arithmetic (finish).
 template <typename TO>
 struct RowsFromLatent {  // o_latent [T, H, 512]
   const TO* x;
-  __device__ __forceinline__ float4 get(int64_t t, int h, int H, int c4) const {
+  typedef float4 Pre;
+  __device__ __forceinline__ void prefetch(int64_t t, int h, int H, int c4, Pre& v) const {
     const TO* p = x + (t * H + h) * D_C + 4 * c4;
-    return make_float4(to_f32(p[0]), to_f32(p[1]), to_f32(p[2]), to_f32(p[3]));
+    v = make_float4(to_f32(p[0]), to_f32(p[1]), to_f32(p[2]), to_f32(p[3]));
   }
+  __device__ __forceinline__ float4 finish(const Pre& v, int64_t, int, int, int) const { return v; }
 };
 template <>
 struct RowsFromLatent<float> {
   const float* x;
-  __device__ __forceinline__ float4 get(int64_t t, int h, int H, int c4) const {
-    return reinterpret_cast<const float4*>(x + (t * H + h) * D_C)[c4];
+  typedef float4 Pre;
+  __device__ __forceinline__ void prefetch(int64_t t, int h, int H, int c4, Pre& v) const {
+    v = reinterpret_cast<const float4*>(x + (t * H + h) * D_C)[c4];
   }
+  __device__ __forceinline__ float4 finish(const Pre& v, int64_t, int, int, int) const { return v; }
 };
 
 struct RowsFromSplits {  // decode partials; writes o_latent and lse as it merges
@@ -101,10 +152,18 @@ struct RowsFromSplits {  // decode partials; writes o_latent and lse as it merge
   int S;
   float* o;
   float* lse;
-  __device__ __forceinline__ float4 get(int64_t b, int h, int H, int c4) const {
+  typedef MergeLoads Pre;  // the loads of a merge over at most MERGE_BATCH splits
+  __device__ __forceinline__ void prefetch(int64_t b, int h, int H, int c4, Pre& ld) const {
+    if (S <= MERGE_BATCH) {  // uniform
+      const int HG = head_blocks(H), hg = h / HB, hh = h % HB;
+      merge_load(part_o, part_ml, S, (b * HG + hg) * S, hh, c4, ld);
+    }
+  }
+  __device__ __forceinline__ float4 finish(const Pre& ld, int64_t b, int h, int H, int c4) const {
     const int HG = head_blocks(H), hg = h / HB, hh = h % HB;
     float M, L;
-    const float4 v = merge_cols4(part_o, part_ml, S, (b * HG + hg) * S, hh, c4, M, L);
+    const float4 v = S <= MERGE_BATCH ? merge_math(ld, S, M, L)
+                                      : merge_cols4(part_o, part_ml, S, (b * HG + hg) * S, hh, c4, M, L);
     reinterpret_cast<float4*>(o + (b * H + h) * D_C)[c4] = v;
     if (lse != nullptr && c4 == 0) lse[b * H + h] = (M + log2f(L)) * 0.69314718055994530942f;
     return v;
@@ -138,6 +197,15 @@ __global__ __launch_bounds__(64 * UPR_WAVES) void up_rows_kernel(Src src, int64_
   const int h = (int)(blockIdx.x % (unsigned)H);
   const int64_t t0 = (int64_t)(blockIdx.x / (unsigned)H) * UPR_TOK;
 
+  // the rows' loads first (thread -> row ri, columns 4 rc4 .. 4 rc4 + 3):
+  // a merge of split partials is on this kernel's critical path, W_UV is not
+  const int ri = tid / (D_C / 4), rc4 = tid % (D_C / 4);
+  const int64_t rt = t0 + ri;
+  const bool has_row = ri < UPR_TOK && rt < T;
+  typename Src::Pre pre;
+  if (has_row) src.prefetch(rt, h, H, rc4, pre);
+  __builtin_amdgcn_sched_barrier(0);
+
   // W_UV[h] rows 128 w + 32 ks + 8 kg + kk, outputs 8 col .. 8 col + 7
   const TW* wh = wuv + (int64_t)h * D_C * D_V + 8 * col;
   uint4 R[4][8];
@@ -147,15 +215,13 @@ __global__ __launch_bounds__(64 * UPR_WAVES) void up_rows_kernel(Src src, int64_
     for (int kk = 0; kk < 8; ++kk)
       R[ks][kk] = raw8_bf16(raw8_load(wh + (int64_t)(128 * w + 32 * ks + 8 * kg + kk) * D_V));
 
-  {  // the rows, as bf16 A-operand source: thread -> (row i, columns 4 c4 .. 4 c4 + 3)
-    const int i = tid / (D_C / 4), c4 = tid % (D_C / 4);
-    const int64_t t = t0 + i;
+  {  // the rows, as bf16 A-operand source
     uint2 packed = make_uint2(0u, 0u);
-    if (i < UPR_TOK && t < T) {
-      const float4 v = src.get(t, h, H, c4);
+    if (has_row) {
+      const float4 v = src.finish(pre, rt, h, H, rc4);
       packed = make_uint2(pack_bf2(v.x, v.y), pack_bf2(v.z, v.w));
     }
-    if (i < UPR_TOK) *reinterpret_cast<uint2*>(&rows[i][4 * c4]) = packed;
+    if (ri < UPR_TOK) *reinterpret_cast<uint2*>(&rows[ri][4 * rc4]) = packed;
   }
   __syncthreads();
 
