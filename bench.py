@@ -68,8 +68,8 @@ def parse():
 TRAFFIC_SOURCES = ("mla_latent_kv_lca_amd/csrc/lca_decode.hip", "mla_latent_kv_lca_amd/csrc/lca_stream.h",
                    "mla_latent_kv_lca_amd/csrc/lca_tile.h", "mla_latent_kv_lca_amd/csrc/lca_device.h",
                    "mla_latent_kv_lca_amd/csrc/lca_up_rows.h")
-TRAFFIC = {"sha256": "73e79272da4cae5c0873ddbd23b167fd4b5b1351c0bec4da377afe28b0a7fa39",
-           "fetch_bytes": 126_788_152, "write_bytes": 9_617_408}
+TRAFFIC = {"sha256": "5f47efbd761031c1dccdd4fc41884c65ec45860344b0a13f7fc4f507d8b51b50",
+           "fetch_bytes": 126_777_943, "write_bytes": 9_617_408}
 
 
 def decode_sources_digest() -> str:
