@@ -783,7 +783,7 @@ static hipError_t up_rows_step(const Src& rows, int B, int H, const void* w_uv, 
                                float sm_scale, const lca_latent_t& reps, int32_t* anchor, int64_t anchor_seq,
                                int32_t* seq_m, int32_t* seq_raw_begin, int32_t* seq_raw_end, int32_t* pos,
                                int64_t* dst_row, hipStream_t stream) {
-  const unsigned n_up = (unsigned)(((B + UPR_TOK - 1) / UPR_TOK) * H);
+  const unsigned n_up = (unsigned)(((B + UpShapeStep::R - 1) / UpShapeStep::R) * H * UpShapeStep::F);
   const dim3 grid(n_up + (unsigned)B);
   with_step(q_dtype, g, cache, B, w, q, q_seq_stride, H, q_ring, q_ring_seq_stride, sm_scale, reps, anchor,
             anchor_seq, seq_m, seq_raw_begin, seq_raw_end, pos, dst_row, [&](auto st) {

@@ -863,6 +863,27 @@ def test_up_proj_bf16_latent_shapes(T, Hh, wdt, ydt):
     assert_close(host(out), O.up_proj(x, w), tol=TOL, what=f"up_proj T={T} H={Hh}")
 
 
+def test_up_proj_row_independent_of_rows_projected_with_it():
+    """mla_up_proj picks its workgroup shape (rows per workgroup, output-column
+    blocks) from the row count, so T = 64, 37, 32, 8, 5, 2 and 1 run different
+    shapes; a row's output is the same bits in every one, and matches the
+    oracle."""
+    rng = np.random.default_rng(21)
+    x = li.bf16_round((0.25 * rng.standard_normal((64, H, 512))).astype(np.float32))
+    w = li.w_uv(21, H)
+    xd, wd = dev(x, torch.float32), dev(w)
+    ref = None
+    for T in (64, 37, 32, 8, 5, 2, 1):
+        out = torch.empty((T, H, 128), dtype=torch.float32, device="cuda")
+        lca.mla_up_proj(xd[:T].contiguous(), wd, out)
+        torch.cuda.synchronize()
+        if ref is None:
+            ref = host(out)
+            assert_close(ref, O.up_proj(x, w), tol=TOL, what="up_proj T=64")
+        else:
+            assert np.array_equal(host(out), ref[:T]), f"T={T} differs from T=64"
+
+
 # ------------------------------------------------------------- HIP graphs --
 def test_graph_replay_matches_eager():
     """Condense + fused decode captured in a HIP graph: every replay, with
