@@ -68,8 +68,8 @@ def parse():
 TRAFFIC_SOURCES = ("mla_latent_kv_lca_amd/csrc/lca_decode.hip", "mla_latent_kv_lca_amd/csrc/lca_stream.h",
                    "mla_latent_kv_lca_amd/csrc/lca_tile.h", "mla_latent_kv_lca_amd/csrc/lca_device.h",
                    "mla_latent_kv_lca_amd/csrc/lca_up_rows.h")
-TRAFFIC = {"sha256": "5f47efbd761031c1dccdd4fc41884c65ec45860344b0a13f7fc4f507d8b51b50",
-           "fetch_bytes": 126_777_943, "write_bytes": 9_617_408}
+TRAFFIC = {"sha256": "a2cde777abec4f95680fcf8b6b85fcf254db4b5189321e4c9ee4348514b03666",
+           "fetch_bytes": 126_764_586, "write_bytes": 9_617_408}
 
 
 def decode_sources_digest() -> str:
