@@ -21,18 +21,17 @@
 //      both halves of a rotary pair in the same lane, so the rotation
 //      happens in registers.
 //   2. q^nope [T, H, 128] (bf16, through the workspace) against W_UK[h]
-//      [512, 128], one head per grid z.
-// Three tile shapes, by token count:
+//      [512, 128].
+// By token count:
 //   - up to 64 tokens (decode): proj_rows_kernel / absorb_rows_kernel,
 //     16 output columns per workgroup over the whole model width, every
 //     load of a wave in flight at once (HBM-bound on the weights);
-//   - fewer than about 4,096 tokens: proj_kernel / absorb_kernel, 128 x 128
-//     tiles, 4 wavefronts of 64 x 64 (four 32x32x16 chains);
-//   - more: proj_big_kernel / absorb_big_kernel, 256 x 256 tiles, 8
-//     wavefronts of 128 x 64.
-// The two tiled shapes stream both operands HBM -> LDS by direct loads in
-// 32-deep k slices through a 4-slice ring (three slices in flight while one
-// is consumed).
+//   - more: proj_kernel (fewer than about 4,096 tokens: 128 x 128 tiles, 4
+//     wavefronts of 64 x 64, four 32x32x16 chains) or proj_big_kernel (256 x
+//     256 tiles, 8 wavefronts of 128 x 64), which stream both operands
+//     HBM -> LDS by direct loads in 32-deep k slices through a 4-slice ring
+//     (three slices in flight while one is consumed); then
+//     absorb_stream_kernel, persistent per head with W_UK[h] in registers.
 #include "lca_stream.h"
 #include "lca_internal.h"
 
@@ -244,7 +243,7 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(ProjArgs pa) {
 // segments four per block, one per wave column (so again both halves of a
 // pair meet in one lane).
 constexpr int PB_BM = 256;                       // tokens per tile
-constexpr int PB_BN = 256;                       // output columns per tile
+static_assert(PB_BM == 256, "a tile is 256 tokens x 256 output columns");
 constexpr int PB_WAVES = 8;
 constexpr int PB_SLOTS = PB_BM * PJ_BK / 8;      // 16-byte slots per operand slice (1024)
 constexpr int PB_SLICE = 2 * PB_SLOTS * 8;       // bf16 per slice, both operands (32 KB)
@@ -435,81 +434,6 @@ __global__ __launch_bounds__(64 * PB_WAVES, 2) void proj_big_kernel(ProjArgs pa)
     }
 }
 
-// The W_UK product on 256 x 256 tiles (the main loop above with K = 128):
-// q_abs[t, h, 256 jb + j] = sum_k qn[t, h, k] W_UK[h][256 jb + j][k].
-template <typename TQ>
-__global__ __launch_bounds__(64 * PB_WAVES, 2) void absorb_big_kernel(const bf16_t* __restrict__ qn, int64_t T,
-                                                                      int H, const bf16_t* __restrict__ wuk,
-                                                                      void* q, int64_t q_stride) {
-  __shared__ __align__(16) bf16_t ring[PJ_NBUF * PB_SLICE];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int jb = blockIdx.y, h = blockIdx.z;
-  const int64_t tok0 = (int64_t)blockIdx.x * PB_BM;
-
-  const bf16_t* ap[PB_DMA];
-  const bf16_t* bp[PB_DMA];
-  const int ch = pj_dma_chunk(lane);
-#pragma unroll
-  for (int i = 0; i < PB_DMA; ++i) {
-    const int r = 16 * (w + PB_WAVES * i) + (lane >> 2);
-    const int64_t t = min(tok0 + r, T - 1);
-    ap[i] = qn + (t * H + h) * D_V + 8 * ch;
-    bp[i] = wuk + ((int64_t)h * D_C + PB_BN * jb + r) * D_V + 8 * ch;
-  }
-  f32x16_t acc[4][2];
-  pb_mainloop(ring, ap, bp, D_V, w, lane, acc);
-
-  const int wm = w >> 2, wn = w & 3, r32 = lane & 31, hk = lane >> 5;
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int64_t t = tok0 + 128 * wm + 32 * mt + 8 * (i >> 2) + 4 * hk + (i & 3);
-      if (t >= T) continue;
-      TQ* dst = reinterpret_cast<TQ*>(q) + t * q_stride + (int64_t)h * D_ROW + PB_BN * jb + 64 * wn + r32;
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) dst[32 * nt] = from_f32<TQ>(acc[mt][nt][i]);
-    }
-}
-
-// q_abs[t, h, 128 jb + j] = sum_k qn[t, h, k] W_UK[h][128 jb + j][k]
-template <typename TQ>
-__global__ __launch_bounds__(256, 2) void absorb_kernel(const bf16_t* __restrict__ qn, int64_t T, int H,
-                                                        const bf16_t* __restrict__ wuk, void* q,
-                                                        int64_t q_stride) {
-  __shared__ __align__(16) bf16_t ring[PJ_NBUF * PJ_SLICE];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int jb = blockIdx.y, h = blockIdx.z;
-  const int64_t tok0 = (int64_t)blockIdx.x * PJ_BM;
-
-  const bf16_t* ap[PJ_DMA];
-  const bf16_t* bp[PJ_DMA];
-  const int ch = pj_dma_chunk(lane);
-#pragma unroll
-  for (int i = 0; i < PJ_DMA; ++i) {
-    const int r = pj_dma_row(w, i, lane);
-    const int64_t t = min(tok0 + r, T - 1);
-    ap[i] = qn + (t * H + h) * D_V + 8 * ch;
-    bp[i] = wuk + ((int64_t)h * D_C + PJ_BN * jb + r) * D_V + 8 * ch;
-  }
-  f32x16_t acc[2][2];
-  pj_mainloop(ring, ap, bp, D_V, w, lane, acc);
-
-  const int wm = w >> 1, wn = w & 1, r32 = lane & 31, hk = lane >> 5;
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int64_t t = tok0 + 64 * wm + 32 * mt + 8 * (i >> 2) + 4 * hk + (i & 3);
-      if (t >= T) continue;
-      TQ* dst = reinterpret_cast<TQ*>(q) + t * q_stride + (int64_t)h * D_ROW + PJ_BN * jb + 64 * wn + r32;
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) dst[32 * nt] = from_f32<TQ>(acc[mt][nt][i]);
-    }
-}
-
 // ---- few tokens (decode): the weights stream once, spread over many
 // workgroups. A workgroup computes 16 output columns for up to 32 tokens over
 // the whole model width. The width is cut into 256-wide k chunks dealt to the
@@ -672,6 +596,120 @@ __global__ __launch_bounds__(256) void absorb_rows_kernel(const bf16_t* __restri
   }
 }
 
+// The absorption for more than a few tokens, q_abs[t, h, n] = sum_k
+// qn[t, h, k] W_UK[h][n][k]: per token and head 256 B read, 1 KB (bf16)
+// written, 131 kflop, so it is bound by the output stores. Persistent
+// workgroups, each bound to one head h for the whole launch (grid = H x
+// groups, heads fastest, so the workgroups of a head sit on one XCD and share
+// its L2 copy of W_UK[h]). Wavefront w keeps output columns [128 w, 128 w +
+// 128) of W_UK[h] in registers as the A operands of 32x32x16 MFMA (four
+// 32-row blocks x 8 k-steps, 128 VGPRs). The workgroup's q^nope rows (tiles
+// of 32 tokens, 8 KB) reach LDS by direct loads, a whole batch of tiles at
+// once, and are read back as B operands; the stores of every tile then
+// stream out with no wait on a load in between. A wave turns its 32 x 128
+// results around in a private LDS area so that each store instruction writes
+// whole 256-byte (bf16) or 512-byte (f32) row pieces of a few tokens rather
+// than 32 bytes of each of 32 tokens.
+constexpr int AS_TOK = 32;                 // tokens per tile (the N extent of a 32x32 block)
+constexpr int AS_TILE = AS_TOK * D_V * 2;  // 8,192 bytes
+// tiles resident at once: the q^nope batch and the four waves' staging areas
+// fill the 160 KB of LDS
+template <typename TQ> constexpr int as_batch() { return sizeof(TQ) == 2 ? 16 : 12; }
+template <typename TQ> constexpr int as_stage() { return AS_TOK * 128 * (int)sizeof(TQ); }  // per wave
+
+// k slots: lane half hf, k-step ks, element e hold k = 64 hf + 8 ks + e, so a
+// lane's 8 operands of one W_UK row lie in one 128-byte line. LDS rows (a
+// token's q^nope, or a token's 128 staged results) keep 16-byte chunk c at
+// slot c ^ (row & 15), so 16 lanes that touch one chunk of 16 rows, or 16
+// chunks of one row, cover all 64 banks once. Row i of a 32-row A block is
+// output column 16 ((i >> 2) & 1) + 4 (i >> 3) + (i & 3) of the block: the 16
+// results a lane holds are then 16 consecutive columns.
+template <typename TQ>
+__global__ __launch_bounds__(256) void absorb_stream_kernel(const bf16_t* __restrict__ qn, int64_t T, int H,
+                                                            const bf16_t* __restrict__ wuk, TQ* __restrict__ q,
+                                                            int64_t q_stride, int n_groups) {
+  constexpr int NB = as_batch<TQ>(), SZ = (int)sizeof(TQ);
+  constexpr int RP = 128 * SZ;      // bytes per staged row (the wave's 128 results of a token)
+  constexpr int CH = RP / 16;        // 16-byte chunks per staged row (16 or 32)
+  __shared__ __align__(16) unsigned char ql[NB * AS_TILE + 4 * as_stage<TQ>()];
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = blockIdx.x % H, grp = blockIdx.x / H;
+  const int64_t n_tiles = (T + AS_TOK - 1) / AS_TOK;
+  if (grp >= n_tiles) return;
+  const int64_t my_tiles = (n_tiles - 1 - grp) / n_groups + 1;  // tiles grp, grp + n_groups, ...
+  const int i = lane & 31, hf = lane >> 5;
+
+  uint4 wa[4][8];
+  {
+    const int n = 128 * w + 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
+    const bf16_t* wr = wuk + ((int64_t)h * D_C + n) * D_V + 64 * hf;
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) wa[jb][ks] = load8_bf16(wr + 32 * jb * D_V + 8 * ks);
+  }
+
+  const uint32_t lds0 = lds_off(ql);
+  unsigned char* stage = ql + NB * AS_TILE + w * as_stage<TQ>();
+  for (int64_t b0 = 0; b0 < my_tiles; b0 += NB) {
+    const int nb = (int)min((int64_t)NB, my_tiles - b0);
+    if (b0 > 0) barrier();  // every wave is done with the previous batch
+    // tile u of the batch: wave w loads slots [128 w, 128 w + 128) (token rows
+    // 8 w .. 8 w + 7); rows past T repeat row T - 1 and are never stored
+    for (int u = 0; u < nb; ++u) {
+      const int64_t tok0 = (grp + (b0 + u) * n_groups) * AS_TOK;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int ii = 2 * w + j, P = 64 * ii + lane, r = P >> 4, c = (P & 15) ^ (r & 15);
+        const int64_t t = min(tok0 + r, T - 1);
+        dma16(qn + (t * H + h) * D_V + 8 * c, lds0 + (uint32_t)(u * AS_TILE) + 1024u * (uint32_t)ii);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    barrier();
+    for (int u = 0; u < nb; ++u) {
+      const unsigned char* tb = ql + u * AS_TILE + 256 * i;
+      uint4 bq[8];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) bq[ks] = *reinterpret_cast<const uint4*>(tb + 16 * ((8 * hf + ks) ^ (i & 15)));
+      f32x16_t acc[4];
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[jb][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) acc[jb] = mfma32x32x16(wa[jb][ks], bq[ks], acc[jb]);
+      // acc[jb][r] = q_abs[token tok0 + i][128 w + 32 jb + 16 hf + r]: into
+      // staged row i, chunks (2 jb + hf) SZ + k, k < SZ, one 16-byte store
+      // each (the wave's own area; its LDS operations run in order, so no
+      // barrier is needed)
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) {
+        float v[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] = acc[jb][r];
+#pragma unroll
+        for (int k = 0; k < SZ; ++k) {
+          TQ* p = reinterpret_cast<TQ*>(stage + RP * i + 16 * (((2 * jb + hf) * SZ + k) ^ (i & 15)));
+          if constexpr (SZ == 2) store8(p, v + 8 * k);
+          else store4(p, v + 4 * k);
+        }
+      }
+      // rows to global memory: lane -> token 64 / CH j + lane / CH, chunk lane % CH
+      const int64_t tok0 = (grp + (b0 + u) * n_groups) * AS_TOK;
+#pragma unroll
+      for (int j = 0; j < CH / 2; ++j) {
+        const int t = (64 / CH) * j + lane / CH, c = lane % CH;
+        const uint4 val = *reinterpret_cast<const uint4*>(stage + RP * t + 16 * (c ^ (t & 15)));
+        if (tok0 + t < T)
+          *reinterpret_cast<uint4*>(q + (tok0 + t) * q_stride + (int64_t)h * D_ROW + 128 * w + c * (16 / SZ)) = val;
+      }
+    }
+  }
+}
+
 hipError_t launch_project(const void* x, int64_t x_stride, int64_t T, int d, const int32_t* pos,
                           double rope_base, const void* w_proj, const void* w_uk, int H, void* rows,
                           int64_t row_stride, const int64_t* dst_row, void* q, int q_dtype,
@@ -680,7 +718,6 @@ hipError_t launch_project(const void* x, int64_t x_stride, int64_t T, int d, con
               (bf16_t*)rows, row_stride, dst_row, q, q_stride, (bf16_t*)qn};
   const unsigned tiles = (unsigned)((T + PJ_BM - 1) / PJ_BM);
   const dim3 g1(tiles, (unsigned)(4 + H + (H + 2) / 2));
-  const dim3 g2(tiles, D_C / PJ_BN, (unsigned)H);
   if (T <= PR_MAX_T && d % (32 * PR_WAVES) == 0) {
     const unsigned chunks = (unsigned)((T + PR_TOK - 1) / PR_TOK);
     hipLaunchKernelGGL(proj_rows_kernel, dim3((unsigned)(D_C / PR_COLS + 12 * H + 4), chunks),
@@ -691,31 +728,26 @@ hipError_t launch_project(const void* x, int64_t x_stride, int64_t T, int d, con
   }
   const int64_t pb_n = (T + PB_BM - 1) / PB_BM * pb_columns(H);
   const dim3 gb((unsigned)(8 * ((pb_n + 7) / 8)));
-  const dim3 gab((unsigned)((T + PB_BM - 1) / PB_BM), D_C / PB_BN, (unsigned)H);
   // 256-wide tiles once they fill most of the chip; below that the 128-wide
   // tiles keep more CUs busy
   const bool big = pb_n >= 224;
-  if (q_dtype == LCA_BF16) {
-    if (big) {
-      hipLaunchKernelGGL(proj_big_kernel<bf16_t>, gb, dim3(64 * PB_WAVES), 0, stream, pa);
-      hipLaunchKernelGGL(absorb_big_kernel<bf16_t>, gab, dim3(64 * PB_WAVES), 0, stream, (const bf16_t*)qn, T, H,
-                         (const bf16_t*)w_uk, q, q_stride);
-    } else {
-      hipLaunchKernelGGL(proj_kernel<bf16_t>, g1, dim3(256), 0, stream, pa);
-      hipLaunchKernelGGL(absorb_kernel<bf16_t>, g2, dim3(256), 0, stream, (const bf16_t*)qn, T, H,
-                         (const bf16_t*)w_uk, q, q_stride);
-    }
+  if (big) {
+    if (q_dtype == LCA_BF16) hipLaunchKernelGGL(proj_big_kernel<bf16_t>, gb, dim3(64 * PB_WAVES), 0, stream, pa);
+    else hipLaunchKernelGGL(proj_big_kernel<float>, gb, dim3(64 * PB_WAVES), 0, stream, pa);
   } else {
-    if (big) {
-      hipLaunchKernelGGL(proj_big_kernel<float>, gb, dim3(64 * PB_WAVES), 0, stream, pa);
-      hipLaunchKernelGGL(absorb_big_kernel<float>, gab, dim3(64 * PB_WAVES), 0, stream, (const bf16_t*)qn, T, H,
-                         (const bf16_t*)w_uk, q, q_stride);
-    } else {
-      hipLaunchKernelGGL(proj_kernel<float>, g1, dim3(256), 0, stream, pa);
-      hipLaunchKernelGGL(absorb_kernel<float>, g2, dim3(256), 0, stream, (const bf16_t*)qn, T, H,
-                         (const bf16_t*)w_uk, q, q_stride);
-    }
+    if (q_dtype == LCA_BF16) hipLaunchKernelGGL(proj_kernel<bf16_t>, g1, dim3(256), 0, stream, pa);
+    else hipLaunchKernelGGL(proj_kernel<float>, g1, dim3(256), 0, stream, pa);
   }
+  const int64_t as_tiles = (T + AS_TOK - 1) / AS_TOK;
+  const int64_t as_fill = as_tiles < 256 / H ? as_tiles : 256 / H;  // one workgroup per CU
+  const int as_groups = as_fill > 1 ? (int)as_fill : 1;
+  const dim3 gs((unsigned)(as_groups * H));
+  if (q_dtype == LCA_BF16)
+    hipLaunchKernelGGL(absorb_stream_kernel<bf16_t>, gs, dim3(256), 0, stream, (const bf16_t*)qn, T, H,
+                       (const bf16_t*)w_uk, (bf16_t*)q, q_stride, as_groups);
+  else
+    hipLaunchKernelGGL(absorb_stream_kernel<float>, gs, dim3(256), 0, stream, (const bf16_t*)qn, T, H,
+                       (const bf16_t*)w_uk, (float*)q, q_stride, as_groups);
   return hipGetLastError();
 }
 
