@@ -318,6 +318,25 @@ def test_project_benchmark_sizes_sampled(T):
     _absorbed_within(q[sample][..., :512], ref_q[..., :512], x[sample], w, wuk, "absorbed query part")
 
 
+@pytest.mark.parametrize("T,q_dtype", [(8230, torch.bfloat16),   # 17 tiles of 32 tokens on two workgroups
+                                       (6170, torch.float32)])   # 13 tiles on one workgroup, ragged tail
+def test_project_absorption_in_batches(T, q_dtype):
+    """The absorption's workgroups hold at most 16 (bf16 output) or 12 (f32)
+    token tiles of q_nope at once; at these sizes some of them take a second
+    batch (and the last, partial tile), checked on every token."""
+    d, H = 64, 16
+    x = li.hidden_states(76, T, d)
+    w = li.w_proj(76, H, d)
+    wuk = li.w_uk(76, H)
+    pos = np.arange(T, dtype=np.int32)
+    dst = np.arange(T, dtype=np.int64)
+    rows, q = _project_gpu(x, pos, w, wuk, dst, T, q_dtype)
+    ref_rows, ref_q = O.project(x, pos, w.T, wuk, H)
+    _within(rows, ref_rows, 2.0 ** -8, 1e-3, "cache rows")
+    _within(q[..., 512:], ref_q[..., 512:], 2.0 ** -8, 1e-3, "rotated query part")
+    _absorbed_within(q[..., :512], ref_q[..., :512], x, w, wuk, "absorbed query part")
+
+
 def test_project_strided_inputs_and_outputs():
     """Hidden states with a token stride wider than d_model, absorbed queries
     written into every other slot of a history buffer, cache rows into a
