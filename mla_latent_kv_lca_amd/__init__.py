@@ -191,14 +191,18 @@ def _stream(stream) -> int:
 
 
 def latent(c: torch.Tensor, kr: torch.Tensor) -> LatentT:
-    """Describe c_KV [B, L, 512] (or [L, 512]) and k_R [B, L, 64] views."""
+    """Describe c_KV [B, L, 512] (or [L, 512]) and k_R [B, L, 64] views. The
+    description holds references to both tensors, so their memory lives as
+    long as it does."""
     if c.dtype != kr.dtype:
         raise TypeError("c and kr must share a dtype")
     if c.shape[-1] != D_C or kr.shape[-1] != D_R or c.stride(-1) != 1 or kr.stride(-1) != 1:
         raise ValueError("c must end in a contiguous 512-wide axis and kr in a 64-wide axis")
     cs = c.stride(0) if c.dim() == 3 else 0
     ks = kr.stride(0) if kr.dim() == 3 else 0
-    return LatentT(c.data_ptr(), kr.data_ptr(), cs, c.stride(-2), ks, kr.stride(-2), dtype_code(c))
+    d = LatentT(c.data_ptr(), kr.data_ptr(), cs, c.stride(-2), ks, kr.stride(-2), dtype_code(c))
+    d._tensors = (c, kr)  # the descriptor keeps its tensors (e.g. temporary copies) alive
+    return d
 
 
 def packed_latent(cache: torch.Tensor) -> LatentT:
@@ -208,15 +212,17 @@ def packed_latent(cache: torch.Tensor) -> LatentT:
 
 def paged_latent(pool: torch.Tensor, block_table: torch.Tensor) -> PagedT:
     """Describe a paged cache: pool [n_pages, page_rows, 576] bf16 (packed rows),
-    block_table int32 [B, pages per sequence] on the device. The tensors must
-    outlive the calls that use the description."""
+    block_table int32 [B, pages per sequence] on the device. The description holds
+    references to both tensors."""
     if pool.dim() != 3 or pool.shape[-1] != D_ROW or pool.stride(-1) != 1:
         raise ValueError("pool must be [n_pages, page_rows, 576] with contiguous rows")
     if pool.stride(0) != pool.shape[1] * pool.stride(1):
         raise ValueError("pages must be contiguous in the pool")
     if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
         raise ValueError("block_table must be an int32 [B, n] tensor with contiguous rows")
-    return PagedT(pool.data_ptr(), pool.stride(1), pool.shape[1], block_table.data_ptr(), block_table.stride(0))
+    d = PagedT(pool.data_ptr(), pool.stride(1), pool.shape[1], block_table.data_ptr(), block_table.stride(0))
+    d._tensors = (pool, block_table)
+    return d
 
 
 # ----------------------------------------------------------------- calls ---

@@ -404,18 +404,23 @@ def test_decode_paged_up_equals_paged_decode_then_up_proj():
         assert_close(host(y2[b:b + 1]), O.up_proj(ro, wuv), what=f"paged decode_up out seq {b}")
 
 
-@pytest.mark.parametrize("B,L,g,with_alpha", [(3, 5000, 16, True), (2, 4100, 8, False), (1, 70000, 16, False)])
-def test_condense_streaming_kernel_equals_general_kernel(B, L, g, with_alpha):
+@pytest.mark.parametrize("B,L,g,with_alpha,Hq,q_dtype", [
+    (3, 5000, 16, True, 16, torch.bfloat16), (2, 4100, 8, False, 16, torch.bfloat16),
+    (1, 70000, 16, False, 16, torch.bfloat16),
+    (2, 3000, 16, False, 32, torch.float32),    # 512 query rows per summary query, f32 queries
+    (2, 3000, 16, False, 48, torch.bfloat16)])  # 768 query rows
+def test_condense_streaming_kernel_equals_general_kernel(B, L, g, with_alpha, Hq, q_dtype):
     """Packed bf16 rows with one summary query per sequence take the streaming
-    kernel; the same rows given as separate c_KV / k_R tensors take the general
-    kernel. Both must agree bit for bit (same arithmetic order), and with the
-    oracle on sampled groups."""
+    kernel; the same rows given as separate c_KV / k_R tensors (temporary
+    copies, kept alive by the description) take the general kernel. Both must
+    agree bit for bit (same arithmetic order), and with the oracle on sampled
+    groups."""
     c, kr = li.latent_cache(15, B, L)
     li.plant_needles(15, c, kr, 3, 12.0, 0, L)
-    q = li.queries(15, B, g, H, rho=0.5)
+    q = li.queries(15, B, g, Hq, rho=0.5)
     m = (L - 64) // g
     cache_t = packed(c, kr)
-    q_t = dev(q)
+    q_t = dev(q, q_dtype)
     outs = []
     for split in (False, True):
         reps = torch.zeros((B, m, 576), dtype=torch.bfloat16, device="cuda")
