@@ -401,7 +401,9 @@ def prefill_leg(Lp):
     def m_of(s):
         return (s - W) // G if s > W else 0
 
-    def run(ev=None):
+    sched = lca.prefill_sched()  # blocks taken from one counter by persistent workgroups
+
+    def run(ev=None, sc=sched):
         m = 0
         for s in range(0, Lp, PF_C):
             ms = m_of(s)
@@ -413,7 +415,7 @@ def prefill_leg(Lp):
             if ev is not None:
                 ev[s // PF_C][0].record()
             lca.mla_latent_attn_prefill_chunk(q[s:e], s, rl if m else None, m, cl, m * G, 1.0,
-                                              o_lat[s:e])
+                                              o_lat[s:e], sched=sc)
             if ev is not None:
                 ev[s // PF_C][1].record()
         if ev is not None:
@@ -437,6 +439,10 @@ def prefill_leg(Lp):
     total_ms = t0.elapsed_time(t1)
     attn_ms = sum(a.elapsed_time(b) for a, b in ev)
     up_ms = ev_up[0].elapsed_time(ev_up[1])
+    # the same chunks through the per-block kernel (one workgroup per block)
+    run(ev, sc=None)
+    torch.cuda.synchronize()
+    attn_pb_ms = sum(a.elapsed_time(b) for a, b in ev)
     # algorithmic flops: every visible (query, entry) pair, 16 heads, QK 576 + PV 512
     pairs = 0
     for s in range(0, Lp, PF_C):
@@ -450,6 +456,8 @@ def prefill_leg(Lp):
             "attention_ms": attn_ms, "attention_tflop": attn_flop / 1e12,
             "attention_tflops": attn_flop / (attn_ms * 1e-3) / 1e12,
             "mfma_frac": attn_flop / (attn_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS,
+            "attention_call": "mla_latent_attn_prefill_chunk_sched",
+            "attention_ms_per_block_kernel": attn_pb_ms,
             "up_proj_tflop": up_flop / 1e12,
             "up_proj_ms": up_ms,
             # latent read + output written + W_UV, bf16
@@ -550,6 +558,8 @@ def paged_leg(B=32, page_rows=64, reps_=20):
     chunks = [(s0, min(Lp, s0 + PF_C), (s0 - W) // G if s0 > W else 0) for s0 in range(0, Lp, PF_C)]
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in chunks]
 
+    psched = lca.prefill_sched()
+
     def prefill(ev=None):
         mm = 0
         for k, (s0, e, ms_) in enumerate(chunks):
@@ -560,7 +570,7 @@ def paged_leg(B=32, page_rows=64, reps_=20):
             if ev is not None:
                 ev[k][0].record(stream)
             lca.mla_latent_attn_prefill_chunk_paged(qp[s0:e], s0, rl_p2 if mm else None, mm, cache, bl, mm * G,
-                                                    1.0, out_p[s0:e])
+                                                    1.0, out_p[s0:e], sched=psched)
             if ev is not None:
                 ev[k][1].record(stream)
 
@@ -579,6 +589,7 @@ def paged_leg(B=32, page_rows=64, reps_=20):
             "condense_us": t_con * 1e6, "condense_gbs": con_bytes / t_con / 1e9,
             "prefill": {"seq_len": Lp, "chunk": PF_C, "attention_ms": pf_ms, "attention_tflops": pf_tflops,
                         "mfma_frac": pf_tflops / MFMA_PEAK_TFLOPS,
+                        "call": "mla_latent_attn_prefill_chunk_paged_sched",
                         "note": "one sequence of the batch, raw rows read through its block table"}}
 
 

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define LCA_VERSION 1003 /* major*1000 + minor */
+#define LCA_VERSION 1004 /* major*1000 + minor */
 #define LCA_D_C 512      /* latent c_KV width */
 #define LCA_D_R 64       /* decoupled RoPE key width */
 #define LCA_D_ROW 576    /* one cached row: c_KV ++ k_R */
@@ -420,6 +420,32 @@ int mla_latent_attn_prefill_chunk_paged(const void* q, int32_t q_dtype, int64_t 
                                         const lca_latent_t* reps, int64_t m, const lca_paged_t* cache,
                                         int32_t seq, int64_t raw_begin, float sm_scale, void* o_latent,
                                         int32_t o_dtype, float* lse, hipStream_t stream);
+
+/* mla_latent_attn_prefill_chunk and mla_latent_attn_prefill_chunk_paged with
+ * a scheduling counter: the same attention (整体框架) and the same outputs,
+ * bit for bit, computed by persistent workgroups (one per CU) that take the
+ * chunk's query blocks (128 query rows each), heaviest first, from `sched`.
+ * Workgroups are otherwise dealt to the XCDs by index, so a slower XCD would
+ * end every chunk late; taken from one counter, the blocks go to whichever
+ * workgroup is free. sched: device memory of two int32, 8-byte aligned,
+ * owned by the caller; it must hold zeros before the first call, and every
+ * call leaves zeros behind (the last workgroup resets it), so one pair
+ * serves any number of calls in a stream or a replayed graph. Calls that can
+ * run at the same time (other streams) need pairs of their own. The counter
+ * is used by the packed-bf16 kernel; layouts that take the register-staged
+ * kernel ignore it. Errors as in the calls above, and LCA_ERR_INVALID_ARG
+ * for a null or misaligned sched. */
+int mla_latent_attn_prefill_chunk_sched(const void* q, int32_t q_dtype, int64_t q_tok_stride,
+                                        int64_t chunk_start, int32_t C, int32_t H,
+                                        const lca_latent_t* reps, int64_t m,
+                                        const lca_latent_t* raw, int64_t raw_begin, float sm_scale,
+                                        void* o_latent, int32_t o_dtype, float* lse,
+                                        int32_t* sched, hipStream_t stream);
+int mla_latent_attn_prefill_chunk_paged_sched(const void* q, int32_t q_dtype, int64_t q_tok_stride,
+                                              int64_t chunk_start, int32_t C, int32_t H,
+                                              const lca_latent_t* reps, int64_t m, const lca_paged_t* cache,
+                                              int32_t seq, int64_t raw_begin, float sm_scale, void* o_latent,
+                                              int32_t o_dtype, float* lse, int32_t* sched, hipStream_t stream);
 
 /* Per-head value up-projection (the MLA page's projection back to the head
  * space, 三.1): out[t, h, :] = o_latent[t, h, :] @ W_UV[h].

@@ -34,7 +34,8 @@ EXPORTS = ("lca_version", "lca_last_error", "lca_plan", "lca_condense_workspace_
            "mla_latent_attn_decode", "mla_latent_attn_decode_paged", "mla_latent_attn_decode_paged_up",
            "mla_latent_attn_decode_paged_up_step",
            "mla_latent_attn_decode_up", "mla_latent_attn_decode_up_noalloc", "mla_latent_attn_prefill_chunk",
-           "mla_latent_attn_prefill_chunk_paged",
+           "mla_latent_attn_prefill_chunk_paged", "mla_latent_attn_prefill_chunk_sched",
+           "mla_latent_attn_prefill_chunk_paged_sched",
            "mla_up_proj",
            "lca_project_workspace_size", "lca_project")
 
@@ -144,6 +145,12 @@ def load() -> ctypes.CDLL:
                                                   c_int32, P(LatentT), c_int64, P(LatentT),
                                                   c_int64, c_float, c_void_p, c_int32, c_void_p,
                                                   c_void_p]
+    lib.mla_latent_attn_prefill_chunk_sched.restype = c_int32
+    lib.mla_latent_attn_prefill_chunk_sched.argtypes = lib.mla_latent_attn_prefill_chunk.argtypes[:-1] + [
+        c_void_p, c_void_p]
+    lib.mla_latent_attn_prefill_chunk_paged_sched.restype = c_int32
+    lib.mla_latent_attn_prefill_chunk_paged_sched.argtypes = lib.mla_latent_attn_prefill_chunk_paged.argtypes[:-1] + [
+        c_void_p, c_void_p]
     lib.mla_up_proj.restype = c_int32
     lib.mla_up_proj.argtypes = [c_void_p, c_int32, c_int64, c_int32, c_void_p, c_int32, c_void_p,
                                 c_int32, c_void_p]
@@ -515,36 +522,58 @@ def mla_latent_attn_decode_up_noalloc(q: torch.Tensor, reps: LatentT | None, m: 
 def mla_latent_attn_prefill_chunk(q: torch.Tensor, chunk_start: int, reps: LatentT | None, m: int,
                                   raw: LatentT, raw_begin: int, sm_scale: float,
                                   o_latent: torch.Tensor, lse: torch.Tensor | None = None,
-                                  stream=None) -> None:
-    """q [C, H, 576] (queries at positions chunk_start ..); o_latent [C, H, 512]."""
+                                  stream=None, sched: torch.Tensor | None = None) -> None:
+    """q [C, H, 576] (queries at positions chunk_start ..); o_latent [C, H, 512].
+    sched (int32 [2] on the device, zeroed once, see prefill_sched()) selects
+    mla_latent_attn_prefill_chunk_sched."""
     if q.dim() != 3 or q.shape[-1] != D_ROW or q.stride(-1) != 1 or q.stride(-2) != D_ROW:
         raise ValueError("q must be [C, H, 576] with contiguous heads")
     C, H = q.shape[0], q.shape[1]
     if not o_latent.is_contiguous() or o_latent.shape != (C, H, D_C):
         raise ValueError("o_latent must be a contiguous [C, H, 512] tensor")
     _check_lse(lse, C, H)
-    _check(load().mla_latent_attn_prefill_chunk(
-        q.data_ptr(), dtype_code(q), q.stride(0), chunk_start, C, H,
-        None if reps is None else ctypes.byref(reps), m, ctypes.byref(raw), raw_begin, sm_scale,
-        o_latent.data_ptr(), dtype_code(o_latent), _ptr(lse), _stream(stream)))
+    args = (q.data_ptr(), dtype_code(q), q.stride(0), chunk_start, C, H,
+            None if reps is None else ctypes.byref(reps), m, ctypes.byref(raw), raw_begin, sm_scale,
+            o_latent.data_ptr(), dtype_code(o_latent), _ptr(lse))
+    if sched is None:
+        _check(load().mla_latent_attn_prefill_chunk(*args, _stream(stream)))
+    else:
+        _check_sched(sched)
+        _check(load().mla_latent_attn_prefill_chunk_sched(*args, sched.data_ptr(), _stream(stream)))
 
 
 def mla_latent_attn_prefill_chunk_paged(q: torch.Tensor, chunk_start: int, reps: LatentT | None, m: int,
                                         cache: PagedT, seq: int, raw_begin: int, sm_scale: float,
                                         o_latent: torch.Tensor, lse: torch.Tensor | None = None,
-                                        stream=None) -> None:
+                                        stream=None, sched: torch.Tensor | None = None) -> None:
     """Chunked prefill of sequence `seq` of a paged cache: q [C, H, 576]
-    (queries at positions chunk_start ..), o_latent [C, H, 512]."""
+    (queries at positions chunk_start ..), o_latent [C, H, 512]. sched as in
+    mla_latent_attn_prefill_chunk."""
     if q.dim() != 3 or q.shape[-1] != D_ROW or q.stride(-1) != 1 or q.stride(-2) != D_ROW:
         raise ValueError("q must be [C, H, 576] with contiguous heads")
     C, H = q.shape[0], q.shape[1]
     if not o_latent.is_contiguous() or o_latent.shape != (C, H, D_C):
         raise ValueError("o_latent must be a contiguous [C, H, 512] tensor")
     _check_lse(lse, C, H)
-    _check(load().mla_latent_attn_prefill_chunk_paged(
-        q.data_ptr(), dtype_code(q), q.stride(0), chunk_start, C, H,
-        None if reps is None else ctypes.byref(reps), m, ctypes.byref(cache), seq, raw_begin, sm_scale,
-        o_latent.data_ptr(), dtype_code(o_latent), _ptr(lse), _stream(stream)))
+    args = (q.data_ptr(), dtype_code(q), q.stride(0), chunk_start, C, H,
+            None if reps is None else ctypes.byref(reps), m, ctypes.byref(cache), seq, raw_begin, sm_scale,
+            o_latent.data_ptr(), dtype_code(o_latent), _ptr(lse))
+    if sched is None:
+        _check(load().mla_latent_attn_prefill_chunk_paged(*args, _stream(stream)))
+    else:
+        _check_sched(sched)
+        _check(load().mla_latent_attn_prefill_chunk_paged_sched(*args, sched.data_ptr(), _stream(stream)))
+
+
+def prefill_sched(device="cuda") -> torch.Tensor:
+    """A zeroed scheduling counter for the *_sched prefill calls (int32 [2];
+    every call leaves it zeroed, so it is reused; one per concurrent stream)."""
+    return torch.zeros(2, dtype=torch.int32, device=device)
+
+
+def _check_sched(sched: torch.Tensor) -> None:
+    if sched.dtype != torch.int32 or sched.numel() < 2 or not sched.is_contiguous():
+        raise ValueError("sched must be a contiguous int32 tensor of at least 2 elements")
 
 
 def mla_up_proj(o_latent: torch.Tensor, w_uv: torch.Tensor, out: torch.Tensor, stream=None) -> None:

@@ -484,12 +484,10 @@ int mla_latent_attn_decode_up_noalloc(const void* q, int32_t q_dtype, int64_t q_
                     "mla_latent_attn_decode_up_noalloc launch");
 }
 
-int mla_latent_attn_prefill_chunk(const void* q, int32_t q_dtype, int64_t q_tok_stride,
-                                  int64_t chunk_start, int32_t C, int32_t H,
-                                  const lca_latent_t* reps, int64_t m,
-                                  const lca_latent_t* raw, int64_t raw_begin, float sm_scale,
-                                  void* o_latent, int32_t o_dtype, float* lse,
-                                  hipStream_t stream) {
+static int prefill_dense(const void* q, int32_t q_dtype, int64_t q_tok_stride, int64_t chunk_start, int32_t C,
+                         int32_t H, const lca_latent_t* reps, int64_t m, const lca_latent_t* raw,
+                         int64_t raw_begin, float sm_scale, void* o_latent, int32_t o_dtype, float* lse,
+                         int32_t* sched, hipStream_t stream) {
   int rc;
   if (q == nullptr || !aligned16(q)) return fail(LCA_ERR_INVALID_ARG, "q must be a non-null 16-byte aligned pointer");
   if (!valid_dtype(q_dtype)) return fail(LCA_ERR_INVALID_ARG, "q_dtype %d is not LCA_BF16/LCA_F32", q_dtype);
@@ -507,15 +505,36 @@ int mla_latent_attn_prefill_chunk(const void* q, int32_t q_dtype, int64_t q_tok_
   if (o_latent == nullptr || !aligned16(o_latent)) return fail(LCA_ERR_INVALID_ARG, "o_latent must be a non-null 16-byte aligned pointer");
   const lca_latent_t none = {nullptr, nullptr, 0, 0, 0, 0, raw->dtype};
   return hip_status(lca::launch_prefill(q, q_dtype, q_tok_stride, chunk_start, C, H, m > 0 ? *reps : none,
-                                        m, *raw, raw_begin, sm_scale, o_latent, o_dtype, lse, stream),
+                                        m, *raw, raw_begin, sm_scale, o_latent, o_dtype, lse, stream, sched),
                     "mla_latent_attn_prefill_chunk launch");
 }
 
-int mla_latent_attn_prefill_chunk_paged(const void* q, int32_t q_dtype, int64_t q_tok_stride,
+int mla_latent_attn_prefill_chunk(const void* q, int32_t q_dtype, int64_t q_tok_stride,
+                                  int64_t chunk_start, int32_t C, int32_t H,
+                                  const lca_latent_t* reps, int64_t m,
+                                  const lca_latent_t* raw, int64_t raw_begin, float sm_scale,
+                                  void* o_latent, int32_t o_dtype, float* lse,
+                                  hipStream_t stream) {
+  return prefill_dense(q, q_dtype, q_tok_stride, chunk_start, C, H, reps, m, raw, raw_begin, sm_scale, o_latent,
+                       o_dtype, lse, nullptr, stream);
+}
+
+int mla_latent_attn_prefill_chunk_sched(const void* q, int32_t q_dtype, int64_t q_tok_stride,
                                         int64_t chunk_start, int32_t C, int32_t H,
-                                        const lca_latent_t* reps, int64_t m, const lca_paged_t* cache,
-                                        int32_t seq, int64_t raw_begin, float sm_scale, void* o_latent,
-                                        int32_t o_dtype, float* lse, hipStream_t stream) {
+                                        const lca_latent_t* reps, int64_t m,
+                                        const lca_latent_t* raw, int64_t raw_begin, float sm_scale,
+                                        void* o_latent, int32_t o_dtype, float* lse,
+                                        int32_t* sched, hipStream_t stream) {
+  if (sched == nullptr || reinterpret_cast<uintptr_t>(sched) % 8 != 0)
+    return fail(LCA_ERR_INVALID_ARG, "sched must be a non-null 8-byte aligned pointer to two int32");
+  return prefill_dense(q, q_dtype, q_tok_stride, chunk_start, C, H, reps, m, raw, raw_begin, sm_scale, o_latent,
+                       o_dtype, lse, sched, stream);
+}
+
+static int prefill_paged(const void* q, int32_t q_dtype, int64_t q_tok_stride, int64_t chunk_start, int32_t C,
+                         int32_t H, const lca_latent_t* reps, int64_t m, const lca_paged_t* cache, int32_t seq,
+                         int64_t raw_begin, float sm_scale, void* o_latent, int32_t o_dtype, float* lse,
+                         int32_t* sched, hipStream_t stream) {
   int rc;
   if (q == nullptr || !aligned16(q)) return fail(LCA_ERR_INVALID_ARG, "q must be a non-null 16-byte aligned pointer");
   if (!valid_dtype(q_dtype)) return fail(LCA_ERR_INVALID_ARG, "q_dtype %d is not LCA_BF16/LCA_F32", q_dtype);
@@ -548,8 +567,29 @@ int mla_latent_attn_prefill_chunk_paged(const void* q, int32_t q_dtype, int64_t 
   if (o_latent == nullptr || !aligned16(o_latent)) return fail(LCA_ERR_INVALID_ARG, "o_latent must be a non-null 16-byte aligned pointer");
   const lca_latent_t none = {nullptr, nullptr, 0, 0, 0, 0, LCA_BF16};
   return hip_status(lca::launch_prefill_paged(q, q_dtype, q_tok_stride, chunk_start, C, H, m > 0 ? *reps : none, m,
-                                              *cache, seq, raw_begin, sm_scale, o_latent, o_dtype, lse, stream),
+                                              *cache, seq, raw_begin, sm_scale, o_latent, o_dtype, lse, stream,
+                                              sched),
                     "mla_latent_attn_prefill_chunk_paged launch");
+}
+
+int mla_latent_attn_prefill_chunk_paged(const void* q, int32_t q_dtype, int64_t q_tok_stride,
+                                        int64_t chunk_start, int32_t C, int32_t H,
+                                        const lca_latent_t* reps, int64_t m, const lca_paged_t* cache,
+                                        int32_t seq, int64_t raw_begin, float sm_scale, void* o_latent,
+                                        int32_t o_dtype, float* lse, hipStream_t stream) {
+  return prefill_paged(q, q_dtype, q_tok_stride, chunk_start, C, H, reps, m, cache, seq, raw_begin, sm_scale,
+                       o_latent, o_dtype, lse, nullptr, stream);
+}
+
+int mla_latent_attn_prefill_chunk_paged_sched(const void* q, int32_t q_dtype, int64_t q_tok_stride,
+                                              int64_t chunk_start, int32_t C, int32_t H,
+                                              const lca_latent_t* reps, int64_t m, const lca_paged_t* cache,
+                                              int32_t seq, int64_t raw_begin, float sm_scale, void* o_latent,
+                                              int32_t o_dtype, float* lse, int32_t* sched, hipStream_t stream) {
+  if (sched == nullptr || reinterpret_cast<uintptr_t>(sched) % 8 != 0)
+    return fail(LCA_ERR_INVALID_ARG, "sched must be a non-null 8-byte aligned pointer to two int32");
+  return prefill_paged(q, q_dtype, q_tok_stride, chunk_start, C, H, reps, m, cache, seq, raw_begin, sm_scale,
+                       o_latent, o_dtype, lse, sched, stream);
 }
 
 int mla_up_proj(const void* o_latent, int32_t o_dtype, int64_t T, int32_t H, const void* w_uv,

@@ -109,14 +109,17 @@ hipError_t launch_decode_up(const void* q, int q_dtype, int64_t q_seq_stride, in
 hipError_t launch_prefill(const void* q, int q_dtype, int64_t q_tok_stride, int64_t chunk_start,
                           int C, int H, const lca_latent_t& reps, int64_t m,
                           const lca_latent_t& raw, int64_t raw_begin, float sm_scale,
-                          void* o_latent, int o_dtype, float* lse, hipStream_t stream);
+                          void* o_latent, int o_dtype, float* lse, hipStream_t stream,
+                          int* sched = nullptr);
 
 // chunked prefill of sequence `seq` of a paged cache (raw rows through its
-// block table; representatives dense, same row stride as the pages)
+// block table; representatives dense, same row stride as the pages). With
+// sched (two ints, zero on entry, zero again when the launch ends) the
+// packed-row kernel runs as persistent workgroups taking blocks from it.
 hipError_t launch_prefill_paged(const void* q, int q_dtype, int64_t q_tok_stride, int64_t chunk_start,
                                 int C, int H, const lca_latent_t& reps, int64_t m, const lca_paged_t& cache,
                                 int seq, int64_t raw_begin, float sm_scale, void* o_latent, int o_dtype,
-                                float* lse, hipStream_t stream);
+                                float* lse, hipStream_t stream, int* sched = nullptr);
 
 // ---- up-projection
 constexpr int UP_SMALL_T = 64;  // token counts up to this use the small-T kernel

@@ -145,18 +145,22 @@ __device__ __forceinline__ float rows4_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// One query block (128 query rows: 128 / Hb tokens x Hb heads of head group
+// hg) of a chunk, by the whole workgroup.
 template <typename TQ, typename TO, class Src>
-__global__ __launch_bounds__(64 * PFW) void prefill_kernel(
-    const TQ* __restrict__ q, int64_t q_tok, int64_t chunk_start, int C, int H, int lhb, Src src,
-    int64_t m, int64_t raw_begin, float scale_log2, TO* __restrict__ o, float* __restrict__ lse) {
-  __shared__ __align__(16) bf16_t ring[PFRING][STILE_ELEMS];
-
-  const int tid = threadIdx.x, lane = tid & 63;
+__device__ __forceinline__ void prefill_block(
+    bf16_t (&ring)[PFRING][STILE_ELEMS], const TQ* __restrict__ q, int64_t q_tok, int64_t chunk_start, int C,
+    int H, int lhb, const Src& src, int64_t m, int64_t raw_begin, float scale_log2, TO* __restrict__ o,
+    float* __restrict__ lse, int blk, int hg) {
+  // an opaque copy of the thread index: in the persistent kernel nothing
+  // derived from it is hoisted out of the block loop (there is no register
+  // to hold it there)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool lead = w < SNW;  // fills the tiles; runs each tile as scores, softmax, values
   const int kg = lane >> 4, col = lane & 15;
-  const int blk = (int)gridDim.x - 1 - (int)blockIdx.x;  // heavy workgroups first
-  const int hg = blockIdx.y;
   // query row R = 16 w + col of the workgroup is (token R >> lhb, head
   // R % Hb), Hb = 2^lhb = min(H, 16): 128 / Hb tokens per workgroup
   const int n_tok = 128 >> lhb, hmask = (1 << lhb) - 1;
@@ -327,6 +331,52 @@ __global__ __launch_bounds__(64 * PFW) void prefill_kernel(
     lse[(int64_t)i_tok * H + head] = (m_run + __log2f(l_row)) * 0.69314718055994530942f;
 }
 
+template <typename TQ, typename TO, class Src>
+__global__ __launch_bounds__(64 * PFW) void prefill_kernel(
+    const TQ* __restrict__ q, int64_t q_tok, int64_t chunk_start, int C, int H, int lhb, Src src,
+    int64_t m, int64_t raw_begin, float scale_log2, TO* __restrict__ o, float* __restrict__ lse) {
+  __shared__ __align__(16) bf16_t ring[PFRING][STILE_ELEMS];
+  // heavy workgroups (latest tokens) first
+  prefill_block<TQ, TO, Src>(ring, q, q_tok, chunk_start, C, H, lhb, src, m, raw_begin, scale_log2, o, lse,
+                             (int)gridDim.x - 1 - (int)blockIdx.x, blockIdx.y);
+}
+
+// The same blocks taken by persistent workgroups from a counter in global
+// memory, heaviest first: workgroups are dealt to the XCDs round robin by
+// index, so with one workgroup per block the hardware balances load only
+// inside each XCD, and a slower XCD ends the chunk late; from the counter,
+// a workgroup that finishes early takes the next block wherever it runs. A
+// block's result does not depend on which workgroup computes it. sched[0]
+// is the next block, sched[1] counts workgroups that found none left; the
+// last of them puts both back to zero, so every launch starts and ends with
+// a zeroed pair (the caller zeroes it once).
+constexpr int PF_SCHED_WG = 256;  // persistent workgroups: one per CU of the part
+
+template <typename TQ, typename TO, class Src>
+__global__ __launch_bounds__(64 * PFW) void prefill_sched_kernel(
+    const TQ* __restrict__ q, int64_t q_tok, int64_t chunk_start, int C, int H, int lhb, Src src,
+    int64_t m, int64_t raw_begin, float scale_log2, TO* __restrict__ o, float* __restrict__ lse,
+    int n_blocks, int n_hg, int* __restrict__ sched) {
+  __shared__ __align__(16) bf16_t ring[PFRING][STILE_ELEMS];
+  __shared__ int next;
+  const int n_items = n_blocks * n_hg;
+  for (;;) {
+    // one barrier per block: the previous block's tile loop had barriers
+    // after every wave read `next`, and its last tile is read by every
+    // wave before the barrier here releases the ring
+    if (threadIdx.x == 0) next = atomicAdd(sched, 1);
+    __syncthreads();
+    const int item = next;
+    if (item < 0 || item >= n_items) break;  // (negative only if sched was not zeroed)
+    prefill_block<TQ, TO, Src>(ring, q, q_tok, chunk_start, C, H, lhb, src, m, raw_begin, scale_log2, o, lse,
+                               n_blocks - 1 - item / n_hg, item % n_hg);
+  }
+  if (threadIdx.x == 0 && atomicAdd(sched + 1, 1) == (int)(gridDim.x * gridDim.y) - 1) {
+    atomicExch(sched, 0);
+    atomicExch(sched + 1, 0);
+  }
+}
+
 template <typename TQ, typename TC, typename TO>
 static void launch_pf_t(dim3 grid, hipStream_t st, const void* q, int64_t q_tok, int64_t cs,
                         int C, int H, int lhb, Seg reps, int64_t m, Seg raw, int64_t rb, float sl2, void* o,
@@ -352,8 +402,18 @@ static bool packed_rows_pf(const lca_latent_t& t) {
 template <typename TQ, class Src>
 static void launch_pf2(int o_dtype, dim3 grid, hipStream_t st, const void* q, int64_t q_tok,
                        int64_t cs, int C, int H, int lhb, const Src& src, int64_t m, int64_t rb, float sl2,
-                       void* o, float* lse) {
+                       void* o, float* lse, int* sched = nullptr) {
   grid.x = (unsigned)((C + (128 >> lhb) - 1) / (128 >> lhb));  // 128 query rows per workgroup
+  if (sched != nullptr) {
+    // one resident workgroup per CU (the ring fills its LDS), at most one per block
+    const int items = (int)(grid.x * grid.y);
+    const dim3 gs((unsigned)(items < PF_SCHED_WG ? items : PF_SCHED_WG));
+    if (o_dtype == LCA_BF16)
+      hipLaunchKernelGGL((prefill_sched_kernel<TQ, bf16_t, Src>), gs, dim3(64 * PFW), 0, st, (const TQ*)q, q_tok, cs, C, H, lhb, src, m, rb, sl2, (bf16_t*)o, lse, (int)grid.x, (int)grid.y, sched);
+    else
+      hipLaunchKernelGGL((prefill_sched_kernel<TQ, float, Src>), gs, dim3(64 * PFW), 0, st, (const TQ*)q, q_tok, cs, C, H, lhb, src, m, rb, sl2, (float*)o, lse, (int)grid.x, (int)grid.y, sched);
+    return;
+  }
   if (o_dtype == LCA_BF16)
     hipLaunchKernelGGL((prefill_kernel<TQ, bf16_t, Src>), grid, dim3(64 * PFW), 0, st, (const TQ*)q, q_tok, cs, C, H, lhb, src, m, rb, sl2, (bf16_t*)o, lse);
   else
@@ -380,7 +440,7 @@ static float fast_scale(float sm_scale) {
 hipError_t launch_prefill_paged(const void* q, int q_dtype, int64_t q_tok_stride, int64_t chunk_start,
                                 int C, int H, const lca_latent_t& reps, int64_t m, const lca_paged_t& cache,
                                 int seq, int64_t raw_begin, float sm_scale, void* o_latent, int o_dtype,
-                                float* lse, hipStream_t stream) {
+                                float* lse, hipStream_t stream, int* sched) {
   int lhb, n_tok;
   pf_rows(H, lhb, n_tok);
   PagedDmaSrc src;
@@ -393,15 +453,15 @@ hipError_t launch_prefill_paged(const void* q, int q_dtype, int64_t q_tok_stride
   src.P = cache.page_rows;
   const float sl2 = fast_scale(sm_scale);
   dim3 grid((unsigned)((C + n_tok - 1) / n_tok), (unsigned)head_blocks(H));
-  if (q_dtype == LCA_BF16) launch_pf2<bf16_t>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, lhb, src, m, raw_begin, sl2, o_latent, lse);
-  else launch_pf2<float>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, lhb, src, m, raw_begin, sl2, o_latent, lse);
+  if (q_dtype == LCA_BF16) launch_pf2<bf16_t>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, lhb, src, m, raw_begin, sl2, o_latent, lse, sched);
+  else launch_pf2<float>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, lhb, src, m, raw_begin, sl2, o_latent, lse, sched);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill(const void* q, int q_dtype, int64_t q_tok_stride, int64_t chunk_start,
                           int C, int H, const lca_latent_t& reps, int64_t m,
                           const lca_latent_t& raw, int64_t raw_begin, float sm_scale,
-                          void* o_latent, int o_dtype, float* lse, hipStream_t stream) {
+                          void* o_latent, int o_dtype, float* lse, hipStream_t stream, int* sched) {
   const float sl2 = sm_scale * 1.44269504088896340736f;
   int lhb, n_tok;
   pf_rows(H, lhb, n_tok);
@@ -415,8 +475,8 @@ hipError_t launch_prefill(const void* q, int q_dtype, int64_t q_tok_stride, int6
     src.tok = raw.c_tok_stride * 2;
     src.m = m;
     dim3 grid((unsigned)((C + n_tok - 1) / n_tok), (unsigned)head_blocks(H));
-    if (q_dtype == LCA_BF16) launch_pf2<bf16_t>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, lhb, src, m, raw_begin, sl2_fast, o_latent, lse);
-    else launch_pf2<float>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, lhb, src, m, raw_begin, sl2_fast, o_latent, lse);
+    if (q_dtype == LCA_BF16) launch_pf2<bf16_t>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, lhb, src, m, raw_begin, sl2_fast, o_latent, lse, sched);
+    else launch_pf2<float>(o_dtype, grid, stream, q, q_tok_stride, chunk_start, C, H, lhb, src, m, raw_begin, sl2_fast, o_latent, lse, sched);
     return hipGetLastError();
   }
   const Seg rs = to_seg(reps), ws = to_seg(raw);

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert lca.lca_version() == 1003
+    assert lca.lca_version() == 1004
 
 
 def test_plan_matches_golden():
