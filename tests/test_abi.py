@@ -325,6 +325,14 @@ def test_prefill_and_up_proj_argument_errors():
     assert pf(64, 0, 9216, 10, 0, 16, None, 0, ctypes.byref(lat), 0, 1.0, 64, 0, None, None) == lca.LCA_ERR_INVALID_ARG
     assert pf(64, 0, 9216, 10, 4, 24, None, 0, ctypes.byref(lat), 0, 1.0, 64, 0, None, None) == lca.LCA_ERR_UNSUPPORTED
     assert pf(64, 0, 9216, 10, 4, 16, None, 0, ctypes.byref(lat), 0, 1.0, 64, 5, None, None) == lca.LCA_ERR_INVALID_ARG
+    # the scheduled forms: a null or misaligned counter, then the shared checks
+    ps = lib.mla_latent_attn_prefill_chunk_sched
+    assert ps(64, 0, 9216, 10, 4, 16, None, 0, ctypes.byref(lat), 0, 1.0, 64, 0, None, None, None) == lca.LCA_ERR_INVALID_ARG
+    assert ps(64, 0, 9216, 10, 4, 16, None, 0, ctypes.byref(lat), 0, 1.0, 64, 0, None, 68, None) == lca.LCA_ERR_INVALID_ARG
+    assert ps(64, 0, 9216, 10, 4, 24, None, 0, ctypes.byref(lat), 0, 1.0, 64, 0, None, 64, None) == lca.LCA_ERR_UNSUPPORTED
+    pps = lib.mla_latent_attn_prefill_chunk_paged_sched
+    assert pps(64, 0, 9216, 10, 4, 16, None, 0, None, 0, 0, 1.0, 64, 0, None, None, None) == lca.LCA_ERR_INVALID_ARG
+    assert pps(64, 0, 9216, 10, 4, 16, None, 0, None, 0, 0, 1.0, 64, 0, None, 64, None) == lca.LCA_ERR_INVALID_ARG
     up = lib.mla_up_proj
     assert up(64, 0, 0, 16, 64, 0, 64, 0, None) == lca.LCA_OK  # T == 0
     assert up(64, 0, -1, 16, 64, 0, 64, 0, None) == lca.LCA_ERR_INVALID_ARG
