@@ -221,6 +221,19 @@ def test_prefill_128k_sampled_rows():
     wuv = li.w_uv(7, H)
     y = torch.empty((L, H, 128), dtype=torch.bfloat16, device="cuda")
     lca.mla_up_proj(out, dev(wuv), y)  # the whole prefill's up-projection in one call
+    # the scheduled call (persistent workgroups, the benchmark's path) on the
+    # full-size chunks 15 and 31: bitwise equal to the per-block kernel
+    sched = lca.prefill_sched()
+    for chunk in (15, 31):
+        s0 = chunk * C
+        ms = O.prefill_plan(s0, W, G)
+        o_s = torch.empty((C, H, 512), dtype=torch.bfloat16, device="cuda")
+        l_s = torch.empty((C, H), dtype=torch.float32, device="cuda")
+        lca.mla_latent_attn_prefill_chunk(q_t[s0:s0 + C], s0, lca.packed_latent(reps), ms, lca.packed_latent(cache),
+                                          ms * G, 1.0, o_s, l_s, sched=sched)
+        torch.cuda.synchronize()
+        assert torch.equal(o_s, out[s0:s0 + C]) and torch.equal(l_s, lse[s0:s0 + C]), f"scheduled chunk {chunk}"
+    assert sched.tolist() == [0, 0]
     torch.cuda.synchronize()
     r = host(reps)
     ga = host(anchor).astype(np.int64)
