@@ -15,7 +15,10 @@
 // accumulates O for all 512 latent columns (32 MFMA 16x16x32 per tile).
 // Workgroups are issued heaviest (latest tokens) first.
 //  prefill_kernel         packed bf16 rows: direct loads into a 4-slot ring,
-//                         8 wavefronts (two per SIMD) per workgroup.
+//                         8 wavefronts (two per SIMD) per workgroup, one
+//                         query block per workgroup.
+//  prefill_sched_kernel   the same block function in persistent workgroups
+//                         that take blocks from a counter in caller memory.
 //  prefill_kernel_staged  any strides / f32 rows: register-staged tiles,
 //                         4 wavefronts per workgroup.
 #include <cfloat>
