@@ -27,21 +27,22 @@ def _dense_inputs(seed, Hq, m, raw_begin, s0, C):
     return c, kr, rc, rk, q
 
 
-# (seed, Hq, m, raw_begin, s0, C, bf16_out): 263 blocks of 8 tokens (more blocks
+# (seed, Hq, m, raw_begin, s0, C, bf16_out, q_dtype): 263 blocks of 8 tokens (more blocks
 # than persistent workgroups, ragged last block), grouped-query heads, two head
-# groups, fewer blocks than workgroups
-SHAPES = [(0, 16, 300, 4800, 5000, 2100, True), (1, 4, 0, 0, 0, 1000, False),
-          (2, 32, 50, 900, 1000, 700, True), (3, 16, 20, 350, 370, 9, False)]
+# groups, fewer blocks than workgroups, and Hg = 8 with f32 queries
+SHAPES = [(0, 16, 300, 4800, 5000, 2100, True, torch.bfloat16), (1, 4, 0, 0, 0, 1000, False, torch.bfloat16),
+          (2, 32, 50, 900, 1000, 700, True, torch.bfloat16), (3, 16, 20, 350, 370, 9, False, torch.bfloat16),
+          (4, 8, 64, 2000, 2048, 1531, True, torch.float32)]
 
 
-@pytest.mark.parametrize("seed,Hq,m,raw_begin,s0,C,bf16_out", SHAPES)
-def test_prefill_sched_equals_per_block_kernel(seed, Hq, m, raw_begin, s0, C, bf16_out):
+@pytest.mark.parametrize("seed,Hq,m,raw_begin,s0,C,bf16_out,q_dtype", SHAPES)
+def test_prefill_sched_equals_per_block_kernel(seed, Hq, m, raw_begin, s0, C, bf16_out, q_dtype):
     c, kr, rc, rk, q = _dense_inputs(seed, Hq, m, raw_begin, s0, C)
     cache_t = packed(c, kr)[0]
     reps_t = packed(rc[:, :m], rk[:, :m])[0] if m else None
     rl = lca.packed_latent(reps_t) if m else None
     odt = torch.bfloat16 if bf16_out else torch.float32
-    q_t = dev(q)
+    q_t = dev(q, q_dtype)
     ref = torch.empty((C, Hq, 512), dtype=odt, device="cuda")
     ref_lse = torch.empty((C, Hq), dtype=torch.float32, device="cuda")
     lca.mla_latent_attn_prefill_chunk(q_t, s0, rl, m, lca.packed_latent(cache_t), raw_begin, 1.0, ref, ref_lse)
